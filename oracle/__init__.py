@@ -1,0 +1,10 @@
+"""fp64 CPU oracle of the VSA forward pass (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package; the product path never does.
+"""
+from .vsa_oracle import (  # noqa: F401
+    check_grid, perm_index, permute, unpermute, pool, coarse_scores,
+    softmax_rows, coarse_attention, topk_lut, fine_attention,
+    fine_attention_masked, combine, vsa_forward,
+)

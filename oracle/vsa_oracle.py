@@ -1,0 +1,277 @@
+"""Plain, slow fp64 CPU oracle of the Video Sparse Attention (VSA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (no kernels, headers, helpers, tables or constants); the seeded input
+generators are the only thing both sides read.
+
+Pages followed (cited by title and section):
+
+* [VSA-ROCm] "VSA: Accelerating Video Diffusion Inference with Sparse
+  Attention on AMD GPUs" (AMD ROCm blog).
+* [VSA-arXiv] "VSA: Faster Video Diffusion with Trainable Sparse Attention"
+  (arXiv 2505.13389), Abstract.
+
+Every function works in float64 on the exact values it is given (bf16 and
+float32 inputs widen to float64 without rounding).  There is no blocking,
+fusion or reordering beyond what each step states.
+
+Readings taken where the pages leave a step open (each is listed again in
+the design doc):
+
+* R1 the "3D space-filling curve" order is cube-major: cubes in raster order
+  over the cube grid, tokens in raster order inside a cube.
+* R2 grids must divide into whole cubes.
+* R3 coarse attention is softmax(scale * Qc Kc^T) over all cubes with
+  scale = 1/sqrt(d), and O_c = P_c Vc; Top-K ranks the same scores.
+* R4 each token of cube i receives O_c[i] (broadcast).
+* R5 gates are elementwise: out = g_f * O_f + g_c * O_c; absent g_f means 1,
+  absent g_c means 0.
+* R6 Top-K ties go to the lower cube index; LUT rows are stored ascending.
+* R7 a query cube with zero valid blocks gets O_f = 0 and LSE = -inf.
+* R8 a LUT entry listed twice is attended twice (gather semantics).
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+(closed forms, invariants, brute force, library special cases); none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Step 0: problem checks (R2) and the reordering, [VSA-ROCm] §Two-Stage
+# Architecture, "Pre-stage: 3D Space-Filling Curve (SFC) Token Reordering".
+# ---------------------------------------------------------------------------
+
+def check_grid(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> None:
+    for name, n, c in (("T", T, ct), ("H", H, ch), ("W", W, cw)):
+        if n <= 0 or c <= 0:
+            raise ValueError(f"{name}={n}, cube={c}: sizes must be positive")
+        if n % c:
+            raise ValueError(f"{name}={n} is not a multiple of the cube edge {c}")
+
+
+def perm_index(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> np.ndarray:
+    """pi[p] = raster index of the token placed at cube-major position p.
+
+    Cubes are visited in raster order over the (T/ct, H/ch, W/cw) cube grid;
+    inside a cube, tokens are visited in raster order over (ct, ch, cw).  So
+    every run of ct*ch*cw consecutive positions is exactly one cube (R1).
+    Written as explicit loops so it can be read against the definition.
+    """
+    check_grid(T, H, W, ct, ch, cw)
+    order = []
+    for cube_t in range(T // ct):
+        for cube_h in range(H // ch):
+            for cube_w in range(W // cw):
+                for lt in range(ct):
+                    for lh in range(ch):
+                        for lw in range(cw):
+                            t = cube_t * ct + lt
+                            h = cube_h * ch + lh
+                            w = cube_w * cw + lw
+                            order.append((t * H + h) * W + w)
+    return np.asarray(order, dtype=np.int64)
+
+
+def permute(x: np.ndarray, pi: np.ndarray) -> np.ndarray:
+    """x'[..., p, :] = x[..., pi[p], :] (raster -> cube-major)."""
+    return x[..., pi, :]
+
+
+def unpermute(xp: np.ndarray, pi: np.ndarray) -> np.ndarray:
+    """out[..., pi[p], :] = x'[..., p, :] (cube-major -> raster)."""
+    out = np.empty_like(xp)
+    out[..., pi, :] = xp
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: coarse selection, [VSA-ROCm] §Two-Stage Architecture
+# ("Stage 1: Coarse Selection") and §Generating Sparsity Patterns.
+# ---------------------------------------------------------------------------
+
+def pool(xp: np.ndarray, vol: int) -> np.ndarray:
+    """Cube mean-pool of a cube-major tensor: xc[..., c, :] is the mean of
+    rows c*vol .. c*vol+vol-1.  Accumulates in float64."""
+    xp = np.asarray(xp, dtype=np.float64)
+    n = xp.shape[-2]
+    if n % vol:
+        raise ValueError("token count is not a multiple of the cube volume")
+    nc = n // vol
+    out = np.zeros(xp.shape[:-2] + (nc, xp.shape[-1]), dtype=np.float64)
+    for c in range(nc):
+        out[..., c, :] = xp[..., c * vol:(c + 1) * vol, :].sum(axis=-2) / vol
+    return out
+
+
+def coarse_scores(qc: np.ndarray, kc: np.ndarray, scale: float) -> np.ndarray:
+    """S[..., i, j] = scale * <Qc[i], Kc[j]> (the einsum of the LUT pseudo-code
+    with the SDPA scale of §The Attention Bottleneck in Video Diffusion)."""
+    return scale * np.matmul(qc, np.swapaxes(kc, -1, -2))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax with max subtraction, float64."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def coarse_attention(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray, scale: float):
+    """Coarse cube-to-cube attention over all cubes (R3): returns (S, P_c, O_c)."""
+    s = coarse_scores(qc, kc, scale)
+    p = softmax_rows(s)
+    return s, p, np.matmul(p, vc)
+
+
+def topk_lut(s: np.ndarray, k: int):
+    """Per query cube, the k key cubes with the highest scores (R6): order by
+    (score descending, index ascending), keep k, store ascending.
+    Returns (kv_block_idx [..., Nc, k] int32, valid_block_num [..., Nc] int32).
+    """
+    nc = s.shape[-1]
+    if not 1 <= k <= nc:
+        raise ValueError(f"top_k={k} outside [1, {nc}]")
+    flat = s.reshape(-1, nc)
+    lut = np.empty((flat.shape[0], k), dtype=np.int32)
+    for r in range(flat.shape[0]):
+        order = np.argsort(-flat[r], kind="stable")   # ties keep ascending index
+        lut[r] = np.sort(order[:k])
+    lut = lut.reshape(s.shape[:-1] + (k,))
+    valid = np.full(s.shape[:-1], k, dtype=np.int32)
+    return lut, valid
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: fine block-sparse attention, [VSA-ROCm] §Two-Stage Architecture
+# ("Stage 2: Fine Computation"), §Block-Sparse Encoding, §Sparse Traversal;
+# [VSA-arXiv] Abstract.  Softmax as in §The Attention Bottleneck in Video
+# Diffusion: softmax(Q K^T / sqrt(d)) V.
+# ---------------------------------------------------------------------------
+
+def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
+                   kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
+                   scale: float, vol: int):
+    """Token-level attention of every query cube over its listed key cubes.
+
+    qp/kp/vp: cube-major [B, heads, N, d].  For query cube i the key set is
+    the concatenation of token ranges [vol*j, vol*j + vol) for the first
+    valid_block_num[i] entries j of row i of the LUT (R8: in LUT order).
+    Returns (O_f [B, heads, N, d], LSE [B, heads, N]) with
+    LSE = log(sum_q exp(scale * q.k)) in natural-log units (R7 for empty rows).
+    """
+    qp = np.asarray(qp, np.float64)
+    kp = np.asarray(kp, np.float64)
+    vp = np.asarray(vp, np.float64)
+    B, nh, N, d = qp.shape
+    nc = N // vol
+    of = np.zeros((B, nh, N, d), dtype=np.float64)
+    lse = np.full((B, nh, N), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(nh):
+            for i in range(nc):
+                cnt = int(valid_block_num[b, h, i])
+                if cnt == 0:
+                    continue
+                blocks = kv_block_idx[b, h, i, :cnt]
+                rows = np.concatenate([np.arange(j * vol, j * vol + vol) for j in blocks])
+                q = qp[b, h, i * vol:(i + 1) * vol]
+                s = scale * (q @ kp[b, h, rows].T)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                den = e.sum(axis=1, keepdims=True)
+                of[b, h, i * vol:(i + 1) * vol] = (e @ vp[b, h, rows]) / den
+                lse[b, h, i * vol:(i + 1) * vol] = (m + np.log(den))[:, 0]
+    return of, lse
+
+
+def fine_attention_masked(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol):
+    """Brute-force form of the same stage: the full N x N mask in which a
+    selected cube pair (i, j) expands to a vol x vol block of allowed entries
+    (the conceptual mask of [VSA-ROCm] §Two-Stage Architecture), then dense
+    masked softmax.  Only for small grids; LUT rows must not repeat an entry.
+    """
+    qp = np.asarray(qp, np.float64)
+    kp = np.asarray(kp, np.float64)
+    vp = np.asarray(vp, np.float64)
+    B, nh, N, d = qp.shape
+    out = np.zeros_like(qp)
+    for b in range(B):
+        for h in range(nh):
+            allowed = np.zeros((N, N), dtype=bool)
+            for p in range(N):
+                i = p // vol
+                cnt = int(valid_block_num[b, h, i])
+                for j in kv_block_idx[b, h, i, :cnt]:
+                    allowed[p, j * vol:(j + 1) * vol] = True
+            s = scale * (qp[b, h] @ kp[b, h].T)
+            s = np.where(allowed, s, -np.inf)
+            has = allowed.any(axis=1)
+            m = np.where(has, s.max(axis=1), 0.0)
+            e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+            den = e.sum(axis=1)
+            o = e @ vp[b, h]
+            out[b, h] = np.where(has[:, None], o / np.where(has, den, 1.0)[:, None], 0.0)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Output combination, [VSA-ROCm] §Two-Stage Architecture (learnable gates
+# between coarse and fine outputs) and §Algorithmic Design; readings R4, R5.
+# ---------------------------------------------------------------------------
+
+def combine(of: np.ndarray, oc: np.ndarray, vol: int,
+            gate_c: Optional[np.ndarray] = None,
+            gate_f: Optional[np.ndarray] = None) -> np.ndarray:
+    """out'[p] = g_f[p] * O_f[p] + g_c[p] * O_c[p // vol] (cube-major)."""
+    of = np.asarray(of, np.float64)
+    oc_tok = np.repeat(np.asarray(oc, np.float64), vol, axis=-2)
+    out = of if gate_f is None else np.asarray(gate_f, np.float64) * of
+    if gate_c is not None:
+        out = out + np.asarray(gate_c, np.float64) * oc_tok
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The whole forward pass, steps in the pages' order.
+# ---------------------------------------------------------------------------
+
+def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                grid, cube, top_k: int,
+                gate_c: Optional[np.ndarray] = None,
+                gate_f: Optional[np.ndarray] = None,
+                kv_block_idx: Optional[np.ndarray] = None,
+                valid_block_num: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """VSA forward on raster inputs [B, heads, N, d]; returns every
+    intermediate.  If a LUT is given it replaces the Top-K selection (used to
+    score a kernel on exactly the LUT it was handed)."""
+    T, H, W = grid
+    ct, ch, cw = cube
+    vol = ct * ch * cw
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d)
+    pi = perm_index(T, H, W, ct, ch, cw)
+    qp, kp, vp = permute(q, pi), permute(k, pi), permute(v, pi)
+    qc, kc, vc = pool(qp, vol), pool(kp, vol), pool(vp, vol)
+    s, pc, oc = coarse_attention(qc, kc, vc, scale)
+    if kv_block_idx is None:
+        kv_block_idx, valid_block_num = topk_lut(s, top_k)
+    of, lse = fine_attention(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol)
+    gcp = None if gate_c is None else permute(np.asarray(gate_c, np.float64), pi)
+    gfp = None if gate_f is None else permute(np.asarray(gate_f, np.float64), pi)
+    outp = combine(of, oc, vol, gcp, gfp)
+    out = unpermute(outp, pi)
+    return dict(pi=pi, qp=qp, kp=kp, vp=vp, qc=qc, kc=kc, vc=vc, scores=s,
+                p_coarse=pc, oc=oc, kv_block_idx=kv_block_idx,
+                valid_block_num=valid_block_num, o_fine=of, lse=lse,
+                out_cube=outp, out=out, scale=scale)

@@ -1,0 +1,105 @@
+"""Mutation checks: plant a plausible mistake in the oracle (on the CPU, by
+monkeypatching one of its steps) and require that at least one pin fails.
+This shows the pins are tight enough to catch a dropped term, a wrong index,
+a transposed operand or a wrong sign."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import vsa_oracle as vo
+import test_oracle_coarse as tc
+import test_oracle_fine as tf
+import test_oracle_reorder as tr
+from block_sparse_video_major_amd import workloads as wl
+
+
+_ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine")}
+
+
+def _raster_perm(T, H, W, ct, ch, cw):
+    return np.arange(T * H * W, dtype=np.int64)
+
+
+def _pool_wrong_divisor(xp, vol):
+    return _ORIG["pool"](xp, vol) * vol / (vol - 1)
+
+
+def _scores_no_scale(qc, kc, scale):
+    return np.matmul(qc, np.swapaxes(kc, -1, -2))
+
+
+def _softmax_wrong_axis(s):
+    m = s.max(axis=-2, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _topk_smallest(s, k):
+    return _ORIG["topk_lut"](-s, k)
+
+
+def _fine_no_scale(qp, kp, vp, lut, valid, scale, vol):
+    return _ORIG["fine_attention"](qp, kp, vp, lut, valid, 1.0, vol)
+
+
+def _fine_q_for_k(qp, kp, vp, lut, valid, scale, vol):
+    return _ORIG["fine_attention"](qp, qp, vp, lut, valid, scale, vol)
+
+
+def _fine_shifted_block(qp, kp, vp, lut, valid, scale, vol):
+    nc = qp.shape[-2] // vol
+    return _ORIG["fine_attention"](qp, kp, vp, (lut + 1) % nc, valid, scale, vol)
+
+
+def _combine_swapped(of, oc, vol, gate_c=None, gate_f=None):
+    return _ORIG["combine"](of, oc, vol, gate_f, gate_c)
+
+
+def _pins():
+    """The pin checks, called directly (each raises AssertionError on failure)."""
+    yield lambda: tr.test_each_block_is_one_cube_in_raster_cube_order((4, 8, 8), (4, 4, 4))
+    yield lambda: tr.test_hand_worked_example()
+    yield lambda: tr.test_pool_one_hot_rows()
+    yield lambda: tr.test_pool_mass_conservation_and_constants()
+    yield lambda: tc.test_coarse_softmax_matches_scipy_and_sums_to_one()
+    yield lambda: tc.test_coarse_output_special_cases()
+    yield lambda: tc.test_topk_characterisation()
+    yield lambda: tc.test_topk_subset_enumeration_tiny()
+    yield lambda: tf.test_all_cubes_selected_is_dense_sdpa(wl.TINY)
+    yield lambda: tf.test_gather_equals_materialised_mask(wl.TINY)
+    yield lambda: tf.test_single_block_is_attention_inside_one_cube()
+    yield lambda: tf.test_gates_select_fine_or_coarse()
+
+
+MUTATIONS = {
+    "raster order instead of cube-major": ("perm_index", _raster_perm),
+    "pool divides by vol-1": ("pool", _pool_wrong_divisor),
+    "coarse scores without 1/sqrt(d)": ("coarse_scores", _scores_no_scale),
+    "coarse softmax over the query axis": ("softmax_rows", _softmax_wrong_axis),
+    "Top-K keeps the smallest scores": ("topk_lut", _topk_smallest),
+    "fine softmax without 1/sqrt(d)": ("fine_attention", _fine_no_scale),
+    "fine uses Q where K belongs": ("fine_attention", _fine_q_for_k),
+    "fine reads the neighbouring cube": ("fine_attention", _fine_shifted_block),
+    "gates swapped": ("combine", _combine_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(vo, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = 0
+    for pin in _pins():
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in _pins():
+        pin()
