@@ -1,0 +1,239 @@
+"""Benchmark of the VSA forward pass on one MI355X.
+
+One step = one pass of the whole forward path over one batch of synthetic
+input resident in HBM: reorder Q, K, V into cubes, pool them, coarse
+attention + Top-K, fine block-sparse attention (with the coarse output
+combined through the gates' default), reorder back.  The default workload is
+the 32,768-token Wan2.1-scale layer (16x32x64 grid, 4x4x4 cubes, 12 heads,
+d=128, bf16, Top-K 154 of 512 cubes = 70% sparsity).
+
+Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step, counting
+only the attention FLOPs of selected (query cube, key cube) pairs
+(4 * heads * N * 64 * K * d).  `roofline` reports the fine kernel against the
+bf16 MFMA peak, with its launch durations measured by HIP events on the stream
+the kernels run on.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--top-k K]
+                       [--no-cpu-baseline] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, published
+MI355X_HBM_PEAK_GBPS = 8000.0        # HBM3E, published
+FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_major_amd", "csrc", "sparse_attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_wan_traffic.md")
+
+
+def _fine_source_hash() -> str:
+    with open(FINE_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _measured_traffic():
+    """HBM bytes per fine-kernel launch from the committed rocprofv3 PMC
+    summary, only if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_b or not m_h or m_h.group(1) != _fine_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(seconds_budget: float = 20.0):
+    """Time the fp64 oracle on a bounded sample of the Wan workload: the whole
+    forward (reorder, pool, coarse, Top-K, fine, combine, reorder back) for
+    one head, extended head by head while the budget allows."""
+    import numpy as np
+    import oracle
+    from block_sparse_video_major_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    w = wl.WAN
+    heads_done, t_total, flops = 0, 0.0, 0
+    for h in range(w.heads):
+        x = wl.make_inputs(w, heads=[h], workers=1)
+        x64 = {n: wl.as_float64(a) for n, a in x.items()}
+        t0 = time.perf_counter()
+        oracle.vsa_forward(x64["q"], x64["k"], x64["v"], (w.T, w.H, w.W), w.cube, w.top_k)
+        t_total += time.perf_counter() - t0
+        heads_done += 1
+        flops += 4 * w.n_tokens * w.cube_volume * w.top_k * w.head_dim
+        if t_total * (heads_done + 1) / heads_done > seconds_budget:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads_done} of {w.heads} heads of the 32,768-token workload, full forward in fp64 "
+                      f"({t_total:.1f} s; same FLOP accounting as value)"}
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--top-k", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import block_sparse_video_major_amd as vsa
+    from block_sparse_video_major_amd import _lib as L
+    from block_sparse_video_major_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+    L.load()
+
+    w = wl.WAN if args.top_k is None else wl.WAN.with_top_k(args.top_k)
+    p = vsa.Problem(w.batch, w.heads, w.T, w.H, w.W, *w.cube, w.head_dim)
+    x = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    del x
+    f = vsa.VsaForward(p, w.top_k, dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.Stream(device=dev)
+    B = L.VSA_BF16
+
+    def step(ev0=None, ev1=None):
+        L.vsa_permute(p, B, q, f.qp, stream)
+        L.vsa_permute(p, B, k, f.kp, stream)
+        L.vsa_permute(p, B, v, f.vp, stream)
+        L.vsa_pool(p, B, f.qp, f.qc, stream)
+        L.vsa_pool(p, B, f.kp, f.kc, stream)
+        L.vsa_pool(p, B, f.vp, f.vc, stream)
+        L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+        L.vsa_unpermute(p, B, f.out_cube, out, stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(*ev[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_total = t_start.elapsed_time(t_end)
+        fine_ms = [a.elapsed_time(b) for a, b in ev]
+
+        # per-stage breakdown (separate, untimed pass)
+        names = ["permute_qkv", "pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute"]
+        reps = max(3, min(10, args.steps))
+        acc = {n: 0.0 for n in names}
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            e[0].record(stream)
+            for t, dst in ((q, f.qp), (k, f.kp), (v, f.vp)):
+                L.vsa_permute(p, B, t, dst, stream)
+            e[1].record(stream)
+            for src, dst in ((f.qp, f.qc), (f.kp, f.kc), (f.vp, f.vc)):
+                L.vsa_pool(p, B, src, dst, stream)
+            e[2].record(stream)
+            L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
+            e[3].record(stream)
+            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
+            e[4].record(stream)
+            L.vsa_unpermute(p, B, f.out_cube, out, stream)
+            e[5].record(stream)
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                acc[n] += e[i].elapsed_time(e[i + 1]) / reps
+    torch.cuda.synchronize()
+
+    flops = w.selected_flops()
+    ms_step = ms_total / args.steps
+    fine_avg = float(np.mean(fine_ms))
+    elem = w.batch * w.heads * w.n_tokens * w.head_dim
+    permute_bytes = 3 * 2 * elem * 2
+    pool_bytes = 3 * (elem * 2 + w.batch * w.heads * w.n_cubes * w.head_dim * 4)
+    unpermute_bytes = 2 * elem * 2
+    achieved = flops / (fine_avg * 1e-3) / 1e12
+    rec = {
+        "metric": "VSA fwd ms/call + effective TFLOP/s (% bf16 peak), 32K tokens @70% sparsity",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"wan2.1-scale layer: grid 16x32x64 (32768 tokens), cube 4x4x4, 12 heads, "
+                               f"d=128, Top-K {w.top_k} of 512 cubes ({w.sparsity:.1%} sparsity)",
+                   "batch": w.batch, "heads": w.heads, "tokens": w.n_tokens, "head_dim": w.head_dim,
+                   "top_k": w.top_k, "n_cubes": w.n_cubes},
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "fine_ms_per_call": round(fine_avg, 4),
+        "fine_tflops": round(achieved, 2),
+        "fine_pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
+        "stages_ms": {n: round(t, 4) for n, t in acc.items()},
+        "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
+                        "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
+                        "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
+                     "traffic": _measured_traffic()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

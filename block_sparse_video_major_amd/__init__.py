@@ -1,0 +1,19 @@
+"""MI355X-native Video Sparse Attention (VSA) forward pass.
+
+The compute lives in libvsa.so (hand-written HIP kernels for gfx950, C ABI in
+include/vsa.h); this package is its Python binding plus the seeded synthetic
+workloads.  Importing the package does not load the library: the first call
+of a binding function does, and raises if the library is missing.
+"""
+from ._lib import (  # noqa: F401
+    Problem, VsaError, VSA_BF16, VSA_F32, load,
+    vsa_permute, vsa_unpermute, vsa_pool, vsa_coarse_topk, vsa_sparse_attn_fwd,
+    vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
+)
+from .pipeline import VsaForward, vsa_forward  # noqa: F401
+
+__all__ = [
+    "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
+    "vsa_permute", "vsa_unpermute", "vsa_pool", "vsa_coarse_topk", "vsa_sparse_attn_fwd",
+    "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
+]

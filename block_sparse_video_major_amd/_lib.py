@@ -1,0 +1,249 @@
+"""ctypes binding of libvsa.so, with the same entry-point names as the C ABI.
+
+Argument marshalling only: the functions check that each torch tensor has the
+shape, dtype, device and layout the C ABI assumes (the C side cannot see
+buffer sizes, so this is what keeps every launch in bounds), then pass raw
+device pointers and the current HIP stream.  All arithmetic runs in the HIP
+kernels.  There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+
+VSA_BF16 = 0
+VSA_F32 = 1
+
+VSA_OK = 0
+VSA_ERR_NULL = -1
+VSA_ERR_SHAPE = -2
+VSA_ERR_TOPK = -3
+VSA_ERR_UNSUPPORTED = -4
+VSA_ERR_HIP = -5
+VSA_ERR_LUT = -6
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({vsa_status_str(status)})")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim")]
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    """Token grid T x H x W, cube (ct, ch, cw), heads and head size."""
+    batch: int
+    heads: int
+    T: int
+    H: int
+    W: int
+    ct: int = 4
+    ch: int = 4
+    cw: int = 4
+    head_dim: int = 128
+
+    @property
+    def n_tokens(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def cube_volume(self) -> int:
+        return self.ct * self.ch * self.cw
+
+    @property
+    def n_cubes(self) -> int:
+        return self.n_tokens // self.cube_volume
+
+    def c_struct(self) -> _Problem:
+        return _Problem(self.batch, self.heads, self.T, self.H, self.W,
+                        self.ct, self.ch, self.cw, self.head_dim)
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libvsa.so (built by block_sparse_video_major_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_video_major_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_Problem)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    sigs = {
+        "vsa_permute": [P, i32, vp, vp, vp],
+        "vsa_unpermute": [P, i32, vp, vp, vp],
+        "vsa_pool": [P, i32, vp, vp, vp],
+        "vsa_coarse_topk": [P, i32, vp, vp, vp, vp, vp, vp, vp],
+        "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
+        "vsa_check_lut": [P, vp, vp, i32, vp, vp],
+        "vsa_perm_index": [P, vp],
+        "vsa_status_str": [ctypes.c_int],
+        "vsa_abi_version": [],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "vsa_status_str" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def vsa_status_str(status: int) -> str:
+    return load().vsa_status_str(int(status)).decode()
+
+
+def vsa_abi_version() -> int:
+    return int(load().vsa_abi_version())
+
+
+# ---------------------------------------------------------------- helpers
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(status: int, where: str) -> None:
+    if status != VSA_OK:
+        raise VsaError(status, where)
+
+
+def _token_dtype(dtype: int):
+    if dtype == VSA_BF16:
+        return torch.bfloat16
+    if dtype == VSA_F32:
+        return torch.float32
+    raise ValueError(f"dtype code {dtype} is not VSA_BF16 or VSA_F32")
+
+
+def _tok_shape(p: Problem):
+    return (p.batch, p.heads, p.n_tokens, p.head_dim)
+
+
+def _cube_shape(p: Problem):
+    return (p.batch, p.heads, p.n_cubes, p.head_dim)
+
+
+# ---------------------------------------------------------------- entry points
+
+def vsa_perm_index(p: Problem) -> torch.Tensor:
+    """pi[p] = raster index of cube-major position p (host int32 tensor)."""
+    out = torch.empty(p.n_tokens, dtype=torch.int32)
+    _check(load().vsa_perm_index(ctypes.byref(p.c_struct()), out.data_ptr()), "vsa_perm_index")
+    return out
+
+
+def vsa_permute(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: torch.Tensor, stream=None) -> None:
+    td = _token_dtype(dtype)
+    _need(x_raster, "x_raster", _tok_shape(p), td)
+    _need(x_cube, "x_cube", _tok_shape(p), td, x_raster.device)
+    _check(load().vsa_permute(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube),
+                              _stream(stream, x_raster.device)), "vsa_permute")
+
+
+def vsa_unpermute(p: Problem, dtype: int, x_cube: torch.Tensor, x_raster: torch.Tensor, stream=None) -> None:
+    td = _token_dtype(dtype)
+    _need(x_cube, "x_cube", _tok_shape(p), td)
+    _need(x_raster, "x_raster", _tok_shape(p), td, x_cube.device)
+    _check(load().vsa_unpermute(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(x_raster),
+                                _stream(stream, x_cube.device)), "vsa_unpermute")
+
+
+def vsa_pool(p: Problem, dtype: int, x_cube: torch.Tensor, xc: torch.Tensor, stream=None) -> None:
+    _need(x_cube, "x_cube", _tok_shape(p), _token_dtype(dtype))
+    _need(xc, "xc", _cube_shape(p), torch.float32, x_cube.device)
+    _check(load().vsa_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(xc),
+                           _stream(stream, x_cube.device)), "vsa_pool")
+
+
+def vsa_coarse_topk(p: Problem, top_k: int, qc: torch.Tensor, kc: torch.Tensor, vc: Optional[torch.Tensor],
+                    kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor, oc: Optional[torch.Tensor],
+                    stream=None) -> None:
+    dev = qc.device
+    _need(qc, "qc", _cube_shape(p), torch.float32)
+    _need(kc, "kc", _cube_shape(p), torch.float32, dev)
+    if vc is not None:
+        _need(vc, "vc", _cube_shape(p), torch.float32, dev)
+    if oc is not None:
+        _need(oc, "oc", _cube_shape(p), torch.float32, dev)
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, top_k), torch.int32, dev)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    _check(load().vsa_coarse_topk(ctypes.byref(p.c_struct()), int(top_k), _ptr(qc), _ptr(kc), _ptr(vc),
+                                  _ptr(kv_block_idx), _ptr(valid_block_num), _ptr(oc),
+                                  _stream(stream, dev)), "vsa_coarse_topk")
+
+
+def vsa_sparse_attn_fwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                        out: torch.Tensor, oc: Optional[torch.Tensor] = None,
+                        gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    dev = q.device
+    ts = _tok_shape(p)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, name, ts, torch.bfloat16, dev)
+    if kv_block_idx.dim() != 4:
+        raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
+    max_kv = kv_block_idx.shape[-1]
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    if oc is not None:
+        _need(oc, "oc", _cube_shape(p), torch.float32, dev)
+    for name, t in (("gate_c", gate_c), ("gate_f", gate_f)):
+        if t is not None:
+            _need(t, name, ts, torch.bfloat16, dev)
+    if lse is not None:
+        _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
+    _check(load().vsa_sparse_attn_fwd(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
+                                      _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
+                                      _stream(stream, dev)), "vsa_sparse_attn_fwd")
+
+
+def vsa_check_lut(p: Problem, kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                  bad_rows: torch.Tensor, stream=None) -> None:
+    dev = kv_block_idx.device
+    if kv_block_idx.dim() != 4:
+        raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
+    max_kv = kv_block_idx.shape[-1]
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    _need(bad_rows, "bad_rows", (1,), torch.int32, dev)
+    _check(load().vsa_check_lut(ctypes.byref(p.c_struct()), _ptr(kv_block_idx), _ptr(valid_block_num),
+                                int(max_kv), _ptr(bad_rows), _stream(stream, dev)), "vsa_check_lut")

@@ -1,0 +1,147 @@
+// Host entry points of libvsa.so (the C ABI declared in include/vsa.h).
+//
+// Every entry point validates its arguments on the host and returns before
+// anything is queued if they are invalid; otherwise it launches its kernels on
+// the caller's stream and returns without synchronising.  No entry point
+// allocates or frees memory.
+#include <limits.h>
+#include <math.h>
+
+#include "vsa_internal.h"
+
+namespace {
+
+using vsa::Geom;
+
+int check_problem(const vsa_problem* p) {
+  if (p == nullptr) return VSA_ERR_NULL;
+  if (p->batch <= 0 || p->heads <= 0 || p->T <= 0 || p->H <= 0 || p->W <= 0 || p->ct <= 0 ||
+      p->ch <= 0 || p->cw <= 0 || p->head_dim <= 0)
+    return VSA_ERR_SHAPE;
+  if (p->T % p->ct || p->H % p->ch || p->W % p->cw) return VSA_ERR_SHAPE;
+  const int64_t n = (int64_t)p->T * p->H * p->W;
+  const int64_t vol = (int64_t)p->ct * p->ch * p->cw;
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  if (n > INT32_MAX || vol > INT32_MAX || bh > INT32_MAX) return VSA_ERR_SHAPE;
+  // every element index must fit comfortably in int64 and every launch grid in 2^31 blocks
+  if (bh * n > ((int64_t)1 << 40)) return VSA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
+int check_dtype(int32_t dtype) {
+  return (dtype == VSA_BF16 || dtype == VSA_F32) ? VSA_OK : VSA_ERR_UNSUPPORTED;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int vsa_abi_version(void) { return (1 << 16) | 0; }
+
+const char* vsa_status_str(int status) {
+  switch (status) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_NULL: return "required pointer is NULL";
+    case VSA_ERR_SHAPE: return "invalid shape (non-positive size, grid not a multiple of the cube, or too large)";
+    case VSA_ERR_TOPK: return "top_k / max_kv_blocks outside [1, Nc]";
+    case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume or cube count";
+    case VSA_ERR_HIP: return "HIP runtime error at launch";
+    case VSA_ERR_LUT: return "invalid LUT";
+    default: return "unknown status";
+  }
+}
+
+int vsa_perm_index(const vsa_problem* p, int32_t* perm_host) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (perm_host == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  int64_t pos = 0;
+  for (int ct_i = 0; ct_i < g.gT; ++ct_i)
+    for (int ch_i = 0; ch_i < g.gH; ++ch_i)
+      for (int cw_i = 0; cw_i < g.gW; ++cw_i)
+        for (int lt = 0; lt < g.ct; ++lt)
+          for (int lh = 0; lh < g.ch; ++lh)
+            for (int lw = 0; lw < g.cw; ++lw) {
+              const int64_t t = (int64_t)ct_i * g.ct + lt, h = (int64_t)ch_i * g.ch + lh,
+                            w = (int64_t)cw_i * g.cw + lw;
+              perm_host[pos++] = (int32_t)((t * g.H + h) * g.W + w);
+            }
+  return VSA_OK;
+}
+
+int vsa_permute(const vsa_problem* p, int32_t dtype, const void* x_raster, void* x_cube, void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_raster == nullptr || x_cube == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_reorder(g, dtype == VSA_BF16 ? 2 : 4, x_raster, x_cube, true,
+                                        (hipStream_t)stream));
+}
+
+int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube, void* x_raster, void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_raster == nullptr || x_cube == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_reorder(g, dtype == VSA_BF16 ? 2 : 4, x_cube, x_raster, false,
+                                        (hipStream_t)stream));
+}
+
+int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube, float* xc, void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_pool(g, dtype, x_cube, xc, (hipStream_t)stream));
+}
+
+int vsa_coarse_topk(const vsa_problem* p, int32_t top_k, const float* qc, const float* kc, const float* vc,
+                    int32_t* kv_block_idx, int32_t* valid_block_num, float* oc, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (qc == nullptr || kc == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr)
+    return VSA_ERR_NULL;
+  if (oc != nullptr && vc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (g.Nc > vsa::kMaxCoarseCubes) return VSA_ERR_UNSUPPORTED;
+  if (top_k < 1 || top_k > g.Nc) return VSA_ERR_TOPK;
+  return hip_status(vsa::launch_coarse_topk(g, top_k, qc, kc, vc, kv_block_idx, valid_block_num, oc,
+                                            (hipStream_t)stream));
+}
+
+int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
+                        const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
+                        void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
+      out == nullptr)
+    return VSA_ERR_NULL;
+  if (gate_c != nullptr && oc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
+  if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  return hip_status(vsa::launch_sparse_attn_fwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc,
+                                                gate_c, gate_f, out, lse, (hipStream_t)stream));
+}
+
+int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                  int32_t max_kv_blocks, int32_t* bad_rows, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (kv_block_idx == nullptr || valid_block_num == nullptr || bad_rows == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  return hip_status(vsa::launch_check_lut(g, kv_block_idx, valid_block_num, max_kv_blocks, bad_rows,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

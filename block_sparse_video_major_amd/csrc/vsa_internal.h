@@ -1,0 +1,65 @@
+// Internal declarations shared by the host entry points and the kernel
+// launchers of libvsa.so.  Not part of the public ABI (include/vsa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vsa.h"
+
+namespace vsa {
+
+// Token grid and cube geometry with the derived sizes every kernel needs.
+struct Geom {
+  int32_t T, H, W;        // token grid
+  int32_t ct, ch, cw;     // cube edges
+  int32_t gT, gH, gW;     // cube grid = grid / cube
+  int32_t vol;            // ct * ch * cw
+  int64_t N;              // tokens per (batch, head)
+  int64_t Nc;             // cubes per (batch, head)
+  int64_t BH;             // batch * heads
+  int32_t D;              // head_dim
+};
+
+inline Geom make_geom(const vsa_problem& p) {
+  Geom g;
+  g.T = p.T; g.H = p.H; g.W = p.W;
+  g.ct = p.ct; g.ch = p.ch; g.cw = p.cw;
+  g.gT = p.T / p.ct; g.gH = p.H / p.ch; g.gW = p.W / p.cw;
+  g.vol = p.ct * p.ch * p.cw;
+  g.N = (int64_t)p.T * p.H * p.W;
+  g.Nc = g.N / g.vol;
+  g.BH = (int64_t)p.batch * p.heads;
+  g.D = p.head_dim;
+  return g;
+}
+
+// Launchers (each returns the hipGetLastError() of its launch).
+hipError_t launch_reorder(const Geom& g, int elem_bytes, const void* src, void* dst,
+                          bool to_cube, hipStream_t s);
+hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, hipStream_t s);
+hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
+                              const float* vc, int32_t* lut, int32_t* valid, float* oc,
+                              hipStream_t s);
+hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                                  const int32_t* lut, const int32_t* valid, int max_kv,
+                                  const float* oc, const void* gate_c, const void* gate_f,
+                                  void* out, float* lse, hipStream_t s);
+hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* valid, int max_kv,
+                            int32_t* bad_rows, hipStream_t s);
+
+// Largest number of cubes per (batch, head) the coarse stage handles.
+constexpr int64_t kMaxCoarseCubes = 4096;
+
+// Workgroups are handed to the 8 XCDs of an MI355X round-robin by id.  This
+// maps a hardware id to a logical id so that each XCD receives one contiguous
+// range of logical ids (neighbouring query cubes share key/value cubes, and
+// each XCD has its own L2).  Bijective on [0, total).
+__device__ __forceinline__ int64_t xcd_remap(int64_t hw_id, int64_t total) {
+  constexpr int kXcd = 8;
+  const int64_t q = total / kXcd, r = total % kXcd;
+  const int64_t x = hw_id % kXcd, idx = hw_id / kXcd;
+  return (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+}
+
+}  // namespace vsa

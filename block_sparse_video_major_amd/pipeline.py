@@ -1,0 +1,82 @@
+"""The whole VSA forward pass as a sequence of C-ABI calls.
+
+Order of the steps ("VSA: Accelerating Video Diffusion Inference with Sparse
+Attention on AMD GPUs", §Two-Stage Architecture): reorder tokens into cubes,
+mean-pool the cubes, coarse cube attention with Top-K selection, fine
+block-sparse attention over the selected cubes combined with the coarse
+output through the gates, and reorder back.  This module only allocates the
+intermediate buffers (through torch) and calls the library; every step runs
+in the HIP kernels of libvsa.so.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import Problem
+
+
+class VsaForward:
+    """Preallocated buffers for one problem size; call() runs one forward pass."""
+
+    def __init__(self, p: Problem, top_k: int, device="cuda", with_gates: bool = False,
+                 with_lse: bool = False):
+        if not 1 <= top_k <= p.n_cubes:
+            raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
+        self.p, self.top_k = p, top_k
+        ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
+        cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
+        bf, f32 = torch.bfloat16, torch.float32
+        self.qp, self.kp, self.vp = (torch.empty(ts, dtype=bf, device=device) for _ in range(3))
+        self.qc, self.kc, self.vc, self.oc = (torch.empty(cs, dtype=f32, device=device) for _ in range(4))
+        self.lut = torch.empty((p.batch, p.heads, p.n_cubes, top_k), dtype=torch.int32, device=device)
+        self.valid = torch.empty((p.batch, p.heads, p.n_cubes), dtype=torch.int32, device=device)
+        self.out_cube = torch.empty(ts, dtype=bf, device=device)
+        self.gc = torch.empty(ts, dtype=bf, device=device) if with_gates else None
+        self.gf = torch.empty(ts, dtype=bf, device=device) if with_gates else None
+        self.lse = torch.empty((p.batch, p.heads, p.n_tokens), dtype=f32, device=device) if with_lse else None
+
+    def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                 gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+        p, B = self.p, L.VSA_BF16
+        L.vsa_permute(p, B, q, self.qp, stream)
+        L.vsa_permute(p, B, k, self.kp, stream)
+        L.vsa_permute(p, B, v, self.vp, stream)
+        gc = gf = None
+        if gate_c is not None:
+            if self.gc is None:
+                raise ValueError("built without gate buffers (with_gates=False)")
+            L.vsa_permute(p, B, gate_c, self.gc, stream)
+            gc = self.gc
+        if gate_f is not None:
+            if self.gf is None:
+                raise ValueError("built without gate buffers (with_gates=False)")
+            L.vsa_permute(p, B, gate_f, self.gf, stream)
+            gf = self.gf
+        L.vsa_pool(p, B, self.qp, self.qc, stream)
+        L.vsa_pool(p, B, self.kp, self.kc, stream)
+        L.vsa_pool(p, B, self.vp, self.vc, stream)
+        L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
+        L.vsa_sparse_attn_fwd(p, self.qp, self.kp, self.vp, self.lut, self.valid, self.out_cube,
+                              oc=self.oc, gate_c=gc, gate_f=gf, lse=self.lse, stream=stream)
+        L.vsa_unpermute(p, B, self.out_cube, out, stream)
+        return out
+
+    def intermediates(self) -> Dict[str, torch.Tensor]:
+        d = dict(qp=self.qp, kp=self.kp, vp=self.vp, qc=self.qc, kc=self.kc, vc=self.vc,
+                 oc=self.oc, kv_block_idx=self.lut, valid_block_num=self.valid, out_cube=self.out_cube)
+        if self.lse is not None:
+            d["lse"] = self.lse
+        return d
+
+
+def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, top_k: int,
+                gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """One VSA forward pass on raster bf16 inputs [B, heads, N, d]."""
+    f = VsaForward(p, top_k, q.device, with_gates=gate_c is not None or gate_f is not None)
+    out = torch.empty_like(q)
+    return f(q, k, v, out, gate_c, gate_f, stream)

@@ -31,7 +31,9 @@ token index n = (t*H + h)*W + w.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, Optional, Sequence
 
 import numpy as np
@@ -150,12 +152,15 @@ def draw_head(w: Workload, b: int, h: int, with_gates: bool = False) -> Dict[str
 
 def make_inputs(w: Workload, with_gates: bool = False,
                 heads: Optional[Sequence[int]] = None,
-                batches: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                batches: Optional[Sequence[int]] = None,
+                workers: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Inputs in raster layout [B', heads', N, d].
 
     For bf16 workloads the arrays are uint16 bf16 bits; for f32 workloads they
     are float32.  ``heads`` / ``batches`` select a subset (defaults: all); the
-    values of a selected head do not depend on which others are selected.
+    values of a selected head do not depend on which others are selected, nor
+    on ``workers`` (heads are drawn in parallel threads, each from its own
+    seeded generator).
     """
     heads = list(range(w.heads)) if heads is None else list(heads)
     batches = list(range(w.batch)) if batches is None else list(batches)
@@ -163,11 +168,22 @@ def make_inputs(w: Workload, with_gates: bool = False,
     N, d = w.n_tokens, w.head_dim
     dt = np.uint16 if w.dtype == "bf16" else np.float32
     res = {n: np.empty((len(batches), len(heads), N, d), dtype=dt) for n in names}
-    for bi, b in enumerate(batches):
-        for hi, h in enumerate(heads):
-            x = draw_head(w, b, h, with_gates)
-            for n in names:
-                res[n][bi, hi] = f32_to_bf16_bits(x[n]) if w.dtype == "bf16" else x[n]
+
+    def one(job):
+        bi, b, hi, h = job
+        x = draw_head(w, b, h, with_gates)
+        for n in names:
+            res[n][bi, hi] = f32_to_bf16_bits(x[n]) if w.dtype == "bf16" else x[n]
+
+    jobs = [(bi, b, hi, h) for bi, b in enumerate(batches) for hi, h in enumerate(heads)]
+    if workers is None:
+        workers = min(len(jobs), 8, os.cpu_count() or 1)
+    if workers <= 1:
+        for j in jobs:
+            one(j)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, jobs))
     return res
 
 

@@ -1,0 +1,163 @@
+/*
+ * vsa.h -- C ABI of libvsa.so: the forward pass of Video Sparse Attention
+ * (VSA) on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [VSA-ROCm]  "VSA: Accelerating Video Diffusion Inference with Sparse
+ *               Attention on AMD GPUs" (AMD ROCm blog).
+ *   [VSA-arXiv] "VSA: Faster Video Diffusion with Trainable Sparse Attention"
+ *               (arXiv 2505.13389), Abstract.
+ *
+ * The forward pass, per attention layer and per (batch, head):
+ *   1. vsa_permute      raster (t,h,w) tokens -> cube-major order
+ *   2. vsa_pool         cube mean-pool -> Qc, Kc, Vc
+ *   3. vsa_coarse_topk  coarse cube attention O_c + Top-K key cubes (LUT)
+ *   4. vsa_sparse_attn_fwd  fine attention over the listed cubes, combined
+ *                       with O_c through the gates
+ *   5. vsa_unpermute    cube-major -> raster order
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, caller-allocated device buffers.  Token
+ *   tensors are [batch, heads, N, head_dim] with N = T*H*W; cube tensors are
+ *   [batch, heads, Nc, head_dim] with Nc = N / (ct*ch*cw).  Raster token index
+ *   is (t*H + h)*W + w.  Cube-major position p = c*vol + l, where cube c runs
+ *   in raster order over the (T/ct, H/ch, W/cw) cube grid and l in raster
+ *   order over (ct, ch, cw) inside the cube.
+ * - The library never allocates, frees or synchronises.  Every call only
+ *   queues work on `stream` (a hipStream_t; NULL is the default stream) and
+ *   returns.  Calls are stateless and re-entrant; two calls may run
+ *   concurrently on different streams if their outputs do not overlap.
+ * - Arguments are checked on the host before anything is queued.  On an
+ *   error nothing is launched and no output is touched.  The library cannot
+ *   see buffer sizes: the caller guarantees each buffer holds the stated
+ *   number of elements.  A launch failure returns VSA_ERR_HIP; faults inside
+ *   a kernel surface at the caller's next synchronisation.
+ * - The softmax scale is fixed at 1/sqrt(head_dim), as in the scaled
+ *   dot-product attention of [VSA-ROCm] §The Attention Bottleneck in Video
+ *   Diffusion.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem statement: token grid, cube edge lengths, heads and head size
+ * ([VSA-ROCm] §Two-Stage Architecture, Stage 1, and §Appendix - Tensor
+ * Specifications). */
+typedef struct vsa_problem {
+  int32_t batch;
+  int32_t heads;
+  int32_t T, H, W;      /* token grid */
+  int32_t ct, ch, cw;   /* cube edges; each grid edge must be a multiple */
+  int32_t head_dim;     /* 64 or 128 */
+} vsa_problem;
+
+/* Element type of token tensors. */
+enum { VSA_BF16 = 0, VSA_F32 = 1 };
+
+/* Status codes. */
+enum {
+  VSA_OK = 0,
+  VSA_ERR_NULL = -1,        /* a required pointer is NULL (or gate_c without oc) */
+  VSA_ERR_SHAPE = -2,       /* a size <= 0, grid not a multiple of the cube, or sizes overflow */
+  VSA_ERR_TOPK = -3,        /* top_k / max_kv_blocks outside [1, Nc] */
+  VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume this build does not handle */
+  VSA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+  VSA_ERR_LUT = -6          /* reserved for LUT validation results */
+};
+
+/* Reorder raster tokens into cube-major order:
+ *   x_cube[b, h, p, :] = x_raster[b, h, pi(p), :]
+ * where pi(p) is the raster index of cube-major position p.  This is the
+ * pre-stage token reordering of [VSA-ROCm] §Two-Stage Architecture: every run
+ * of vol = ct*ch*cw consecutive positions is one spatio-temporal cube.
+ * x_raster, x_cube: [batch, heads, N, head_dim] of `dtype` (VSA_BF16 or
+ * VSA_F32).  Bit copy: the result is exact.  Buffers must not overlap. */
+int vsa_permute(const vsa_problem* p, int32_t dtype, const void* x_raster,
+                void* x_cube, void* stream);
+
+/* Inverse of vsa_permute: x_raster[b, h, pi(p), :] = x_cube[b, h, p, :].
+ * Hands the output back in the model's token order.  Same layouts and rules
+ * as vsa_permute. */
+int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube,
+                  void* x_raster, void* stream);
+
+/* Cube mean-pool ([VSA-ROCm] §Two-Stage Architecture, Stage 1):
+ *   xc[b, h, c, :] = (1/vol) * sum_{l < vol} x_cube[b, h, c*vol + l, :]
+ * x_cube: [batch, heads, N, head_dim] of `dtype`, cube-major.
+ * xc:     [batch, heads, Nc, head_dim] float32, accumulated in float32 in a
+ *         fixed order (deterministic). */
+int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube,
+             float* xc, void* stream);
+
+/* Coarse stage ([VSA-ROCm] §Two-Stage Architecture, Stage 1, and
+ * §Generating Sparsity Patterns; [VSA-arXiv] Abstract).  Per (b, h) and query
+ * cube i, with S[i, j] = <qc[i], kc[j]> / sqrt(head_dim) over all Nc cubes:
+ *   kv_block_idx[b, h, i, 0:top_k] = the top_k cubes j with the largest
+ *       S[i, j], ties to the lower j, stored in ascending j;
+ *   valid_block_num[b, h, i] = top_k;
+ *   oc[b, h, i, :] = sum_j softmax_j(S[i, :]) * vc[j, :]   (if oc != NULL).
+ * qc, kc, vc, oc: [batch, heads, Nc, head_dim] float32 (vc may be NULL when
+ * oc is NULL).  kv_block_idx: [batch, heads, Nc, top_k] int32 (row stride
+ * top_k).  valid_block_num: [batch, heads, Nc] int32.  Scores and the
+ * selection are computed in float32.  Nc up to 4096. */
+int vsa_coarse_topk(const vsa_problem* p, int32_t top_k, const float* qc,
+                    const float* kc, const float* vc, int32_t* kv_block_idx,
+                    int32_t* valid_block_num, float* oc, void* stream);
+
+/* Fine block-sparse attention with the gated combination
+ * ([VSA-ROCm] §Two-Stage Architecture Stage 2, §Block-Sparse Encoding,
+ * §Kernel Architecture, §Sparse Traversal; [VSA-arXiv] Abstract).
+ * For query cube i of (b, h) and n = valid_block_num[b, h, i], the keys are
+ * the tokens of cubes kv_block_idx[b, h, i, 0..n-1] (each listed entry
+ * attended once per listing), and for every query token p of cube i:
+ *   O_f[p] = sum_q softmax_q(<q_p, k_q> / sqrt(head_dim)) v_q
+ *   out[p] = g_f[p] * O_f[p] + g_c[p] * oc[b, h, i]         (bf16, RNE)
+ *   lse[p] = log(sum_q exp(<q_p, k_q> / sqrt(head_dim)))   (natural log)
+ * gate_f == NULL means g_f = 1; gate_c == NULL means g_c = 0 (then oc may be
+ * NULL).  A row with n == 0 gives O_f = 0 and lse = -inf.
+ * q, k, v, out, gate_c, gate_f: [batch, heads, N, head_dim] bf16 cube-major.
+ * kv_block_idx: [batch, heads, Nc, max_kv_blocks] int32; each of the first
+ *   n entries of a row must lie in [0, Nc) (not checked here; see
+ *   vsa_check_lut).  valid_block_num: [batch, heads, Nc] int32, each in
+ *   [0, max_kv_blocks].
+ * oc: [batch, heads, Nc, head_dim] float32; lse: [batch, heads, N] float32,
+ *   cube-major, or NULL.
+ * Requires cube volume 64 and head_dim 64 or 128.  out must not alias an
+ * input. */
+int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k,
+                        const void* v, const int32_t* kv_block_idx,
+                        const int32_t* valid_block_num, int32_t max_kv_blocks,
+                        const float* oc, const void* gate_c,
+                        const void* gate_f, void* out, float* lse,
+                        void* stream);
+
+/* Device-side LUT validator (optional, asynchronous).  Writes to
+ * *bad_rows (one device int32) the number of LUT rows whose count is
+ * outside [0, max_kv_blocks] or which list a cube outside [0, Nc).
+ * Read it after synchronising the stream; 0 means the LUT is safe to pass
+ * to vsa_sparse_attn_fwd ([VSA-ROCm] §Block-Sparse Encoding). */
+int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx,
+                  const int32_t* valid_block_num, int32_t max_kv_blocks,
+                  int32_t* bad_rows, void* stream);
+
+/* Host helper: perm_host[p] = pi(p) for p < N (the order vsa_permute
+ * applies).  perm_host is a host array of N int32.  No device work. */
+int vsa_perm_index(const vsa_problem* p, int32_t* perm_host);
+
+/* Static description of a status code (never NULL). */
+const char* vsa_status_str(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int vsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H_ */

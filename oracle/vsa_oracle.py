@@ -158,7 +158,7 @@ def topk_lut(s: np.ndarray, k: int):
 
 def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
                    kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
-                   scale: float, vol: int):
+                   scale: float, vol: int, query_cubes=None):
     """Token-level attention of every query cube over its listed key cubes.
 
     qp/kp/vp: cube-major [B, heads, N, d].  For query cube i the key set is
@@ -166,6 +166,8 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     valid_block_num[i] entries j of row i of the LUT (R8: in LUT order).
     Returns (O_f [B, heads, N, d], LSE [B, heads, N]) with
     LSE = log(sum_q exp(scale * q.k)) in natural-log units (R7 for empty rows).
+    ``query_cubes`` (optional iterable of (b, h, i)) limits the work to those
+    query cubes, for spot checks at full size; other rows stay 0 / -inf.
     """
     qp = np.asarray(qp, np.float64)
     kp = np.asarray(kp, np.float64)
@@ -174,21 +176,21 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     nc = N // vol
     of = np.zeros((B, nh, N, d), dtype=np.float64)
     lse = np.full((B, nh, N), -np.inf, dtype=np.float64)
-    for b in range(B):
-        for h in range(nh):
-            for i in range(nc):
-                cnt = int(valid_block_num[b, h, i])
-                if cnt == 0:
-                    continue
-                blocks = kv_block_idx[b, h, i, :cnt]
-                rows = np.concatenate([np.arange(j * vol, j * vol + vol) for j in blocks])
-                q = qp[b, h, i * vol:(i + 1) * vol]
-                s = scale * (q @ kp[b, h, rows].T)
-                m = s.max(axis=1, keepdims=True)
-                e = np.exp(s - m)
-                den = e.sum(axis=1, keepdims=True)
-                of[b, h, i * vol:(i + 1) * vol] = (e @ vp[b, h, rows]) / den
-                lse[b, h, i * vol:(i + 1) * vol] = (m + np.log(den))[:, 0]
+    todo = ((b, h, i) for b in range(B) for h in range(nh) for i in range(nc)) \
+        if query_cubes is None else query_cubes
+    for b, h, i in todo:
+        cnt = int(valid_block_num[b, h, i])
+        if cnt == 0:
+            continue
+        blocks = kv_block_idx[b, h, i, :cnt]
+        rows = np.concatenate([np.arange(j * vol, j * vol + vol) for j in blocks])
+        q = qp[b, h, i * vol:(i + 1) * vol]
+        s = scale * (q @ kp[b, h, rows].T)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        den = e.sum(axis=1, keepdims=True)
+        of[b, h, i * vol:(i + 1) * vol] = (e @ vp[b, h, rows]) / den
+        lse[b, h, i * vol:(i + 1) * vol] = (m + np.log(den))[:, 0]
     return of, lse
 
 

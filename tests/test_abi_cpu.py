@@ -1,0 +1,151 @@
+"""CPU-side checks of the C ABI: libvsa.so loads, exports every entry point
+that include/vsa.h declares, its host helper matches the oracle, and every
+argument error is reported before anything is launched (no GPU needed: each
+call below fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_video_major_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libvsa.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"vsa_permute", "vsa_unpermute", "vsa_pool", "vsa_coarse_topk",
+            "vsa_sparse_attn_fwd"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_abi_version_and_status_strings():
+    assert L.vsa_abi_version() >> 16 == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.vsa_status_str(code) and L.vsa_status_str(code) != "unknown status"
+    assert L.vsa_status_str(42) == "unknown status"
+
+
+@pytest.mark.parametrize("grid,cube", [((4, 8, 8), (4, 4, 4)), ((16, 32, 64), (4, 4, 4)),
+                                       ((2, 4, 6), (2, 2, 2)), ((3, 6, 4), (3, 2, 1)),
+                                       ((32, 48, 80), (4, 4, 4))])
+def test_host_perm_index_matches_oracle(grid, cube):
+    p = L.Problem(1, 1, *grid, *cube, 64)
+    got = L.vsa_perm_index(p).numpy()
+    assert np.array_equal(got, oracle.perm_index(*grid, *cube))
+
+
+# ----------------------------------------------------------------- errors
+DUMMY = 0x1000   # never dereferenced: each call fails validation first
+
+
+def _raw():
+    return L.load()
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, T=8, H=16, W=16, ct=4, ch=4, cw=4, head_dim=64)
+    base.update(kw)
+    return L.Problem(**base).c_struct()
+
+
+def _perm(prob, dtype=L.VSA_BF16, src=DUMMY, dst=DUMMY):
+    return _raw().vsa_permute(ctypes.byref(prob) if prob is not None else None, dtype, src, dst, None)
+
+
+def test_permute_errors():
+    assert _perm(None) == L.VSA_ERR_NULL
+    assert _perm(_prob(T=6)) == L.VSA_ERR_SHAPE            # 6 is not a multiple of 4
+    assert _perm(_prob(W=0)) == L.VSA_ERR_SHAPE
+    assert _perm(_prob(batch=-1)) == L.VSA_ERR_SHAPE
+    assert _perm(_prob(head_dim=96)) == L.VSA_ERR_UNSUPPORTED
+    assert _perm(_prob(), dtype=7) == L.VSA_ERR_UNSUPPORTED
+    assert _perm(_prob(), src=None) == L.VSA_ERR_NULL
+    assert _perm(_prob(), dst=None) == L.VSA_ERR_NULL
+    assert _raw().vsa_unpermute(ctypes.byref(_prob(H=10)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert _raw().vsa_unpermute(ctypes.byref(_prob()), 0, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert _perm(_prob(T=1 << 14, H=1 << 14, W=1 << 14, ct=1, ch=1, cw=1)) == L.VSA_ERR_SHAPE
+
+
+def test_pool_errors():
+    lib = _raw()
+    assert lib.vsa_pool(ctypes.byref(_prob()), 0, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_pool(ctypes.byref(_prob()), 0, DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_pool(ctypes.byref(_prob(cw=3)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_pool(ctypes.byref(_prob()), 3, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
+
+
+def test_coarse_topk_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob())          # Nc = 8*16*16/64 = 32
+
+    def call(k=8, qc=DUMMY, kc=DUMMY, vc=DUMMY, lut=DUMMY, valid=DUMMY, oc=DUMMY, prob=pr):
+        return lib.vsa_coarse_topk(prob, k, qc, kc, vc, lut, valid, oc, None)
+
+    assert call(k=0) == L.VSA_ERR_TOPK
+    assert call(k=33) == L.VSA_ERR_TOPK
+    assert call(qc=None) == L.VSA_ERR_NULL
+    assert call(kc=None) == L.VSA_ERR_NULL
+    assert call(lut=None) == L.VSA_ERR_NULL
+    assert call(valid=None) == L.VSA_ERR_NULL
+    assert call(vc=None) == L.VSA_ERR_NULL                  # oc requested without vc
+    big = ctypes.byref(_prob(T=64, H=64, W=32))             # Nc = 2048 is fine
+    assert call(k=0, prob=big) == L.VSA_ERR_TOPK
+    huge = ctypes.byref(_prob(T=64, H=64, W=128))           # Nc = 8192 > 4096
+    assert call(prob=huge) == L.VSA_ERR_UNSUPPORTED
+
+
+def test_sparse_attn_errors():
+    lib = _raw()
+
+    def call(prob=None, q=DUMMY, k=DUMMY, v=DUMMY, lut=DUMMY, valid=DUMMY, maxkv=8, oc=None,
+             gc=None, gf=None, out=DUMMY, lse=None):
+        prob = ctypes.byref(prob or _prob())
+        return lib.vsa_sparse_attn_fwd(prob, q, k, v, lut, valid, maxkv, oc, gc, gf, out, lse, None)
+
+    assert call(q=None) == L.VSA_ERR_NULL
+    assert call(k=None) == L.VSA_ERR_NULL
+    assert call(v=None) == L.VSA_ERR_NULL
+    assert call(out=None) == L.VSA_ERR_NULL
+    assert call(lut=None) == L.VSA_ERR_NULL
+    assert call(valid=None) == L.VSA_ERR_NULL
+    assert call(gc=DUMMY) == L.VSA_ERR_NULL                # gate_c needs oc
+    assert call(maxkv=0) == L.VSA_ERR_TOPK
+    assert call(maxkv=33) == L.VSA_ERR_TOPK
+    assert call(prob=_prob(ct=2, ch=2, cw=2)) == L.VSA_ERR_UNSUPPORTED   # cube volume 8
+    assert call(prob=_prob(head_dim=32)) == L.VSA_ERR_UNSUPPORTED
+    assert call(prob=_prob(T=5)) == L.VSA_ERR_SHAPE
+
+
+def test_check_lut_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob())
+    assert lib.vsa_check_lut(pr, DUMMY, DUMMY, 0, DUMMY, None) == L.VSA_ERR_TOPK
+    assert lib.vsa_check_lut(pr, DUMMY, DUMMY, 8, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_check_lut(pr, None, DUMMY, 8, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_perm_index(ctypes.byref(_prob()), None) == L.VSA_ERR_NULL
+
+
+def test_python_binding_rejects_wrong_shapes_before_the_library():
+    import torch
+    p = L.Problem(1, 1, 4, 8, 8, 4, 4, 4, 64)
+    cpu = torch.zeros((1, 1, 256, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.vsa_permute(p, L.VSA_BF16, cpu, cpu)                # not device tensors
+    with pytest.raises(ValueError):
+        L._token_dtype(5)
