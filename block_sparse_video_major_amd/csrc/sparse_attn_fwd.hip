@@ -42,7 +42,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // register-promotable 16-byte chunk
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kBlk = 64;        // tokens per cube: query tile and key tile
@@ -130,39 +132,47 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   float m_used = -INFINITY;  // log2-domain offset used for exponentiation
   float l_part = 0.f;        // this lane's partial row sum (its 16 keys per block)
 
-  uint4 kreg[C::LOADS], vreg[C::LOADS];
-  auto fetch = [&](int it) {
-    int blk = lrow[it];
-    blk = blk < 0 ? 0 : (blk >= Nc ? Nc - 1 : blk);   // memory-safety clamp
-    const uint4* kt = reinterpret_cast<const uint4*>(k + head_off + (int64_t)blk * kBlk * D);
-    const uint4* vt = reinterpret_cast<const uint4*>(v + head_off + (int64_t)blk * kBlk * D);
+  // Per-thread staging of one K tile and one V tile: chunk c = tid + u*256 of
+  // the contiguous 64 x D tile is row c / CPR, 16-byte column c % CPR.
+  u32x4 kreg[C::LOADS], vreg[C::LOADS];
+  int st_k[C::LOADS], st_v[C::LOADS];   // LDS byte offsets of the chunks (stage 0)
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      kreg[u] = kt[tid + u * kThreads];
-      vreg[u] = vt[tid + u * kThreads];
-    }
-  };
-  auto stash = [&](int stage) {
-    char* base = smem + stage * C::STAGE_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int c = tid + u * kThreads;
-      const int row = c / C::CPR, col = c % C::CPR;
-      *reinterpret_cast<uint4*>(base + (row * C::KSTR + col * 8) * 2) = kreg[u];
-      *reinterpret_cast<uint4*>(base + C::K_BYTES + (row * C::VSTR + col * 8) * 2) = vreg[u];
-    }
-  };
+  for (int u = 0; u < C::LOADS; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / C::CPR, col = c % C::CPR;
+    st_k[u] = (row * C::KSTR + col * 8) * 2;
+    st_v[u] = C::K_BYTES + (row * C::VSTR + col * 8) * 2;
+  }
+#define VSA_FETCH(IT)                                                                    \
+  do {                                                                                   \
+    int blk_ = lrow[(IT)];                                                               \
+    blk_ = blk_ < 0 ? 0 : (blk_ >= Nc ? Nc - 1 : blk_); /* memory-safety clamp */        \
+    const u32x4* kt_ = reinterpret_cast<const u32x4*>(k + head_off + (int64_t)blk_ * kBlk * D); \
+    const u32x4* vt_ = reinterpret_cast<const u32x4*>(v + head_off + (int64_t)blk_ * kBlk * D); \
+    _Pragma("unroll") for (int u = 0; u < C::LOADS; ++u) {                               \
+      kreg[u] = kt_[tid + u * kThreads];                                                 \
+      vreg[u] = vt_[tid + u * kThreads];                                                 \
+    }                                                                                    \
+  } while (0)
+#define VSA_STASH(STAGE)                                                                 \
+  do {                                                                                   \
+    char* base_ = smem + (STAGE) * C::STAGE_BYTES;                                       \
+    _Pragma("unroll") for (int u = 0; u < C::LOADS; ++u) {                               \
+      *reinterpret_cast<u32x4*>(base_ + st_k[u]) = kreg[u];                              \
+      *reinterpret_cast<u32x4*>(base_ + st_v[u]) = vreg[u];                              \
+    }                                                                                    \
+  } while (0)
 
   if (nblk > 0) {
-    fetch(0);
-    stash(0);
+    VSA_FETCH(0);
+    VSA_STASH(0);
   }
   __syncthreads();
 
   for (int it = 0; it < nblk; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < nblk;
-    if (more) fetch(it + 1);
+    if (more) VSA_FETCH(it + 1);
     const char* kbase = smem + cur * C::STAGE_BYTES;
     const char* vbase = kbase + C::K_BYTES;
 
@@ -218,19 +228,18 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
             (lds_i16x4*)(vbase + (key0 * C::VSTR + col) * 2));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4*)(vbase + ((key0 + 8) * C::VSTR + col) * 2));
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = __builtin_bit_cast(__bf16, lo[e]);
-          a[4 + e] = __builtin_bit_cast(__bf16, hi[e]);
-        }
+        // concatenate as whole vectors (element-wise bf16 inserts are avoided)
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j], o[t], 0, 0, 0);
       }
     }
 
-    if (more) stash(cur ^ 1);
+    if (more) VSA_STASH(cur ^ 1);
     __syncthreads();
   }
+
+#undef VSA_FETCH
+#undef VSA_STASH
 
   // ---- merge the two key halves, normalise, combine, store ----
   const float l_row = pair_sum(l_part);
