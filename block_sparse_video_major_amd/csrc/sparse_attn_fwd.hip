@@ -11,28 +11,40 @@
 // Attention", Abstract.  Softmax(QK^T / sqrt(d)) V as in §The Attention
 // Bottleneck in Video Diffusion.
 //
-// Work decomposition (one workgroup per (batch, head, query cube)):
-//   * 256 threads = 4 wavefronts.  Wave w owns query half qh = w & 1 (32 of
-//     the cube's 64 query tokens) and key half kh = w >> 1 (32 of the 64
-//     tokens of every selected key cube).  The two key halves keep separate
-//     online-softmax states that are merged once at the end.
+// Work decomposition:
+//   * One workgroup (512 threads, 8 wavefronts) per CU, persistent.  Each
+//     workgroup takes a PAIR of neighbouring query cubes (2p, 2p+1) of one
+//     (batch, head): waves 0-3 serve cube A, waves 4-7 cube B.  Each XCD owns
+//     one contiguous range of pairs and its workgroups walk it in rounds, so
+//     neighbouring pairs sweep similar key cubes at the same time (L2 reuse).
+//   * Step schedule.  Neighbouring query cubes select largely the same key
+//     cubes.  The two LUT rows are turned into one list of steps: first every
+//     key cube both rows list (loaded once, used by both halves), then the
+//     remaining cubes of A paired with the remaining cubes of B (two tiles
+//     per step).  Every step keeps all 8 waves busy whenever the rows have
+//     equal counts, and K/V tiles are fetched once per pair instead of once
+//     per cube for the shared part.  Attention sums over its key set, so the
+//     visiting order only changes fp32 rounding.  Rows that list a cube twice
+//     (allowed: each listing is attended) fall back to positional pairing.
+//   * Within a half, wave w owns query half qh = w & 1 (32 of the cube's 64
+//     query tokens) and key half kh = (w >> 1) & 1 (32 of the 64 tokens of
+//     each key cube); the two key halves keep separate online-softmax states,
+//     merged once per query cube.
 //   * Scores are formed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand, Q is
-//     held in registers as the B operand for the whole kernel.  In the
-//     accumulator layout each lane then owns one query (lane % 32) and 16 of
-//     its keys, so the row max is a 16-way local max plus one
-//     v_permlane32_swap, and all softmax state is lane-local.
-//   * O^T += V^T P^T: P (bf16) is already in B-operand layout; V^T comes from
-//     the V tile kept in its natural [key][d] layout in LDS through
-//     ds_read_b64_tr_b16 transposing reads.
-//   * Key/value cube tiles are double-buffered in LDS: the tiles of list entry
-//     i+1 are fetched from global memory into registers while entry i is
-//     computed, then written to the other LDS stage; one barrier per entry.
-//   * Rescaling of O is lazy: the running max used for exponentiation only
-//     moves when a block's max exceeds it by more than 8 (log2 units), which
-//     keeps every exp2 <= 256 and is exact because numerator and denominator
-//     share the same offset.
-//   * Epilogue: the two key halves are merged through LDS, O is normalised,
+//     v_mfma_f32_32x32x16_bf16: K rows from LDS as the A operand, Q in
+//     registers as the B operand.  In the accumulator layout each lane owns
+//     one query (lane % 32) and 16 of its keys, so the row max is a local max
+//     plus one v_permlane32_swap and all softmax state is lane-local.
+//   * O^T += V^T P^T: P (bf16) is already in B-operand layout; V^T is read
+//     from the V tile in its natural [key][d] order with ds_read_b64_tr_b16.
+//   * Tiles arrive by direct global->LDS loads (16 bytes per lane, no
+//     registers) into a ring of 4 K/V positions (8 at d = 64), filled as far
+//     ahead as the ring allows.  Tiles are unpadded; 16-byte chunks are XOR
+//     swizzled per row so every LDS read pattern is bank-conflict free.
+//   * Rescaling of O is lazy: the exponent offset only moves when a block's
+//     max exceeds it by more than 8 (log2 units), keeping every exp2 <= 256;
+//     exact, because numerator and denominator share the offset.
+//   * Epilogue per query cube: key halves merged through LDS, O normalised,
 //     staged in LDS, combined with the gates and the broadcast coarse output
 //     and written with coalesced 16-byte stores.
 #include "vsa_internal.h"
@@ -42,31 +54,32 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // register-promotable 16-byte chunk
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef const __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBlk = 64;        // tokens per cube: query tile and key tile
-constexpr int kThreads = 256;
-constexpr float kTau = 8.0f;    // lazy-rescale threshold (log2 units)
+constexpr int kBlk = 64;          // tokens per cube: query tile and key tile
+constexpr int kThreads = 512;     // two query cubes x 4 wavefronts
+constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+constexpr int kRingBytes = 128 * 1024;
 
 template <int D>
 struct Cfg {
-  static constexpr int KSTR = D + 8;                 // K tile row stride (bf16): conflict-free b128 reads
-  static constexpr int VSTR = D + 32;                // V tile row stride (bf16): conflict-free transposing reads
-  static constexpr int K_BYTES = kBlk * KSTR * 2;
-  static constexpr int V_BYTES = kBlk * VSTR * 2;
-  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
-  static constexpr int LOADS = kBlk * CPR / kThreads;  // chunks per thread per tile
-  static constexpr int OT = D / 32;                  // 32-row output tiles of O^T
+  static constexpr int ROWB = D * 2;                 // bytes per token row
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE = kBlk * ROWB;           // one K or V cube tile
+  static constexpr int LOADS = TILE / (kThreads * 16);  // 16-byte loads per wave per tile
+  static constexpr int R = kRingBytes / (2 * TILE);  // ring positions (one K + one V tile each)
+  static constexpr int V_BASE = R * TILE;
+  static constexpr int OT = D / 32;                  // 32-row tiles of O^T
   static constexpr int NOV = OT * 16;                // O^T accumulators per lane
-  static constexpr int MERGE_BYTES = 2 * (NOV + 2) * 64 * 4;
+  static constexpr int MERGE_G = 2 * (NOV + 2) * 64 * 4;   // merge buffer of one half
   static constexpr int OSTR = D + 4;                 // fp32 staging row stride
-  static constexpr int OST_BYTES = kBlk * OSTR * 4;
-  static constexpr int LDS_BYTES =
-      (2 * STAGE_BYTES > MERGE_BYTES + OST_BYTES) ? 2 * STAGE_BYTES : MERGE_BYTES + OST_BYTES;
+  static constexpr int OST_G = kBlk * OSTR * 4;      // staging of one half
+  static constexpr int EPI_BYTES = 2 * (MERGE_G + OST_G);
+  // Chunk swizzles: the logical 16-byte chunk c of row r sits at c ^ f(r).
+  __device__ static constexpr int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static constexpr int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -93,252 +106,468 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& raw, float* f) {
   }
 }
 
+// One direct global->LDS load: every lane moves the 16 bytes at base + voff
+// (base: wave-uniform pointer, voff: per-lane byte offset) to LDS byte address
+// lds_base + 16 * lane.  Issued through inline assembly so that the compiler
+// does not track these LDS writes; completion is enforced explicitly
+// (wait_vmem + barrier) before any wave reads the slot.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// (expcnt and lgkmcnt fields at their no-wait maxima).  The builtin form is
+// visible to the compiler's own wait-count tracking.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `tiles` tiles' worth of this wave's loads (2*L load
+// instructions per tile: K and V) are still pending.
+template <int L>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  switch (tiles) {
+    case 0: wait_vmem<0>(); break;
+    case 1: wait_vmem<2 * L>(); break;
+    case 2: wait_vmem<4 * L>(); break;
+    case 3: wait_vmem<6 * L>(); break;
+    case 4: wait_vmem<8 * L>(); break;
+    case 5: wait_vmem<10 * L>(); break;
+    case 6: wait_vmem<12 * L>(); break;
+    default: wait_vmem<14 * L>(); break;
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
     const float* __restrict__ oc, const __bf16* __restrict__ gate_c, const __bf16* __restrict__ gate_f,
-    __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total, float c_log2) {
+    __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  // schedule: schedA[s], schedB[s] (int16 key cube ids, -1 = none) after the ring
+  int16_t* schedA = reinterpret_cast<int16_t*>(smem + kRingBytes);
+  int16_t* schedB = schedA + max_kv;
+  int* flags = reinterpret_cast<int*>(smem + kRingBytes + 4 * ((max_kv + 1) / 2 * 2));   // [0]: duplicate seen
+  uint32_t* bmA = reinterpret_cast<uint32_t*>(flags + 4);               // Nc-bit membership maps
+  const int nwords = (Nc + 31) >> 5;
+  uint32_t* bmB = bmA + nwords;
 
-  const int64_t wg = xcd_remap((int64_t)blockIdx.x, total);   // = bh * Nc + cube
-  const int64_t bh = wg / Nc;
-  const int cube = (int)(wg - bh * Nc);
-  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;      // element offset of this (b, h)
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                  // 0: cube A, 1: cube B
+  const int w4 = wave & 3;
+  const int qh = w4 & 1, kh = w4 >> 1;
   const int n32 = lane & 31, g = lane >> 5;
   const int l16 = lane & 15, h16 = (lane >> 4) & 1;
 
-  int nblk = valid[wg];
-  nblk = nblk < 0 ? 0 : (nblk > max_kv ? max_kv : nblk);
-  const int32_t* lrow = lut + wg * (int64_t)max_kv;
-
-  // Q as the B operand of S^T = K Q^T: query 32*qh + n32, d = 16*s + 8*g + 0..7.
-  bf16x8 qf[D / 16];
+  // ---- per-lane constant offsets ------------------------------------------
+  // Direct loads: lane i of load n of wave w fills LDS chunk L = (w*LOADS+n)*64+i
+  // of a tile, which holds logical chunk (L % CPR) ^ f(row) of row L / CPR.
+  uint32_t kg_off[C::LOADS], vg_off[C::LOADS];
+#pragma unroll
+  for (int n = 0; n < C::LOADS; ++n) {
+    const int L = (wave * C::LOADS + n) * 64 + lane;
+    const int r = L / C::CPR, x = L % C::CPR;
+    kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16);
+    vg_off[n] = r * C::ROWB + ((x ^ C::vswz(r)) * 16);
+  }
+  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * C::LOADS * 1024));
+  // K A-operand reads: key row 32*kh + n32, logical chunk 2*ks + g.
+  int k_off[D / 16];
   {
-    const __bf16* qrow = q + head_off + (int64_t)(cube * kBlk + 32 * qh + n32) * D + 8 * g;
+    const int r = 32 * kh + n32;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = r * C::ROWB + (((2 * ks + g) ^ C::kswz(r)) * 16);
+  }
+  // V^T A-operand transposing reads: source lane l16 addresses key row
+  // 32*kh + 16*j + 8*hi + 4*g + l16/4 and d columns 32*t + 16*h16 + 4*(l16%4).
+  // The swizzle depends on the row only through bits that the +16*j + 8*hi
+  // row steps (added as immediates) do not change.
+  int v_off[C::OT];
+  {
+    const int r = 32 * kh + 4 * g + (l16 >> 2);
+    const int byte_base = 32 * h16 + 8 * (l16 & 3);
+#pragma unroll
+    for (int t = 0; t < C::OT; ++t) {
+      const int b = 64 * t + byte_base;
+      v_off[t] = C::V_BASE + r * C::ROWB + ((((b >> 4) ^ C::vswz(r)) << 4) | (b & 15));
+    }
   }
 
-  f32x16 o[C::OT];
-#pragma unroll
-  for (int t = 0; t < C::OT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_used = -INFINITY;  // log2-domain offset used for exponentiation
-  float l_part = 0.f;        // this lane's partial row sum (its 16 keys per block)
+  // The two halves share every SIMD (waves w and w+4) and meet at the same
+  // barrier each step.  Half A runs at a higher issue priority, so it leads
+  // each phase: its exponentials then overlap half B's MFMAs and vice versa.
+  if (grp == 0) __builtin_amdgcn_s_setprio(1);
 
-  // Per-thread staging of one K tile and one V tile: chunk c = tid + u*256 of
-  // the contiguous 64 x D tile is row c / CPR, 16-byte column c % CPR.
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  int st_k[C::LOADS], st_v[C::LOADS];   // LDS byte offsets of the chunks (stage 0)
-#pragma unroll
-  for (int u = 0; u < C::LOADS; ++u) {
-    const int c = tid + u * kThreads;
-    const int row = c / C::CPR, col = c % C::CPR;
-    st_k[u] = (row * C::KSTR + col * 8) * 2;
-    st_v[u] = C::K_BYTES + (row * C::VSTR + col * 8) * 2;
-  }
-#define VSA_FETCH(IT)                                                                    \
-  do {                                                                                   \
-    int blk_ = lrow[(IT)];                                                               \
-    blk_ = blk_ < 0 ? 0 : (blk_ >= Nc ? Nc - 1 : blk_); /* memory-safety clamp */        \
-    const u32x4* kt_ = reinterpret_cast<const u32x4*>(k + head_off + (int64_t)blk_ * kBlk * D); \
-    const u32x4* vt_ = reinterpret_cast<const u32x4*>(v + head_off + (int64_t)blk_ * kBlk * D); \
-    _Pragma("unroll") for (int u = 0; u < C::LOADS; ++u) {                               \
-      kreg[u] = kt_[tid + u * kThreads];                                                 \
-      vreg[u] = vt_[tid + u * kThreads];                                                 \
-    }                                                                                    \
-  } while (0)
-#define VSA_STASH(STAGE)                                                                 \
-  do {                                                                                   \
-    char* base_ = smem + (STAGE) * C::STAGE_BYTES;                                       \
-    _Pragma("unroll") for (int u = 0; u < C::LOADS; ++u) {                               \
-      *reinterpret_cast<u32x4*>(base_ + st_k[u]) = kreg[u];                              \
-      *reinterpret_cast<u32x4*>(base_ + st_v[u]) = vreg[u];                              \
-    }                                                                                    \
-  } while (0)
+  const int pairs_per_head = (Nc + 1) >> 1;
+  const int64_t per_xcd = (total_pairs + 7) / 8;
+  const int xcd = blockIdx.x % 8;
+  const int64_t lo = (int64_t)xcd * per_xcd;
+  const int64_t end = lo + per_xcd < total_pairs ? lo + per_xcd : total_pairs;
+  const int64_t stride = gridDim.x / 8;
 
-  if (nblk > 0) {
-    VSA_FETCH(0);
-    VSA_STASH(0);
-  }
-  __syncthreads();
+  for (int64_t pid = lo + blockIdx.x / 8; pid < end; pid += stride) {
+    const int64_t bh = pid / pairs_per_head;
+    const int cubeA = (int)(pid - bh * pairs_per_head) * 2;
+    const bool hasB = cubeA + 1 < Nc;
+    const int64_t rowA = bh * Nc + cubeA;
+    const int64_t head_off = bh * (int64_t)Nc * kBlk * D;   // element offset of this (b, h)
+    const char* k_head = reinterpret_cast<const char*>(k + head_off);
+    const char* v_head = reinterpret_cast<const char*>(v + head_off);
+    auto count_of = [&](int64_t row) {
+      const int n = valid[row];
+      return n < 0 ? 0 : (n > max_kv ? max_kv : n);
+    };
+    const int nA = count_of(rowA);
+    const int nB = hasB ? count_of(rowA + 1) : 0;
+    const int32_t* lrowA = lut + rowA * (int64_t)max_kv;
+    const int32_t* lrowB = lrowA + max_kv;
+    auto clampc = [&](int b) { return b < 0 ? 0 : (b >= Nc ? Nc - 1 : b); };   // memory-safety clamp
+    const int S = nA > nB ? nA : nB;   // steps
 
-  for (int it = 0; it < nblk; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nblk;
-    if (more) VSA_FETCH(it + 1);
-    const char* kbase = smem + cur * C::STAGE_BYTES;
-    const char* vbase = kbase + C::K_BYTES;
-
-    // S^T tile: keys 32*kh + (8*(r/4) + 4*g + r%4), query n32.
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const char* krow = kbase + ((32 * kh + n32) * C::KSTR + 8 * g) * 2;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+    // ---- build the step schedule -------------------------------------------
+    for (int i = tid; i < 2 * nwords; i += kThreads) bmA[i] = 0u;
+    if (tid == 0) flags[0] = 0;
+    __syncthreads();
+    for (int i = tid; i < nA + nB; i += kThreads) {
+      const bool inA = i < nA;
+      const int c = clampc(inA ? lrowA[i] : lrowB[i - nA]);
+      uint32_t* bm = inA ? bmA : bmB;
+      const uint32_t bit = 1u << (c & 31);
+      if (atomicOr(&bm[c >> 5], bit) & bit) flags[0] = 1;   // a row lists a cube twice
+    }
+    __syncthreads();
+    const bool dup = flags[0] != 0;
+    if (dup) {
+      // positional pairing: step s = (A[s], B[s])
+      for (int s = tid; s < S; s += kThreads) {
+        schedA[s] = (int16_t)(s < nA ? clampc(lrowA[s]) : -1);
+        schedB[s] = (int16_t)(s < nB ? clampc(lrowB[s]) : -1);
+      }
+    } else if (wave < 2) {
+      // wave 0 walks row A (shared and A-only cubes), wave 1 row B (B-only
+      // cubes).  Shared cubes take steps 0..nS-1 in row order; the others
+      // take steps nS.. in row order.
+      const int n_me = wave == 0 ? nA : nB;
+      const int32_t* row = wave == 0 ? lrowA : lrowB;
+      const uint32_t* other = wave == 0 ? bmB : bmA;
+      int16_t* mine = wave == 0 ? schedA : schedB;
+      const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int n_sh = 0;   // shared cubes in this row (the same set for both rows)
+      for (int base = 0; base < n_me; base += 64) {
+        const int i = base + lane;
+        bool sh = false;
+        if (i < n_me) {
+          const int c = clampc(row[i]);
+          sh = (other[c >> 5] >> (c & 31)) & 1u;
+        }
+        n_sh += __popcll(__ballot(sh));
+      }
+      int sh_seen = 0, ex_seen = 0;
+      for (int base = 0; base < n_me; base += 64) {
+        const int i = base + lane;
+        const bool in = i < n_me;
+        int c = 0;
+        bool sh = false;
+        if (in) {
+          c = clampc(row[i]);
+          sh = (other[c >> 5] >> (c & 31)) & 1u;
+        }
+        const uint64_t msh = __ballot(in && sh), mex = __ballot(in && !sh);
+        if (in) {
+          if (sh) {
+            if (wave == 0) {
+              const int s = sh_seen + __popcll(msh & lt);
+              schedA[s] = (int16_t)c;
+              schedB[s] = (int16_t)c;
+            }
+          } else {
+            mine[n_sh + ex_seen + __popcll(mex & lt)] = (int16_t)c;
+          }
+        }
+        sh_seen += __popcll(msh);
+        ex_seen += __popcll(mex);
+      }
+      for (int s = n_sh + ex_seen + lane; s < S; s += 64) mine[s] = (int16_t)-1;
     }
 
-    // online softmax (log2 domain)
-    float mx = s[0];
+    // Q of this half's cube as the B operand: query 32*qh + n32, d = 16*s + 8*g + 0..7
+    const int my_cube = cubeA + grp;
+    const bool my_valid = grp == 0 || hasB;
+    bf16x8 qf[D / 16];
+    if (my_valid) {
+      const __bf16* qrow = q + head_off + (int64_t)(my_cube * kBlk + 32 * qh + n32) * D + 8 * g;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = pair_max(mx) * c_log2;
-    if (__ballot(mx > m_used + kTau) != 0ull) {
-      const float m_new = fmaxf(m_used, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
-      l_part *= alpha;
+      for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    }
+    wait_vmem<0>();
+    __syncthreads();   // schedule complete; bitmaps no longer needed
+
+    auto tiles_of = [&](int s, int& ta, int& tb) {
+      ta = __builtin_amdgcn_readfirstlane((int)schedA[s]);
+      tb = __builtin_amdgcn_readfirstlane((int)schedB[s]);
+      return (ta >= 0 ? 1 : 0) + ((tb >= 0 && tb != ta) ? 1 : 0);
+    };
+    auto load_tile = [&](int blk, int pos) {
+      const uint32_t slot_off = (uint32_t)((pos % C::R) * C::TILE);
+      const char* ks = uniform_ptr(k_head + (int64_t)blk * C::TILE);
+      const char* vs = uniform_ptr(v_head + (int64_t)blk * C::TILE);
+#pragma unroll
+      for (int n = 0; n < C::LOADS; ++n) {
+        dma16(ks, kg_off[n], lds_ring + slot_off + n * 1024);
+        dma16(vs, vg_off[n], lds_ring + C::V_BASE + slot_off + n * 1024);
+      }
+    };
+    // issue pointer (step si at ring position pi) and compute position pc
+    int si = 0, pi = 0, pc = 0;
+    auto issue_ahead = [&]() {
+      while (si < S) {
+        int ta, tb;
+        const int n = tiles_of(si, ta, tb);
+        if (pi + n > pc + C::R) break;
+        if (ta >= 0) load_tile(ta, pi);
+        if (tb >= 0 && tb != ta) load_tile(tb, pi + (ta >= 0 ? 1 : 0));
+        pi += n;
+        ++si;
+      }
+    };
+    issue_ahead();
+
+    f32x16 o[C::OT];
+#pragma unroll
+    for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+    float m_used = -INFINITY;  // log2-domain offset used for exponentiation
+    float l_part = 0.f;        // this lane's partial row sum
+
+    for (int s = 0; s < S; ++s) {
+      int ta, tb;
+      const int n = tiles_of(s, ta, tb);
+      // this step's tiles must have landed for every wave; later ones may fly
+      wait_tiles<C::LOADS>(pi - (pc + n));
+      __syncthreads();
+      issue_ahead();   // positions before pc are free: every wave finished step s-1
+
+      const int mine = grp == 0 ? ta : tb;
+      if (mine >= 0) {
+        const int slot = (grp == 1 && ta >= 0 && tb != ta) ? (pc + 1) % C::R : pc % C::R;
+        const char* base = smem + slot * C::TILE;
+        // All K operand reads are issued before the first MFMA so that their
+        // LDS latencies overlap instead of adding up.
+        bf16x8 ka[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(base + k_off[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T tile: keys 32*kh + (8*(r/4) + 4*g + r%4), query n32
+        f32x16 sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sc, 0, 0, 0);
+        // V^T operands do not depend on the softmax: read them now, so their
+        // latency hides behind the exponentials.  For k-step j the A operand
+        // of lane (g, d-row) holds keys base + 0..3 and base + 8..11 with
+        // base = 32*kh + 16*j + 4*g: exactly the keys of pb[j]'s slots.
+        bf16x8 va[C::OT][2];
+#pragma unroll
+        for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(base + v_off[t] + (16 * j) * C::ROWB));
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(base + v_off[t] + (16 * j + 8) * C::ROWB));
+            va[t][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        // online softmax (log2 domain)
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, sc[r]), sc[r + 1]);
+        mx = fmaxf(mx, sc[15]);
+        mx = pair_max(mx) * c_log2;
+        if (__ballot(mx > m_used + kTau) != 0ull) {
+          const float m_new = fmaxf(m_used, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+          l_part *= alpha;
+#pragma unroll
+          for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+          m_used = m_new;
+        }
+        // P^T as the B operand: k-step j covers registers 8j..8j+7, i.e. keys
+        // 16j + 8*(e/4) + 4*g + e%4 for slot e.  The row sum is kept in fp32
+        // from the unrounded probabilities (accurate log-sum-exp).
+        bf16x8 pb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], c_log2, -m_used));
+            l_part += p;
+            pb[j][e] = (__bf16)p;
+          }
+        // O^T (d x query) += V^T (d x key) P^T (key x query)
+#pragma unroll
+        for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t][j], pb[j], o[t], 0, 0, 0);
+      }
+      pc += n;
+    }
+    __syncthreads();   // every wave is done with the ring before it is reused
+
+    // ---- merge the two key halves, normalise, combine, store ----
+    const float l_row = pair_sum(l_part);
+    float* mbuf = reinterpret_cast<float*>(smem + grp * C::MERGE_G);                 // [qh][2 + NOV][64]
+    float* ost = reinterpret_cast<float*>(smem + 2 * C::MERGE_G + grp * C::OST_G);   // [64][OSTR]
+    if (kh == 1) {
+      float* b = mbuf + qh * (C::NOV + 2) * 64;
+      b[lane] = m_used;
+      b[64 + lane] = l_row;
 #pragma unroll
       for (int t = 0; t < C::OT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-      m_used = m_new;
+        for (int r = 0; r < 16; ++r) b[(2 + t * 16 + r) * 64 + lane] = o[t][r];
     }
-    // P^T as the B operand: k-step j covers registers 8j..8j+7, i.e. keys
-    // 16j + 8*(e/4) + 4*g + e%4 for slot e.
-    bf16x8 pb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * j + e], c_log2, -m_used));
-        l_part += p;
-        pb[j][e] = (__bf16)p;
-      }
-    }
-
-    // O^T (d x query) += V^T (d x key) P^T (key x query).  For k-step j the
-    // A operand of lane (g, d-row) holds keys base + 0..3 and base + 8..11
-    // with base = 32*kh + 16*j + 4*g: exactly the keys of pb[j]'s slots.
-#pragma unroll
-    for (int t = 0; t < C::OT; ++t) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int key0 = 32 * kh + 16 * j + 4 * g + (l16 >> 2);
-        const int col = 32 * t + 16 * h16 + 4 * (l16 & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbase + (key0 * C::VSTR + col) * 2));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbase + ((key0 + 8) * C::VSTR + col) * 2));
-        // concatenate as whole vectors (element-wise bf16 inserts are avoided)
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j], o[t], 0, 0, 0);
-      }
-    }
-
-    if (more) VSA_STASH(cur ^ 1);
     __syncthreads();
-  }
-
-#undef VSA_FETCH
-#undef VSA_STASH
-
-  // ---- merge the two key halves, normalise, combine, store ----
-  const float l_row = pair_sum(l_part);
-  float* mbuf = reinterpret_cast<float*>(smem);                      // [qh][2 + NOV][64]
-  float* ost = reinterpret_cast<float*>(smem + C::MERGE_BYTES);      // [64][OSTR]
-  if (kh == 1) {
-    float* b = mbuf + qh * (C::NOV + 2) * 64;
-    b[lane] = m_used;
-    b[64 + lane] = l_row;
+    if (kh == 0) {
+      const float* b = mbuf + qh * (C::NOV + 2) * 64;
+      const float m1 = b[lane], l1 = b[64 + lane];
+      const float m = fmaxf(m_used, m1);
+      const float a0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_used - m);
+      const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      const float l = l_row * a0 + l1 * a1;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* orow = ost + (32 * qh + n32) * C::OSTR;
 #pragma unroll
-    for (int t = 0; t < C::OT; ++t)
+      for (int t = 0; t < C::OT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) b[(2 + t * 16 + r) * 64 + lane] = o[t][r];
-  }
-  __syncthreads();
-  if (kh == 0) {
-    const float* b = mbuf + qh * (C::NOV + 2) * 64;
-    const float m1 = b[lane], l1 = b[64 + lane];
-    const float m = fmaxf(m_used, m1);
-    const float a0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_used - m);
-    const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-    const float l = l_row * a0 + l1 * a1;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* orow = ost + (32 * qh + n32) * C::OSTR;
-#pragma unroll
-    for (int t = 0; t < C::OT; ++t)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float4 w;
-        w.x = (o[t][4 * rq + 0] * a0 + b[(2 + t * 16 + 4 * rq + 0) * 64 + lane] * a1) * inv;
-        w.y = (o[t][4 * rq + 1] * a0 + b[(2 + t * 16 + 4 * rq + 1) * 64 + lane] * a1) * inv;
-        w.z = (o[t][4 * rq + 2] * a0 + b[(2 + t * 16 + 4 * rq + 2) * 64 + lane] * a1) * inv;
-        w.w = (o[t][4 * rq + 3] * a0 + b[(2 + t * 16 + 4 * rq + 3) * 64 + lane] * a1) * inv;
-        // d = 32*t + 8*rq + 4*g + 0..3
-        *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
+        for (int rq = 0; rq < 4; ++rq) {
+          float4 w;
+          w.x = (o[t][4 * rq + 0] * a0 + b[(2 + t * 16 + 4 * rq + 0) * 64 + lane] * a1) * inv;
+          w.y = (o[t][4 * rq + 1] * a0 + b[(2 + t * 16 + 4 * rq + 1) * 64 + lane] * a1) * inv;
+          w.z = (o[t][4 * rq + 2] * a0 + b[(2 + t * 16 + 4 * rq + 2) * 64 + lane] * a1) * inv;
+          w.w = (o[t][4 * rq + 3] * a0 + b[(2 + t * 16 + 4 * rq + 3) * 64 + lane] * a1) * inv;
+          // d = 32*t + 8*rq + 4*g + 0..3
+          *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
+        }
+      if (lse != nullptr && g == 0 && my_valid) {
+        const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+        lse[(rowA + grp) * kBlk + 32 * qh + n32] = val;
       }
-    if (lse != nullptr && g == 0) {
-      const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-      lse[wg * kBlk + 32 * qh + n32] = val;
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  const float* ocrow = oc ? oc + wg * (int64_t)D : nullptr;
+    if (my_valid) {
+      const int64_t my_row = rowA + grp;
+      const float* ocrow = oc ? oc + my_row * (int64_t)D : nullptr;
+      const int gt = tid & 255;   // thread index within the half
 #pragma unroll
-  for (int u = 0; u < C::LOADS; ++u) {
-    const int c = tid + u * kThreads;
-    const int row = c / C::CPR, col = c % C::CPR;
-    const int64_t gidx = head_off + (int64_t)(cube * kBlk + row) * D + col * 8;
-    float val[8];
-    const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
-    const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
-    val[0] = v0.x; val[1] = v0.y; val[2] = v0.z; val[3] = v0.w;
-    val[4] = v1.x; val[5] = v1.y; val[6] = v1.z; val[7] = v1.w;
-    if (gate_f != nullptr) {
-      float gf[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_f + gidx), gf);
+      for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
+        const int c = gt + u * 256;
+        const int row = c / C::CPR, col = c % C::CPR;
+        const int64_t gidx = head_off + (int64_t)(my_cube * kBlk + row) * D + col * 8;
+        float val[8];
+        const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
+        const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
+        val[0] = v0.x; val[1] = v0.y; val[2] = v0.z; val[3] = v0.w;
+        val[4] = v1.x; val[5] = v1.y; val[6] = v1.z; val[7] = v1.w;
+        if (gate_f != nullptr) {
+          float gf[8];
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_f + gidx), gf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] *= gf[e];
+          for (int e = 0; e < 8; ++e) val[e] *= gf[e];
+        }
+        if (gate_c != nullptr) {
+          float gc[8];
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_c + gidx), gc);
+          const float4 c0 = *reinterpret_cast<const float4*>(ocrow + col * 8);
+          const float4 c1 = *reinterpret_cast<const float4*>(ocrow + col * 8 + 4);
+          const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] = fmaf(gc[e], cv[e], val[e]);
+        }
+        uint4 packed;
+        packed.x = pack_bf16x2(val[0], val[1]);
+        packed.y = pack_bf16x2(val[2], val[3]);
+        packed.z = pack_bf16x2(val[4], val[5]);
+        packed.w = pack_bf16x2(val[6], val[7]);
+        *reinterpret_cast<uint4*>(out + gidx) = packed;
+      }
     }
-    if (gate_c != nullptr) {
-      float gc[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_c + gidx), gc);
-      const float4 c0 = *reinterpret_cast<const float4*>(ocrow + col * 8);
-      const float4 c1 = *reinterpret_cast<const float4*>(ocrow + col * 8 + 4);
-      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] = fmaf(gc[e], cv[e], val[e]);
-    }
-    uint4 packed;
-    packed.x = pack_bf16x2(val[0], val[1]);
-    packed.y = pack_bf16x2(val[2], val[3]);
-    packed.z = pack_bf16x2(val[4], val[5]);
-    packed.w = pack_bf16x2(val[6], val[7]);
-    *reinterpret_cast<uint4*>(out + gidx) = packed;
+    __syncthreads();   // staging reads done before the next pair reuses LDS
   }
 }
+
+// Per-device launch state: the CU count and the dynamic-LDS limit already
+// granted to each instantiation.
+struct DevState {
+  int cus = 0;
+  int lds_granted[2] = {0, 0};
+};
 
 template <int D>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                     const void* gate_f, void* out, float* lse, hipStream_t s) {
   using C = Cfg<D>;
-  auto kern = sparse_attn_fwd_kernel<D>;
-  // The dynamic-LDS limit is raised once per device.
-  static bool attr_set[64] = {};
+  static DevState dev_state[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
+  DevState& st = dev_state[dev];
+  auto kern = sparse_attn_fwd_kernel<D>;
+  // LDS: ring + schedule (+flags and two Nc-bit maps), or the epilogue buffers
+  const size_t nwords = (size_t)(g.Nc + 31) / 32;
+  const size_t sched = 4 * (((size_t)max_kv + 1) / 2 * 2) + 16 + 2 * 4 * nwords;
+  size_t lds = kRingBytes + sched;
+  if (lds < (size_t)C::EPI_BYTES) lds = C::EPI_BYTES;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const int di = D == 128 ? 1 : 0;
+  if (st.lds_granted[di] < (int)lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    st.lds_granted[di] = (int)lds;
   }
-  const int64_t total = g.BH * g.Nc;
+  if (st.cus == 0) {
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cus <= 0) return hipErrorInvalidDevice;
+    st.cus = cus;
+  }
+  const int64_t total_pairs = g.BH * ((g.Nc + 1) / 2);
+  // persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD)
+  int64_t grid = ((int64_t)st.cus + 7) / 8 * 8;
+  const int64_t need = (total_pairs + 7) / 8 * 8;
+  if (grid > need) grid = need;
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(kThreads), C::LDS_BYTES, s, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, lut, valid, max_kv, oc, (const __bf16*)gate_c,
-                     (const __bf16*)gate_f, (__bf16*)out, lse, (int)g.Nc, total, c_log2);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, lut, valid, max_kv, oc, (const __bf16*)gate_c, (const __bf16*)gate_f,
+                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2);
   return hipGetLastError();
 }
 
