@@ -121,6 +121,10 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
       : "memory", "m0");
 }
 
+__device__ __forceinline__ uint32_t pack_step(int ta, int tb) {
+  return (uint32_t)(ta < 0 ? 0xffff : ta) | ((uint32_t)(tb < 0 ? 0xffff : tb) << 16);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
@@ -165,10 +169,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // schedule: schedA[s], schedB[s] (int16 key cube ids, -1 = none) after the ring
-  int16_t* schedA = reinterpret_cast<int16_t*>(smem + kRingBytes);
-  int16_t* schedB = schedA + max_kv;
-  int* flags = reinterpret_cast<int*>(smem + kRingBytes + 4 * ((max_kv + 1) / 2 * 2));   // [0]: duplicate seen
+  // schedule after the ring: sched[s] packs the key cube of half A (low 16
+  // bits) and of half B (high 16 bits) of step s; 0xffff = none.
+  uint32_t* sched = reinterpret_cast<uint32_t*>(smem + kRingBytes);
+  int* flags = reinterpret_cast<int*>(sched + max_kv);   // [0] duplicate, [1] unsorted, [2] shared count
   uint32_t* bmA = reinterpret_cast<uint32_t*>(flags + 4);               // Nc-bit membership maps
   const int nwords = (Nc + 31) >> 5;
   uint32_t* bmB = bmA + nwords;
@@ -248,8 +252,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const int S = nA > nB ? nA : nB;   // steps
 
     // ---- build the step schedule -------------------------------------------
+    // Scratch for the build lives in the ring, which is idle until the first
+    // tile load below: SH = cubes both rows list, EXA / EXB = cubes only one
+    // row lists, PK = the sort key of each exclusive pair.
+    int* SH = reinterpret_cast<int*>(smem);
+    int* EXA = SH + max_kv;
+    int* EXB = EXA + max_kv;
+    int* PK = EXB + max_kv;
     for (int i = tid; i < 2 * nwords; i += kThreads) bmA[i] = 0u;
-    if (tid == 0) flags[0] = 0;
+    if (tid < 4) flags[tid] = 0;
     __syncthreads();
     for (int i = tid; i < nA + nB; i += kThreads) {
       const bool inA = i < nA;
@@ -257,60 +268,83 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       uint32_t* bm = inA ? bmA : bmB;
       const uint32_t bit = 1u << (c & 31);
       if (atomicOr(&bm[c >> 5], bit) & bit) flags[0] = 1;   // a row lists a cube twice
+      const int nrow = inA ? nA : nB;
+      const int idx = inA ? i : i - nA;
+      if (idx + 1 < nrow && clampc(inA ? lrowA[i + 1] : lrowB[idx + 1]) <= c) flags[1] = 1;   // not ascending
     }
     __syncthreads();
     const bool dup = flags[0] != 0;
+    const bool sorted = flags[1] == 0;
     if (dup) {
       // positional pairing: step s = (A[s], B[s])
-      for (int s = tid; s < S; s += kThreads) {
-        schedA[s] = (int16_t)(s < nA ? clampc(lrowA[s]) : -1);
-        schedB[s] = (int16_t)(s < nB ? clampc(lrowB[s]) : -1);
-      }
-    } else if (wave < 2) {
-      // wave 0 walks row A (shared and A-only cubes), wave 1 row B (B-only
-      // cubes).  Shared cubes take steps 0..nS-1 in row order; the others
-      // take steps nS.. in row order.
-      const int n_me = wave == 0 ? nA : nB;
-      const int32_t* row = wave == 0 ? lrowA : lrowB;
-      const uint32_t* other = wave == 0 ? bmB : bmA;
-      int16_t* mine = wave == 0 ? schedA : schedB;
-      const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-      int n_sh = 0;   // shared cubes in this row (the same set for both rows)
-      for (int base = 0; base < n_me; base += 64) {
-        const int i = base + lane;
-        bool sh = false;
-        if (i < n_me) {
-          const int c = clampc(row[i]);
-          sh = (other[c >> 5] >> (c & 31)) & 1u;
-        }
-        n_sh += __popcll(__ballot(sh));
-      }
-      int sh_seen = 0, ex_seen = 0;
-      for (int base = 0; base < n_me; base += 64) {
-        const int i = base + lane;
-        const bool in = i < n_me;
-        int c = 0;
-        bool sh = false;
-        if (in) {
-          c = clampc(row[i]);
-          sh = (other[c >> 5] >> (c & 31)) & 1u;
-        }
-        const uint64_t msh = __ballot(in && sh), mex = __ballot(in && !sh);
-        if (in) {
-          if (sh) {
-            if (wave == 0) {
-              const int s = sh_seen + __popcll(msh & lt);
-              schedA[s] = (int16_t)c;
-              schedB[s] = (int16_t)c;
-            }
-          } else {
-            mine[n_sh + ex_seen + __popcll(mex & lt)] = (int16_t)c;
+      for (int s = tid; s < S; s += kThreads)
+        sched[s] = pack_step(s < nA ? clampc(lrowA[s]) : -1, s < nB ? clampc(lrowB[s]) : -1);
+    } else {
+      // wave 0 splits row A into shared / A-only cubes, wave 1 row B into
+      // B-only cubes (row order kept; ranks from wavefront ballots).
+      if (wave < 2) {
+        const int n_me = wave == 0 ? nA : nB;
+        const int32_t* row = wave == 0 ? lrowA : lrowB;
+        const uint32_t* other = wave == 0 ? bmB : bmA;
+        int* ex = wave == 0 ? EXA : EXB;
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        int sh_seen = 0, ex_seen = 0;
+        for (int base = 0; base < n_me; base += 64) {
+          const int i = base + lane;
+          const bool in = i < n_me;
+          int c = 0;
+          bool sh = false;
+          if (in) {
+            c = clampc(row[i]);
+            sh = (other[c >> 5] >> (c & 31)) & 1u;
           }
+          const uint64_t msh = __ballot(in && sh), mex = __ballot(in && !sh);
+          if (in) {
+            if (!sh) ex[ex_seen + __popcll(mex & lt)] = c;
+            else if (wave == 0) SH[sh_seen + __popcll(msh & lt)] = c;
+          }
+          sh_seen += __popcll(msh);
+          ex_seen += __popcll(mex);
         }
-        sh_seen += __popcll(msh);
-        ex_seen += __popcll(mex);
+        if (lane == 0 && wave == 0) flags[2] = sh_seen;
       }
-      for (int s = n_sh + ex_seen + lane; s < S; s += 64) mine[s] = (int16_t)-1;
+      __syncthreads();
+      const int nS = flags[2];
+      const int nExA = nA - nS, nExB = nB - nS;
+      const int nP = nExA > nExB ? nExA : nExB;   // exclusive steps; nS + nP == S
+      for (int i = tid; i < nP; i += kThreads) {
+        const int ka = i < nExA ? EXA[i] : 0x7fffffff;
+        const int kb = i < nExB ? EXB[i] : 0x7fffffff;
+        PK[i] = ka < kb ? ka : kb;
+      }
+      __syncthreads();
+      if (sorted) {
+        // Merge the shared cubes and the exclusive pairs into one ascending
+        // order of key cube index, so that the workgroups of an XCD sweep the
+        // key cubes together.  Both lists are ascending and never share a
+        // value, so rank-by-binary-search gives a bijection onto [0, S).
+        auto count_below = [](const int* a, int n, int x) {   // #{a[j] < x}, a ascending
+          int lo = 0, hi = n;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (a[mid] < x) lo = mid + 1; else hi = mid;
+          }
+          return lo;
+        };
+        for (int g2 = tid; g2 < nS; g2 += kThreads) {
+          const int pos = g2 + count_below(PK, nP, SH[g2]);
+          sched[pos] = pack_step(SH[g2], SH[g2]);
+        }
+        for (int i = tid; i < nP; i += kThreads) {
+          const int pos = i + count_below(SH, nS, PK[i]);
+          sched[pos] = pack_step(i < nExA ? EXA[i] : -1, i < nExB ? EXB[i] : -1);
+        }
+      } else {
+        // any order is exact: shared cubes first, then the exclusive pairs
+        for (int g2 = tid; g2 < nS; g2 += kThreads) sched[g2] = pack_step(SH[g2], SH[g2]);
+        for (int i = tid; i < nP; i += kThreads)
+          sched[nS + i] = pack_step(i < nExA ? EXA[i] : -1, i < nExB ? EXB[i] : -1);
+      }
     }
 
     // Q of this half's cube as the B operand: query 32*qh + n32, d = 16*s + 8*g + 0..7
@@ -325,9 +359,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     wait_vmem<0>();
     __syncthreads();   // schedule complete; bitmaps no longer needed
 
-    auto tiles_of = [&](int s, int& ta, int& tb) {
-      ta = __builtin_amdgcn_readfirstlane((int)schedA[s]);
-      tb = __builtin_amdgcn_readfirstlane((int)schedB[s]);
+    // Steps are read from registers: lane j of sv0 / sv1 holds step
+    // win + j / win + 64 + j.  The window moves by 64 steps when the compute
+    // step leaves its first half; the issue pointer runs at most R steps
+    // ahead, so it always stays inside the window.
+    int win = 0;
+    uint32_t sv0 = lane < S ? sched[lane] : 0xffffffffu;
+    uint32_t sv1 = 64 + lane < S ? sched[64 + lane] : 0xffffffffu;
+    auto tiles_of = [&](int st, int& ta, int& tb) {
+      const int rel = st - win;
+      const uint32_t e = rel < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)sv0, rel)
+                                  : (uint32_t)__builtin_amdgcn_readlane((int)sv1, rel - 64);
+      ta = (e & 0xffffu) == 0xffffu ? -1 : (int)(e & 0xffffu);
+      tb = (e >> 16) == 0xffffu ? -1 : (int)(e >> 16);
       return (ta >= 0 ? 1 : 0) + ((tb >= 0 && tb != ta) ? 1 : 0);
     };
     auto load_tile = [&](int blk, int pos) {
@@ -364,6 +408,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     float l_part = 0.f;        // this lane's partial row sum
 
     for (int s = 0; s < S; ++s) {
+      if (s - win == 64) {   // slide the register window by 64 steps
+        win += 64;
+        sv0 = sv1;
+        sv1 = win + 64 + lane < S ? sched[win + 64 + lane] : 0xffffffffu;
+      }
       int ta, tb;
       const int n = tiles_of(s, ta, tb);
       // this step's tiles must have landed for every wave; later ones may fly
