@@ -60,17 +60,16 @@ typedef const __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBlk = 64;          // tokens per cube: query tile and key tile
 constexpr int kThreads = 512;     // two query cubes x 4 wavefronts
+constexpr int kIssueThreads = 256;   // the four wavefronts of half A issue every tile load
 constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
-constexpr int kRingBytes = 128 * 1024;
+constexpr float kNegBig = -1.0e30f;   // initial exponent offset
 
 template <int D>
 struct Cfg {
   static constexpr int ROWB = D * 2;                 // bytes per token row
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int TILE = kBlk * ROWB;           // one K or V cube tile
-  static constexpr int LOADS = TILE / (kThreads * 16);  // 16-byte loads per wave per tile
-  static constexpr int R = kRingBytes / (2 * TILE);  // ring positions (one K + one V tile each)
-  static constexpr int V_BASE = R * TILE;
+  static constexpr int LOADS = TILE / (kIssueThreads * 16);  // 16-byte loads per issuing wave per tile
   static constexpr int OT = D / 32;                  // 32-row tiles of O^T
   static constexpr int NOV = OT * 16;                // O^T accumulators per lane
   static constexpr int MERGE_G = 2 * (NOV + 2) * 64 * 4;   // merge buffer of one half
@@ -112,6 +111,9 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& raw, float* f) {
 // does not track these LDS writes; completion is enforced explicitly
 // (wait_vmem + barrier) before any wave reads the slot.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  // M0 must come from a scalar register: force the (wave-uniform) address
+  // there even where the compiler kept it in a vector register.
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -145,34 +147,55 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until at most `tiles` tiles' worth of this wave's loads (2*L load
-// instructions per tile: K and V) are still pending.
+// Wait until at most `parts` K or V tiles' worth of this wave's loads (L load
+// instructions per tile) are still pending.  Counts beyond the field width
+// or the cases below wait for fewer pending loads, which is merely
+// conservative.
+template <int N>
+__device__ __forceinline__ void wait_vmem_capped() {
+  wait_vmem<(N < 63 ? N : 63)>();
+}
+
 template <int L>
-__device__ __forceinline__ void wait_tiles(int tiles) {
-  switch (tiles) {
+__device__ __forceinline__ void wait_parts(int parts) {
+  switch (parts) {
     case 0: wait_vmem<0>(); break;
-    case 1: wait_vmem<2 * L>(); break;
-    case 2: wait_vmem<4 * L>(); break;
-    case 3: wait_vmem<6 * L>(); break;
-    case 4: wait_vmem<8 * L>(); break;
-    case 5: wait_vmem<10 * L>(); break;
-    case 6: wait_vmem<12 * L>(); break;
-    default: wait_vmem<14 * L>(); break;
+    case 1: wait_vmem_capped<1 * L>(); break;
+    case 2: wait_vmem_capped<2 * L>(); break;
+    case 3: wait_vmem_capped<3 * L>(); break;
+    case 4: wait_vmem_capped<4 * L>(); break;
+    case 5: wait_vmem_capped<5 * L>(); break;
+    case 6: wait_vmem_capped<6 * L>(); break;
+    case 7: wait_vmem_capped<7 * L>(); break;
+    case 8: wait_vmem_capped<8 * L>(); break;
+    case 9: wait_vmem_capped<9 * L>(); break;
+    case 10: wait_vmem_capped<10 * L>(); break;
+    case 11: wait_vmem_capped<11 * L>(); break;
+    case 12: wait_vmem_capped<12 * L>(); break;
+    case 13: wait_vmem_capped<13 * L>(); break;
+    case 14: wait_vmem_capped<14 * L>(); break;
+    case 15: wait_vmem_capped<15 * L>(); break;
+    default: wait_vmem_capped<16 * L>(); break;
   }
 }
 
-template <int D>
+// RK / RV: positions of the K and V tile rings.
+template <int D, int RK, int RV>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
     const float* __restrict__ oc, const __bf16* __restrict__ gate_c, const __bf16* __restrict__ gate_f,
     __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2) {
   using C = Cfg<D>;
+  constexpr int V_BASE = RK * C::TILE;           // V ring after the K ring
+  constexpr int RING = (RK + RV) * C::TILE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // schedule after the ring: sched[s] packs the key cube of half A (low 16
   // bits) and of half B (high 16 bits) of step s; 0xffff = none.
-  uint32_t* sched = reinterpret_cast<uint32_t*>(smem + kRingBytes);
-  int* flags = reinterpret_cast<int*>(sched + max_kv);   // [0] duplicate, [1] unsorted, [2] shared count
+  uint32_t* sched = reinterpret_cast<uint32_t*>(smem + RING);
+  // plan[s] = kpos(s) | F(s) << 16, s = 0..S+1 (see the load plan below)
+  uint32_t* plan = sched + max_kv;
+  int* flags = reinterpret_cast<int*>(plan + max_kv + 2);   // [0] duplicate, [1] unsorted, [2] shared count
   uint32_t* bmA = reinterpret_cast<uint32_t*>(flags + 4);               // Nc-bit membership maps
   const int nwords = (Nc + 31) >> 5;
   uint32_t* bmB = bmA + nwords;
@@ -187,17 +210,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   const int l16 = lane & 15, h16 = (lane >> 4) & 1;
 
   // ---- per-lane constant offsets ------------------------------------------
-  // Direct loads: lane i of load n of wave w fills LDS chunk L = (w*LOADS+n)*64+i
-  // of a tile, which holds logical chunk (L % CPR) ^ f(row) of row L / CPR.
+  // Direct loads (issued by half A only): lane i of load n of wave w fills
+  // LDS chunk L = (w*LOADS+n)*64+i of a tile, which holds logical chunk
+  // (L % CPR) ^ f(row) of row L / CPR.
   uint32_t kg_off[C::LOADS], vg_off[C::LOADS];
 #pragma unroll
   for (int n = 0; n < C::LOADS; ++n) {
-    const int L = (wave * C::LOADS + n) * 64 + lane;
+    const int L = ((wave & 3) * C::LOADS + n) * 64 + lane;
     const int r = L / C::CPR, x = L % C::CPR;
     kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16);
     vg_off[n] = r * C::ROWB + ((x ^ C::vswz(r)) * 16);
   }
-  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * C::LOADS * 1024));
+  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)((wave & 3) * C::LOADS * 1024));
   // K A-operand reads: key row 32*kh + n32, logical chunk 2*ks + g.
   int k_off[D / 16];
   {
@@ -216,14 +240,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
 #pragma unroll
     for (int t = 0; t < C::OT; ++t) {
       const int b = 64 * t + byte_base;
-      v_off[t] = C::V_BASE + r * C::ROWB + ((((b >> 4) ^ C::vswz(r)) << 4) | (b & 15));
+      v_off[t] = V_BASE + r * C::ROWB + ((((b >> 4) ^ C::vswz(r)) << 4) | (b & 15));
     }
   }
-
-  // The two halves share every SIMD (waves w and w+4) and meet at the same
-  // barrier each step.  Half A runs at a higher issue priority, so it leads
-  // each phase: its exponentials then overlap half B's MFMAs and vice versa.
-  if (grp == 0) __builtin_amdgcn_s_setprio(1);
 
   const int pairs_per_head = (Nc + 1) >> 1;
   const int64_t per_xcd = (total_pairs + 7) / 8;
@@ -359,88 +378,175 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     wait_vmem<0>();
     __syncthreads();   // schedule complete; bitmaps no longer needed
 
-    // Steps are read from registers: lane j of sv0 / sv1 holds step
-    // win + j / win + 64 + j.  The window moves by 64 steps when the compute
-    // step leaves its first half; the issue pointer runs at most R steps
-    // ahead, so it always stays inside the window.
+    // ---- load plan ----------------------------------------------------------
+    // Ring positions are assigned to tiles in step order: step s owns
+    // positions kpos(s) .. kpos(s + 1) - 1, its A tile (if any) first, then
+    // its B tile if that differs.  kpos(s) = tiles of steps < s, for
+    // s = 0..S + 1 (kpos(S + 1) = kpos(S)).
+    if (wave == 0) {
+      const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int carry = 0;
+      for (int base = 0; base <= S; base += 64) {
+        const int st = base + lane;
+        int n = 0;
+        if (st < S) {
+          const uint32_t e = sched[st];
+          const uint32_t a = e & 0xffffu, b = e >> 16;
+          n = (a != 0xffffu ? 1 : 0) + ((b != 0xffffu && b != a) ? 1 : 0);
+        }
+        const uint64_t b1 = __ballot(n >= 1), b2 = __ballot(n == 2);
+        if (st <= S) plan[st] = (uint32_t)(carry + __popcll(b1 & lt) + __popcll(b2 & lt));
+        carry += __popcll(b1) + __popcll(b2);
+      }
+      if (lane == 0) plan[S + 1] = (uint32_t)carry;
+    }
+    __syncthreads();
+    // Load group g = the K tiles of step g and the V tiles of step g - 1 (V
+    // is consumed one step after K).  At step barrier p the K positions of
+    // steps < p and the V positions of steps < p - 1 are free, so group g
+    // may be in flight once kpos(g + 1) <= kpos(p) + RK and
+    // kpos(g) <= kpos(p - 1) + RV.  F(p) = the last such group (<= S);
+    // F(p - 1) >= p, so group p is always in flight by barrier p.
+    {
+      int* fscr = reinterpret_cast<int*>(smem);   // the ring is idle until the first load
+      for (int pp = tid; pp <= S; pp += kThreads) {
+        const int kcap = (int)plan[pp] + RK;
+        const int vcap = (pp > 0 ? (int)plan[pp - 1] : 0) + RV;
+        int glo = 0, ghi = S;   // group 0 always fits
+        while (glo < ghi) {
+          const int mid = (glo + ghi + 1) >> 1;
+          if ((int)plan[mid + 1] <= kcap && (int)plan[mid] <= vcap) glo = mid; else ghi = mid - 1;
+        }
+        fscr[pp] = glo;
+      }
+      __syncthreads();
+      for (int pp = tid; pp <= S; pp += kThreads) plan[pp] |= (uint32_t)fscr[pp] << 16;
+      __syncthreads();
+    }
+
+    // Steps and plan entries are read from registers: lane j of sv0 / sv1
+    // (pv0 / pv1) holds entry win + j / win + 64 + j.  The window moves by 64
+    // when the main loop leaves its first half; loads run at most RK + 1
+    // steps ahead, so every read stays inside it.
     int win = 0;
     uint32_t sv0 = lane < S ? sched[lane] : 0xffffffffu;
     uint32_t sv1 = 64 + lane < S ? sched[64 + lane] : 0xffffffffu;
-    auto tiles_of = [&](int st, int& ta, int& tb) {
-      const int rel = st - win;
-      const uint32_t e = rel < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)sv0, rel)
-                                  : (uint32_t)__builtin_amdgcn_readlane((int)sv1, rel - 64);
-      ta = (e & 0xffffu) == 0xffffu ? -1 : (int)(e & 0xffffu);
-      tb = (e >> 16) == 0xffffu ? -1 : (int)(e >> 16);
-      return (ta >= 0 ? 1 : 0) + ((tb >= 0 && tb != ta) ? 1 : 0);
+    uint32_t pv0 = lane <= S + 1 ? plan[lane] : 0u;
+    uint32_t pv1 = 64 + lane <= S + 1 ? plan[64 + lane] : 0u;
+    auto rd = [&](uint32_t w0, uint32_t w1, int idx) -> uint32_t {
+      const int rel = idx - win;
+      return rel < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)w0, rel)
+                      : (uint32_t)__builtin_amdgcn_readlane((int)w1, rel - 64);
     };
-    auto load_tile = [&](int blk, int pos) {
-      const uint32_t slot_off = (uint32_t)((pos % C::R) * C::TILE);
-      const char* ks = uniform_ptr(k_head + (int64_t)blk * C::TILE);
-      const char* vs = uniform_ptr(v_head + (int64_t)blk * C::TILE);
+    auto load_k = [&](uint32_t blk, int pos) {
+      const uint32_t slot_off = (uint32_t)((pos % RK) * C::TILE);
+      const char* src = uniform_ptr(k_head + (int64_t)blk * C::TILE);
 #pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) {
-        dma16(ks, kg_off[n], lds_ring + slot_off + n * 1024);
-        dma16(vs, vg_off[n], lds_ring + C::V_BASE + slot_off + n * 1024);
+      for (int n = 0; n < C::LOADS; ++n) dma16(src, kg_off[n], lds_ring + slot_off + n * 1024);
+    };
+    auto load_v = [&](uint32_t blk, int pos) {
+      const uint32_t slot_off = (uint32_t)(V_BASE + (pos % RV) * C::TILE);
+      const char* src = uniform_ptr(v_head + (int64_t)blk * C::TILE);
+#pragma unroll
+      for (int n = 0; n < C::LOADS; ++n) dma16(src, vg_off[n], lds_ring + slot_off + n * 1024);
+    };
+    // Issue state (half A): next group gi, kpos(gi), kpos(gi - 1), and the
+    // tiles of step gi - 1 (whose V part belongs to group gi).
+    int gi = 0, i_kg = 0, i_kgm1 = 0;
+    uint32_t i_e = 0xffffffffu;
+    auto issue_to = [&](int last) {
+      for (; gi <= last; ++gi) {
+        const int kg1 = (int)(rd(pv0, pv1, gi + 1) & 0xffffu);
+        const uint32_t e = gi < S ? rd(sv0, sv1, gi) : 0xffffffffu;
+        if (kg1 > i_kg) {
+          const uint32_t a = e & 0xffffu, b = e >> 16;
+          load_k(a != 0xffffu ? a : b, i_kg);
+          if (kg1 - i_kg == 2) load_k(b, i_kg + 1);
+        }
+        if (i_kg > i_kgm1) {
+          const uint32_t a = i_e & 0xffffu, b = i_e >> 16;
+          load_v(a != 0xffffu ? a : b, i_kgm1);
+          if (i_kg - i_kgm1 == 2) load_v(b, i_kgm1 + 1);
+        }
+        i_kgm1 = i_kg;
+        i_kg = kg1;
+        i_e = e;
       }
     };
-    // issue pointer (step si at ring position pi) and compute position pc
-    int si = 0, pi = 0, pc = 0;
-    auto issue_ahead = [&]() {
-      while (si < S) {
-        int ta, tb;
-        const int n = tiles_of(si, ta, tb);
-        if (pi + n > pc + C::R) break;
-        if (ta >= 0) load_tile(ta, pi);
-        if (tb >= 0 && tb != ta) load_tile(tb, pi + (ta >= 0 ? 1 : 0));
-        pi += n;
-        ++si;
-      }
-    };
-    issue_ahead();
+    if (grp == 0) issue_to((int)(rd(pv0, pv1, 0) >> 16));
 
     f32x16 o[C::OT];
 #pragma unroll
     for (int t = 0; t < C::OT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-    float m_used = -INFINITY;  // log2-domain offset used for exponentiation
+    // Exponent offset (log2 units).  It starts at a large finite negative
+    // value rather than -inf so that offset arithmetic never forms inf - inf;
+    // the first real block always moves it (exp2 of the difference is 0).
+    float m_used = kNegBig;
     float l_part = 0.f;        // this lane's partial row sum
+    f32x16 sc;                 // scores of the previous step: keys 32*kh + 8*(r/4) + 4*g + r%4, query n32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    float mx_prev = kNegBig;   // their row max (log2 units)
 
-    for (int s = 0; s < S; ++s) {
-      if (s - win == 64) {   // slide the register window by 64 steps
+    // Step barrier p: every wave has finished iteration p - 1.  Half A waits
+    // for its loads of group p (K of step p, V of step p - 1), the barrier
+    // publishes them, and half A issues the groups that became free.
+    uint32_t e_c = 0xffffffffu, e_p = 0xffffffffu;   // tiles of steps p and p - 1
+    int kc = 0, vc = 0;                                 // kpos(p), kpos(p - 1)
+    auto step_barrier = [&](int p) {
+      if (p - win == 64) {   // slide the register windows by 64 entries
         win += 64;
         sv0 = sv1;
         sv1 = win + 64 + lane < S ? sched[win + 64 + lane] : 0xffffffffu;
+        pv0 = pv1;
+        pv1 = win + 64 + lane <= S + 1 ? plan[win + 64 + lane] : 0u;
       }
-      int ta, tb;
-      const int n = tiles_of(s, ta, tb);
-      // this step's tiles must have landed for every wave; later ones may fly
-      wait_tiles<C::LOADS>(pi - (pc + n));
+      e_p = e_c;
+      vc = kc;
+      const uint32_t w = rd(pv0, pv1, p);
+      kc = (int)(w & 0xffffu);
+      e_c = p < S ? rd(sv0, sv1, p) : 0xffffffffu;
+      if (grp == 0) {
+        const int kp1 = (int)(rd(pv0, pv1, p + 1) & 0xffffu);
+        wait_parts<C::LOADS>((i_kg - kp1) + (i_kgm1 - kc));
+      }
       __syncthreads();
-      issue_ahead();   // positions before pc are free: every wave finished step s-1
+      if (grp == 0) issue_to((int)(w >> 16));
+    };
 
-      const int mine = grp == 0 ? ta : tb;
-      if (mine >= 0) {
-        const int slot = (grp == 1 && ta >= 0 && tb != ta) ? (pc + 1) % C::R : pc % C::R;
-        const char* base = smem + slot * C::TILE;
-        // All K operand reads are issued before the first MFMA so that their
-        // LDS latencies overlap instead of adding up.
-        bf16x8 ka[D / 16];
+    // Iteration p, software pipelined within each wave: QK of step p runs on
+    // the matrix cores while the exponentials of step p - 1 run on the vector
+    // ALU, then PV of step p - 1 runs while the row max of step p is formed.
+    // The MFMAs are unconditional (one code path keeps every accumulator in
+    // one register set): a missing tile has zero operands, and a missing
+    // previous step is exponentiated with an infinite offset, giving P = 0.
+    for (int p = 0; p <= S; ++p) {
+      step_barrier(p);
+      const uint32_t ac = e_c & 0xffffu, bc = e_c >> 16;   // step p
+      const uint32_t ap = e_p & 0xffffu, bp = e_p >> 16;   // step p - 1
+      const bool has_c = (grp == 0 ? ac : bc) != 0xffffu;  // this half has a tile in step p
+      const bool has_p = (grp == 0 ? ap : bp) != 0xffffu;  // ... in step p - 1
+      bf16x8 ka[D / 16];
+      bf16x8 va[C::OT][2];
+      if (has_c) {
+        const int pos = kc + ((grp == 1 && ac != 0xffffu && bc != ac) ? 1 : 0);
+        const char* base = smem + (pos % RK) * C::TILE;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(base + k_off[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        // S^T tile: keys 32*kh + (8*(r/4) + 4*g + r%4), query n32
-        f32x16 sc;
+      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+        for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sc, 0, 0, 0);
-        // V^T operands do not depend on the softmax: read them now, so their
-        // latency hides behind the exponentials.  For k-step j the A operand
-        // of lane (g, d-row) holds keys base + 0..3 and base + 8..11 with
-        // base = 32*kh + 16*j + 4*g: exactly the keys of pb[j]'s slots.
-        bf16x8 va[C::OT][2];
+          for (int e = 0; e < 8; ++e) ka[ks][e] = (__bf16)0.f;
+      }
+      if (has_p) {
+        // For k-step j the A operand of lane (g, d-row) holds keys base +
+        // 0..3 and base + 8..11 with base = 32*kh + 16*j + 4*g: exactly the
+        // keys of pb[j]'s slots.
+        const int pos = vc + ((grp == 1 && ap != 0xffffu && bp != ap) ? 1 : 0);
+        const char* base = smem + (pos % RV) * C::TILE;   // v_off includes the V ring base
 #pragma unroll
         for (int t = 0; t < C::OT; ++t)
 #pragma unroll
@@ -451,41 +557,63 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
                 (lds_i16x4*)(base + v_off[t] + (16 * j + 8) * C::ROWB));
             va[t][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-        // online softmax (log2 domain)
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, sc[r]), sc[r + 1]);
-        mx = fmaxf(mx, sc[15]);
-        mx = pair_max(mx) * c_log2;
-        if (__ballot(mx > m_used + kTau) != 0ull) {
-          const float m_new = fmaxf(m_used, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
-          l_part *= alpha;
-#pragma unroll
-          for (int t = 0; t < C::OT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-          m_used = m_new;
-        }
-        // P^T as the B operand: k-step j covers registers 8j..8j+7, i.e. keys
-        // 16j + 8*(e/4) + 4*g + e%4 for slot e.  The row sum is kept in fp32
-        // from the unrounded probabilities (accurate log-sum-exp).
-        bf16x8 pb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], c_log2, -m_used));
-            l_part += p;
-            pb[j][e] = (__bf16)p;
-          }
-        // O^T (d x query) += V^T (d x key) P^T (key x query)
+      } else {
 #pragma unroll
         for (int t = 0; t < C::OT; ++t)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t][j], pb[j], o[t], 0, 0, 0);
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) va[t][j][e] = (__bf16)0.f;
       }
-      pc += n;
+      // Lazy rescale for step p - 1: the offset only moves when the block max
+      // exceeds it by more than kTau.  o already holds PV of step p - 2.
+      if (has_p && __ballot(mx_prev > m_used + kTau) != 0ull) {
+        const float m_new = fmaxf(m_used, mx_prev);
+        const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        m_used = m_new;
+      }
+      const float m_off = has_p ? m_used : INFINITY;
+
+      // QK(p) with the exponentials of step p - 1.  P^T is the B operand:
+      // k-step j covers registers 8j..8j+7, i.e. keys 16j + 8*(e/4) + 4*g +
+      // e%4 for slot e.  The row sum is kept in fp32 from the unrounded
+      // probabilities (accurate log-sum-exp).
+      constexpr int NQK = D / 16;          // QK MFMAs per step
+      constexpr int EPM = 16 / NQK;        // exponentials per MFMA
+      f32x16 sn;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i], sn, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < EPM; ++u) {
+          const int e = i * EPM + u;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sc[e], c_log2, -m_off));
+          l_part += pr;
+          pb[e >> 3][e & 7] = (__bf16)pr;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // PV(p-1) with the row max of step p.
+      float mx = kNegBig;
+#pragma unroll
+      for (int i = 0; i < 2 * C::OT; ++i) {
+        const int t = i % C::OT, j = i / C::OT;
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t][j], pb[j], o[t], 0, 0, 0);
+        constexpr int MPM = 16 / (2 * C::OT);   // max inputs per MFMA
+#pragma unroll
+        for (int u = 0; u < MPM; ++u) mx = fmaxf(mx, sn[i * MPM + u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mx_prev = pair_max(mx) * c_log2;
+      sc = sn;
     }
     __syncthreads();   // every wave is done with the ring before it is reused
 
@@ -576,30 +704,28 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
 // granted to each instantiation.
 struct DevState {
   int cus = 0;
-  int lds_granted[2] = {0, 0};
+  int lds_granted[4] = {0, 0, 0, 0};
 };
 
-template <int D>
-hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
-                    const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
-                    const void* gate_f, void* out, float* lse, hipStream_t s) {
+constexpr int kLdsMax = 160 * 1024;
+
+template <int D, int RK, int RV>
+hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
+                       const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
+                       const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot) {
   using C = Cfg<D>;
   static DevState dev_state[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   DevState& st = dev_state[dev];
-  auto kern = sparse_attn_fwd_kernel<D>;
-  // LDS: ring + schedule (+flags and two Nc-bit maps), or the epilogue buffers
-  const size_t nwords = (size_t)(g.Nc + 31) / 32;
-  const size_t sched = 4 * (((size_t)max_kv + 1) / 2 * 2) + 16 + 2 * 4 * nwords;
-  size_t lds = kRingBytes + sched;
+  auto kern = sparse_attn_fwd_kernel<D, RK, RV>;
+  size_t lds = (size_t)(RK + RV) * C::TILE + sched_bytes;
   if (lds < (size_t)C::EPI_BYTES) lds = C::EPI_BYTES;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const int di = D == 128 ? 1 : 0;
-  if (st.lds_granted[di] < (int)lds) {
+  if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
+  if (st.lds_granted[slot] < (int)lds) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    st.lds_granted[di] = (int)lds;
+    st.lds_granted[slot] = (int)lds;
   }
   if (st.cus == 0) {
     int cus = 0;
@@ -620,7 +746,47 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   return hipGetLastError();
 }
 
+// LDS after the tile ring: step list, load plan, flags and two Nc-bit maps.
+size_t sched_bytes(const Geom& g, int max_kv) {
+  const size_t nwords = (size_t)(g.Nc + 31) / 32;
+  return 4 * (size_t)max_kv + 4 * ((size_t)max_kv + 2) + 16 + 2 * 4 * nwords;
+}
+
+constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8 at d = 64
+
+// The deeper ring is used whenever the schedule (and the schedule build's
+// scratch, which lives in the ring) fits beside it in LDS.
+template <int D>
+hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
+                    const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
+                    const void* gate_f, void* out, float* lse, hipStream_t s) {
+  using C = Cfg<D>;
+  constexpr int RK_DEEP = D == 128 ? 5 : 10, RV_DEEP = D == 128 ? 4 : 8;
+  constexpr int R_BASE = D == 128 ? 4 : 8;
+  static_assert((size_t)2 * R_BASE * C::TILE == kBaseRingBytes, "base ring size");
+  if (!sparse_attn_fwd_fits(g, max_kv)) return hipErrorInvalidValue;
+  const size_t sched = sched_bytes(g, max_kv);
+  const size_t build_scratch = 16 * (size_t)max_kv;   // SH, EXA, EXB, PK
+  const int base_slot = D == 128 ? 2 : 0;
+  if ((size_t)(RK_DEEP + RV_DEEP) * C::TILE + sched <= (size_t)kLdsMax &&
+      build_scratch <= (size_t)(RK_DEEP + RV_DEEP) * C::TILE)
+    return launch_ring<D, RK_DEEP, RV_DEEP>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
+                                            sched, base_slot);
+  if (build_scratch > (size_t)(2 * R_BASE) * C::TILE) return hipErrorInvalidValue;
+  return launch_ring<D, R_BASE, R_BASE>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, sched,
+                                        base_slot + 1);
+}
+
 }  // namespace
+
+// Cube ids and ring positions are 16-bit fields of the step list and the
+// load plan, and the per-pair schedule must fit in LDS beside the base ring
+// (its build scratch, 16 bytes per entry, lives in the ring).
+bool sparse_attn_fwd_fits(const Geom& g, int max_kv) {
+  if (g.Nc < 1 || g.Nc > 0xfffe || max_kv < 1 || max_kv > 0x7fff) return false;
+  if (kBaseRingBytes + sched_bytes(g, max_kv) > (size_t)kLdsMax) return false;
+  return 16 * (size_t)max_kv <= kBaseRingBytes;
+}
 
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,

@@ -129,6 +129,7 @@ int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, cons
   const Geom g = vsa::make_geom(*p);
   if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
   if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  if (!vsa::sparse_attn_fwd_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
   return hip_status(vsa::launch_sparse_attn_fwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc,
                                                 gate_c, gate_f, out, lse, (hipStream_t)stream));
 }

@@ -41,6 +41,8 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, 
 hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
                               const float* vc, int32_t* lut, int32_t* valid, float* oc,
                               hipStream_t s);
+// Whether the fine kernel handles this cube count and LUT row length.
+bool sparse_attn_fwd_fits(const Geom& g, int max_kv);
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,

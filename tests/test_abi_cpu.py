@@ -130,6 +130,11 @@ def test_sparse_attn_errors():
     assert call(prob=_prob(ct=2, ch=2, cw=2)) == L.VSA_ERR_UNSUPPORTED   # cube volume 8
     assert call(prob=_prob(head_dim=32)) == L.VSA_ERR_UNSUPPORTED
     assert call(prob=_prob(T=5)) == L.VSA_ERR_SHAPE
+    # 16-bit cube ids: Nc = 65536 is beyond the fine kernel
+    assert call(prob=_prob(T=4, H=4, W=4 * 65536)) == L.VSA_ERR_UNSUPPORTED
+    # the per-row schedule must fit beside the tile ring in LDS (Nc = 4096)
+    big = _prob(T=64, H=64, W=64)
+    assert call(prob=big, maxkv=4000) == L.VSA_ERR_UNSUPPORTED
 
 
 def test_check_lut_errors():
