@@ -148,35 +148,27 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // Wait until at most `parts` K or V tiles' worth of this wave's loads (L load
-// instructions per tile) are still pending.  Counts beyond the field width
-// or the cases below wait for fewer pending loads, which is merely
-// conservative.
+// instructions per tile) are still pending.  The waits run from the loosest
+// to the tightest and stop at `parts`: a wait that is already satisfied costs
+// almost nothing, and the chain has no taken branch before its exit.  Counts
+// beyond MAXP (or the field width) wait for fewer pending loads, which is
+// merely conservative.
 template <int N>
 __device__ __forceinline__ void wait_vmem_capped() {
   wait_vmem<(N < 63 ? N : 63)>();
 }
 
-template <int L>
-__device__ __forceinline__ void wait_parts(int parts) {
-  switch (parts) {
-    case 0: wait_vmem<0>(); break;
-    case 1: wait_vmem_capped<1 * L>(); break;
-    case 2: wait_vmem_capped<2 * L>(); break;
-    case 3: wait_vmem_capped<3 * L>(); break;
-    case 4: wait_vmem_capped<4 * L>(); break;
-    case 5: wait_vmem_capped<5 * L>(); break;
-    case 6: wait_vmem_capped<6 * L>(); break;
-    case 7: wait_vmem_capped<7 * L>(); break;
-    case 8: wait_vmem_capped<8 * L>(); break;
-    case 9: wait_vmem_capped<9 * L>(); break;
-    case 10: wait_vmem_capped<10 * L>(); break;
-    case 11: wait_vmem_capped<11 * L>(); break;
-    case 12: wait_vmem_capped<12 * L>(); break;
-    case 13: wait_vmem_capped<13 * L>(); break;
-    case 14: wait_vmem_capped<14 * L>(); break;
-    case 15: wait_vmem_capped<15 * L>(); break;
-    default: wait_vmem_capped<16 * L>(); break;
+template <int L, int K>
+__device__ __forceinline__ void wait_chain(int parts) {
+  wait_vmem_capped<K * L>();
+  if constexpr (K > 0) {
+    if (parts < K) wait_chain<L, K - 1>(parts);
   }
+}
+
+template <int L, int MAXP>
+__device__ __forceinline__ void wait_parts(int parts) {
+  wait_chain<L, MAXP>(parts);
 }
 
 // RK / RV: positions of the K and V tile rings.
@@ -510,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       e_c = p < S ? rd(sv0, sv1, p) : 0xffffffffu;
       if (grp == 0) {
         const int kp1 = (int)(rd(pv0, pv1, p + 1) & 0xffffu);
-        wait_parts<C::LOADS>((i_kg - kp1) + (i_kgm1 - kc));
+        wait_parts<C::LOADS, RK + RV>((i_kg - kp1) + (i_kgm1 - kc));
       }
       __syncthreads();
       if (grp == 0) issue_to((int)(w >> 16));
