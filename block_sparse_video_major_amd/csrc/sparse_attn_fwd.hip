@@ -37,9 +37,17 @@
 //     plus one v_permlane32_swap and all softmax state is lane-local.
 //   * O^T += V^T P^T: P (bf16) is already in B-operand layout; V^T is read
 //     from the V tile in its natural [key][d] order with ds_read_b64_tr_b16.
+//   * Software pipeline, one barrier per step: each wave overlaps the QK
+//     MFMAs of step p with the exponentials of step p - 1, and the PV MFMAs
+//     of step p - 1 with the row max of step p.
 //   * Tiles arrive by direct global->LDS loads (16 bytes per lane, no
-//     registers) into a ring of 4 K/V positions (8 at d = 64), filled as far
-//     ahead as the ring allows.  Tiles are unpadded; 16-byte chunks are XOR
+//     registers).  K and V have separate rings (5 + 4 tiles at d = 128 when
+//     the schedule fits beside them, else 4 + 4; twice that at d = 64)
+//     because V is consumed one step after K.  Ring positions and, for
+//     every step, the last load group the rings can take are computed once
+//     per pair; the four waves of half A issue all loads right after the step
+//     barrier, as far ahead as the rings allow, and wait for them with a
+//     short chain of vmcnt waits.  Tiles are unpadded; 16-byte chunks are XOR
 //     swizzled per row so every LDS read pattern is bank-conflict free.
 //   * Rescaling of O is lazy: the exponent offset only moves when a block's
 //     max exceeds it by more than 8 (log2 units), keeping every exp2 <= 256;
@@ -47,6 +55,10 @@
 //   * Epilogue per query cube: key halves merged through LDS, O normalised,
 //     staged in LDS, combined with the gates and the broadcast coarse output
 //     and written with coalesced 16-byte stores.
+//   * What bounds it: on the 32K-token workload the CU's ingest of K/V tiles
+//     (about 1.4 tiles of 32 KiB per step per pair, mostly L2 hits) takes
+//     longer than the 32 MFMAs of a step; larger groups of query cubes per
+//     workgroup would cut those bytes further.
 #include "vsa_internal.h"
 
 namespace vsa {
