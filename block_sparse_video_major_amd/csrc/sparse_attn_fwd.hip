@@ -55,10 +55,11 @@
 //   * Epilogue per query cube: key halves merged through LDS, O normalised,
 //     staged in LDS, combined with the gates and the broadcast coarse output
 //     and written with coalesced 16-byte stores.
-//   * What bounds it: on the 32K-token workload the CU's ingest of K/V tiles
-//     (about 1.4 tiles of 32 KiB per step per pair, mostly L2 hits) takes
-//     longer than the 32 MFMAs of a step; larger groups of query cubes per
-//     workgroup would cut those bytes further.
+//   * What bounds it: on the 32K-token workload neither the tile bytes nor
+//     the MFMAs alone.  Cutting the bytes a workgroup fetches by a quarter
+//     gains about 5%; the per-step barrier and the scalar bookkeeping of the
+//     schedule (slot, offset and wait arithmetic) cost more, because every
+//     wave issues them between its MFMAs.
 #include "vsa_internal.h"
 
 namespace vsa {
