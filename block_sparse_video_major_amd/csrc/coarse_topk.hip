@@ -8,16 +8,23 @@
 // the pooled-query / pooled-key inner products, Top-K per query row);
 // "VSA: Faster Video Diffusion with Trainable Sparse Attention", Abstract.
 //
-// One workgroup = R query cubes of one (batch, head).
-//   phase 1  all threads: raw scores s[r][j] = <qc[i0+r], kc[j]> in float32
-//            (sequential FMA over d), kept in LDS;
+// One workgroup = R query cubes of one (batch, head): R = 8 with eight
+// wavefronts, or R = 4 with four when eight score rows do not fit in LDS.  Key and value cubes are staged
+// through LDS 64 at a time with coalesced 16-byte loads.
+//   phase 1  raw scores s[r][j] = <qc[i0+r], kc[j]> in float32, a sequential
+//            FMA chain over d per score; thread (key j, wave w) forms the
+//            wave's rows of column j, the query values coming through the
+//            scalar cache.  Rows are kept in LDS;
 //   phase 2  one wavefront per row: Top-K by radix select over the 32-bit
-//            order-preserving key of each score, one bit per pass, counting
-//            with wavefront ballots; the selected indices are emitted in
-//            ascending order through a ballot prefix count.  Ties at the
-//            threshold go to the lower index.  Then the row softmax
-//            p_j = exp(scale*(s_j - max)), summed in a fixed order;
-//   phase 3  all threads: O_c[r] = sum_j p_j * vc[j] / sum_j p_j.
+//            order-preserving key of each score, held in registers, one bit
+//            per pass, counting with wavefront ballots; the selected indices
+//            are emitted in ascending order through a ballot prefix count.
+//            Ties at the threshold go to the lower index.  Then the row
+//            softmax p_j = exp(scale*(s_j - max)), summed in a fixed order;
+//   phase 3  O_c[r] = sum_j p_j * vc[j] / sum_j p_j; thread (4 columns of d,
+//            row group) reads four probabilities and four value rows per
+//            16-byte LDS read; with few rows the key range is split across
+//            row groups and the partial sums are added in a fixed order.
 // The scale 1/sqrt(d) > 0 does not change the ranking, so ranking uses the
 // raw scores.
 #include "vsa_internal.h"
@@ -25,8 +32,7 @@
 namespace vsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 64;   // key / value cubes staged per LDS pass
 
 // Order-preserving map float -> uint32 (larger float -> larger key).  -0 is
 // folded onto +0 so that equal scores compare equal.
@@ -50,95 +56,138 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int D>
+// Row stride of the score rows in LDS: a multiple of 4 floats so that four
+// consecutive probabilities are one aligned 16-byte read.
+__host__ __device__ inline int padded_cols(int Nc) { return (Nc + 3) & ~3; }
+
+// Cubes [c0, c0 + kChunk) of one (batch, head) pass through registers
+// (loaded one chunk ahead, so the global latency overlaps the previous
+// chunk's arithmetic) into LDS rows of D + 4 floats; the pad makes a 16-lane
+// group's row reads hit distinct banks.  Cubes past Nc read as zero.
+template <int D, int kThreads>
+struct ChunkStage {
+  static constexpr int C4 = D / 4;
+  static constexpr int PER = kChunk * C4 / kThreads;   // 16-byte pieces per thread
+  float4 v[PER];
+  __device__ __forceinline__ void load(const float* src, int c0, int Nc, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / C4, c4 = e - row * C4;
+      v[i] = c0 + row < Nc ? reinterpret_cast<const float4*>(src)[(int64_t)(c0 + row) * C4 + c4]
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(float* chunk, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / C4, c4 = e - row * C4;
+      *reinterpret_cast<float4*>(chunk + row * (D + 4) + 4 * c4) = v[i];
+    }
+  }
+};
+
+template <int D, int R, int NS, int kThreads>
 __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
     int32_t* __restrict__ lut, int32_t* __restrict__ valid, float* __restrict__ oc, int Nc, int top_k,
-    int R, int tiles_per_head, float scale) {
+    int tiles_per_head, float scale) {
+  constexpr int kWaves = kThreads / 64;
+  static_assert(R % kWaves == 0, "rows per workgroup");
   extern __shared__ float smem[];
-  float* qs = smem;                 // [R][D]
-  float* srow = smem + R * D;       // [R][Nc]
-  float* inv_sum = srow + (int64_t)R * Nc;  // [R]
+  const int NcP = padded_cols(Nc);
+  float* chunk = smem;                       // [kChunk][D + 4]
+  float* srow = chunk + kChunk * (D + 4);    // [R][NcP]
+  float* inv_sum = srow + (int64_t)R * NcP;  // [R]
 
   const int64_t bh = blockIdx.x / tiles_per_head;
   const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * R;
   const int rows = min(R, Nc - i0);
-  const float* qh = qc + bh * (int64_t)Nc * D;
   const float* kh = kc + bh * (int64_t)Nc * D;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  for (int e = tid; e < R * D; e += kThreads) {
-    const int r = e / D;
-    qs[e] = (r < rows) ? qh[(int64_t)(i0 + r) * D + (e - r * D)] : 0.f;
-  }
-  __syncthreads();
-
-  // phase 1: raw scores
-  for (int j = tid; j < Nc; j += kThreads) {
-    const float4* kr = reinterpret_cast<const float4*>(kh + (int64_t)j * D);
-    for (int r0 = 0; r0 < R; r0 += 8) {
-      float acc[8];
+  // phase 1: raw scores.  A wave's query rows are uniform across its lanes,
+  // so they are read straight from global memory through the scalar cache
+  // (rows past the last cube repeat it; their scores are never used).
+  constexpr int RW = R / kWaves;   // rows per thread
+  const float* qrow[RW];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-#pragma unroll 4
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 kv = kr[d4];
+  for (int u = 0; u < RW; ++u)
+    qrow[u] = qc + (bh * Nc + min(i0 + wave + kWaves * u, Nc - 1)) * (int64_t)D;
+  ChunkStage<D, kThreads> st;
+  st.load(kh, 0, Nc, tid);
+  for (int c0 = 0; c0 < Nc; c0 += kChunk) {
+    __syncthreads();   // previous chunk fully read
+    st.store(chunk, tid);
+    __syncthreads();
+    if (c0 + kChunk < Nc) st.load(kh, c0 + kChunk, Nc, tid);
+    float acc[RW];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          if (r0 + r < R) {
-            const float4 qv = *reinterpret_cast<const float4*>(qs + (r0 + r) * D + 4 * d4);
-            acc[r] = fmaf(qv.x, kv.x, acc[r]);
-            acc[r] = fmaf(qv.y, kv.y, acc[r]);
-            acc[r] = fmaf(qv.z, kv.z, acc[r]);
-            acc[r] = fmaf(qv.w, kv.w, acc[r]);
-          }
-        }
+    for (int u = 0; u < RW; ++u) acc[u] = 0.f;
+    const float* kr = chunk + lane * (D + 4);
+#pragma unroll 8
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * d4);
+#pragma unroll
+      for (int u = 0; u < RW; ++u) {
+        const float4 qv = *reinterpret_cast<const float4*>(qrow[u] + 4 * d4);
+        acc[u] = fmaf(qv.x, kv.x, acc[u]);
+        acc[u] = fmaf(qv.y, kv.y, acc[u]);
+        acc[u] = fmaf(qv.z, kv.z, acc[u]);
+        acc[u] = fmaf(qv.w, kv.w, acc[u]);
       }
+    }
+    if (c0 + lane < Nc) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r0 + r < R) srow[(int64_t)(r0 + r) * Nc + j] = acc[r];
+      for (int u = 0; u < RW; ++u) srow[(int64_t)(wave + kWaves * u) * NcP + c0 + lane] = acc[u];
     }
   }
+  // The first value chunk is in flight during the selection.
+  const float* vh = vc + bh * (int64_t)Nc * D;
+  if (oc != nullptr) st.load(vh, 0, Nc, tid);
   __syncthreads();
 
   // phase 2: per-row Top-K and softmax weights, one wavefront per row
-  const int nslots = (Nc + 63) / 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = wave; r < rows; r += kWaves) {
-    float* sr = srow + (int64_t)r * Nc;
+    float* sr = srow + (int64_t)r * NcP;
     const int64_t row = bh * Nc + i0 + r;
     int32_t* out_idx = lut + row * top_k;
+    // Keys of this row, slot s = cube s*64 + lane; 0 (below every candidate
+    // threshold, which always has a bit set) past Nc.
+    uint32_t key[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s * 64 + lane;
+      key[s] = j < Nc ? order_key(sr[j]) : 0u;
+    }
     // K-th largest key: build the threshold from the top bit down.
     uint32_t thr = 0u;
     if (top_k < Nc) {
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = thr | (1u << bit);
         int cnt = 0;
-        for (int s = 0; s < nslots; ++s) {
-          const int j = s * 64 + lane;
-          const bool ge = (j < Nc) && (order_key(sr[j]) >= cand);
-          cnt += popc64(__ballot(ge));
-        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) cnt += popc64(__ballot(key[s] >= cand));
         if (cnt >= top_k) thr = cand;
       }
     }
     int gt = 0;
-    for (int s = 0; s < nslots; ++s) {
-      const int j = s * 64 + lane;
-      gt += popc64(__ballot((j < Nc) && (order_key(sr[j]) > thr)));
-    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) gt += popc64(__ballot(s * 64 + lane < Nc && key[s] > thr));
     const int need = top_k - gt;   // >= 1 entries equal to thr are taken
     int eq_before = 0, sel_before = 0;
-    for (int s = 0; s < nslots; ++s) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
       const int j = s * 64 + lane;
-      const uint32_t key = (j < Nc) ? order_key(sr[j]) : 0u;
       const bool in = j < Nc;
-      const bool eq = in && key == thr;
+      const bool eq = in && key[s] == thr;
       const uint64_t eqm = __ballot(eq);
       const int eq_rank = eq_before + popc64(eqm & lt_mask);
-      const bool take = in && (key > thr || (eq && eq_rank < need));
+      const bool take = in && (key[s] > thr || (eq && eq_rank < need));
       const uint64_t tm = __ballot(take);
       if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
       sel_before += popc64(tm);
@@ -151,9 +200,9 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
       for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[j]);
       m = wave_max(m);
       float sum = 0.f;
-      for (int j = lane; j < Nc; j += 64) {
-        const float p = expf(scale * (sr[j] - m));
-        sr[j] = p;
+      for (int j = lane; j < NcP; j += 64) {
+        const float p = j < Nc ? expf(scale * (sr[j] - m)) : 0.f;
+        sr[j] = p;   // the pad columns hold 0
         sum += p;
       }
       sum = wave_sum(sum);
@@ -161,60 +210,128 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     }
   }
   if (oc == nullptr) return;
-  __syncthreads();
 
-  // phase 3: O_c rows; thread -> (column d, row phase)
-  const float* vh = vc + bh * (int64_t)Nc * D;
-  constexpr int G = kThreads / D;
-  const int d = tid % D;
-  const int ph = tid / D;
-  for (int r0 = ph; r0 < rows; r0 += 4 * G) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < Nc; ++j) {
-      const float vv = vh[(int64_t)j * D + d];
+  // phase 3: O_c rows
+  constexpr int C4 = D / 4;                     // 16-byte column groups
+  constexpr int NRG = kThreads / C4;            // row groups
+  constexpr int RPT = R >= NRG ? R / NRG : 1;   // rows per thread
+  constexpr int KS = R >= NRG ? 1 : NRG / R;    // key splits
+  static_assert(RPT * NRG == R || KS * R == NRG, "phase 3 mapping");
+  const int c4 = tid % C4;
+  const int rg = tid / C4;
+  const int r_first = KS == 1 ? rg : rg % R;
+  const int ks = KS == 1 ? 0 : rg / R;
+  float4 acc[RPT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * G;
-        if (r < rows) acc[u] = fmaf(srow[(int64_t)r * Nc + j], vv, acc[u]);
+  for (int u = 0; u < RPT; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < Nc; c0 += kChunk) {
+    __syncthreads();   // phase 2 done / previous chunk fully read
+    st.store(chunk, tid);
+    __syncthreads();
+    if (c0 + kChunk < Nc) st.load(vh, c0 + kChunk, Nc, tid);
+    const int jend = min(kChunk, NcP - c0);   // multiple of 4; pad columns carry p = 0
+    for (int j = 4 * ks; j < jend; j += 4 * KS) {
+      const float4 v0 = *reinterpret_cast<const float4*>(chunk + (j + 0) * (D + 4) + 4 * c4);
+      const float4 v1 = *reinterpret_cast<const float4*>(chunk + (j + 1) * (D + 4) + 4 * c4);
+      const float4 v2 = *reinterpret_cast<const float4*>(chunk + (j + 2) * (D + 4) + 4 * c4);
+      const float4 v3 = *reinterpret_cast<const float4*>(chunk + (j + 3) * (D + 4) + 4 * c4);
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        const int r = r_first + NRG * u;
+        const float4 p = *reinterpret_cast<const float4*>(srow + (int64_t)r * NcP + c0 + j);
+        acc[u].x = fmaf(p.x, v0.x, acc[u].x); acc[u].y = fmaf(p.x, v0.y, acc[u].y);
+        acc[u].z = fmaf(p.x, v0.z, acc[u].z); acc[u].w = fmaf(p.x, v0.w, acc[u].w);
+        acc[u].x = fmaf(p.y, v1.x, acc[u].x); acc[u].y = fmaf(p.y, v1.y, acc[u].y);
+        acc[u].z = fmaf(p.y, v1.z, acc[u].z); acc[u].w = fmaf(p.y, v1.w, acc[u].w);
+        acc[u].x = fmaf(p.z, v2.x, acc[u].x); acc[u].y = fmaf(p.z, v2.y, acc[u].y);
+        acc[u].z = fmaf(p.z, v2.z, acc[u].z); acc[u].w = fmaf(p.z, v2.w, acc[u].w);
+        acc[u].x = fmaf(p.w, v3.x, acc[u].x); acc[u].y = fmaf(p.w, v3.y, acc[u].y);
+        acc[u].z = fmaf(p.w, v3.z, acc[u].z); acc[u].w = fmaf(p.w, v3.w, acc[u].w);
       }
     }
+  }
+  if (KS > 1) {
+    // Partial sums of the key splits, added in split order.
+    __syncthreads();
+    float4* part = reinterpret_cast<float4*>(chunk);   // [KS][R][C4]
+    part[(ks * R + r_first) * C4 + c4] = acc[0];
+    __syncthreads();
+    if (ks == 0) {
+      float4 t = part[r_first * C4 + c4];
+      for (int k2 = 1; k2 < KS; ++k2) {
+        const float4 o = part[(k2 * R + r_first) * C4 + c4];
+        t.x += o.x; t.y += o.y; t.z += o.z; t.w += o.w;
+      }
+      acc[0] = t;
+    }
+  }
+  if (ks != 0) return;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = r0 + u * G;
-      if (r < rows) oc[(bh * Nc + i0 + r) * D + d] = acc[u] * inv_sum[r];
+  for (int u = 0; u < RPT; ++u) {
+    const int r = r_first + NRG * u;
+    if (r < rows) {
+      const float is = inv_sum[r];
+      const float4 a = acc[u];
+      reinterpret_cast<float4*>(oc + (bh * Nc + i0 + r) * D)[c4] =
+          make_float4(a.x * is, a.y * is, a.z * is, a.w * is);
     }
   }
 }
 
 }  // namespace
 
-static size_t coarse_lds_bytes(int R, int64_t Nc, int D) {
-  return sizeof(float) * ((size_t)R * D + (size_t)R * Nc + R);
+static size_t coarse_lds_bytes(int R, int Nc, int D) {
+  return sizeof(float) * ((size_t)kChunk * (D + 4) + (size_t)R * padded_cols(Nc) + R);
+}
+
+constexpr size_t kCoarseLdsMax = 160 * 1024;
+
+template <int D, int R, int NS, int T>
+static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
+                             int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  const int Nc = (int)g.Nc;
+  const int tiles = (Nc + R - 1) / R;
+  const int64_t blocks = g.BH * tiles;
+  const size_t lds = coarse_lds_bytes(R, Nc, D);
+  const float scale = 1.0f / sqrtf((float)D);
+  auto k = coarse_topk_kernel<D, R, NS, T>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(T), lds, s, qc, kc, vc, lut, valid, oc, Nc, top_k,
+                     tiles, scale);
+  return hipGetLastError();
+}
+
+template <int D, int R, int T>
+static hipError_t launch_r(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
+                           int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  const int slots = (int)((g.Nc + 63) / 64);
+  if (slots <= 8) return launch_rns<D, R, 8, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 16) return launch_rns<D, R, 16, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 32) return launch_rns<D, R, 32, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return launch_rns<D, R, 64, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+}
+
+// Eight query cubes per 512-thread workgroup where their score rows fit in
+// LDS, else four per 256 threads: measured on 12 heads x 512 cubes, more,
+// smaller workgroups hide the staging latency better than larger ones.
+template <int D>
+static hipError_t launch_d(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
+                           int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  if (coarse_lds_bytes(8, (int)g.Nc, D) <= kCoarseLdsMax)
+    return launch_r<D, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return launch_r<D, 4, 256>(g, top_k, qc, kc, vc, lut, valid, oc, s);
 }
 
 hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
                               const float* vc, int32_t* lut, int32_t* valid, float* oc,
                               hipStream_t s) {
-  const int Nc = (int)g.Nc;
-  const int R = Nc > 1536 ? 4 : 8;
-  const int tiles = (Nc + R - 1) / R;
-  const int64_t blocks = g.BH * tiles;
-  const size_t lds = coarse_lds_bytes(R, Nc, g.D);
-  const float scale = 1.0f / sqrtf((float)g.D);
-  if (g.D == 64) {
-    auto k = coarse_topk_kernel<64>;
-    if (lds > 65536) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), lds, s, qc, kc, vc, lut, valid, oc, Nc,
-                       top_k, R, tiles, scale);
-  } else if (g.D == 128) {
-    auto k = coarse_topk_kernel<128>;
-    if (lds > 65536) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), lds, s, qc, kc, vc, lut, valid, oc, Nc,
-                       top_k, R, tiles, scale);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (g.Nc < 1 || g.Nc > kMaxCoarseCubes) return hipErrorInvalidValue;
+  if (g.D == 64) return launch_d<64>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (g.D == 128) return launch_d<128>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace vsa

@@ -195,6 +195,37 @@ def test_coarse_topk_ties_take_lower_index():
         assert np.array_equal(lut.cpu().numpy(), want), f"K={k}"
 
 
+# Cube counts outside the workloads: the largest Nc the coarse stage accepts
+# at both head sizes (fewer query rows per workgroup, the key range split
+# across row groups for the coarse output, keys in 64 slots per lane), a
+# count that is not a multiple of 4 (padded score rows) and one between.
+COARSE_GEOM = [(128, (64, 64, 64), 192), (64, (64, 64, 64), 100),
+               (64, (20, 36, 44), 37), (128, (4, 4, 6124), 64)]
+
+
+@pytest.mark.parametrize("d,dims,k", COARSE_GEOM, ids=[f"d{c[0]}-nc{c[1][0] * c[1][1] * c[1][2] // 64}"
+                                                       for c in COARSE_GEOM])
+def test_coarse_topk_cube_counts(d, dims, k):
+    T, H, W = dims
+    p = L.Problem(1, 1, T, H, W, 4, 4, 4, d)
+    nc = p.n_cubes
+    _log(f"coarse_topk Nc={nc} d={d} K={k}")
+    rng = np.random.default_rng(11)
+    host = {n: rng.standard_normal((1, 1, nc, d)).astype(np.float32) for n in ("q", "k", "v")}
+    lut = torch.full((1, 1, nc, k), -7, dtype=torch.int32, device="cuda")
+    valid = torch.full((1, 1, nc), -7, dtype=torch.int32, device="cuda")
+    oc = torch.full((1, 1, nc, d), float("nan"), dtype=torch.float32, device="cuda")
+    L.vsa_coarse_topk(p, k, dev(host["q"]), dev(host["k"]), dev(host["v"]), lut, valid, oc)
+    _sync()
+    q64, k64, v64 = (host[n].astype(np.float64) for n in ("q", "k", "v"))
+    s, _, oc_want = oracle.coarse_attention(q64, k64, v64, 1.0 / math.sqrt(d))
+    lut_want, _ = oracle.topk_lut(s, k)
+    differ = check_lut_against_scores(lut.cpu().numpy(), valid.cpu().numpy(), s, k, lut_want)
+    oc_err = err(host64(oc), oc_want)
+    assert oc_err[0] <= OC_MAX_ABS, f"O_c max-abs {oc_err[0]:.3e}"
+    print(f"rows differing within the tie window: {differ}")
+
+
 # ------------------------------------------------------------------ fine attention
 def _fine_case(w, k, check_cubes, gates=True, lse=True, heads_checked=None, lut_kind="oracle"):
     """Fine kernel on oracle-permuted inputs with a LUT covering every head.
