@@ -1,8 +1,8 @@
 """Benchmark of the VSA forward pass on one MI355X.
 
 One step = one pass of the whole forward path over one batch of synthetic
-input resident in HBM: reorder Q, K, V into cubes, pool them, coarse
-attention + Top-K, fine block-sparse attention (with the coarse output
+input resident in HBM: reorder Q, K, V into cubes and pool them (one fused
+pass per tensor), coarse attention + Top-K, fine block-sparse attention (with the coarse output
 combined through the gates' default), reorder back.  The default workload is
 the 32,768-token Wan2.1-scale layer (16x32x64 grid, 4x4x4 cubes, 12 heads,
 d=128, bf16, Top-K 154 of 512 cubes = 70% sparsity).
@@ -136,12 +136,9 @@ def main() -> int:
     B = L.VSA_BF16
 
     def step(ev0=None, ev1=None):
-        L.vsa_permute(p, B, q, f.qp, stream)
-        L.vsa_permute(p, B, k, f.kp, stream)
-        L.vsa_permute(p, B, v, f.vp, stream)
-        L.vsa_pool(p, B, f.qp, f.qc, stream)
-        L.vsa_pool(p, B, f.kp, f.kc, stream)
-        L.vsa_pool(p, B, f.vp, f.vc, stream)
+        L.vsa_permute_pool(p, B, q, f.qp, f.qc, stream)
+        L.vsa_permute_pool(p, B, k, f.kp, f.kc, stream)
+        L.vsa_permute_pool(p, B, v, f.vp, f.vc, stream)
         L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
         if ev0 is not None:
             ev0.record(stream)
@@ -168,12 +165,13 @@ def main() -> int:
         ms_total = t_start.elapsed_time(t_end)
         fine_ms = [a.elapsed_time(b) for a, b in ev]
 
-        # per-stage breakdown (separate, untimed pass)
-        names = ["permute_qkv", "pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute"]
+        # per-stage breakdown (separate, untimed pass); the step runs the
+        # fused permute_pool, the separate permute and pool are timed too
+        names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute"]
         reps = max(3, min(10, args.steps))
         acc = {n: 0.0 for n in names}
         for _ in range(reps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
             e[0].record(stream)
             for t, dst in ((q, f.qp), (k, f.kp), (v, f.vp)):
                 L.vsa_permute(p, B, t, dst, stream)
@@ -181,12 +179,15 @@ def main() -> int:
             for src, dst in ((f.qp, f.qc), (f.kp, f.kc), (f.vp, f.vc)):
                 L.vsa_pool(p, B, src, dst, stream)
             e[2].record(stream)
-            L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
+            for t, dst, dc in ((q, f.qp, f.qc), (k, f.kp, f.kc), (v, f.vp, f.vc)):
+                L.vsa_permute_pool(p, B, t, dst, dc, stream)
             e[3].record(stream)
-            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
+            L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
             e[4].record(stream)
-            L.vsa_unpermute(p, B, f.out_cube, out, stream)
+            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
             e[5].record(stream)
+            L.vsa_unpermute(p, B, f.out_cube, out, stream)
+            e[6].record(stream)
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 acc[n] += e[i].elapsed_time(e[i + 1]) / reps
@@ -199,6 +200,7 @@ def main() -> int:
     permute_bytes = 3 * 2 * elem * 2
     pool_bytes = 3 * (elem * 2 + w.batch * w.heads * w.n_cubes * w.head_dim * 4)
     unpermute_bytes = 2 * elem * 2
+    permute_pool_bytes = 3 * (2 * elem * 2 + w.batch * w.heads * w.n_cubes * w.head_dim * 4)
     achieved = flops / (fine_avg * 1e-3) / 1e12
     rec = {
         "metric": "VSA fwd ms/call + effective TFLOP/s (% bf16 peak), 32K tokens @70% sparsity",
@@ -224,6 +226,7 @@ def main() -> int:
         "stages_ms": {n: round(t, 4) for n, t in acc.items()},
         "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
                         "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
+                        "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9, 1),
                         "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),

@@ -89,6 +89,7 @@ def load() -> ctypes.CDLL:
         "vsa_permute": [P, i32, vp, vp, vp],
         "vsa_unpermute": [P, i32, vp, vp, vp],
         "vsa_pool": [P, i32, vp, vp, vp],
+        "vsa_permute_pool": [P, i32, vp, vp, vp, vp],
         "vsa_coarse_topk": [P, i32, vp, vp, vp, vp, vp, vp, vp],
         "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_check_lut": [P, vp, vp, i32, vp, vp],
@@ -190,6 +191,16 @@ def vsa_pool(p: Problem, dtype: int, x_cube: torch.Tensor, xc: torch.Tensor, str
     _need(xc, "xc", _cube_shape(p), torch.float32, x_cube.device)
     _check(load().vsa_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(xc),
                            _stream(stream, x_cube.device)), "vsa_pool")
+
+
+def vsa_permute_pool(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: torch.Tensor, xc: torch.Tensor,
+                     stream=None) -> None:
+    td = _token_dtype(dtype)
+    _need(x_raster, "x_raster", _tok_shape(p), td)
+    _need(x_cube, "x_cube", _tok_shape(p), td, x_raster.device)
+    _need(xc, "xc", _cube_shape(p), torch.float32, x_raster.device)
+    _check(load().vsa_permute_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube), _ptr(xc),
+                                   _stream(stream, x_raster.device)), "vsa_permute_pool")
 
 
 def vsa_coarse_topk(p: Problem, top_k: int, qc: torch.Tensor, kc: torch.Tensor, vc: Optional[torch.Tensor],

@@ -1,0 +1,217 @@
+// Token reordering between raster (t, h, w) order and cube-major order, the
+// cube mean-pool, and both fused into one pass.
+//
+// "VSA: Accelerating Video Diffusion Inference with Sparse Attention on AMD
+// GPUs", §Two-Stage Architecture: before Stage 1 the sequence is reordered so
+// that every run of ct*ch*cw consecutive tokens is one spatio-temporal cube
+// (cube-major order: cubes in raster order over the cube grid, tokens in
+// raster order inside a cube), and Stage 1 mean-pools each cube into one
+// cube-level vector (Qc, Kc, Vc).
+//
+// One workgroup per cube of one (batch, head) (grid-stride beyond 2^20).  The cube's vol token rows of
+// CPR 16-byte chunks are spread over 256 threads: thread t always handles
+// column chunk t % CPR of rows t / CPR, t / CPR + RG, ... (RG = 256 / CPR),
+// so a wavefront touches whole rows.  On the cube-major side the cube is
+// vol * row_bytes contiguous bytes; on the raster side it is ct * ch runs of
+// cw tokens (cw * row_bytes contiguous bytes, 1 KiB for 4 bf16 tokens of
+// d = 128).  All index arithmetic is 32-bit within a (batch, head) and done
+// once per row, so the kernels stay HBM-bound.
+//
+// Pooling sums a thread's rows in increasing order in float32, then the RG
+// partial rows in phase order through LDS, then divides by vol: the order
+// never depends on timing, so results are bit-reproducible, and the fused
+// pass produces exactly the bits of the separate reorder and pool passes.
+#include <type_traits>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kMaxGrid = 1 << 20;   // larger problems loop over cubes
+
+enum Mode { kToCube = 0, kToRaster = 1, kPool = 2, kToCubePool = 3 };
+
+template <typename T>
+__device__ __forceinline__ void widen(const uint4& raw, float* out);
+
+template <>
+__device__ __forceinline__ void widen<__bf16>(const uint4& raw, float* out) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void widen<float>(const uint4& raw, float* out) {
+  out[0] = __uint_as_float(raw.x);
+  out[1] = __uint_as_float(raw.y);
+  out[2] = __uint_as_float(raw.z);
+  out[3] = __uint_as_float(raw.w);
+}
+
+// 16-byte load; NT marks it non-temporal (streamed once, not kept in the
+// caches).  Measured on the 32K-token, 12-head, d = 128 tensors: plain
+// reorders and the pool read 10-20% faster that way, the fused pass does
+// not (its cube-major output is what the next stage reads).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if (!NT) return *p;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// Geometry of one launch, all sizes that the row mapping needs.
+struct CubeArgs {
+  int32_t H, W;           // token grid (T is implied by the cube count)
+  int32_t ct, ch, cw;     // cube edges
+  int32_t gH, gW;         // cube grid
+  int32_t vol;            // tokens per cube
+  int32_t N;              // tokens per (batch, head)
+  int32_t Nc;             // cubes per (batch, head)
+  int64_t units;          // batch * heads * Nc
+};
+
+// Raster offset, from the cube's first token, of token l of the cube.
+__device__ __forceinline__ int32_t row_offset(int32_t l, const CubeArgs& a) {
+  const int32_t plane = a.ch * a.cw;
+  const int32_t lt = l / plane;
+  const int32_t rem = l - lt * plane;
+  const int32_t lh = rem / a.cw;
+  const int32_t lw = rem - lh * a.cw;
+  return (lt * a.H + lh) * a.W + lw;
+}
+
+// T = element type (pool modes), D = head_dim; CPR = 16-byte chunks per row.
+// Grid-stride over units = (batch*head) * Nc + cube.
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __restrict__ src,
+                                                             uint4* __restrict__ dst,
+                                                             float* __restrict__ xc, CubeArgs a) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int CPR = D / E;
+  constexpr int RG = kThreads / CPR;
+  constexpr int KB = RG >= 64 ? 1 : 64 / RG;   // rows per thread in flight: a 64-token cube in one batch
+  constexpr bool kPooling = MODE == kPool || MODE == kToCubePool;
+  constexpr bool kCopy = MODE != kPool;
+  constexpr bool kFromRaster = MODE == kToCube || MODE == kToCubePool;
+  constexpr bool kStreamLoads = MODE != kToCubePool;
+  __shared__ float part[kPooling ? RG : 1][kPooling ? D + 1 : 1];
+  const int col = threadIdx.x % CPR;
+  const int phase = threadIdx.x / CPR;
+
+  for (int64_t unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
+    const int64_t bh = unit / a.Nc;
+    const int32_t c = (int32_t)(unit - bh * a.Nc);
+    const int32_t cw_i = c % a.gW;
+    const int32_t ch_i = (c / a.gW) % a.gH;
+    const int32_t ct_i = c / (a.gW * a.gH);
+    const int64_t head_rows = bh * (int64_t)a.N;
+    const int64_t raster0 = head_rows + (ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw;
+    const int64_t cube0 = head_rows + (int64_t)c * a.vol;
+    float acc[kPooling ? E : 1];
+#pragma unroll
+    for (int e = 0; e < (kPooling ? E : 1); ++e) acc[e] = 0.f;
+
+    // Batches of KB rows per thread.  A full batch issues all its loads
+    // before the first store; only a cube's ragged last batch is guarded.
+    auto batch = [&](int32_t l0, auto guarded) {
+      uint4 buf[KB];
+      int64_t rrow[KB];   // raster row of token l0 + b*RG
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const int32_t l = l0 + b * RG;
+        if (!guarded.value || l < a.vol) {
+          rrow[b] = raster0 + row_offset(l, a);
+          buf[b] = load16<kStreamLoads>(src + (kFromRaster ? rrow[b] : cube0 + l) * CPR + col);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const int32_t l = l0 + b * RG;
+        if (!guarded.value || l < a.vol) {
+          if (kCopy) dst[(kFromRaster ? cube0 + l : rrow[b]) * CPR + col] = buf[b];
+          if (kPooling) {
+            float v[E];
+            widen<T>(buf[b], v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += v[e];
+          }
+        }
+      }
+    };
+    int32_t l0 = phase;
+    for (; l0 + (KB - 1) * RG < a.vol; l0 += KB * RG) batch(l0, std::false_type{});
+    if (l0 < a.vol) batch(l0, std::true_type{});
+    if (kPooling) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) part[phase][col * E + e] = acc[e];
+      __syncthreads();
+      const float fvol = (float)a.vol;
+      for (int d = threadIdx.x; d < D; d += kThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < RG; ++p) s += part[p][d];
+        xc[unit * D + d] = s / fvol;
+      }
+      __syncthreads();   // part is reused by the next unit
+    }
+  }
+}
+
+CubeArgs cube_args(const Geom& g) {
+  CubeArgs a;
+  a.H = g.H; a.W = g.W;
+  a.ct = g.ct; a.ch = g.ch; a.cw = g.cw;
+  a.gH = g.gH; a.gW = g.gW;
+  a.vol = g.vol;
+  a.N = (int32_t)g.N;
+  a.Nc = (int32_t)g.Nc;
+  a.units = g.BH * g.Nc;
+  return a;
+}
+
+template <typename T, int MODE>
+hipError_t launch_mode(const Geom& g, const void* src, void* dst, float* xc, hipStream_t s) {
+  const CubeArgs a = cube_args(g);
+  const dim3 grid((unsigned)(a.units < kMaxGrid ? a.units : kMaxGrid));
+  if (g.D == 64)
+    hipLaunchKernelGGL((cube_pass_kernel<T, 64, MODE>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+                       (uint4*)dst, xc, a);
+  else if (g.D == 128)
+    hipLaunchKernelGGL((cube_pass_kernel<T, 128, MODE>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+                       (uint4*)dst, xc, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_dtype(const Geom& g, int dtype, const void* src, void* dst, float* xc, hipStream_t s) {
+  return dtype == VSA_BF16 ? launch_mode<__bf16, MODE>(g, src, dst, xc, s)
+                           : launch_mode<float, MODE>(g, src, dst, xc, s);
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const Geom& g, int dtype, const void* src, void* dst, bool to_cube,
+                          hipStream_t s) {
+  return to_cube ? launch_dtype<kToCube>(g, dtype, src, dst, nullptr, s)
+                 : launch_dtype<kToRaster>(g, dtype, src, dst, nullptr, s);
+}
+
+hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, hipStream_t s) {
+  return launch_dtype<kPool>(g, dtype, x_cube, nullptr, xc, s);
+}
+
+hipError_t launch_permute_pool(const Geom& g, int dtype, const void* x_raster, void* x_cube, float* xc,
+                               hipStream_t s) {
+  return launch_dtype<kToCubePool>(g, dtype, x_raster, x_cube, xc, s);
+}
+
+}  // namespace vsa

@@ -79,8 +79,7 @@ int vsa_permute(const vsa_problem* p, int32_t dtype, const void* x_raster, void*
   if (st != VSA_OK) return st;
   if (x_raster == nullptr || x_cube == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  return hip_status(vsa::launch_reorder(g, dtype == VSA_BF16 ? 2 : 4, x_raster, x_cube, true,
-                                        (hipStream_t)stream));
+  return hip_status(vsa::launch_reorder(g, dtype, x_raster, x_cube, true, (hipStream_t)stream));
 }
 
 int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube, void* x_raster, void* stream) {
@@ -89,8 +88,7 @@ int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube, void*
   if (st != VSA_OK) return st;
   if (x_raster == nullptr || x_cube == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  return hip_status(vsa::launch_reorder(g, dtype == VSA_BF16 ? 2 : 4, x_cube, x_raster, false,
-                                        (hipStream_t)stream));
+  return hip_status(vsa::launch_reorder(g, dtype, x_cube, x_raster, false, (hipStream_t)stream));
 }
 
 int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube, float* xc, void* stream) {
@@ -100,6 +98,16 @@ int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube, float* xc,
   if (x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
   return hip_status(vsa::launch_pool(g, dtype, x_cube, xc, (hipStream_t)stream));
+}
+
+int vsa_permute_pool(const vsa_problem* p, int32_t dtype, const void* x_raster, void* x_cube, float* xc,
+                     void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_raster == nullptr || x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_permute_pool(g, dtype, x_raster, x_cube, xc, (hipStream_t)stream));
 }
 
 int vsa_coarse_topk(const vsa_problem* p, int32_t top_k, const float* qc, const float* kc, const float* vc,

@@ -35,9 +35,11 @@ inline Geom make_geom(const vsa_problem& p) {
 }
 
 // Launchers (each returns the hipGetLastError() of its launch).
-hipError_t launch_reorder(const Geom& g, int elem_bytes, const void* src, void* dst,
-                          bool to_cube, hipStream_t s);
+hipError_t launch_reorder(const Geom& g, int dtype, const void* src, void* dst, bool to_cube,
+                          hipStream_t s);
 hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, hipStream_t s);
+hipError_t launch_permute_pool(const Geom& g, int dtype, const void* x_raster, void* x_cube, float* xc,
+                               hipStream_t s);
 hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
                               const float* vc, int32_t* lut, int32_t* valid, float* oc,
                               hipStream_t s);

@@ -1,8 +1,8 @@
 """The whole VSA forward pass as a sequence of C-ABI calls.
 
 Order of the steps ("VSA: Accelerating Video Diffusion Inference with Sparse
-Attention on AMD GPUs", §Two-Stage Architecture): reorder tokens into cubes,
-mean-pool the cubes, coarse cube attention with Top-K selection, fine
+Attention on AMD GPUs", §Two-Stage Architecture): reorder tokens into cubes
+and mean-pool them (one fused pass per tensor), coarse cube attention with Top-K selection, fine
 block-sparse attention over the selected cubes combined with the coarse
 output through the gates, and reorder back.  This module only allocates the
 intermediate buffers (through torch) and calls the library; every step runs
@@ -42,9 +42,9 @@ class VsaForward:
                  gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
         p, B = self.p, L.VSA_BF16
-        L.vsa_permute(p, B, q, self.qp, stream)
-        L.vsa_permute(p, B, k, self.kp, stream)
-        L.vsa_permute(p, B, v, self.vp, stream)
+        L.vsa_permute_pool(p, B, q, self.qp, self.qc, stream)
+        L.vsa_permute_pool(p, B, k, self.kp, self.kc, stream)
+        L.vsa_permute_pool(p, B, v, self.vp, self.vc, stream)
         gc = gf = None
         if gate_c is not None:
             if self.gc is None:
@@ -56,9 +56,6 @@ class VsaForward:
                 raise ValueError("built without gate buffers (with_gates=False)")
             L.vsa_permute(p, B, gate_f, self.gf, stream)
             gf = self.gf
-        L.vsa_pool(p, B, self.qp, self.qc, stream)
-        L.vsa_pool(p, B, self.kp, self.kc, stream)
-        L.vsa_pool(p, B, self.vp, self.vc, stream)
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
         L.vsa_sparse_attn_fwd(p, self.qp, self.kp, self.vp, self.lut, self.valid, self.out_cube,
                               oc=self.oc, gate_c=gc, gate_f=gf, lse=self.lse, stream=stream)

@@ -95,6 +95,16 @@ int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube,
 int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube,
              float* xc, void* stream);
 
+/* vsa_permute followed by vsa_pool in one pass over the tokens
+ * ([VSA-ROCm] §Two-Stage Architecture: the pre-stage reordering and the
+ * Stage 1 cube pooling; every token is read once):
+ *   x_cube[b, h, p, :] = x_raster[b, h, pi(p), :]
+ *   xc[b, h, c, :]     = (1/vol) * sum_{l < vol} x_cube[b, h, c*vol + l, :]
+ * Same layouts and rules as vsa_permute and vsa_pool; x_cube and xc hold
+ * exactly the bits the two separate calls produce. */
+int vsa_permute_pool(const vsa_problem* p, int32_t dtype, const void* x_raster,
+                     void* x_cube, float* xc, void* stream);
+
 /* Coarse stage ([VSA-ROCm] §Two-Stage Architecture, Stage 1, and
  * §Generating Sparsity Patterns; [VSA-arXiv] Abstract).  Per (b, h) and query
  * cube i, with S[i, j] = <qc[i], kc[j]> / sqrt(head_dim) over all Nc cubes:

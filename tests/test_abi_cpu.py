@@ -90,6 +90,16 @@ def test_pool_errors():
     assert lib.vsa_pool(ctypes.byref(_prob()), 3, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
 
 
+def test_permute_pool_errors():
+    lib = _raw()
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, None, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(None, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(ctypes.byref(_prob(W=10)), 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 2, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
+
+
 def test_coarse_topk_errors():
     lib = _raw()
     pr = ctypes.byref(_prob())          # Nc = 8*16*16/64 = 32

@@ -77,6 +77,21 @@ def test_reorder_bit_exact(name, dims, dtype):
     want = np.take(x, pi, axis=2)
     assert np.array_equal(bits(xc), want.view(bits(xc).dtype))
     assert np.array_equal(bits(back), x.view(bits(back).dtype))
+    # the fused reorder + pool writes the same bits as the two separate passes
+    pooled_shape = (p.batch, p.heads, p.n_cubes, p.head_dim)
+    pooled = torch.empty(pooled_shape, dtype=torch.float32, device="cuda")
+    pooled_fused = torch.empty(pooled_shape, dtype=torch.float32, device="cuda")
+    xc_fused = torch.empty_like(xt)
+    L.vsa_pool(p, dtype, xc, pooled)
+    L.vsa_permute_pool(p, dtype, xt, xc_fused, pooled_fused)
+    _sync()
+    assert np.array_equal(bits(xc_fused), bits(xc))
+    # random bit patterns include NaNs, whose payload the two passes may pick
+    # from either operand of an add: NaN positions must agree, other bits too
+    a, b = pooled_fused.cpu().numpy(), pooled.cpu().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    keep = ~np.isnan(a)
+    assert np.array_equal(a[keep].view(np.uint32), b[keep].view(np.uint32))
 
 
 # ------------------------------------------------------------------ pool
@@ -92,7 +107,12 @@ def _pool_case(w, heads=None):
         L.vsa_permute(p, dtype, xt, xcube)
         pooled = torch.empty((p.batch, p.heads, p.n_cubes, p.head_dim), dtype=torch.float32, device="cuda")
         L.vsa_pool(p, dtype, xcube, pooled)
+        xcube2 = torch.empty_like(xt)
+        pooled2 = torch.empty_like(pooled)
+        L.vsa_permute_pool(p, dtype, xt, xcube2, pooled2)
         _sync()
+        assert torch.equal(xcube2, xcube)
+        assert np.array_equal(bits(pooled2), bits(pooled)), "fused pool differs from vsa_pool"
         hs = range(w.heads) if heads is None else heads
         got = host64(pooled)[:, list(hs)]
         x64 = wl.as_float64(x[n][:, list(hs)])
