@@ -39,7 +39,10 @@
 //     from the V tile in its natural [key][d] order with ds_read_b64_tr_b16.
 //   * Software pipeline, one barrier per step: each wave overlaps the QK
 //     MFMAs of step p with the exponentials of step p - 1, and the PV MFMAs
-//     of step p - 1 with the row max of step p.
+//     of step p - 1 with the row max of step p.  The step loop is unrolled by
+//     two so the two score tiles swap roles without register copies, and the
+//     step schedule is read with one readlane from a 64-entry register
+//     window that slides every 32 steps.
 //   * Tiles arrive by direct global->LDS loads (16 bytes per lane, no
 //     registers).  K and V have separate rings (5 + 4 tiles at d = 128 when
 //     the schedule fits beside them, else 4 + 4; twice that at d = 64)
@@ -429,19 +432,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       __syncthreads();
     }
 
-    // Steps and plan entries are read from registers: lane j of sv0 / sv1
-    // (pv0 / pv1) holds entry win + j / win + 64 + j.  The window moves by 64
-    // when the main loop leaves its first half; loads run at most RK + 1
-    // steps ahead, so every read stays inside it.
+    // Steps and plan entries are read from registers: lane j of sv (pv) holds
+    // entry win + j.  The window moves by 32 entries every 32 steps; entries
+    // are read at most RK + 1 steps ahead, so every read stays inside it.
+    // The next window is read from LDS one slide ahead.
     int win = 0;
-    uint32_t sv0 = lane < S ? sched[lane] : 0xffffffffu;
-    uint32_t sv1 = 64 + lane < S ? sched[64 + lane] : 0xffffffffu;
-    uint32_t pv0 = lane <= S + 1 ? plan[lane] : 0u;
-    uint32_t pv1 = 64 + lane <= S + 1 ? plan[64 + lane] : 0u;
-    auto rd = [&](uint32_t w0, uint32_t w1, int idx) -> uint32_t {
-      const int rel = idx - win;
-      return rel < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)w0, rel)
-                      : (uint32_t)__builtin_amdgcn_readlane((int)w1, rel - 64);
+    uint32_t sv = lane < S ? sched[lane] : 0xffffffffu;
+    uint32_t pv = lane <= S + 1 ? plan[lane] : 0u;
+    uint32_t nsv = 32 + lane < S ? sched[32 + lane] : 0xffffffffu;
+    uint32_t npv = 32 + lane <= S + 1 ? plan[32 + lane] : 0u;
+    auto rd = [&](uint32_t w, int idx) -> uint32_t {
+      return (uint32_t)__builtin_amdgcn_readlane((int)w, idx - win);
     };
     auto load_k = [&](uint32_t blk, int pos) {
       const uint32_t slot_off = (uint32_t)((pos % RK) * C::TILE);
@@ -461,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     uint32_t i_e = 0xffffffffu;
     auto issue_to = [&](int last) {
       for (; gi <= last; ++gi) {
-        const int kg1 = (int)(rd(pv0, pv1, gi + 1) & 0xffffu);
-        const uint32_t e = gi < S ? rd(sv0, sv1, gi) : 0xffffffffu;
+        const int kg1 = (int)(rd(pv, gi + 1) & 0xffffu);
+        const uint32_t e = gi < S ? rd(sv, gi) : 0xffffffffu;
         if (kg1 > i_kg) {
           const uint32_t a = e & 0xffffu, b = e >> 16;
           load_k(a != 0xffffu ? a : b, i_kg);
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         i_e = e;
       }
     };
-    if (grp == 0) issue_to((int)(rd(pv0, pv1, 0) >> 16));
+    if (grp == 0) issue_to((int)(rd(pv, 0) >> 16));
 
     f32x16 o[C::OT];
 #pragma unroll
@@ -501,20 +502,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     uint32_t e_c = 0xffffffffu, e_p = 0xffffffffu;   // tiles of steps p and p - 1
     int kc = 0, vc = 0;                                 // kpos(p), kpos(p - 1)
     auto step_barrier = [&](int p) {
-      if (p - win == 64) {   // slide the register windows by 64 entries
-        win += 64;
-        sv0 = sv1;
-        sv1 = win + 64 + lane < S ? sched[win + 64 + lane] : 0xffffffffu;
-        pv0 = pv1;
-        pv1 = win + 64 + lane <= S + 1 ? plan[win + 64 + lane] : 0u;
+      if (p - win == 32) {   // slide the register windows by 32 entries
+        win += 32;
+        sv = nsv;
+        pv = npv;
+        nsv = win + 32 + lane < S ? sched[win + 32 + lane] : 0xffffffffu;
+        npv = win + 32 + lane <= S + 1 ? plan[win + 32 + lane] : 0u;
       }
       e_p = e_c;
       vc = kc;
-      const uint32_t w = rd(pv0, pv1, p);
+      const uint32_t w = rd(pv, p);
       kc = (int)(w & 0xffffu);
-      e_c = p < S ? rd(sv0, sv1, p) : 0xffffffffu;
+      e_c = p < S ? rd(sv, p) : 0xffffffffu;
       if (grp == 0) {
-        const int kp1 = (int)(rd(pv0, pv1, p + 1) & 0xffffu);
+        const int kp1 = (int)(rd(pv, p + 1) & 0xffffu);
         wait_parts<C::LOADS, RK + RV>((i_kg - kp1) + (i_kgm1 - kc));
       }
       __syncthreads();
@@ -527,7 +528,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     // The MFMAs are unconditional (one code path keeps every accumulator in
     // one register set): a missing tile has zero operands, and a missing
     // previous step is exponentiated with an infinite offset, giving P = 0.
-    for (int p = 0; p <= S; ++p) {
+    // sc holds the scores of step p - 1, sn receives those of step p; the
+    // loop is unrolled by two so the two score tiles swap roles instead of
+    // being copied.
+    auto iter = [&](int p, const f32x16& sc, f32x16& sn) {
       step_barrier(p);
       const uint32_t ac = e_c & 0xffffu, bc = e_c >> 16;   // step p
       const uint32_t ap = e_p & 0xffffu, bp = e_p >> 16;   // step p - 1
@@ -590,7 +594,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       // probabilities (accurate log-sum-exp).
       constexpr int NQK = D / 16;          // QK MFMAs per step
       constexpr int EPM = 16 / NQK;        // exponentials per MFMA
-      f32x16 sn;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[r] = 0.f;
       bf16x8 pb[2];
@@ -618,7 +621,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       mx_prev = pair_max(mx) * c_log2;
-      sc = sn;
+    };
+    f32x16 sc2;
+    for (int p = 0; p <= S; p += 2) {
+      iter(p, sc, sc2);
+      if (p + 1 > S) break;
+      iter(p + 1, sc2, sc);
     }
     __syncthreads();   // every wave is done with the ring before it is reused
 
