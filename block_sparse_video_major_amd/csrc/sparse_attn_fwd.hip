@@ -121,22 +121,42 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& raw, float* f) {
   }
 }
 
-// One direct global->LDS load: every lane moves the 16 bytes at base + voff
-// (base: wave-uniform pointer, voff: per-lane byte offset) to LDS byte address
-// lds_base + 16 * lane.  Issued through inline assembly so that the compiler
-// does not track these LDS writes; completion is enforced explicitly
-// (wait_vmem + barrier) before any wave reads the slot.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+// Direct global->LDS loads of one wave's share of a tile: for piece
+// n = 0..N-1 every lane moves the 16 bytes at base + voff[n] + 1024 n (base:
+// wave-uniform pointer, voff: per-lane byte offsets) to LDS byte address
+// lds_base + 1024 n + 16 * lane.  Issued through inline assembly so that the
+// compiler does not track these LDS writes; completion is enforced
+// explicitly (wait_vmem + barrier) before any wave reads the slot.
+template <int N>
+__device__ __forceinline__ void dma_tile(const void* base, const uint32_t (&voff)[N], uint32_t lds_base) {
   // M0 must come from a scalar register: force the (wave-uniform) address
-  // there even where the compiler kept it in a vector register.
+  // there even where the compiler kept it in a vector register.  The
+  // instruction offset n * 1024 moves both the global source and the LDS
+  // destination of load n, so M0 is set once per tile; voff[n] holds the
+  // lane's source offset minus n * 1024.
   lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(lds_base)
-      : "memory", "m0");
+  static_assert(N == 2 || N == 4, "loads per tile");
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %5\n\t"
+        "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:3072"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(lds_base), "s"(base)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:1024"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "s"(lds_base), "s"(base)
+        : "memory", "m0");
+  }
 }
 
 __device__ __forceinline__ uint32_t pack_step(int ta, int tb) {
@@ -203,7 +223,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   uint32_t* sched = reinterpret_cast<uint32_t*>(smem + RING);
   // plan[s] = kpos(s) | F(s) << 16, s = 0..S+1 (see the load plan below)
   uint32_t* plan = sched + max_kv;
-  int* flags = reinterpret_cast<int*>(plan + max_kv + 2);   // [0] duplicate, [1] unsorted, [2] shared count
+  // dsc[p] = what step p needs (slots, presence, wait and issue counts) and
+  // tlist = every tile load of the pair in issue order (see below)
+  uint32_t* dsc = plan + max_kv + 2;
+  uint32_t* tlist = dsc + max_kv + 1;
+  int* flags = reinterpret_cast<int*>(tlist + 4 * max_kv);   // [0] duplicate, [1] unsorted, [2] shared count
   uint32_t* bmA = reinterpret_cast<uint32_t*>(flags + 4);               // Nc-bit membership maps
   const int nwords = (Nc + 31) >> 5;
   uint32_t* bmB = bmA + nwords;
@@ -226,8 +250,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   for (int n = 0; n < C::LOADS; ++n) {
     const int L = ((wave & 3) * C::LOADS + n) * 64 + lane;
     const int r = L / C::CPR, x = L % C::CPR;
-    kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16);
-    vg_off[n] = r * C::ROWB + ((x ^ C::vswz(r)) * 16);
+    // minus n * 1024: the load's instruction offset adds it back (>= 0,
+    // since piece n of the tile covers source bytes [L0, L0 + 1024) with
+    // L0 >= n * 1024)
+    kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16) - n * 1024;
+    vg_off[n] = r * C::ROWB + ((x ^ C::vswz(r)) * 16) - n * 1024;
   }
   const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)((wave & 3) * C::LOADS * 1024));
   // K A-operand reads: key row 32*kh + n32, logical chunk 2*ks + g.
@@ -432,54 +459,98 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       __syncthreads();
     }
 
-    // Steps and plan entries are read from registers: lane j of sv (pv) holds
-    // entry win + j.  The window moves by 32 entries every 32 steps; entries
-    // are read at most RK + 1 steps ahead, so every read stays inside it.
-    // The next window is read from LDS one slide ahead.
-    int win = 0;
-    uint32_t sv = lane < S ? sched[lane] : 0xffffffffu;
-    uint32_t pv = lane <= S + 1 ? plan[lane] : 0u;
-    uint32_t nsv = 32 + lane < S ? sched[32 + lane] : 0xffffffffu;
-    uint32_t npv = 32 + lane <= S + 1 ? plan[32 + lane] : 0u;
-    auto rd = [&](uint32_t w, int idx) -> uint32_t {
-      return (uint32_t)__builtin_amdgcn_readlane((int)w, idx - win);
-    };
-    auto load_k = [&](uint32_t blk, int pos) {
-      const uint32_t slot_off = (uint32_t)((pos % RK) * C::TILE);
-      const char* src = uniform_ptr(k_head + (int64_t)blk * C::TILE);
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) dma16(src, kg_off[n], lds_ring + slot_off + n * 1024);
-    };
-    auto load_v = [&](uint32_t blk, int pos) {
-      const uint32_t slot_off = (uint32_t)(V_BASE + (pos % RV) * C::TILE);
-      const char* src = uniform_ptr(v_head + (int64_t)blk * C::TILE);
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) dma16(src, vg_off[n], lds_ring + slot_off + n * 1024);
-    };
-    // Issue state (half A): next group gi, kpos(gi), kpos(gi - 1), and the
-    // tiles of step gi - 1 (whose V part belongs to group gi).
-    int gi = 0, i_kg = 0, i_kgm1 = 0;
-    uint32_t i_e = 0xffffffffu;
-    auto issue_to = [&](int last) {
-      for (; gi <= last; ++gi) {
-        const int kg1 = (int)(rd(pv, gi + 1) & 0xffffu);
-        const uint32_t e = gi < S ? rd(sv, gi) : 0xffffffffu;
-        if (kg1 > i_kg) {
+    // ---- per-step descriptors and the tile list --------------------------
+    // Loads are issued group by group (group g = the K tiles of step g, then
+    // the V tiles of step g - 1), so the tiles of group g occupy list entries
+    // kpos(g) + kpos(g - 1) onward.  tlist[i] = cube | ring slot << 16 |
+    // (1 if V) << 20.  Before the loop groups 0..F(0) are issued; after
+    // barrier p, groups F(p - 1) + 1 .. F(p).  issued(p) = the list length
+    // issued before barrier p; at barrier p the wave waits until only the
+    // tiles after group p, issued(p) - kpos(p + 1) - kpos(p), remain in
+    // flight.  dsc[p]:
+    //   bits 0-3 / 4-7    K ring slot of half A's / half B's tile of step p
+    //   bits 8-11 / 12-15 V ring slot of half A's / half B's tile of step p-1
+    //   bits 16 / 17      half A / half B has a tile in step p
+    //   bits 18 / 19      half A / half B had a tile in step p - 1
+    //   bits 20-24        tiles to leave in flight at barrier p
+    //   bits 25-29        tiles to issue after barrier p
+    {
+      auto kpos = [&](int st) { return st < 0 ? 0 : (int)(plan[st] & 0xffffu); };
+      auto fr = [&](int st) { return (int)(plan[st] >> 16); };
+      auto issued_through = [&](int grpi) { return kpos(grpi + 1) + kpos(grpi); };
+      for (int pp = tid; pp <= S; pp += kThreads) {
+        uint32_t d = 0;
+        if (pp < S) {
+          const uint32_t e = sched[pp];
           const uint32_t a = e & 0xffffu, b = e >> 16;
-          load_k(a != 0xffffu ? a : b, i_kg);
-          if (kg1 - i_kg == 2) load_k(b, i_kg + 1);
+          const int k0 = kpos(pp);
+          const int kb = k0 + ((a != 0xffffu && b != a) ? 1 : 0);
+          d |= (uint32_t)(k0 % RK) | ((uint32_t)(kb % RK) << 4);
+          d |= (a != 0xffffu ? 1u << 16 : 0u) | (b != 0xffffu ? 1u << 17 : 0u);
         }
-        if (i_kg > i_kgm1) {
-          const uint32_t a = i_e & 0xffffu, b = i_e >> 16;
-          load_v(a != 0xffffu ? a : b, i_kgm1);
-          if (i_kg - i_kgm1 == 2) load_v(b, i_kgm1 + 1);
+        if (pp > 0) {
+          const uint32_t e = sched[pp - 1];
+          const uint32_t a = e & 0xffffu, b = e >> 16;
+          const int v0 = kpos(pp - 1);
+          const int vb = v0 + ((a != 0xffffu && b != a) ? 1 : 0);
+          d |= ((uint32_t)(v0 % RV) << 8) | ((uint32_t)(vb % RV) << 12);
+          d |= (a != 0xffffu ? 1u << 18 : 0u) | (b != 0xffffu ? 1u << 19 : 0u);
         }
-        i_kgm1 = i_kg;
-        i_kg = kg1;
-        i_e = e;
+        const int before = issued_through(fr(pp > 0 ? pp - 1 : 0));   // issued before barrier pp
+        const int after = issued_through(fr(pp));                     // ... after it
+        d |= (uint32_t)(before - issued_through(pp)) << 20;
+        d |= (uint32_t)(after - before) << 25;
+        dsc[pp] = d;
+      }
+      for (int gg = tid; gg <= S; gg += kThreads) {
+        int i = kpos(gg) + kpos(gg - 1);
+        if (gg < S) {
+          const uint32_t e = sched[gg];
+          const uint32_t a = e & 0xffffu, b = e >> 16;
+          const int k0 = kpos(gg), nk = kpos(gg + 1) - k0;
+          if (nk >= 1) tlist[i++] = (a != 0xffffu ? a : b) | ((uint32_t)(k0 % RK) << 16);
+          if (nk == 2) tlist[i++] = b | ((uint32_t)((k0 + 1) % RK) << 16);
+        }
+        if (gg > 0) {
+          const uint32_t e = sched[gg - 1];
+          const uint32_t a = e & 0xffffu, b = e >> 16;
+          const int v0 = kpos(gg - 1), nv = kpos(gg) - v0;
+          if (nv >= 1) tlist[i++] = (a != 0xffffu ? a : b) | ((uint32_t)(v0 % RV) << 16) | (1u << 20);
+          if (nv == 2) tlist[i++] = b | ((uint32_t)((v0 + 1) % RV) << 16) | (1u << 20);
+        }
+      }
+      __syncthreads();
+    }
+    const int n_init = (int)(plan[(int)(plan[0] >> 16) + 1] & 0xffffu) + (int)(plan[(int)(plan[0] >> 16)] & 0xffffu);
+
+    // Descriptors and list entries are read from registers: lane j of dw
+    // holds dsc[dwin + j], lane j of tw holds tlist[twin + j].  Each window
+    // slides by 32 entries when its reads would leave the first half (a step
+    // issues at most RK + RV < 32 tiles), and the next window is read from
+    // LDS one slide ahead.
+    int dwin = 0, twin = 0;
+    uint32_t dw = lane <= S ? dsc[lane] : 0u;
+    uint32_t ndw = 32 + lane <= S ? dsc[32 + lane] : 0u;
+    const int n_list = 2 * (int)(plan[S] & 0xffffu);
+    uint32_t tw = lane < n_list ? tlist[lane] : 0u;
+    uint32_t ntw = 32 + lane < n_list ? tlist[32 + lane] : 0u;
+    int i_tile = 0;   // next list entry to issue (half A)
+    auto issue = [&](int count) {
+      if (i_tile - twin >= 32) {
+        twin += 32;
+        tw = ntw;
+        ntw = twin + 32 + lane < n_list ? tlist[twin + 32 + lane] : 0u;
+      }
+      for (int c = 0; c < count; ++c, ++i_tile) {
+        const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)tw, i_tile - twin);
+        const uint32_t blk = e & 0xffffu, slot = (e >> 16) & 15u;
+        if (e & (1u << 20))
+          dma_tile(uniform_ptr(v_head + (int64_t)blk * C::TILE), vg_off, lds_ring + V_BASE + slot * C::TILE);
+        else
+          dma_tile(uniform_ptr(k_head + (int64_t)blk * C::TILE), kg_off, lds_ring + slot * C::TILE);
       }
     };
-    if (grp == 0) issue_to((int)(rd(pv, 0) >> 16));
+    if (grp == 0) issue(n_init);
 
     f32x16 o[C::OT];
 #pragma unroll
@@ -499,27 +570,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     // Step barrier p: every wave has finished iteration p - 1.  Half A waits
     // for its loads of group p (K of step p, V of step p - 1), the barrier
     // publishes them, and half A issues the groups that became free.
-    uint32_t e_c = 0xffffffffu, e_p = 0xffffffffu;   // tiles of steps p and p - 1
-    int kc = 0, vc = 0;                                 // kpos(p), kpos(p - 1)
+    uint32_t d_c = 0;   // dsc of the current step
     auto step_barrier = [&](int p) {
-      if (p - win == 32) {   // slide the register windows by 32 entries
-        win += 32;
-        sv = nsv;
-        pv = npv;
-        nsv = win + 32 + lane < S ? sched[win + 32 + lane] : 0xffffffffu;
-        npv = win + 32 + lane <= S + 1 ? plan[win + 32 + lane] : 0u;
+      if (p - dwin == 32) {   // slide the descriptor window by 32 entries
+        dwin += 32;
+        dw = ndw;
+        ndw = dwin + 32 + lane <= S ? dsc[dwin + 32 + lane] : 0u;
       }
-      e_p = e_c;
-      vc = kc;
-      const uint32_t w = rd(pv, p);
-      kc = (int)(w & 0xffffu);
-      e_c = p < S ? rd(sv, p) : 0xffffffffu;
-      if (grp == 0) {
-        const int kp1 = (int)(rd(pv, p + 1) & 0xffffu);
-        wait_parts<C::LOADS, RK + RV>((i_kg - kp1) + (i_kgm1 - kc));
-      }
+      d_c = (uint32_t)__builtin_amdgcn_readlane((int)dw, p - dwin);
+      if (grp == 0) wait_parts<C::LOADS, RK + RV>((int)((d_c >> 20) & 31u));
       __syncthreads();
-      if (grp == 0) issue_to((int)(w >> 16));
+      if (grp == 0) issue((int)((d_c >> 25) & 31u));
     };
 
     // Iteration p, software pipelined within each wave: QK of step p runs on
@@ -533,15 +594,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     // being copied.
     auto iter = [&](int p, const f32x16& sc, f32x16& sn) {
       step_barrier(p);
-      const uint32_t ac = e_c & 0xffffu, bc = e_c >> 16;   // step p
-      const uint32_t ap = e_p & 0xffffu, bp = e_p >> 16;   // step p - 1
-      const bool has_c = (grp == 0 ? ac : bc) != 0xffffu;  // this half has a tile in step p
-      const bool has_p = (grp == 0 ? ap : bp) != 0xffffu;  // ... in step p - 1
+      const bool has_c = (d_c >> (16 + grp)) & 1u;   // this half has a tile in step p
+      const bool has_p = (d_c >> (18 + grp)) & 1u;   // ... in step p - 1
+      const uint32_t kslot = (d_c >> (4 * grp)) & 15u;
+      const uint32_t vslot = (d_c >> (8 + 4 * grp)) & 15u;
       bf16x8 ka[D / 16];
       bf16x8 va[C::OT][2];
       if (has_c) {
-        const int pos = kc + ((grp == 1 && ac != 0xffffu && bc != ac) ? 1 : 0);
-        const char* base = smem + (pos % RK) * C::TILE;
+        const char* base = smem + kslot * C::TILE;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(base + k_off[ks]);
       } else {
@@ -554,8 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         // For k-step j the A operand of lane (g, d-row) holds keys base +
         // 0..3 and base + 8..11 with base = 32*kh + 16*j + 4*g: exactly the
         // keys of pb[j]'s slots.
-        const int pos = vc + ((grp == 1 && ap != 0xffffu && bp != ap) ? 1 : 0);
-        const char* base = smem + (pos % RV) * C::TILE;   // v_off includes the V ring base
+        const char* base = smem + vslot * C::TILE;   // v_off includes the V ring base
 #pragma unroll
         for (int t = 0; t < C::OT; ++t)
 #pragma unroll
@@ -759,10 +818,12 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   return hipGetLastError();
 }
 
-// LDS after the tile ring: step list, load plan, flags and two Nc-bit maps.
+// LDS after the tile ring: step list, load plan, step descriptors, tile
+// list, flags and two Nc-bit maps.
 size_t sched_bytes(const Geom& g, int max_kv) {
   const size_t nwords = (size_t)(g.Nc + 31) / 32;
-  return 4 * (size_t)max_kv + 4 * ((size_t)max_kv + 2) + 16 + 2 * 4 * nwords;
+  const size_t m = (size_t)max_kv;
+  return 4 * m + 4 * (m + 2) + 4 * (m + 1) + 16 * m + 16 + 2 * 4 * nwords;
 }
 
 constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8 at d = 64

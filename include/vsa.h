@@ -139,8 +139,8 @@ int vsa_coarse_topk(const vsa_problem* p, int32_t top_k, const float* qc,
  * oc: [batch, heads, Nc, head_dim] float32; lse: [batch, heads, N] float32,
  *   cube-major, or NULL.
  * Requires cube volume 64, head_dim 64 or 128, Nc <= 65534, and a LUT row
- * length whose per-row schedule fits in on-chip memory (8 * max_kv_blocks +
- * Nc / 4 bytes <= 32 KiB, about max_kv_blocks <= 2000 at Nc = 4096);
+ * length whose per-row schedule fits in on-chip memory (28 * max_kv_blocks +
+ * Nc / 4 bytes <= 32 KiB, about max_kv_blocks <= 1130 at Nc = 4096);
  * otherwise VSA_ERR_UNSUPPORTED.  out must not alias an input. */
 int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k,
                         const void* v, const int32_t* kv_block_idx,
