@@ -2,9 +2,10 @@
 
 One step = one pass of the whole forward path over one batch of synthetic
 input resident in HBM: reorder Q, K, V into cubes and pool them (one fused
-pass per tensor), coarse attention + Top-K, fine block-sparse attention (with the coarse output
-combined through the gates' default), reorder back.  The default workload is
-the 32,768-token Wan2.1-scale layer (16x32x64 grid, 4x4x4 cubes, 12 heads,
+pass per tensor), coarse attention + Top-K, fine block-sparse attention
+(with the coarse output combined through the gates' default) writing the
+output back in raster order from its epilogue.  The default workload is the
+32,768-token Wan2.1-scale layer (16x32x64 grid, 4x4x4 cubes, 12 heads,
 d=128, bf16, Top-K 154 of 512 cubes = 70% sparsity).
 
 Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step, counting
@@ -132,6 +133,7 @@ def main() -> int:
     del x
     f = vsa.VsaForward(p, w.top_k, dev)
     out = torch.empty_like(q)
+    out_cube = torch.empty_like(q)   # cube-major output of the separate fine + unpermute breakdown
     stream = torch.cuda.Stream(device=dev)
     B = L.VSA_BF16
 
@@ -142,10 +144,9 @@ def main() -> int:
         L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
         if ev0 is not None:
             ev0.record(stream)
-        L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
+        L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
         if ev1 is not None:
             ev1.record(stream)
-        L.vsa_unpermute(p, B, f.out_cube, out, stream)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -167,7 +168,8 @@ def main() -> int:
 
         # per-stage breakdown (separate, untimed pass); the step runs the
         # fused permute_pool, the separate permute and pool are timed too
-        names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute"]
+        names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute",
+                 "sparse_attn_fwd_raster"]
         reps = max(3, min(10, args.steps))
         acc = {n: 0.0 for n in names}
         for _ in range(reps):
@@ -184,10 +186,12 @@ def main() -> int:
             e[3].record(stream)
             L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
             e[4].record(stream)
-            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, f.out_cube, oc=f.oc, stream=stream)
+            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, out_cube, oc=f.oc, stream=stream)
             e[5].record(stream)
-            L.vsa_unpermute(p, B, f.out_cube, out, stream)
+            L.vsa_unpermute(p, B, out_cube, out, stream)
             e[6].record(stream)
+            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
+            e[7].record(stream)
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 acc[n] += e[i].elapsed_time(e[i + 1]) / reps

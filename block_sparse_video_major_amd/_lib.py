@@ -92,6 +92,7 @@ def load() -> ctypes.CDLL:
         "vsa_permute_pool": [P, i32, vp, vp, vp, vp],
         "vsa_coarse_topk": [P, i32, vp, vp, vp, vp, vp, vp, vp],
         "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
+        "vsa_sparse_attn_fwd_raster": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_check_lut": [P, vp, vp, i32, vp, vp],
         "vsa_perm_index": [P, vp],
         "vsa_status_str": [ctypes.c_int],
@@ -225,6 +226,19 @@ def vsa_sparse_attn_fwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
                         out: torch.Tensor, oc: Optional[torch.Tensor] = None,
                         gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, False)
+
+
+def vsa_sparse_attn_fwd_raster(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                               out: torch.Tensor, oc: Optional[torch.Tensor] = None,
+                               gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """As vsa_sparse_attn_fwd, with gate_c, gate_f, out and lse in raster token order."""
+    _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, True)
+
+
+def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, raster):
     dev = q.device
     ts = _tok_shape(p)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
@@ -241,10 +255,11 @@ def vsa_sparse_attn_fwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
             _need(t, name, ts, torch.bfloat16, dev)
     if lse is not None:
         _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
-    _check(load().vsa_sparse_attn_fwd(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
-                                      _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
-                                      _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
-                                      _stream(stream, dev)), "vsa_sparse_attn_fwd")
+    name = "vsa_sparse_attn_fwd_raster" if raster else "vsa_sparse_attn_fwd"
+    _check(getattr(load(), name)(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
+                                 _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
+                                 _stream(stream, dev)), name)
 
 
 def vsa_check_lut(p: Problem, kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,

@@ -208,12 +208,33 @@ __device__ __forceinline__ void wait_parts(int parts) {
 }
 
 // RK / RV: positions of the K and V tile rings.
+// Token order of out, gate_c, gate_f and lse: cube-major (on == 0) or raster
+// (t, h, w) order (on == 1; the reorder back fused into the epilogue).
+struct TokenMap {
+  int32_t on;
+  int32_t H, W;         // token grid (rows and columns of a frame)
+  int32_t ct, ch, cw;   // cube edges
+  int32_t gH, gW;       // cube grid
+};
+
+// Position of token l (< 64) of cube c within its (batch, head) in the
+// order the map selects.
+__device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, int32_t l) {
+  if (!m.on) return c * kBlk + l;
+  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
+  const int32_t plane = m.ch * m.cw;
+  const int32_t lt = l / plane, rem = l - lt * plane;
+  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
+  return ((ct_i * m.ct + lt) * m.H + ch_i * m.ch + lh) * m.W + cw_i * m.cw + lw;
+}
+
 template <int D, int RK, int RV>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
     const float* __restrict__ oc, const __bf16* __restrict__ gate_c, const __bf16* __restrict__ gate_f,
-    __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2) {
+    __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2,
+    TokenMap tmap) {
   using C = Cfg<D>;
   constexpr int V_BASE = RK * C::TILE;           // V ring after the K ring
   constexpr int RING = (RK + RV) * C::TILE;
@@ -726,7 +747,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         }
       if (lse != nullptr && g == 0 && my_valid) {
         const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-        lse[(rowA + grp) * kBlk + 32 * qh + n32] = val;
+        lse[bh * (int64_t)Nc * kBlk + token_pos(tmap, my_cube, 32 * qh + n32)] = val;
       }
     }
     __syncthreads();
@@ -739,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;
         const int row = c / C::CPR, col = c % C::CPR;
-        const int64_t gidx = head_off + (int64_t)(my_cube * kBlk + row) * D + col * 8;
+        const int64_t gidx = head_off + (int64_t)token_pos(tmap, my_cube, row) * D + col * 8;
         float val[8];
         const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
         const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
@@ -784,7 +805,8 @@ constexpr int kLdsMax = 160 * 1024;
 template <int D, int RK, int RV>
 hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                        const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
-                       const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot) {
+                       const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot,
+                       const TokenMap& tmap) {
   using C = Cfg<D>;
   static DevState dev_state[64];
   int dev = 0;
@@ -814,7 +836,7 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, lut, valid, max_kv, oc, (const __bf16*)gate_c, (const __bf16*)gate_f,
-                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2);
+                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2, tmap);
   return hipGetLastError();
 }
 
@@ -833,7 +855,7 @@ constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8
 template <int D>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
-                    const void* gate_f, void* out, float* lse, hipStream_t s) {
+                    const void* gate_f, void* out, float* lse, hipStream_t s, const TokenMap& tmap) {
   using C = Cfg<D>;
   constexpr int RK_DEEP = D == 128 ? 5 : 10, RV_DEEP = D == 128 ? 4 : 8;
   constexpr int R_BASE = D == 128 ? 4 : 8;
@@ -845,10 +867,10 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   if ((size_t)(RK_DEEP + RV_DEEP) * C::TILE + sched <= (size_t)kLdsMax &&
       build_scratch <= (size_t)(RK_DEEP + RV_DEEP) * C::TILE)
     return launch_ring<D, RK_DEEP, RV_DEEP>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
-                                            sched, base_slot);
+                                            sched, base_slot, tmap);
   if (build_scratch > (size_t)(2 * R_BASE) * C::TILE) return hipErrorInvalidValue;
   return launch_ring<D, R_BASE, R_BASE>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, sched,
-                                        base_slot + 1);
+                                        base_slot + 1, tmap);
 }
 
 }  // namespace
@@ -865,9 +887,14 @@ bool sparse_attn_fwd_fits(const Geom& g, int max_kv) {
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, hipStream_t s) {
-  if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s);
-  if (g.D == 64) return launch_d<64>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s);
+                                  void* out, float* lse, bool raster_out, hipStream_t s) {
+  TokenMap m;
+  m.on = raster_out ? 1 : 0;
+  m.H = g.H; m.W = g.W;
+  m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
+  m.gH = g.gH; m.gW = g.gW;
+  if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 64) return launch_d<64>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   return hipErrorInvalidValue;
 }
 

@@ -124,10 +124,11 @@ int vsa_coarse_topk(const vsa_problem* p, int32_t top_k, const float* qc, const 
                                             (hipStream_t)stream));
 }
 
-int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, const void* v,
-                        const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
-                        const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
-                        void* stream) {
+namespace {
+int sparse_attn_fwd_common(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
+                           const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
+                           bool raster_out, void* stream) {
   int st = check_problem(p);
   if (st != VSA_OK) return st;
   if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
@@ -139,7 +140,24 @@ int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, cons
   if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
   if (!vsa::sparse_attn_fwd_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
   return hip_status(vsa::launch_sparse_attn_fwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc,
-                                                gate_c, gate_f, out, lse, (hipStream_t)stream));
+                                                gate_c, gate_f, out, lse, raster_out, (hipStream_t)stream));
+}
+}  // namespace
+
+int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
+                        const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
+                        void* stream) {
+  return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
+                                out, lse, false, stream);
+}
+
+int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                               int32_t max_kv_blocks, const float* oc, const void* gate_c, const void* gate_f,
+                               void* out, float* lse, void* stream) {
+  return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
+                                out, lse, true, stream);
 }
 
 int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32_t* valid_block_num,

@@ -48,7 +48,7 @@ bool sparse_attn_fwd_fits(const Geom& g, int max_kv);
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, hipStream_t s);
+                                  void* out, float* lse, bool raster_out, hipStream_t s);
 hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* valid, int max_kv,
                             int32_t* bad_rows, hipStream_t s);
 

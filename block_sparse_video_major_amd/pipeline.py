@@ -2,11 +2,12 @@
 
 Order of the steps ("VSA: Accelerating Video Diffusion Inference with Sparse
 Attention on AMD GPUs", §Two-Stage Architecture): reorder tokens into cubes
-and mean-pool them (one fused pass per tensor), coarse cube attention with Top-K selection, fine
-block-sparse attention over the selected cubes combined with the coarse
-output through the gates, and reorder back.  This module only allocates the
-intermediate buffers (through torch) and calls the library; every step runs
-in the HIP kernels of libvsa.so.
+and mean-pool them (one fused pass per tensor), coarse cube attention with
+Top-K selection, fine block-sparse attention over the selected cubes combined
+with the coarse output through the gates, written straight back in the
+model's token order (the reorder back runs in the fine kernel's epilogue).
+This module only allocates the intermediate buffers (through torch) and calls
+the library; every step runs in the HIP kernels of libvsa.so.
 """
 from __future__ import annotations
 
@@ -23,6 +24,9 @@ class VsaForward:
 
     def __init__(self, p: Problem, top_k: int, device="cuda", with_gates: bool = False,
                  with_lse: bool = False):
+        # with_gates is accepted for callers that pass gates; the raster-order
+        # gates are read directly, so no buffer is needed for them.  lse (if
+        # kept) is in raster token order.
         if not 1 <= top_k <= p.n_cubes:
             raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
         self.p, self.top_k = p, top_k
@@ -33,9 +37,6 @@ class VsaForward:
         self.qc, self.kc, self.vc, self.oc = (torch.empty(cs, dtype=f32, device=device) for _ in range(4))
         self.lut = torch.empty((p.batch, p.heads, p.n_cubes, top_k), dtype=torch.int32, device=device)
         self.valid = torch.empty((p.batch, p.heads, p.n_cubes), dtype=torch.int32, device=device)
-        self.out_cube = torch.empty(ts, dtype=bf, device=device)
-        self.gc = torch.empty(ts, dtype=bf, device=device) if with_gates else None
-        self.gf = torch.empty(ts, dtype=bf, device=device) if with_gates else None
         self.lse = torch.empty((p.batch, p.heads, p.n_tokens), dtype=f32, device=device) if with_lse else None
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
@@ -45,26 +46,16 @@ class VsaForward:
         L.vsa_permute_pool(p, B, q, self.qp, self.qc, stream)
         L.vsa_permute_pool(p, B, k, self.kp, self.kc, stream)
         L.vsa_permute_pool(p, B, v, self.vp, self.vc, stream)
-        gc = gf = None
-        if gate_c is not None:
-            if self.gc is None:
-                raise ValueError("built without gate buffers (with_gates=False)")
-            L.vsa_permute(p, B, gate_c, self.gc, stream)
-            gc = self.gc
-        if gate_f is not None:
-            if self.gf is None:
-                raise ValueError("built without gate buffers (with_gates=False)")
-            L.vsa_permute(p, B, gate_f, self.gf, stream)
-            gf = self.gf
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
-        L.vsa_sparse_attn_fwd(p, self.qp, self.kp, self.vp, self.lut, self.valid, self.out_cube,
-                              oc=self.oc, gate_c=gc, gate_f=gf, lse=self.lse, stream=stream)
-        L.vsa_unpermute(p, B, self.out_cube, out, stream)
+        # fine attention reading the raster-order gates and writing the
+        # raster-order output directly (the reorder back is in its epilogue)
+        L.vsa_sparse_attn_fwd_raster(p, self.qp, self.kp, self.vp, self.lut, self.valid, out,
+                                     oc=self.oc, gate_c=gate_c, gate_f=gate_f, lse=self.lse, stream=stream)
         return out
 
     def intermediates(self) -> Dict[str, torch.Tensor]:
         d = dict(qp=self.qp, kp=self.kp, vp=self.vp, qc=self.qc, kc=self.kc, vc=self.vc,
-                 oc=self.oc, kv_block_idx=self.lut, valid_block_num=self.valid, out_cube=self.out_cube)
+                 oc=self.oc, kv_block_idx=self.lut, valid_block_num=self.valid)
         if self.lse is not None:
             d["lse"] = self.lse
         return d

@@ -149,6 +149,22 @@ int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k,
                         const void* gate_f, void* out, float* lse,
                         void* stream);
 
+/* vsa_sparse_attn_fwd followed by vsa_unpermute of out (and of lse) in one
+ * pass ([VSA-ROCm] §Two-Stage Architecture: the output is handed back in
+ * the model's token order): q, k, v, kv_block_idx, valid_block_num and oc
+ * as for vsa_sparse_attn_fwd (cube-major); gate_c, gate_f and out are
+ * [batch, heads, N, head_dim] bf16 and lse [batch, heads, N] float32 in
+ * raster (t, h, w) token order.  out[b, h, pi(p), :] holds exactly the bits
+ * vsa_sparse_attn_fwd writes to its out[b, h, p, :] when given the
+ * cube-major gates.  Same requirements and errors as vsa_sparse_attn_fwd. */
+int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q,
+                               const void* k, const void* v,
+                               const int32_t* kv_block_idx,
+                               const int32_t* valid_block_num,
+                               int32_t max_kv_blocks, const float* oc,
+                               const void* gate_c, const void* gate_f,
+                               void* out, float* lse, void* stream);
+
 /* Device-side LUT validator (optional, asynchronous).  Writes to
  * *bad_rows (one device int32) the number of LUT rows whose count is
  * outside [0, max_kv_blocks] or which list a cube outside [0, Nc).

@@ -376,6 +376,42 @@ def test_sparse_attn_empty_rows_give_gated_coarse_output():
     assert err(host64(out), want)[0] <= 2.0 ** -8 * np.abs(want).max()
 
 
+def test_sparse_attn_raster_output_matches_unpermute():
+    """vsa_sparse_attn_fwd_raster = vsa_sparse_attn_fwd on cube-major gates
+    followed by vsa_unpermute of out and lse, bit for bit."""
+    _log("fine raster output")
+    for name, k in (("small", 8), ("wan", 154)):
+        w = wl.WORKLOADS[name]
+        p = problem(w)
+        x = inputs(name, with_gates=True)
+        raster = {n: dev(x[n]) for n in ("q", "k", "v", "gate_c", "gate_f")}
+        cube = {}
+        for n, t in raster.items():
+            cube[n] = torch.empty_like(t)
+            L.vsa_permute(p, L.VSA_BF16, t, cube[n])
+        rng = np.random.default_rng(5)
+        lut = np.sort(rng.permuted(np.tile(np.arange(p.n_cubes, dtype=np.int32), (1, p.heads, p.n_cubes, 1)),
+                                   axis=-1)[..., :k], axis=-1)
+        lut_d, valid_d = dev(lut), dev(np.full((1, p.heads, p.n_cubes), k, np.int32))
+        oc = torch.randn((1, p.heads, p.n_cubes, p.head_dim), device="cuda")
+        out_c = torch.empty_like(cube["q"])
+        lse_c = torch.empty((1, p.heads, p.n_tokens), dtype=torch.float32, device="cuda")
+        L.vsa_sparse_attn_fwd(p, cube["q"], cube["k"], cube["v"], lut_d, valid_d, out_c, oc=oc,
+                              gate_c=cube["gate_c"], gate_f=cube["gate_f"], lse=lse_c)
+        out_r = torch.full_like(out_c, float("nan"))
+        lse_r = torch.full_like(lse_c, float("nan"))
+        L.vsa_sparse_attn_fwd_raster(p, cube["q"], cube["k"], cube["v"], lut_d, valid_d, out_r, oc=oc,
+                                     gate_c=raster["gate_c"], gate_f=raster["gate_f"], lse=lse_r)
+        back = torch.empty_like(out_c)
+        L.vsa_unpermute(p, L.VSA_BF16, out_c, back)
+        _sync()
+        assert np.array_equal(bits(out_r), bits(back)), name
+        pi = oracle.perm_index(w.T, w.H, w.W, *w.cube)
+        lse_back = np.empty_like(lse_c.cpu().numpy())
+        lse_back[..., pi] = lse_c.cpu().numpy()
+        assert np.array_equal(lse_r.cpu().numpy().view(np.uint32), lse_back.view(np.uint32)), name
+
+
 def test_sparse_attn_deterministic():
     _log("sparse_attn_fwd determinism")
     w = wl.WAN
