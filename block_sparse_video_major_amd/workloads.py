@@ -192,3 +192,37 @@ def as_float64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return bf16_bits_to_f32(a).astype(np.float64)
     return a.astype(np.float64)
+
+
+def block_relation_mask(w: Workload, k_importance: int, n_condition: int, seed: int = 4) -> np.ndarray:
+    """A block relation matrix of the kind a block-mask method hands to the
+    fine stage (page "VSA: Accelerating Video Diffusion Inference with Sparse
+    Attention on AMD GPUs", §Comparison with Jenga: the union of an
+    importance mask, a condition mask and an adjacency mask).  Shape
+    [B, heads, Nc, Nc], uint8, 1 = query cube i attends key cube j.  Purely
+    structural stand-ins, drawn per (batch, head) like the activations:
+
+    * importance: k_importance cubes per row chosen uniformly at random;
+    * condition: cubes 0 .. n_condition - 1 for every row (stands in for the
+      blocks that carry the text-condition tokens; this token grid has none);
+    * adjacency: every cube within one cube step in t, h and w (the 3 x 3 x 3
+      neighbourhood in the cube grid, clipped at the edges).
+
+    Row counts therefore vary from row to row.
+    """
+    gT, gH, gW = w.T // w.cube[0], w.H // w.cube[1], w.W // w.cube[2]
+    nc = gT * gH * gW
+    t, h, x = np.meshgrid(np.arange(gT), np.arange(gH), np.arange(gW), indexing="ij")
+    t, h, x = t.ravel(), h.ravel(), x.ravel()
+    adj = ((np.abs(t[:, None] - t[None, :]) <= 1) & (np.abs(h[:, None] - h[None, :]) <= 1)
+           & (np.abs(x[:, None] - x[None, :]) <= 1))
+    out = np.zeros((w.batch, w.heads, nc, nc), dtype=np.uint8)
+    for b in range(w.batch):
+        for hh in range(w.heads):
+            rng = np.random.default_rng(np.random.SeedSequence([seed, b, hh]))
+            imp = np.argsort(rng.random((nc, nc)), axis=1)[:, :k_importance]
+            m = adj.copy()
+            np.put_along_axis(m, imp, True, axis=1)
+            m[:, :n_condition] = True
+            out[b, hh] = m
+    return out

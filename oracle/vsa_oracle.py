@@ -31,6 +31,9 @@ DESIGN.md):
 * R6 Top-K ties go to the lower cube index; LUT rows are stored ascending.
 * R7 a query cube with zero valid blocks gets O_f = 0 and LSE = -inf.
 * R8 a LUT entry listed twice is attended twice (gather semantics).
+* R9 a block relation matrix becomes an index list in ascending order; rows
+  with more selected blocks than the list holds keep the first ones and are
+  counted as overflows.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, invariants, brute force, library special cases); none is
@@ -222,6 +225,33 @@ def fine_attention_masked(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol)
             o = e @ vp[b, h]
             out[b, h] = np.where(has[:, None], o / np.where(has, den, 1.0)[:, None], 0.0)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Block relation matrix -> index list, [VSA-ROCm] §Comparison with Jenga,
+# "Sparse Encoding in CK Tile": a block-mask method keeps the full M x M
+# one-hot relation B (B[i][j] = 1: query block i attends key block j), VSA
+# keeps per query block the selected key-block indices and their count
+# (§Block-Sparse Encoding).  Both describe the same pattern.  Reading R9:
+# indices are listed in ascending order; a row with more than max_kv
+# selected blocks keeps its first max_kv and is counted as an overflow.
+# ---------------------------------------------------------------------------
+
+def mask_to_lut(mask: np.ndarray, max_kv: int):
+    """Returns (kv_block_idx, valid_block_num, overflow_rows) for a relation
+    matrix [..., M, M]; entries past a row's count are 0."""
+    m = np.asarray(mask) != 0
+    lead, M = m.shape[:-2], m.shape[-2]
+    lut = np.zeros(lead + (M, max_kv), dtype=np.int32)
+    valid = np.zeros(lead + (M,), dtype=np.int32)
+    overflow = 0
+    for idx in np.ndindex(*lead, M):
+        cols = [j for j in range(m.shape[-1]) if m[idx][j]]
+        n = min(len(cols), max_kv)
+        lut[idx][:n] = cols[:n]
+        valid[idx] = n
+        overflow += int(len(cols) > max_kv)
+    return lut, valid, overflow
 
 
 # ---------------------------------------------------------------------------

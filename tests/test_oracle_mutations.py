@@ -11,11 +11,12 @@ import oracle
 from oracle import vsa_oracle as vo
 import test_oracle_coarse as tc
 import test_oracle_fine as tf
+import test_oracle_mask as tm
 import test_oracle_reorder as tr
 from block_sparse_video_major_amd import workloads as wl
 
 
-_ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine")}
+_ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut")}
 
 
 def _raster_perm(T, H, W, ct, ch, cw):
@@ -57,6 +58,30 @@ def _combine_swapped(of, oc, vol, gate_c=None, gate_f=None):
     return _ORIG["combine"](of, oc, vol, gate_f, gate_c)
 
 
+def _mask_descending(mask, max_kv):
+    lut, valid, over = _ORIG["mask_to_lut"](mask, max_kv)
+    out = lut.copy()
+    for idx in np.ndindex(*valid.shape):
+        n = valid[idx]
+        out[idx][:n] = lut[idx][:n][::-1]
+    return out, valid, over
+
+
+def _mask_transposed(mask, max_kv):
+    return _ORIG["mask_to_lut"](np.swapaxes(np.asarray(mask), -1, -2), max_kv)
+
+
+def _mask_last_blocks_on_overflow(mask, max_kv):
+    m = np.asarray(mask)[..., ::-1]
+    lut, valid, over = _ORIG["mask_to_lut"](m, max_kv)
+    nc = m.shape[-1]
+    out = lut.copy()
+    for idx in np.ndindex(*valid.shape):
+        n = valid[idx]
+        out[idx][:n] = np.sort(nc - 1 - lut[idx][:n])
+    return out, valid, over
+
+
 def _pins():
     """The pin checks, called directly (each raises AssertionError on failure)."""
     yield lambda: tr.test_each_block_is_one_cube_in_raster_cube_order((4, 8, 8), (4, 4, 4))
@@ -71,6 +96,9 @@ def _pins():
     yield lambda: tf.test_gather_equals_materialised_mask(wl.TINY)
     yield lambda: tf.test_single_block_is_attention_inside_one_cube()
     yield lambda: tf.test_gates_select_fine_or_coarse()
+    yield lambda: tm.test_relation_matrix_of_a_topk_lut_gives_the_lut_back()
+    yield lambda: tm.test_masked_fine_attention_is_dense_masked_softmax()
+    yield lambda: tm.test_overflow_rows_are_counted_and_keep_their_first_blocks()
 
 
 MUTATIONS = {
@@ -83,6 +111,9 @@ MUTATIONS = {
     "fine uses Q where K belongs": ("fine_attention", _fine_q_for_k),
     "fine reads the neighbouring cube": ("fine_attention", _fine_shifted_block),
     "gates swapped": ("combine", _combine_swapped),
+    "mask rows listed descending": ("mask_to_lut", _mask_descending),
+    "mask read transposed": ("mask_to_lut", _mask_transposed),
+    "mask overflow keeps the last blocks": ("mask_to_lut", _mask_last_blocks_on_overflow),
 }
 
 
