@@ -195,6 +195,28 @@ def main() -> int:
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 acc[n] += e[i].elapsed_time(e[i + 1]) / reps
+        # second workload: a block relation matrix (union of importance,
+        # condition and adjacency masks; a different count per row) converted
+        # by vsa_mask_to_lut and run through the fine kernel
+        mask = wl.block_relation_mask(w, 48, 4)
+        maxk = int(mask.astype(np.int64).sum(axis=-1).max())
+        mask_d = torch.from_numpy(mask).to(dev)
+        lut_m = torch.zeros((w.batch, w.heads, w.n_cubes, maxk), dtype=torch.int32, device=dev)
+        valid_m = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
+        over_m = torch.empty((1,), dtype=torch.int32, device=dev)
+        mt = {"mask_to_lut": 0.0, "fine": 0.0}
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            L.vsa_mask_to_lut(p, mask_d, lut_m, valid_m, over_m, stream)
+            e[1].record(stream)
+            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, lut_m, valid_m, out_cube, oc=f.oc, stream=stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            mt["mask_to_lut"] += e[0].elapsed_time(e[1]) / reps
+            mt["fine"] += e[1].elapsed_time(e[2]) / reps
+        pairs_m = int(valid_m.sum().item())
+        flops_m = 4 * 64 * 64 * w.head_dim * pairs_m   # per selected (query cube, key cube) pair
     torch.cuda.synchronize()
 
     flops = w.selected_flops()
@@ -232,6 +254,11 @@ def main() -> int:
                         "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
                         "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9, 1),
                         "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
+        "mask_workload": {"pattern": "union of 48 random + 4 fixed + 3x3x3-neighbour key cubes per query cube",
+                          "mean_key_cubes_per_query_cube": round(pairs_m / (w.batch * w.heads * w.n_cubes), 1),
+                          "overflow_rows": int(over_m.item()),
+                          "mask_to_lut_ms": round(mt["mask_to_lut"], 4), "fine_ms": round(mt["fine"], 4),
+                          "fine_tflops": round(flops_m / (mt["fine"] * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},

@@ -94,6 +94,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_sparse_attn_fwd_raster": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_check_lut": [P, vp, vp, i32, vp, vp],
+        "vsa_mask_to_lut": [P, vp, i32, vp, vp, vp, vp],
         "vsa_perm_index": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
@@ -273,3 +274,19 @@ def vsa_check_lut(p: Problem, kv_block_idx: torch.Tensor, valid_block_num: torch
     _need(bad_rows, "bad_rows", (1,), torch.int32, dev)
     _check(load().vsa_check_lut(ctypes.byref(p.c_struct()), _ptr(kv_block_idx), _ptr(valid_block_num),
                                 int(max_kv), _ptr(bad_rows), _stream(stream, dev)), "vsa_check_lut")
+
+
+def vsa_mask_to_lut(p: Problem, mask: torch.Tensor, kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                    overflow_rows: torch.Tensor, stream=None) -> None:
+    """Block relation matrix [B, heads, Nc, Nc] (uint8) -> LUT rows and counts."""
+    dev = mask.device
+    _need(mask, "mask", (p.batch, p.heads, p.n_cubes, p.n_cubes), torch.uint8)
+    if kv_block_idx.dim() != 4:
+        raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
+    max_kv = kv_block_idx.shape[-1]
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    _need(overflow_rows, "overflow_rows", (1,), torch.int32, dev)
+    _check(load().vsa_mask_to_lut(ctypes.byref(p.c_struct()), _ptr(mask), int(max_kv), _ptr(kv_block_idx),
+                                  _ptr(valid_block_num), _ptr(overflow_rows), _stream(stream, dev)),
+           "vsa_mask_to_lut")

@@ -171,4 +171,16 @@ int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32
                                           (hipStream_t)stream));
 }
 
+int vsa_mask_to_lut(const vsa_problem* p, const uint8_t* mask, int32_t max_kv_blocks, int32_t* kv_block_idx,
+                    int32_t* valid_block_num, int32_t* overflow_rows, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (mask == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr || overflow_rows == nullptr)
+    return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  return hip_status(vsa::launch_mask_to_lut(g, mask, max_kv_blocks, kv_block_idx, valid_block_num, overflow_rows,
+                                            (hipStream_t)stream));
+}
+
 }  // extern "C"

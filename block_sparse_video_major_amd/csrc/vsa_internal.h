@@ -51,6 +51,8 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
                                   void* out, float* lse, bool raster_out, hipStream_t s);
 hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* valid, int max_kv,
                             int32_t* bad_rows, hipStream_t s);
+hipError_t launch_mask_to_lut(const Geom& g, const uint8_t* mask, int max_kv, int32_t* lut, int32_t* valid,
+                              int32_t* overflow_rows, hipStream_t s);
 
 // Largest number of cubes per (batch, head) the coarse stage handles.
 constexpr int64_t kMaxCoarseCubes = 4096;

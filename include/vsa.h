@@ -174,6 +174,25 @@ int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx,
                   const int32_t* valid_block_num, int32_t max_kv_blocks,
                   int32_t* bad_rows, void* stream);
 
+/* Block relation matrix -> index list ([VSA-ROCm] §Comparison with Jenga,
+ * "Sparse Encoding in CK Tile", and §Block-Sparse Encoding): turns the M x M
+ * one-hot encoding a block-mask method keeps into the LUT the fine kernel
+ * consumes, so such patterns (e.g. a union of importance, condition and
+ * adjacency masks, with a different count per row) run on
+ * vsa_sparse_attn_fwd unchanged.
+ * mask: [batch, heads, Nc, Nc] uint8 on the device, nonzero = query cube i
+ *   attends key cube j.
+ * kv_block_idx: [batch, heads, Nc, max_kv_blocks] int32: the j of each row
+ *   with mask != 0, ascending; entries past the row's count are not written.
+ * valid_block_num: [batch, heads, Nc] int32 = min(row count, max_kv_blocks).
+ * overflow_rows: one device int32, set to the number of rows with more than
+ *   max_kv_blocks selected cubes (those keep their first max_kv_blocks).
+ * max_kv_blocks in [1, Nc], else VSA_ERR_TOPK. */
+int vsa_mask_to_lut(const vsa_problem* p, const uint8_t* mask,
+                    int32_t max_kv_blocks, int32_t* kv_block_idx,
+                    int32_t* valid_block_num, int32_t* overflow_rows,
+                    void* stream);
+
 /* Host helper: perm_host[p] = pi(p) for p < N (the order vsa_permute
  * applies).  perm_host is a host array of N int32.  No device work. */
 int vsa_perm_index(const vsa_problem* p, int32_t* perm_host);

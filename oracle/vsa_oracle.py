@@ -31,7 +31,7 @@ DESIGN.md):
 * R6 Top-K ties go to the lower cube index; LUT rows are stored ascending.
 * R7 a query cube with zero valid blocks gets O_f = 0 and LSE = -inf.
 * R8 a LUT entry listed twice is attended twice (gather semantics).
-* R9 a block relation matrix becomes an index list in ascending order; rows
+* R15 a block relation matrix becomes an index list in ascending order; rows
   with more selected blocks than the list holds keep the first ones and are
   counted as overflows.
 
@@ -232,7 +232,7 @@ def fine_attention_masked(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol)
 # "Sparse Encoding in CK Tile": a block-mask method keeps the full M x M
 # one-hot relation B (B[i][j] = 1: query block i attends key block j), VSA
 # keeps per query block the selected key-block indices and their count
-# (§Block-Sparse Encoding).  Both describe the same pattern.  Reading R9:
+# (§Block-Sparse Encoding).  Both describe the same pattern.  Reading R15:
 # indices are listed in ascending order; a row with more than max_kv
 # selected blocks keeps its first max_kv and is counted as an overflow.
 # ---------------------------------------------------------------------------

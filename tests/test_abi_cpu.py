@@ -100,6 +100,18 @@ def test_permute_pool_errors():
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 2, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
 
 
+def test_mask_to_lut_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob())          # Nc = 32
+    assert lib.vsa_mask_to_lut(pr, None, 4, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_mask_to_lut(pr, DUMMY, 4, None, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_mask_to_lut(pr, DUMMY, 4, DUMMY, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_mask_to_lut(pr, DUMMY, 4, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_mask_to_lut(pr, DUMMY, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
+    assert lib.vsa_mask_to_lut(pr, DUMMY, 33, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
+    assert lib.vsa_mask_to_lut(ctypes.byref(_prob(H=10)), DUMMY, 4, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+
+
 def test_coarse_topk_errors():
     lib = _raw()
     pr = ctypes.byref(_prob())          # Nc = 8*16*16/64 = 32

@@ -480,6 +480,112 @@ def test_check_lut():
     assert int(counter.item()) == 0
 
 
+# ------------------------------------------------------------------ block relation matrix -> LUT
+MASKS = [("small-random", "small", None), ("small-overflow", "small", 6), ("wan-union", "wan", None),
+         ("large-union", "large", None)]
+
+
+def _mask_for(name, w):
+    if name.endswith("random"):
+        rng = np.random.default_rng(31)
+        m = (rng.random((w.batch, w.heads, w.n_cubes, w.n_cubes)) < 0.3).astype(np.uint8)
+        m[0, 0, 0, :] = 0
+        m[0, 1, 1, :] = 1
+        return m
+    if name.endswith("overflow"):
+        return np.tril(np.ones((w.n_cubes, w.n_cubes), np.uint8))[None, None].repeat(w.heads, axis=1)
+    return wl.block_relation_mask(w, 48 if w.name == "wan" else 64, 4)
+
+
+@pytest.mark.parametrize("case,name,maxk", MASKS, ids=[m[0] for m in MASKS])
+def test_mask_to_lut(case, name, maxk):
+    """Converted rows and counts match the oracle exactly; entries past a
+    row's count stay untouched; the overflow count is exact."""
+    _log(f"mask_to_lut {case}")
+    w = wl.WORKLOADS[name]
+    p = problem(w)
+    mask = _mask_for(case, w)
+    rows_max = int(mask.astype(np.int64).sum(axis=-1).max())
+    maxk = maxk or rows_max
+    lut = torch.full((w.batch, w.heads, w.n_cubes, maxk), -7, dtype=torch.int32, device="cuda")
+    valid = torch.full((w.batch, w.heads, w.n_cubes), -7, dtype=torch.int32, device="cuda")
+    over = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    L.vsa_mask_to_lut(p, torch.from_numpy(mask).cuda(), lut, valid, over)
+    _sync()
+    hs = [0, w.heads - 1] if w.heads > 4 else list(range(w.heads))
+    want_lut, want_valid, want_over = oracle.mask_to_lut(mask[:, hs], maxk)
+    got_lut, got_valid = lut.cpu().numpy()[:, hs], valid.cpu().numpy()[:, hs]
+    assert np.array_equal(got_valid, want_valid)
+    for idx in np.ndindex(*want_valid.shape):
+        n = want_valid[idx]
+        assert np.array_equal(got_lut[idx][:n], want_lut[idx][:n]), idx
+        assert np.all(got_lut[idx][n:] == -7), idx
+    total_over = int((mask.astype(np.int64).sum(axis=-1) > maxk).sum())
+    assert int(over.item()) == total_over
+    if len(hs) == w.heads:
+        assert want_over == total_over
+
+
+def test_mask_to_lut_odd_cube_count():
+    """Nc = 45 (not a multiple of 4: one mask byte per lane per pass)."""
+    _log("mask_to_lut odd Nc")
+    p = L.Problem(2, 3, 12, 12, 20, 4, 4, 4, 64)    # Nc = 3 * 3 * 5 = 45
+    nc = p.n_cubes
+    rng = np.random.default_rng(32)
+    mask = (rng.random((2, 3, nc, nc)) < 0.5).astype(np.uint8)
+    mask[1, 2, 7, :] = 0
+    maxk = 20
+    lut = torch.full((2, 3, nc, maxk), -7, dtype=torch.int32, device="cuda")
+    valid = torch.full((2, 3, nc), -7, dtype=torch.int32, device="cuda")
+    over = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    L.vsa_mask_to_lut(p, torch.from_numpy(mask).cuda(), lut, valid, over)
+    _sync()
+    want_lut, want_valid, want_over = oracle.mask_to_lut(mask, maxk)
+    got_lut, got_valid = lut.cpu().numpy(), valid.cpu().numpy()
+    assert np.array_equal(got_valid, want_valid)
+    for idx in np.ndindex(*want_valid.shape):
+        n = want_valid[idx]
+        assert np.array_equal(got_lut[idx][:n], want_lut[idx][:n]), idx
+    assert int(over.item()) == want_over
+
+
+@pytest.mark.parametrize("name", ["small", "wan"])
+def test_sparse_attn_on_union_mask(name):
+    """The fine kernel on the LUT of a union mask (importance + condition +
+    adjacency; a different count per row) against the oracle on the same
+    list.  The pattern comes from vsa_mask_to_lut."""
+    _log(f"sparse_attn on union mask {name}")
+    w = wl.WORKLOADS[name]
+    p = problem(w)
+    x = inputs(w.name, with_gates=False)
+    pi = oracle.perm_index(w.T, w.H, w.W, *w.cube)
+    mask = wl.block_relation_mask(w, 48 if name == "wan" else 3, 2)
+    maxk = int(mask.astype(np.int64).sum(axis=-1).max())
+    lut = torch.zeros((w.batch, w.heads, w.n_cubes, maxk), dtype=torch.int32, device="cuda")
+    valid = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device="cuda")
+    over = torch.empty((1,), dtype=torch.int32, device="cuda")
+    L.vsa_mask_to_lut(p, torch.from_numpy(mask).cuda(), lut, valid, over)
+    xp = {n: np.take(x[n], pi, axis=2) for n in ("q", "k", "v")}
+    q, kk, v = (dev(xp[n]) for n in ("q", "k", "v"))
+    out = torch.full_like(q, float("nan"))
+    lse_t = torch.full((p.batch, p.heads, p.n_tokens), float("nan"), device="cuda")
+    L.vsa_sparse_attn_fwd(p, q, kk, v, lut, valid, out, lse=lse_t)
+    _sync()
+    assert int(over.item()) == 0
+    hs = [0, w.heads - 1] if w.heads > 4 else list(range(w.heads))
+    cubes = _all_cubes(w) if name == "small" else _sampled_cubes(w)
+    lut_h, valid_h, _ = oracle.mask_to_lut(mask[:, hs], maxk)
+    q64, k64, v64 = (wl.as_float64(xp[n][:, hs]) for n in ("q", "k", "v"))
+    of, lse_w = oracle.fine_attention(q64, k64, v64, lut_h, valid_h, 1.0 / math.sqrt(w.head_dim),
+                                      w.cube_volume, query_cubes=[(0, hi, i) for hi in range(len(hs)) for i in cubes])
+    rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in cubes])
+    got = host64(out)[:, hs]
+    mx, mean = assert_out_close(got[:, :, rows], of[:, :, rows], f"union mask {name}")
+    le = err(host64(lse_t)[:, hs][:, :, rows], lse_w[:, :, rows])
+    assert le[0] <= LSE_MAX_ABS, f"lse max-abs {le[0]:.3e}"
+    print(f"row counts {int(valid_h.min())}..{int(valid_h.max())}; max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
 # ------------------------------------------------------------------ whole pipeline
 def _pipeline_case(w, k, cubes, heads_checked):
     p = problem(w)

@@ -3,7 +3,7 @@
 Source: "VSA: Accelerating Video Diffusion Inference with Sparse Attention on
 AMD GPUs", §Comparison with Jenga ("Sparse Encoding in CK Tile": a block-mask
 method stores the M x M one-hot relation matrix, VSA the selected indices and
-their count) and §Block-Sparse Encoding.  Reading R9: ascending order; rows
+their count) and §Block-Sparse Encoding.  Reading R15: ascending order; rows
 with more selected blocks than the list holds keep the first ones and count
 as overflows.
 """
