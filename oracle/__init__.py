@@ -6,5 +6,5 @@ leg may import this package; the product path never does.
 from .vsa_oracle import (  # noqa: F401
     check_grid, perm_index, permute, unpermute, pool, coarse_scores,
     softmax_rows, coarse_attention, topk_lut, fine_attention,
-    fine_attention_masked, combine, vsa_forward, mask_to_lut,
+    fine_attention_masked, fine_attention_bwd, combine, vsa_forward, mask_to_lut,
 )

@@ -197,6 +197,49 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     return of, lse
 
 
+def fine_attention_bwd(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
+                       kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
+                       scale: float, vol: int, of: np.ndarray, lse: np.ndarray,
+                       dof: np.ndarray):
+    """Gradients of the fine stage ([VSA-arXiv] Abstract: the method is
+    trained end to end; the forward is the block-sparse softmax attention of
+    fine_attention).  For query cube i with key rows R (the listed cubes'
+    tokens, in LUT order, R8), P = exp(scale * Q_i K_R^T - LSE_i) is the
+    attention matrix of the forward; with D = rowsum(dO_i * O_i):
+        dV_R += P^T dO_i,   dP = dO_i V_R^T,   dS = P * (dP - D),
+        dQ_i  = scale * dS K_R,   dK_R += scale * dS^T Q_i.
+    A cube listed twice receives both contributions.  Returns (dq, dk, dv),
+    cube-major like the inputs."""
+    qp = np.asarray(qp, np.float64)
+    kp = np.asarray(kp, np.float64)
+    vp = np.asarray(vp, np.float64)
+    of = np.asarray(of, np.float64)
+    dof = np.asarray(dof, np.float64)
+    B, nh, N, d = qp.shape
+    nc = N // vol
+    dq = np.zeros_like(qp)
+    dk = np.zeros_like(kp)
+    dv = np.zeros_like(vp)
+    for b in range(B):
+        for h in range(nh):
+            for i in range(nc):
+                cnt = int(valid_block_num[b, h, i])
+                if cnt == 0:
+                    continue
+                rows = np.concatenate([np.arange(j * vol, j * vol + vol)
+                                       for j in kv_block_idx[b, h, i, :cnt]])
+                qs = slice(i * vol, (i + 1) * vol)
+                q, do, o = qp[b, h, qs], dof[b, h, qs], of[b, h, qs]
+                p = np.exp(scale * (q @ kp[b, h, rows].T) - lse[b, h, qs][:, None])
+                dmat = (do * o).sum(axis=1, keepdims=True)
+                dp = do @ vp[b, h, rows].T
+                ds = p * (dp - dmat)
+                dq[b, h, qs] = scale * (ds @ kp[b, h, rows])
+                np.add.at(dk[b, h], rows, scale * (ds.T @ q))
+                np.add.at(dv[b, h], rows, p.T @ do)
+    return dq, dk, dv
+
+
 def fine_attention_masked(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol):
     """Brute-force form of the same stage: the full N x N mask in which a
     selected cube pair (i, j) expands to a vol x vol block of allowed entries

@@ -11,12 +11,14 @@ import oracle
 from oracle import vsa_oracle as vo
 import test_oracle_coarse as tc
 import test_oracle_fine as tf
+import test_oracle_bwd as tb
 import test_oracle_mask as tm
 import test_oracle_reorder as tr
 from block_sparse_video_major_amd import workloads as wl
 
 
-_ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut")}
+_ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut",
+                                     "fine_attention_bwd")}
 
 
 def _raster_perm(T, H, W, ct, ch, cw):
@@ -82,6 +84,21 @@ def _mask_last_blocks_on_overflow(mask, max_kv):
     return out, valid, over
 
 
+def _bwd_dk_no_scale(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
+    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof)
+    return dq, dk / scale, dv
+
+
+def _bwd_no_rowsum_term(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
+    # D = rowsum(dO * O) dropped: equivalent to passing O = 0
+    return _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, np.zeros_like(of), lse, dof)
+
+
+def _bwd_dv_from_q(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
+    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof)
+    return dq, dk, dq
+
+
 def _pins():
     """The pin checks, called directly (each raises AssertionError on failure)."""
     yield lambda: tr.test_each_block_is_one_cube_in_raster_cube_order((4, 8, 8), (4, 4, 4))
@@ -96,6 +113,8 @@ def _pins():
     yield lambda: tf.test_gather_equals_materialised_mask(wl.TINY)
     yield lambda: tf.test_single_block_is_attention_inside_one_cube()
     yield lambda: tf.test_gates_select_fine_or_coarse()
+    yield lambda: tb.test_backward_matches_autograd_with_duplicates_and_empty_rows()
+    yield lambda: tb.test_dv_of_uniform_attention_is_column_sum()
     yield lambda: tm.test_relation_matrix_of_a_topk_lut_gives_the_lut_back()
     yield lambda: tm.test_masked_fine_attention_is_dense_masked_softmax()
     yield lambda: tm.test_overflow_rows_are_counted_and_keep_their_first_blocks()
@@ -112,6 +131,9 @@ MUTATIONS = {
     "fine reads the neighbouring cube": ("fine_attention", _fine_shifted_block),
     "gates swapped": ("combine", _combine_swapped),
     "mask rows listed descending": ("mask_to_lut", _mask_descending),
+    "backward dK without the softmax scale": ("fine_attention_bwd", _bwd_dk_no_scale),
+    "backward dS without the rowsum(dO*O) term": ("fine_attention_bwd", _bwd_no_rowsum_term),
+    "backward dV taken from dQ": ("fine_attention_bwd", _bwd_dv_from_q),
     "mask read transposed": ("mask_to_lut", _mask_transposed),
     "mask overflow keeps the last blocks": ("mask_to_lut", _mask_last_blocks_on_overflow),
 }
