@@ -216,6 +216,26 @@ def main() -> int:
             mt["mask_to_lut"] += e[0].elapsed_time(e[1]) / reps
             mt["fine"] += e[1].elapsed_time(e[2]) / reps
         pairs_m = int(valid_m.sum().item())
+
+        # sparsity sweep (a diffusion run changes the sparsity from step to
+        # step): coarse stage + fine kernel at each Top-K on the same inputs
+        sweep = {}
+        for kk in wl.SWEEP_TOPK:
+            lut_s = torch.empty((w.batch, w.heads, w.n_cubes, kk), dtype=torch.int32, device=dev)
+            valid_s = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
+            L.vsa_coarse_topk(p, kk, f.qc, f.kc, f.vc, lut_s, valid_s, f.oc, stream)
+            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
+            tsum = 0.0
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
+                e[1].record(stream)
+                torch.cuda.synchronize()
+                tsum += e[0].elapsed_time(e[1]) / reps
+            fl = w.selected_flops(kk)
+            sweep[str(kk)] = {"sparsity": round(1 - kk / w.n_cubes, 3), "fine_ms": round(tsum, 4),
+                              "fine_tflops": round(fl / (tsum * 1e-3) / 1e12, 2)}
         flops_m = 4 * 64 * 64 * w.head_dim * pairs_m   # per selected (query cube, key cube) pair
     torch.cuda.synchronize()
 
@@ -254,6 +274,7 @@ def main() -> int:
                         "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
                         "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9, 1),
                         "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
+        "topk_sweep": sweep,
         "mask_workload": {"pattern": "union of 48 random + 4 fixed + 3x3x3-neighbour key cubes per query cube",
                           "mean_key_cubes_per_query_cube": round(pairs_m / (w.batch * w.heads * w.n_cubes), 1),
                           "overflow_rows": int(over_m.item()),
