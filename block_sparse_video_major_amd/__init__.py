@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     Problem, VsaError, VSA_BF16, VSA_F32, load,
     vsa_permute, vsa_unpermute, vsa_pool, vsa_coarse_topk, vsa_sparse_attn_fwd,
     vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
+    vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size,
+    vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
 )
 from .pipeline import VsaForward, vsa_forward  # noqa: F401
 
@@ -16,4 +18,6 @@ __all__ = [
     "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
     "vsa_permute", "vsa_unpermute", "vsa_pool", "vsa_coarse_topk", "vsa_sparse_attn_fwd",
     "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
+    "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size",
+    "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
 ]

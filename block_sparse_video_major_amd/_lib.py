@@ -28,6 +28,7 @@ VSA_ERR_TOPK = -3
 VSA_ERR_UNSUPPORTED = -4
 VSA_ERR_HIP = -5
 VSA_ERR_LUT = -6
+VSA_ERR_WORKSPACE = -7
 
 
 class VsaError(RuntimeError):
@@ -95,6 +96,8 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd_raster": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_check_lut": [P, vp, vp, i32, vp, vp],
         "vsa_mask_to_lut": [P, vp, i32, vp, vp, vp, vp],
+        "vsa_sparse_attn_bwd_workspace_size": [P, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "vsa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "vsa_perm_index": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
@@ -290,3 +293,38 @@ def vsa_mask_to_lut(p: Problem, mask: torch.Tensor, kv_block_idx: torch.Tensor, 
     _check(load().vsa_mask_to_lut(ctypes.byref(p.c_struct()), _ptr(mask), int(max_kv), _ptr(kv_block_idx),
                                   _ptr(valid_block_num), _ptr(overflow_rows), _stream(stream, dev)),
            "vsa_mask_to_lut")
+
+
+def vsa_sparse_attn_bwd_workspace_size(p: Problem, max_kv_blocks: int) -> int:
+    """Bytes of device workspace vsa_sparse_attn_bwd needs."""
+    n = ctypes.c_size_t(0)
+    _check(load().vsa_sparse_attn_bwd_workspace_size(ctypes.byref(p.c_struct()), int(max_kv_blocks),
+                                                       ctypes.byref(n)), "vsa_sparse_attn_bwd_workspace_size")
+    return int(n.value)
+
+
+def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                        o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor,
+                        dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                        workspace: torch.Tensor, stream=None) -> None:
+    """Gradients of the fine attention (all tensors cube-major; dq, dk, dv float32)."""
+    dev = q.device
+    ts = _tok_shape(p)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _need(t, name, ts, torch.bfloat16, dev)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, ts, torch.float32, dev)
+    if kv_block_idx.dim() != 4:
+        raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
+    max_kv = kv_block_idx.shape[-1]
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
+    if workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D byte tensor")
+    _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    _check(load().vsa_sparse_attn_bwd(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
+                                      _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                      int(workspace.numel()), _stream(stream, dev)), "vsa_sparse_attn_bwd")

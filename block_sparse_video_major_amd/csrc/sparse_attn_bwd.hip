@@ -1,0 +1,653 @@
+// Backward of the fine block-sparse attention stage, for gfx950.
+//
+// "VSA: Faster Video Diffusion with Trainable Sparse Attention", Abstract: the
+// sparse attention is trained end to end, so the fine stage needs gradients
+// with respect to its queries, keys and values.  The function differentiated
+// is the fine attention of "VSA: Accelerating Video Diffusion Inference with
+// Sparse Attention on AMD GPUs", §Two-Stage Architecture (Stage 2), over the
+// index list of §Block-Sparse Encoding: for query cube i and its listed key
+// cubes R, O_i = softmax(scale * Q_i K_R^T) V_R.  With the forward's
+// log-sum-exp LSE and Drow = rowsum(dO * O), the attention matrix is
+// recomputed as P = exp(scale * Q K^T - LSE) and
+//   dP = dO V^T,   dS = P * (dP - Drow),
+//   dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO,
+// each product summed over the listed (query cube, key cube) pairs only.
+//
+// Work decomposition (no atomics on any gradient; every output element is
+// written once, by one workgroup, so results are identical run to run):
+//   * prep: one pass over O and dO writes, per token, the 8-byte record
+//     (LSE * log2 e, Drow), which both gradient kernels read.
+//   * transposed index list: for every key cube, the query cubes whose rows
+//     list it, ascending (a cube listed twice by one row appears twice).  Built
+//     without ordering races in three passes: per block of 16 rows the count
+//     of each key cube, one scan per (batch, head) that turns counts into
+//     list offsets, and a scatter in which one wavefront walks its block's
+//     rows in order (lanes of one instruction that hit the same key cube
+//     carry the same query cube, so their relative order is immaterial).
+//   * dQ kernel: one workgroup (4 wavefronts) per query cube walks the cube's
+//     index row.  Wave w owns query half qh = w & 1 and key half kh = w >> 1.
+//     Scores are formed transposed, S^T = K Q^T and dP^T = V dO^T, with Q and
+//     dO in registers as MFMA B operands, so each lane owns one query and its
+//     LSE and Drow are per-lane scalars; dS^T is formed in registers and
+//     becomes the B operand of dQ^T += K^T dS^T, whose A operand is read from
+//     the K tile with transposing LDS reads.  The two key halves are summed
+//     through LDS at the end.
+//   * dK/dV kernel: one workgroup per key cube walks the cube's transposed
+//     list, with K and V in registers as B operands: S = Q K^T and
+//     dP = dO V^T (rows = queries), P and dS formed in registers (LSE and
+//     Drow of the lane's 16 queries read from LDS), then dV^T += dO^T P and
+//     dK^T += Q^T dS with transposing reads of the dO and Q tiles.  The two
+//     query halves are summed through LDS at the end.
+//   * Tiles (64 tokens x d bf16) arrive by direct global->LDS loads into a
+//     two-stage ring, one barrier per step.  One chunk swizzle serves both LDS
+//     read patterns (16 consecutive rows at one 16-byte chunk, and 4
+//     consecutive rows at 4 consecutive chunks) without bank conflicts.
+//   * Workgroups are mapped to XCDs in contiguous ranges of cubes, so the
+//     workgroups sharing an L2 walk overlapping lists.
+#include "mfma_util.h"
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kBlk = 64;            // tokens per cube
+constexpr int kThreads = 256;       // four wavefronts per cube
+constexpr int kRowsPerBlk = 16;     // LUT rows per block of the transposed-list build
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BCfg {
+  static constexpr int ROWB = D * 2;                       // bytes per token row
+  static constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  static constexpr int TILE = kBlk * ROWB;                 // one 64-token tile
+  static constexpr int LOADS = TILE / (kThreads * 16);     // 16-byte loads per lane per tile
+  static constexpr int OT = D / 32;                        // 32-row tiles of a d x 32 product
+  static constexpr int KS = D / 16;                        // k-steps of a contraction over d
+  static constexpr int SSTR = D + 4;                       // fp32 staging row stride
+  static constexpr int STAGE = kBlk * SSTR * 4;            // one 64 x d fp32 staging tile
+  // Logical 16-byte chunk c of row r sits at c ^ swz(r).  Row reads touch 16
+  // consecutive rows at one chunk: swz is a bijection on every aligned group
+  // of 16 rows (d = 128) or on the 8 rows of one parity in it (d = 64, two
+  // rows per 256 bytes).  Transposing reads touch 4 consecutive rows (aligned
+  // to 4) at 4 consecutive chunks: bits 2-3 of swz differ across those rows.
+  __device__ static constexpr int swz(int r) {
+    return D == 128 ? ((4 * (r & 3)) | ((r >> 2) & 3)) : ((4 * ((r >> 1) & 1)) | ((r >> 2) & 3));
+  }
+};
+
+__device__ __forceinline__ int clamp_cube(int c, int Nc) { return c < 0 ? 0 : (c >= Nc ? Nc - 1 : c); }
+__device__ __forceinline__ int clamp_count(int n, int max_kv) { return n < 0 ? 0 : (n > max_kv ? max_kv : n); }
+
+// One 16-byte direct global->LDS load per lane: base + voff -> lds_base + 16 * lane.
+__device__ __forceinline__ void dma_piece(const void* base, uint32_t voff, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %2"
+      :
+      : "v"(voff), "s"(lds_base), "s"(base)
+      : "memory", "m0");
+}
+
+// Per-lane LDS offsets shared by both gradient kernels.  `half` is the 32-row
+// half of the tile this wave reads as MFMA A operands (key half in the dQ
+// kernel, query half in the dK/dV kernel).
+template <int D>
+struct LaneOffsets {
+  using C = BCfg<D>;
+  uint32_t g_off[C::LOADS];   // direct-load source offsets (minus the instruction offset)
+  int row_off[C::KS];         // row reads: row 32*half + n32, logical chunk 2*ks + g
+  int tr_off[C::OT][2];       // transposing reads, row step 8*hi
+  __device__ __forceinline__ LaneOffsets(int wave, int lane, int half) {
+    const int n32 = lane & 31, g = lane >> 5, l16 = lane & 15, h16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int n = 0; n < C::LOADS; ++n) {
+      const int L = (wave * C::LOADS + n) * 64 + lane;
+      const int r = L / C::CPR, x = L % C::CPR;
+      g_off[n] = (uint32_t)(r * C::ROWB + ((x ^ C::swz(r)) * 16) - n * 1024);
+    }
+    {
+      const int r = 32 * half + n32;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = r * C::ROWB + (((2 * ks + g) ^ C::swz(r)) * 16);
+    }
+    // Source lane l16 of a transposing read addresses row
+    // 32*half + 16*j + 8*hi + 4*g + l16/4 and columns 32*t + 16*h16 + 4*(l16%4);
+    // the 16*j row step leaves the swizzle unchanged and is added at the read.
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 32 * half + 8 * hi + 4 * g + (l16 >> 2);
+      const int byte_base = 32 * h16 + 8 * (l16 & 3);
+#pragma unroll
+      for (int t = 0; t < C::OT; ++t) {
+        const int b = 64 * t + byte_base;
+        tr_off[t][hi] = r * C::ROWB + ((((b >> 4) ^ C::swz(r)) << 4) | (b & 15));
+      }
+    }
+  }
+};
+
+// A operand of a d x 16 block of a transposed tile: for k-step j, the lane of
+// (g, row m) receives tile rows 32*half + 16*j + 4*g + {0..3, 8..11} at column
+// 32*t + m, the row order in which a lane of an accumulator holds its 16 rows.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const char* tile, const LaneOffsets<D>& o, int t, int j) {
+  using C = BCfg<D>;
+  const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o.tr_off[t][0] + (16 * j) * C::ROWB));
+  const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o.tr_off[t][1] + (16 * j) * C::ROWB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 32 tokens x d of a cube tile as MFMA B operands: token 32*half + n32,
+// columns 16*s + 8*g + 0..7.
+template <int D>
+__device__ __forceinline__ void load_b_operand(const __bf16* tile_rows, int half, int lane, bf16x8 (&f)[D / 16]) {
+  const __bf16* row = tile_rows + (int64_t)(32 * half + (lane & 31)) * D + 8 * (lane >> 5);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = *reinterpret_cast<const bf16x8*>(row + 16 * s);
+}
+
+// Accumulator tiles acc[t] (rows d = 32*t + 8*(r/4) + 4*g + r%4, column = this
+// lane's token 32*half + n32) to and from an fp32 staging tile [64][SSTR].
+template <int D>
+__device__ __forceinline__ void stage_store(float* stg, const f32x16 (&acc)[D / 32], int half, int lane,
+                                            float mul) {
+  using C = BCfg<D>;
+  float* row = stg + (32 * half + (lane & 31)) * C::SSTR + 4 * (lane >> 5);
+#pragma unroll
+  for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      float4 w;
+      w.x = acc[t][4 * rq + 0] * mul;
+      w.y = acc[t][4 * rq + 1] * mul;
+      w.z = acc[t][4 * rq + 2] * mul;
+      w.w = acc[t][4 * rq + 3] * mul;
+      *reinterpret_cast<float4*>(row + 32 * t + 8 * rq) = w;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_add(float* stg, const f32x16 (&acc)[D / 32], int half, int lane, float mul) {
+  using C = BCfg<D>;
+  float* row = stg + (32 * half + (lane & 31)) * C::SSTR + 4 * (lane >> 5);
+#pragma unroll
+  for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      float4* p = reinterpret_cast<float4*>(row + 32 * t + 8 * rq);
+      const float4 u = *p;
+      float4 w;
+      w.x = (acc[t][4 * rq + 0] + u.x) * mul;
+      w.y = (acc[t][4 * rq + 1] + u.y) * mul;
+      w.z = (acc[t][4 * rq + 2] + u.z) * mul;
+      w.w = (acc[t][4 * rq + 3] + u.w) * mul;
+      *p = w;
+    }
+}
+
+// Coalesced copy of a staged 64 x d fp32 tile to 64 consecutive token rows.
+template <int D>
+__device__ __forceinline__ void stage_flush(const float* stg, float* dst, int tid) {
+  using C = BCfg<D>;
+  constexpr int V4 = D / 4;   // float4 per row
+#pragma unroll
+  for (int u = 0; u < kBlk * V4 / kThreads; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / V4, col = c % V4;
+    *reinterpret_cast<float4*>(dst + (int64_t)row * D + 4 * col) =
+        *reinterpret_cast<const float4*>(stg + row * C::SSTR + 4 * col);
+  }
+}
+
+// Sliding 64-entry register window over an int32 list: lane l holds
+// list[win + l]; entries are clamped to [0, Nc).
+struct ListWindow {
+  const int32_t* list;
+  int n, Nc, win, w;
+  __device__ __forceinline__ ListWindow(const int32_t* l, int n_, int Nc_, int lane)
+      : list(l), n(n_), Nc(Nc_), win(0) {
+    w = lane < n ? clamp_cube(list[lane], Nc) : 0;
+  }
+  __device__ __forceinline__ int at(int s, int lane) {   // s ascending, wave-uniform
+    if (s - win >= 64) {
+      win += 64;
+      w = win + lane < n ? clamp_cube(list[win + lane], Nc) : 0;
+    }
+    return __builtin_amdgcn_readlane(w, s - win);
+  }
+};
+
+// ---- prep: (LSE * log2 e, Drow) per token ------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ o,
+                                                       const __bf16* __restrict__ dout,
+                                                       const float* __restrict__ lse, float2* __restrict__ ld,
+                                                       int64_t total) {
+  constexpr int TPT = D / 8;   // lanes per token, 8 elements each
+  const int64_t tok = (int64_t)blockIdx.x * (256 / TPT) + threadIdx.x / TPT;
+  const int part = threadIdx.x % TPT;
+  float acc = 0.f;
+  if (tok < total) {
+    float a[8], b[8];
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(o + tok * D + part * 8), a);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(dout + tok * D + part * 8), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+  }
+#pragma unroll
+  for (int m = TPT / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (tok < total && part == 0) ld[tok] = make_float2(lse[tok] * kLog2e, acc);
+}
+
+// ---- transposed index list ----------------------------------------------------
+// blkcnt[bh][rb][j] = how often rows 16*rb .. 16*rb + 15 of (b, h) list key cube j.
+__global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ lut,
+                                                        const int32_t* __restrict__ valid, int max_kv, int Nc,
+                                                        int nrb, int32_t* __restrict__ blkcnt) {
+  extern __shared__ int cnt[];
+  const int64_t bh = blockIdx.x / nrb;
+  const int rb = (int)(blockIdx.x - bh * nrb);
+  for (int j = threadIdx.x; j < Nc; j += 256) cnt[j] = 0;
+  __syncthreads();
+  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nc ? r0 + kRowsPerBlk : Nc;
+  for (int i = r0; i < r1; ++i) {
+    const int64_t row = bh * Nc + i;
+    const int n = clamp_count(valid[row], max_kv);
+    for (int e = threadIdx.x; e < n; e += 256) atomicAdd(&cnt[clamp_cube(lut[row * max_kv + e], Nc)], 1);
+  }
+  __syncthreads();
+  int32_t* out = blkcnt + (bh * nrb + rb) * (int64_t)Nc;
+  for (int j = threadIdx.x; j < Nc; j += 256) out[j] = cnt[j];
+}
+
+// Per (b, h): blkcnt becomes the exclusive prefix over row blocks, and
+// coloff[j] the start of key cube j's list (coloff[Nc] = total entries).
+__global__ __launch_bounds__(256) void csr_scan_kernel(int32_t* __restrict__ blkcnt, int Nc, int nrb,
+                                                       int32_t* __restrict__ coloff) {
+  extern __shared__ int tot[];
+  __shared__ int part[256];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  int32_t* base = blkcnt + bh * nrb * (int64_t)Nc;
+  for (int j = tid; j < Nc; j += 256) {
+    int run = 0;
+    for (int rb = 0; rb < nrb; ++rb) {
+      int32_t* p = base + (int64_t)rb * Nc + j;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
+    tot[j] = run;
+  }
+  __syncthreads();
+  const int per = (Nc + 255) / 256;
+  const int j0 = tid * per, j1 = j0 + per < Nc ? j0 + per : Nc;
+  int s = 0;
+  for (int j = j0; j < j1; ++j) s += tot[j];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int c = part[i];
+      part[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int run = part[tid];
+  int32_t* co = coloff + bh * (int64_t)(Nc + 1);
+  for (int j = j0; j < j1; ++j) {
+    co[j] = run;
+    run += tot[j];
+  }
+  if (tid == 255) co[Nc] = run;
+}
+
+// One wavefront per row block writes the query cube of every listing into its
+// key cube's list, rows in ascending order.
+__global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ lut,
+                                                         const int32_t* __restrict__ valid, int max_kv, int Nc,
+                                                         int nrb, const int32_t* __restrict__ blkcnt,
+                                                         const int32_t* __restrict__ coloff,
+                                                         int32_t* __restrict__ csr) {
+  extern __shared__ int cur[];
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x / nrb;
+  const int rb = (int)(blockIdx.x - bh * nrb);
+  const int32_t* bc = blkcnt + (bh * nrb + rb) * (int64_t)Nc;
+  const int32_t* co = coloff + bh * (int64_t)(Nc + 1);
+  for (int j = lane; j < Nc; j += 64) cur[j] = co[j] + bc[j];
+  __syncthreads();
+  int32_t* out = csr + bh * (int64_t)Nc * max_kv;
+  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nc ? r0 + kRowsPerBlk : Nc;
+  for (int i = r0; i < r1; ++i) {
+    const int64_t row = bh * Nc + i;
+    const int n = clamp_count(valid[row], max_kv);
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + lane;
+      if (e < n) {
+        const int j = clamp_cube(lut[row * max_kv + e], Nc);
+        out[atomicAdd(&cur[j], 1)] = i;
+      }
+    }
+  }
+}
+
+// ---- dQ -------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const int32_t* __restrict__ lut, const int32_t* __restrict__ valid,
+    int max_kv, const float2* __restrict__ ld, float* __restrict__ dq, int Nc, int64_t total_cubes,
+    float c_log2, float scale) {
+  using C = BCfg<D>;
+  constexpr int SLOT = 2 * C::TILE;   // K tile, then V tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = wave & 1, kh = wave >> 1;
+
+  const int64_t cube = xcd_remap(blockIdx.x, total_cubes);   // = LUT row
+  const int64_t bh = cube / Nc;
+  const int ci = (int)(cube - bh * Nc);
+  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;
+  const char* k_head = reinterpret_cast<const char*>(k + head_off);
+  const char* v_head = reinterpret_cast<const char*>(v + head_off);
+  const int n = clamp_count(valid[cube], max_kv);
+  ListWindow lw(lut + cube * (int64_t)max_kv, n, Nc, lane);
+
+  const LaneOffsets<D> off(wave, lane, kh);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * C::LOADS * 1024));
+  auto issue = [&](int s, int stage) {
+    const int cb = lw.at(s, lane);
+    dma_tile(uniform_ptr(k_head + (int64_t)cb * C::TILE), off.g_off, lds0 + stage * SLOT);
+    dma_tile(uniform_ptr(v_head + (int64_t)cb * C::TILE), off.g_off, lds0 + stage * SLOT + C::TILE);
+  };
+  if (n > 0) issue(0, 0);
+
+  // Q and dO of this wave's 32 queries as B operands; this lane's query
+  // 32*qh + n32 has its (LSE * log2 e, Drow) in registers.
+  bf16x8 qf[C::KS], df[C::KS];
+  load_b_operand<D>(q + head_off + (int64_t)ci * kBlk * D, qh, lane, qf);
+  load_b_operand<D>(dout + head_off + (int64_t)ci * kBlk * D, qh, lane, df);
+  const float2 ldv = ld[cube * kBlk + 32 * qh + (lane & 31)];
+  f32x16 acc[C::OT];
+#pragma unroll
+  for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  wait_vmem<0>();
+  __syncthreads();
+
+  for (int s = 0; s < n; ++s) {
+    const int st = s & 1;
+    if (s + 1 < n) issue(s + 1, st ^ 1);
+    const char* kt = smem + st * SLOT;
+    const char* vt = kt + C::TILE;
+    f32x16 sT, pT;   // S^T and dP^T: rows = keys 32*kh + 8*(r/4) + 4*g + r%4, column = query
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sT[r] = 0.f; pT[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + off.row_off[ks]);
+      sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sT, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + off.row_off[ks]);
+      pT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[ks], pT, 0, 0, 0);
+    }
+    // dS^T = P^T * (dP^T - Drow) as the B operand of k-steps j = 0, 1
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sT[r], c_log2, -ldv.x));
+      dsb[r >> 3][r & 7] = (__bf16)(p * (pT[r] - ldv.y));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < C::OT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kt, off, t, j), dsb[j], acc[t], 0, 0, 0);
+    wait_vmem<0>();
+    __syncthreads();
+  }
+
+  // dQ^T of the two key halves summed through LDS, scaled, stored.
+  float* stg = reinterpret_cast<float*>(smem);
+  if (kh == 1) stage_store<D>(stg, acc, qh, lane, 1.f);
+  __syncthreads();
+  if (kh == 0) stage_add<D>(stg, acc, qh, lane, scale);
+  __syncthreads();
+  stage_flush<D>(stg, dq + head_off + (int64_t)ci * kBlk * D, tid);
+}
+
+// ---- dK, dV ---------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const int32_t* __restrict__ coloff, const int32_t* __restrict__ csr,
+    int max_kv, const float2* __restrict__ ld, float* __restrict__ dk, float* __restrict__ dv, int Nc,
+    int64_t total_cubes, float c_log2, float scale) {
+  using C = BCfg<D>;
+  constexpr int SLOT = 2 * C::TILE + 1024;   // Q tile, dO tile, (LSE log2 e, Drow) of 64 queries
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = wave & 1, kh = wave >> 1;
+  const int g = lane >> 5;
+
+  const int64_t cube = xcd_remap(blockIdx.x, total_cubes);
+  const int64_t bh = cube / Nc;
+  const int cj = (int)(cube - bh * Nc);
+  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;
+  const char* q_head = reinterpret_cast<const char*>(q + head_off);
+  const char* d_head = reinterpret_cast<const char*>(dout + head_off);
+  const char* ld_head = reinterpret_cast<const char*>(ld + bh * (int64_t)Nc * kBlk);
+  const int32_t* co = coloff + bh * (int64_t)(Nc + 1);
+  const int b0 = co[cj];
+  const int n = co[cj + 1] - b0;
+  ListWindow lw(csr + bh * (int64_t)Nc * max_kv + b0, n, Nc, lane);
+
+  const LaneOffsets<D> off(wave, lane, qh);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t lds0 = lds_base + (uint32_t)(wave * C::LOADS * 1024);
+  const uint32_t ld_off = 16u * (uint32_t)(lane & 31);   // 512 bytes; lanes 32-63 repeat them
+  auto issue = [&](int s, int stage) {
+    const int ci = lw.at(s, lane);
+    dma_tile(uniform_ptr(q_head + (int64_t)ci * C::TILE), off.g_off, lds0 + stage * SLOT);
+    dma_tile(uniform_ptr(d_head + (int64_t)ci * C::TILE), off.g_off, lds0 + stage * SLOT + C::TILE);
+    if (wave == 0)
+      dma_piece(uniform_ptr(ld_head + (int64_t)ci * kBlk * 8), ld_off, lds_base + stage * SLOT + 2 * C::TILE);
+  };
+  if (n > 0) issue(0, 0);
+
+  bf16x8 kf[C::KS], vf[C::KS];
+  load_b_operand<D>(k + head_off + (int64_t)cj * kBlk * D, kh, lane, kf);
+  load_b_operand<D>(v + head_off + (int64_t)cj * kBlk * D, kh, lane, vf);
+  f32x16 acc_v[C::OT], acc_k[C::OT];
+#pragma unroll
+  for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { acc_v[t][r] = 0.f; acc_k[t][r] = 0.f; }
+  wait_vmem<0>();
+  __syncthreads();
+
+  for (int s = 0; s < n; ++s) {
+    const int st = s & 1;
+    if (s + 1 < n) issue(s + 1, st ^ 1);
+    const char* qt = smem + st * SLOT;
+    const char* dt = qt + C::TILE;
+    const float* lds_ld = reinterpret_cast<const float*>(qt + 2 * C::TILE);
+    f32x16 sS, dP;   // rows = queries 32*qh + 8*(r/4) + 4*g + r%4, column = key 32*kh + n32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sS[r] = 0.f; dP[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + off.row_off[ks]);
+      sS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sS, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dt + off.row_off[ks]);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dP, 0, 0, 0);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      // records of queries 32*qh + 8*rq + 4*g + 0..3
+      const float* rec = lds_ld + 2 * (32 * qh + 8 * rq + 4 * g);
+      const float4 l0 = *reinterpret_cast<const float4*>(rec);
+      const float4 l1 = *reinterpret_cast<const float4*>(rec + 4);
+      const float lse2[4] = {l0.x, l0.z, l1.x, l1.z};
+      const float drow[4] = {l0.y, l0.w, l1.y, l1.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * rq + u;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sS[r], c_log2, -lse2[u]));
+        pb[r >> 3][r & 7] = (__bf16)p;
+        dsb[r >> 3][r & 7] = (__bf16)(p * (dP[r] - drow[u]));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < C::OT; ++t) {
+        acc_v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(dt, off, t, j), pb[j], acc_v[t], 0, 0, 0);
+        acc_k[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(qt, off, t, j), dsb[j], acc_k[t], 0, 0, 0);
+      }
+    wait_vmem<0>();
+    __syncthreads();
+  }
+
+  // dV^T and dK^T of the two query halves summed through LDS, stored.
+  float* stg_v = reinterpret_cast<float*>(smem);
+  float* stg_k = reinterpret_cast<float*>(smem + C::STAGE);
+  if (qh == 1) {
+    stage_store<D>(stg_v, acc_v, kh, lane, 1.f);
+    stage_store<D>(stg_k, acc_k, kh, lane, 1.f);
+  }
+  __syncthreads();
+  if (qh == 0) {
+    stage_add<D>(stg_v, acc_v, kh, lane, 1.f);
+    stage_add<D>(stg_k, acc_k, kh, lane, scale);
+  }
+  __syncthreads();
+  stage_flush<D>(stg_v, dv + head_off + (int64_t)cj * kBlk * D, tid);
+  stage_flush<D>(stg_k, dk + head_off + (int64_t)cj * kBlk * D, tid);
+}
+
+constexpr int kLdsMax = 160 * 1024;
+
+template <int D>
+constexpr int dq_lds() {
+  using C = BCfg<D>;
+  return 4 * C::TILE > C::STAGE ? 4 * C::TILE : C::STAGE;
+}
+template <int D>
+constexpr int dkdv_lds() {
+  using C = BCfg<D>;
+  return 2 * (2 * C::TILE + 1024) > 2 * C::STAGE ? 2 * (2 * C::TILE + 1024) : 2 * C::STAGE;
+}
+
+template <typename K>
+hipError_t grant_lds(K kern, int bytes, int& granted) {
+  if (granted >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) granted = bytes;
+  return e;
+}
+
+struct WsLayout {
+  size_t ld, blkcnt, coloff, csr, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const Geom& g, int max_kv) {
+  const size_t nrb = (size_t)(g.Nc + kRowsPerBlk - 1) / kRowsPerBlk;
+  WsLayout w;
+  w.ld = 0;
+  w.blkcnt = w.ld + align256((size_t)g.BH * g.N * 8);
+  w.coloff = w.blkcnt + align256((size_t)g.BH * nrb * g.Nc * 4);
+  w.csr = w.coloff + align256((size_t)g.BH * (g.Nc + 1) * 4);
+  w.total = w.csr + align256((size_t)g.BH * g.Nc * max_kv * 4);
+  return w;
+}
+
+template <int D>
+hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
+                    const int32_t* valid, int max_kv, const void* o, const float* lse, const void* dout,
+                    float* dq, float* dk, float* dv, char* ws, hipStream_t s) {
+  static int granted[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const WsLayout w = ws_layout(g, max_kv);
+  float2* ld = reinterpret_cast<float2*>(ws + w.ld);
+  int32_t* blkcnt = reinterpret_cast<int32_t*>(ws + w.blkcnt);
+  int32_t* coloff = reinterpret_cast<int32_t*>(ws + w.coloff);
+  int32_t* csr = reinterpret_cast<int32_t*>(ws + w.csr);
+  const int Nc = (int)g.Nc;
+  const int nrb = (Nc + kRowsPerBlk - 1) / kRowsPerBlk;
+  const int64_t total_tok = g.BH * g.N;
+  const int64_t total_cubes = g.BH * g.Nc;
+
+  constexpr int TOK_PER_BLOCK = 256 / (D / 8);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((total_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK)),
+                     dim3(256), 0, s, (const __bf16*)o, (const __bf16*)dout, lse, ld, total_tok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t cnt_lds = (size_t)Nc * 4;
+  hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)(g.BH * nrb)), dim3(256), cnt_lds, s, lut, valid, max_kv,
+                     Nc, nrb, blkcnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)g.BH), dim3(256), cnt_lds, s, blkcnt, Nc, nrb, coloff);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)(g.BH * nrb)), dim3(64), cnt_lds, s, lut, valid, max_kv,
+                     Nc, nrb, blkcnt, coloff, csr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  const float c_log2 = kLog2e / sqrtf((float)D);
+  const float scale = 1.0f / sqrtf((float)D);
+  auto kq = sparse_attn_bwd_dq_kernel<D>;
+  auto kkv = sparse_attn_bwd_dkdv_kernel<D>;
+  if ((e = grant_lds(kq, dq_lds<D>(), granted[dev][0])) != hipSuccess) return e;
+  if ((e = grant_lds(kkv, dkdv_lds<D>(), granted[dev][1])) != hipSuccess) return e;
+  hipLaunchKernelGGL(kq, dim3((unsigned)total_cubes), dim3(kThreads), dq_lds<D>(), s, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lut, valid, max_kv,
+                     (const float2*)ld, dq, Nc, total_cubes, c_log2, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(kkv, dim3((unsigned)total_cubes), dim3(kThreads), dkdv_lds<D>(), s, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const int32_t*)coloff,
+                     (const int32_t*)csr, max_kv, (const float2*)ld, dk, dv, Nc, total_cubes, c_log2, scale);
+  return hipGetLastError();
+}
+
+static_assert(dq_lds<128>() <= kLdsMax && dkdv_lds<128>() <= kLdsMax, "LDS budget");
+
+}  // namespace
+
+size_t sparse_attn_bwd_workspace(const Geom& g, int max_kv) { return ws_layout(g, max_kv).total; }
+
+bool sparse_attn_bwd_fits(const Geom& g) {
+  // LDS counters of the transposed-list build hold one int per key cube;
+  // every launch grid stays below 2^31 workgroups.
+  return g.Nc >= 1 && g.Nc <= kMaxBwdCubes && g.BH * g.Nc < ((int64_t)1 << 31);
+}
+
+hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
+                                  const int32_t* valid, int max_kv, const void* o, const float* lse,
+                                  const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                                  hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  if (g.D == 64) return launch_d<64>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vsa

@@ -39,7 +39,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (1 << 16) | 0; }
+int vsa_abi_version(void) { return (1 << 16) | 1; }
 
 const char* vsa_status_str(int status) {
   switch (status) {
@@ -50,6 +50,7 @@ const char* vsa_status_str(int status) {
     case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume or cube count";
     case VSA_ERR_HIP: return "HIP runtime error at launch";
     case VSA_ERR_LUT: return "invalid LUT";
+    case VSA_ERR_WORKSPACE: return "workspace smaller than vsa_sparse_attn_bwd_workspace_size reports";
     default: return "unknown status";
   }
 }
@@ -158,6 +159,42 @@ int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q, const void* 
                                void* out, float* lse, void* stream) {
   return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
                                 out, lse, true, stream);
+}
+
+namespace {
+int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  const Geom g = vsa::make_geom(*p);
+  if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
+  if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  if (!vsa::sparse_attn_bwd_fits(g)) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+}  // namespace
+
+int vsa_sparse_attn_bwd_workspace_size(const vsa_problem* p, int32_t max_kv_blocks, size_t* bytes) {
+  if (bytes == nullptr) return VSA_ERR_NULL;
+  const int st = sparse_attn_bwd_check(p, max_kv_blocks);
+  if (st != VSA_OK) return st;
+  *bytes = vsa::sparse_attn_bwd_workspace(vsa::make_geom(*p), max_kv_blocks);
+  return VSA_OK;
+}
+
+int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
+                        const void* o, const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = sparse_attn_bwd_check(p, max_kv_blocks);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
+      o == nullptr || lse == nullptr || d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
+      workspace == nullptr)
+    return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (workspace_bytes < vsa::sparse_attn_bwd_workspace(g, max_kv_blocks)) return VSA_ERR_WORKSPACE;
+  return hip_status(vsa::launch_sparse_attn_bwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, o, lse,
+                                                d_o, dq, dk, dv, workspace, (hipStream_t)stream));
 }
 
 int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32_t* valid_block_num,

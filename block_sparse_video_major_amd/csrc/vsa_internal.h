@@ -54,8 +54,20 @@ hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* va
 hipError_t launch_mask_to_lut(const Geom& g, const uint8_t* mask, int max_kv, int32_t* lut, int32_t* valid,
                               int32_t* overflow_rows, hipStream_t s);
 
+// Backward of the fine stage: the workspace it needs (bytes), whether it
+// handles this geometry, and the launcher (prep, transposed index list, dQ,
+// then dK/dV, all on stream s).
+size_t sparse_attn_bwd_workspace(const Geom& g, int max_kv);
+bool sparse_attn_bwd_fits(const Geom& g);
+hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
+                                  const int32_t* valid, int max_kv, const void* o, const float* lse,
+                                  const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                                  hipStream_t s);
+
 // Largest number of cubes per (batch, head) the coarse stage handles.
 constexpr int64_t kMaxCoarseCubes = 4096;
+// ... and the backward (one LDS counter per key cube in the list build).
+constexpr int64_t kMaxBwdCubes = 8192;
 
 // Workgroups are handed to the 8 XCDs of an MI355X round-robin by id.  This
 // maps a hardware id to a logical id so that each XCD receives one contiguous

@@ -15,6 +15,7 @@
  *   4. vsa_sparse_attn_fwd  fine attention over the listed cubes, combined
  *                       with O_c through the gates
  *   5. vsa_unpermute    cube-major -> raster order
+ * and the backward of step 4's attention (vsa_sparse_attn_bwd), for training.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -40,6 +41,7 @@
 #ifndef VSA_H_
 #define VSA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -68,7 +70,8 @@ enum {
   VSA_ERR_TOPK = -3,        /* top_k / max_kv_blocks outside [1, Nc] */
   VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume this build does not handle */
   VSA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
-  VSA_ERR_LUT = -6          /* reserved for LUT validation results */
+  VSA_ERR_LUT = -6,         /* reserved for LUT validation results */
+  VSA_ERR_WORKSPACE = -7    /* workspace_bytes below what the workspace query reports */
 };
 
 /* Reorder raster tokens into cube-major order:
@@ -192,6 +195,47 @@ int vsa_mask_to_lut(const vsa_problem* p, const uint8_t* mask,
                     int32_t max_kv_blocks, int32_t* kv_block_idx,
                     int32_t* valid_block_num, int32_t* overflow_rows,
                     void* stream);
+
+/* Workspace of vsa_sparse_attn_bwd, in bytes, for this problem and LUT row
+ * length (host only, no device work).  Same argument checks and errors as
+ * vsa_sparse_attn_bwd. */
+int vsa_sparse_attn_bwd_workspace_size(const vsa_problem* p,
+                                       int32_t max_kv_blocks, size_t* bytes);
+
+/* Backward of the fine attention O_f of vsa_sparse_attn_fwd
+ * ([VSA-arXiv] Abstract: the sparse attention is trained end to end;
+ * [VSA-ROCm] §Two-Stage Architecture Stage 2 and §Block-Sparse Encoding for
+ * the function differentiated).  For query cube i with listed key tokens R,
+ * scale = 1/sqrt(head_dim), P = exp(scale * Q_i K_R^T - lse_i) and
+ * Drow = rowsum(dO_i * O_i):
+ *   dP = dO_i V_R^T,  dS = P * (dP - Drow),
+ *   dq_i = scale * dS K_R,  dk_R += scale * dS^T Q_i,  dv_R += P^T dO_i,
+ * summed over every listing (a cube listed twice contributes twice); tokens of
+ * cubes no row lists get dk = dv = 0, rows with count 0 get dq = 0.
+ * q, k, v, kv_block_idx, valid_block_num, max_kv_blocks: exactly as passed to
+ *   vsa_sparse_attn_fwd (cube-major; every listed entry in [0, Nc)).
+ * o:   [batch, heads, N, head_dim] bf16, cube-major: O_f, i.e. the out of
+ *      vsa_sparse_attn_fwd called with gate_c == NULL and gate_f == NULL.
+ * lse: [batch, heads, N] float32, cube-major: the lse of that call.
+ * d_o: [batch, heads, N, head_dim] bf16, cube-major: the gradient of the loss
+ *      with respect to O_f (the gates' own chain rule, elementwise, is the
+ *      caller's).
+ * dq, dk, dv: [batch, heads, N, head_dim] float32, cube-major, fully written
+ *      (no accumulation into prior contents); the products run on bf16 MFMA
+ *      with float32 accumulation, P and dS rounded to bf16 as operands.
+ * workspace: device memory of workspace_bytes >= the size
+ *      vsa_sparse_attn_bwd_workspace_size reports, else VSA_ERR_WORKSPACE;
+ *      its contents on entry do not matter and are clobbered.
+ * Deterministic: no atomics touch dq, dk or dv; repeated calls give the same
+ * bits.  Requires cube volume 64, head_dim 64 or 128 and Nc <= 8192, else
+ * VSA_ERR_UNSUPPORTED; max_kv_blocks outside [1, Nc] is VSA_ERR_TOPK.
+ * Outputs must not alias inputs or the workspace. */
+int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k,
+                        const void* v, const int32_t* kv_block_idx,
+                        const int32_t* valid_block_num, int32_t max_kv_blocks,
+                        const void* o, const float* lse, const void* d_o,
+                        float* dq, float* dk, float* dv, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Host helper: perm_host[p] = pi(p) for p < N (the order vsa_permute
  * applies).  perm_host is a host array of N int32.  No device work. */

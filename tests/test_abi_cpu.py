@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     assert L.vsa_abi_version() >> 16 == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.vsa_status_str(code) and L.vsa_status_str(code) != "unknown status"
     assert L.vsa_status_str(42) == "unknown status"
 
@@ -110,6 +110,42 @@ def test_mask_to_lut_errors():
     assert lib.vsa_mask_to_lut(pr, DUMMY, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
     assert lib.vsa_mask_to_lut(pr, DUMMY, 33, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
     assert lib.vsa_mask_to_lut(ctypes.byref(_prob(H=10)), DUMMY, 4, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+
+
+def test_sparse_attn_bwd_workspace_and_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob(head_dim=128))     # 8 x 16 x 16 grid, 32 cubes, 2 heads
+    n = ctypes.c_size_t(0)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 8, ctypes.byref(n)) == L.VSA_OK
+    # per-token records, per-row-block counts, list offsets, list entries (each 256-byte aligned)
+    al = lambda x: (x + 255) // 256 * 256
+    bh, nc, ntok = 2, 32, 2048
+    assert n.value == al(bh * ntok * 8) + al(bh * 2 * nc * 4) + al(bh * (nc + 1) * 4) + al(bh * nc * 8 * 4)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 8, None) == L.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 0, ctypes.byref(n)) == L.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 33, ctypes.byref(n)) == L.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(_prob(ct=2)), 8, ctypes.byref(n)) == \
+        L.VSA_ERR_UNSUPPORTED
+    big = L.Problem(1, 1, 32, 64, 64, 2, 2, 2, 64)    # vol 8: not handled
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(big.c_struct()), 8, ctypes.byref(n)) == \
+        L.VSA_ERR_UNSUPPORTED
+    many = L.Problem(1, 1, 64, 64, 144, 4, 4, 4, 64)  # 9216 cubes: above the backward's limit
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(many.c_struct()), 8, ctypes.byref(n)) == \
+        L.VSA_ERR_UNSUPPORTED
+
+    def call(q=DUMMY, k=DUMMY, v=DUMMY, lut=DUMMY, valid=DUMMY, maxkv=8, o=DUMMY, lse=DUMMY, do=DUMMY,
+             dq=DUMMY, dk=DUMMY, dv=DUMMY, ws=DUMMY, wsb=None, prob=pr):
+        return lib.vsa_sparse_attn_bwd(prob, q, k, v, lut, valid, maxkv, o, lse, do, dq, dk, dv, ws,
+                                       size if wsb is None else wsb, None)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 8, ctypes.byref(n)) == L.VSA_OK
+    size = n.value
+    for name in ("q", "k", "v", "lut", "valid", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert call(**{name: None}) == L.VSA_ERR_NULL, name
+    assert call(wsb=size - 1) == L.VSA_ERR_WORKSPACE
+    assert call(maxkv=0) == L.VSA_ERR_TOPK
+    assert call(maxkv=33) == L.VSA_ERR_TOPK
+    assert call(prob=ctypes.byref(_prob(head_dim=96))) == L.VSA_ERR_UNSUPPORTED
+    assert call(prob=None) == L.VSA_ERR_NULL
 
 
 def test_coarse_topk_errors():
