@@ -237,6 +237,30 @@ def main() -> int:
             sweep[str(kk)] = {"sparsity": round(1 - kk / w.n_cubes, 3), "fine_ms": round(tsum, 4),
                               "fine_tflops": round(fl / (tsum * 1e-3) / 1e12, 2)}
         flops_m = 4 * 64 * 64 * w.head_dim * pairs_m   # per selected (query cube, key cube) pair
+
+        # backward of the fine stage (training): dQ, dK, dV from the forward's
+        # O_f and log-sum-exp on the same LUT, with a seeded output gradient
+        o_f = torch.empty_like(q)
+        lse_f = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device=dev)
+        L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse_f, stream=stream)
+        gen = torch.Generator(device=dev).manual_seed(5)
+        d_o = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+        ws = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, w.top_k), dtype=torch.uint8, device=dev)
+
+        def bwd():
+            L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, d_o, *grads, ws, stream)
+        bwd()
+        torch.cuda.synchronize()
+        t_bwd = 0.0
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            bwd()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            t_bwd += e[0].elapsed_time(e[1]) / reps
+        del grads, ws, d_o, o_f, lse_f
     torch.cuda.synchronize()
 
     flops = w.selected_flops()
@@ -280,6 +304,10 @@ def main() -> int:
                           "overflow_rows": int(over_m.item()),
                           "mask_to_lut_ms": round(mt["mask_to_lut"], 4), "fine_ms": round(mt["fine"], 4),
                           "fine_tflops": round(flops_m / (mt["fine"] * 1e-3) / 1e12, 2)},
+        "backward": {"ms_per_call": round(t_bwd, 4),
+                     "tflops": round(2.5 * flops / (t_bwd * 1e-3) / 1e12, 2),
+                     "pct_bf16_peak": round(100 * 2.5 * flops / (t_bwd * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2),
+                     "flop_accounting": "5 products of 2*64*64*d per selected pair (S, dP, dQ, dK, dV)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},
