@@ -38,10 +38,20 @@
 //     Drow of the lane's 16 queries read from LDS), then dV^T += dO^T P and
 //     dK^T += Q^T dS with transposing reads of the dO and Q tiles.  The two
 //     query halves are summed through LDS at the end.
-//   * Tiles (64 tokens x d bf16) arrive by direct global->LDS loads into a
-//     two-stage ring, one barrier per step.  One chunk swizzle serves both LDS
-//     read patterns (16 consecutive rows at one 16-byte chunk, and 4
-//     consecutive rows at 4 consecutive chunks) without bank conflicts.
+//   * Tiles (64 tokens x d bf16) arrive by direct global->LDS loads, one
+//     barrier per step: a two-stage ring in the dQ kernel (two workgroups
+//     share a CU, so each SIMD runs two waves that cover each other's
+//     stalls), a four-stage ring with two steps of loads in flight in the
+//     dK/dV kernel (its 128 accumulator registers per lane leave one wave per
+//     SIMD, so it overlaps the matrix cores with its own vector work in a
+//     two-phase software pipeline).  One chunk swizzle serves both LDS read
+//     patterns (16 consecutive rows at one 16-byte chunk, and 4 consecutive
+//     rows at 4 consecutive chunks) without bank conflicts.
+//   * What bounds it (32K-token layer): neither kernel reaches the matrix-core
+//     bound.  Per dK/dV step (~2500 cycles against 1024 of MFMA work) the
+//     direct loads cost the issuing waves ~60 cycles per 1 KiB piece while
+//     the CU's load path and LDS are busy, the exponentials and dS arithmetic
+//     ~700 cycles of vector issue, and barrier plus load wait ~300.
 //   * Workgroups are mapped to XCDs in contiguous ranges of cubes, so the
 //     workgroups sharing an L2 walk overlapping lists.
 #include "mfma_util.h"
@@ -87,6 +97,23 @@ __device__ __forceinline__ void dma_piece(const void* base, uint32_t voff, uint3
       "global_load_lds_dwordx4 %0, %2"
       :
       : "v"(voff), "s"(lds_base), "s"(base)
+      : "memory", "m0");
+}
+
+// Piece N of a tile by direct load: every lane moves the 16 bytes at
+// base + voff + 1024 N to LDS byte address lds_base + 1024 N + 16 * lane
+// (voff as in the tile offsets, which subtract 1024 N).  Issuing the pieces of
+// a step one at a time between MFMAs keeps the CU's address unit (about 16
+// cycles per 1 KiB piece) from backing up and stalling the issuing waves.
+template <int N>
+__device__ __forceinline__ void dma_one(const void* base, uint32_t voff, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %2 offset:%3"
+      :
+      : "v"(voff), "s"(lds_base), "s"(base), "i"(N * 1024)
       : "memory", "m0");
 }
 
@@ -427,14 +454,29 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
 }
 
 // ---- dK, dV ---------------------------------------------------------------------
+// Software pipeline (one wavefront per SIMD, so the overlap has to come from
+// within each wave).  Iteration s: phase A forms S and dP of step s on the
+// matrix cores, turning S into P (exponentials) while the dP products run;
+// phase B runs the dV and dK products of step s - 1 while dS of step s is
+// formed.  Tiles live in a four-stage ring: steps s + 1 and s + 2 load while
+// steps s and s - 1 are read, and the loads of step s + 2 are issued one
+// 1 KiB piece at a time between the MFMAs of phase A.
 template <int D>
-__global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const int32_t* __restrict__ coloff, const int32_t* __restrict__ csr,
     int max_kv, const float2* __restrict__ ld, float* __restrict__ dk, float* __restrict__ dv, int Nc,
     int64_t total_cubes, float c_log2, float scale) {
   using C = BCfg<D>;
   constexpr int SLOT = 2 * C::TILE + 1024;   // Q tile, dO tile, (LSE log2 e, Drow) of 64 queries
+  constexpr int NST = 4;                     // ring stages
+  constexpr int G1 = 2 * C::KS;              // S and dP MFMAs per step
+  constexpr int NTR = 4 * C::OT;             // dV and dK MFMAs per step
+  constexpr int RPA = 16 / C::KS;            // P entries formed per dP MFMA
+  constexpr int RPB = 16 / NTR;              // dS entries formed per dV/dK MFMA
+  constexpr int NP = 2 * C::LOADS;           // tile pieces per wave per step
+  constexpr int PF = 4;                      // operand reads kept in flight ahead of their MFMA
+  static_assert(2 * NP <= G1, "pieces fit in phase A");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -458,14 +500,46 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dkdv_kernel(
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t lds0 = lds_base + (uint32_t)(wave * C::LOADS * 1024);
   const uint32_t ld_off = 16u * (uint32_t)(lane & 31);   // 512 bytes; lanes 32-63 repeat them
-  auto issue = [&](int s, int stage) {
-    const int ci = lw.at(s, lane);
-    dma_tile(uniform_ptr(q_head + (int64_t)ci * C::TILE), off.g_off, lds0 + stage * SLOT);
-    dma_tile(uniform_ptr(d_head + (int64_t)ci * C::TILE), off.g_off, lds0 + stage * SLOT + C::TILE);
-    if (wave == 0)
-      dma_piece(uniform_ptr(ld_head + (int64_t)ci * kBlk * 8), ld_off, lds_base + stage * SLOT + 2 * C::TILE);
+  auto stage = [&](int s) { return smem + (s % NST) * SLOT; };
+
+  // The loads of one step: the Q and dO tiles of its query cube (NP pieces
+  // per wave) and, from wave 0, the cube's 64 (LSE log2 e, Drow) records.
+  struct StepLoads {
+    const char* qb;
+    const char* db;
+    const char* lb;
+    uint32_t so;   // stage offset
+    bool on;
   };
-  if (n > 0) issue(0, 0);
+  auto prepare = [&](int s) {
+    StepLoads x;
+    x.on = s < n;
+    const int ci = x.on ? lw.at(s, lane) : 0;
+    x.qb = uniform_ptr(q_head + (int64_t)ci * C::TILE);
+    x.db = uniform_ptr(d_head + (int64_t)ci * C::TILE);
+    x.lb = uniform_ptr(ld_head + (int64_t)ci * kBlk * 8);
+    x.so = (uint32_t)((s % NST) * SLOT);
+    return x;
+  };
+  auto piece = [&](const StepLoads& x, int i) {   // i < NP: Q pieces, then dO pieces
+    const char* base = i < C::LOADS ? x.qb : x.db;
+    const uint32_t dst = lds0 + x.so + (i < C::LOADS ? 0u : (uint32_t)C::TILE);
+    switch (i % C::LOADS) {
+      case 0: dma_one<0>(base, off.g_off[0], dst); break;
+      case 1: dma_one<1>(base, off.g_off[1], dst); break;
+      case 2: if constexpr (C::LOADS > 2) dma_one<2>(base, off.g_off[C::LOADS > 2 ? 2 : 0], dst); break;
+      default: if constexpr (C::LOADS > 3) dma_one<3>(base, off.g_off[C::LOADS > 3 ? 3 : 0], dst); break;
+    }
+  };
+  auto records_piece = [&](const StepLoads& x) {
+    if (wave == 0) dma_piece(x.lb, ld_off, lds_base + x.so + 2 * C::TILE);
+  };
+  auto issue_all = [&](int s) {
+    const StepLoads x = prepare(s);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) piece(x, i);
+    records_piece(x);
+  };
 
   bf16x8 kf[C::KS], vf[C::KS];
   load_b_operand<D>(k + head_off + (int64_t)cj * kBlk * D, kh, lane, kf);
@@ -475,55 +549,131 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dkdv_kernel(
   for (int t = 0; t < C::OT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc_v[t][r] = 0.f; acc_k[t][r] = 0.f; }
-  wait_vmem<0>();
-  __syncthreads();
 
-  for (int s = 0; s < n; ++s) {
-    const int st = s & 1;
-    if (s + 1 < n) issue(s + 1, st ^ 1);
-    const char* qt = smem + st * SLOT;
-    const char* dt = qt + C::TILE;
-    const float* lds_ld = reinterpret_cast<const float*>(qt + 2 * C::TILE);
-    f32x16 sS, dP;   // rows = queries 32*qh + 8*(r/4) + 4*g + r%4, column = key 32*kh + n32
+  // (LSE log2 e, Drow) of the lane's 16 queries 32*qh + 8*(r/4) + 4*g + r%4.
+  auto read_records = [&](const char* st, float4 (&rec)[8]) {
+    const float* base = reinterpret_cast<const float*>(st + 2 * C::TILE) + 2 * (32 * qh + 4 * g);
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      rec[2 * rq] = *reinterpret_cast<const float4*>(base + 16 * rq);
+      rec[2 * rq + 1] = *reinterpret_cast<const float4*>(base + 16 * rq + 4);
+    }
+  };
+  auto rec_at = [](const float4 (&rec)[8], int r) -> const float4& { return rec[2 * (r >> 2) + ((r >> 1) & 1)]; };
+  // Operand i of the dV / dK products of a step: dO^T (i < 2*OT) or Q^T,
+  // k-step j, d tile t, read transposed from that step's stage.
+  auto read_tr_op = [&](const char* tp, int i) {
+    const int which = i / (2 * C::OT), j = (i / C::OT) & 1, t = i % C::OT;
+    return read_tr<D>(tp + (which == 0 ? C::TILE : 0), off, t, j);
+  };
+
+  // Phase A: S and dP of one step (rows = queries 32*qh + 8*(r/4) + 4*g + r%4,
+  // column = key 32*kh + n32); while the dP products run, P = exp2(S c -
+  // LSE log2 e) is formed (fp32 in pf, bf16 operand in pbn).  Also issues the
+  // pieces of `nx` and, when `prev`, starts the transposed reads of the
+  // previous step's first dV / dK operands.
+  auto phase_a = [&](const char* tc, const float4 (&rec)[8], f32x16& sS, f32x16& dP, float (&pf)[16],
+                     bf16x8 (&pbn)[2], const StepLoads& nx, bool prev, const char* tp, bf16x8 (&tr)[PF]) {
+    auto row_op = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(tc + (i < C::KS ? 0 : C::TILE) + off.row_off[i % C::KS]);
+    };
+    bf16x8 a[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = row_op(i);
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sS[r] = 0.f; dP[r] = 0.f; }
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + off.row_off[ks]);
-      sS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sS, 0, 0, 0);
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dt + off.row_off[ks]);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dP, 0, 0, 0);
-    }
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      // records of queries 32*qh + 8*rq + 4*g + 0..3
-      const float* rec = lds_ld + 2 * (32 * qh + 8 * rq + 4 * g);
-      const float4 l0 = *reinterpret_cast<const float4*>(rec);
-      const float4 l1 = *reinterpret_cast<const float4*>(rec + 4);
-      const float lse2[4] = {l0.x, l0.z, l1.x, l1.z};
-      const float drow[4] = {l0.y, l0.w, l1.y, l1.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * rq + u;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sS[r], c_log2, -lse2[u]));
-        pb[r >> 3][r & 7] = (__bf16)p;
-        dsb[r >> 3][r & 7] = (__bf16)(p * (dP[r] - drow[u]));
+    for (int i = 0; i < G1; ++i) {
+      if (i < C::KS)
+        sS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % PF], kf[i], sS, 0, 0, 0);
+      else
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % PF], vf[i - C::KS], dP, 0, 0, 0);
+      if (i + PF < G1) a[i % PF] = row_op(i + PF);
+      if (nx.on) {
+        if ((i & 1) == 0 && i / 2 < NP) piece(nx, i / 2);
+        if (i == 1) records_piece(nx);
       }
-    }
+      if (i >= C::KS) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < C::OT; ++t) {
-        acc_v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(dt, off, t, j), pb[j], acc_v[t], 0, 0, 0);
-        acc_k[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(qt, off, t, j), dsb[j], acc_k[t], 0, 0, 0);
+        for (int u = 0; u < RPA; ++u) {
+          const int r = (i - C::KS) * RPA + u;
+          const float4& rr = rec_at(rec, r);
+          pf[r] = __builtin_amdgcn_exp2f(fmaf(sS[r], c_log2, -((r & 1) ? rr.z : rr.x)));
+          pbn[r >> 3][r & 7] = (__bf16)pf[r];
+        }
       }
-    wait_vmem<0>();
+      if (prev && i >= G1 - PF) tr[i - (G1 - PF)] = read_tr_op(tp, i - (G1 - PF));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Phase B: dV^T += dO^T P and dK^T += Q^T dS of the previous step (when
+  // `prev`; operands 0..PF-1 already in tr) while dS = P (dP - Drow) of this
+  // step is formed (when `cur`).
+  auto phase_b = [&](bool prev, const char* tp, const bf16x8 (&pbp)[2], const bf16x8 (&dsbp)[2],
+                     bf16x8 (&tr)[PF], bool cur, const f32x16& dP, const float (&pf)[16], const float4 (&rec)[8],
+                     bf16x8 (&dsbn)[2]) {
+#pragma unroll
+    for (int i = 0; i < NTR; ++i) {
+      if (prev) {
+        const int which = i / (2 * C::OT), j = (i / C::OT) & 1, t = i % C::OT;
+        if (which == 0)
+          acc_v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[i % PF], pbp[j], acc_v[t], 0, 0, 0);
+        else
+          acc_k[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[i % PF], dsbp[j], acc_k[t], 0, 0, 0);
+        if (i + PF < NTR) tr[i % PF] = read_tr_op(tp, i + PF);
+      }
+      if (cur) {
+#pragma unroll
+        for (int u = 0; u < RPB; ++u) {
+          const int r = i * RPB + u;
+          const float4& rr = rec_at(rec, r);
+          dsbn[r >> 3][r & 7] = (__bf16)(pf[r] * (dP[r] - ((r & 1) ? rr.w : rr.y)));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  f32x16 sS, dP;
+  float pf[16];
+  float4 rec[8];
+  bf16x8 pb[2], dsb[2], pbn[2], dsbn[2], tr[PF];
+  // Top of step s: wait for this wave's loads of step s (those of step s + 1
+  // may stay in flight) and publish them with the barrier, which also frees
+  // the stage of step s - 2 for the loads of step s + 2.
+  auto top = [&](int s) {
+    if (s + 1 < n) {
+      if (wave == 0) wait_vmem<NP + 1>(); else wait_vmem<NP>();
+    } else {
+      wait_vmem<0>();
+    }
     __syncthreads();
+  };
+  if (n > 0) issue_all(0);
+  if (n > 1) issue_all(1);
+  if (n > 0) {
+    // step 0: S, dP, then P and dS
+    top(0);
+    read_records(stage(0), rec);
+    phase_a(stage(0), rec, sS, dP, pf, pb, prepare(2), false, stage(0), tr);
+    phase_b(false, stage(0), pb, dsb, tr, true, dP, pf, rec, dsb);
+    for (int s = 1; s < n; ++s) {
+      top(s);
+      const char* tc = stage(s);
+      const char* tp = stage(s - 1);
+      read_records(tc, rec);
+      phase_a(tc, rec, sS, dP, pf, pbn, prepare(s + 2), true, tp, tr);
+      phase_b(true, tp, pb, dsb, tr, true, dP, pf, rec, dsbn);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) { pb[j] = pbn[j]; dsb[j] = dsbn[j]; }
+    }
+    // the last step's dV and dK products
+    const char* tp = stage(n - 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) tr[i] = read_tr_op(tp, i);
+    phase_b(true, tp, pb, dsb, tr, false, dP, pf, rec, dsbn);
   }
+  __syncthreads();   // every wave is done with the ring
 
   // dV^T and dK^T of the two query halves summed through LDS, stored.
   float* stg_v = reinterpret_cast<float*>(smem);
@@ -552,7 +702,7 @@ constexpr int dq_lds() {
 template <int D>
 constexpr int dkdv_lds() {
   using C = BCfg<D>;
-  return 2 * (2 * C::TILE + 1024) > 2 * C::STAGE ? 2 * (2 * C::TILE + 1024) : 2 * C::STAGE;
+  return 4 * (2 * C::TILE + 1024) > 2 * C::STAGE ? 4 * (2 * C::TILE + 1024) : 2 * C::STAGE;
 }
 
 template <typename K>
