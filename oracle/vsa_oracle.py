@@ -34,6 +34,8 @@ DESIGN.md):
 * R15 a block relation matrix becomes an index list in ascending order; rows
   with more selected blocks than the list holds keep the first ones and are
   counted as overflows.
+* R17 the backward differentiates the layer with its LUT held fixed (Top-K
+  selection has no gradient); P is recomputed from the forward's LSE.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, invariants, brute force, library special cases); none is
@@ -350,3 +352,90 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 p_coarse=pc, oc=oc, kv_block_idx=kv_block_idx,
                 valid_block_num=valid_block_num, o_fine=of, lse=lse,
                 out_cube=outp, out=out, scale=scale)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the remaining steps, so that a whole layer can be trained end to
+# end ([VSA-arXiv] Abstract); the LUT is a constant (R17).
+# ---------------------------------------------------------------------------
+
+def combine_bwd(dout: np.ndarray, of: np.ndarray, oc: np.ndarray, vol: int,
+                gate_c: Optional[np.ndarray] = None,
+                gate_f: Optional[np.ndarray] = None):
+    """Gradients of out' = g_f * O_f + g_c * O_c[p // vol] (R4, R5) for the
+    upstream gradient dout (cube-major).  Returns (dO_f, dO_c, dg_c, dg_f):
+    dO_f = g_f * dout; dO_c[c] sums g_c * dout over the vol tokens of cube c
+    (the adjoint of the broadcast); dg_c = dout * O_c[p // vol];
+    dg_f = dout * O_f.  An absent gate has no gradient (None); an absent g_c
+    gives dO_c = 0."""
+    dout = np.asarray(dout, np.float64)
+    of = np.asarray(of, np.float64)
+    oc = np.asarray(oc, np.float64)
+    dof = dout if gate_f is None else np.asarray(gate_f, np.float64) * dout
+    dgf = None if gate_f is None else dout * of
+    if gate_c is None:
+        return dof, np.zeros_like(oc), None, dgf
+    gd = np.asarray(gate_c, np.float64) * dout
+    n = gd.shape[-2]
+    doc = np.zeros_like(oc)
+    for c in range(n // vol):
+        doc[..., c, :] = gd[..., c * vol:(c + 1) * vol, :].sum(axis=-2)
+    dgc = dout * np.repeat(oc, vol, axis=-2)
+    return dof, doc, dgc, dgf
+
+
+def coarse_attention_bwd(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray,
+                         scale: float, doc: np.ndarray):
+    """Gradients of O_c = softmax(scale * Qc Kc^T) Vc over all cubes (R3)
+    given dO_c.  With P the coarse probabilities and Dc = rowsum(dO_c * O_c):
+        dVc = P^T dO_c,   dP = dO_c Vc^T,   dS = P * (dP - Dc),
+        dQc = scale * dS Kc,   dKc = scale * dS^T Qc.
+    Returns (dQc, dKc, dVc)."""
+    qc = np.asarray(qc, np.float64)
+    kc = np.asarray(kc, np.float64)
+    vc = np.asarray(vc, np.float64)
+    doc = np.asarray(doc, np.float64)
+    _, p, oc = coarse_attention(qc, kc, vc, scale)
+    dvc = np.matmul(np.swapaxes(p, -1, -2), doc)
+    dp = np.matmul(doc, np.swapaxes(vc, -1, -2))
+    dmat = (doc * oc).sum(axis=-1, keepdims=True)
+    ds = p * (dp - dmat)
+    dqc = scale * np.matmul(ds, kc)
+    dkc = scale * np.matmul(np.swapaxes(ds, -1, -2), qc)
+    return dqc, dkc, dvc
+
+
+def pool_bwd(dxc: np.ndarray, vol: int) -> np.ndarray:
+    """Gradient of the cube mean (pool): every one of the vol tokens of cube c
+    receives dxc[c] / vol."""
+    return np.repeat(np.asarray(dxc, np.float64), vol, axis=-2) / vol
+
+
+def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
+                 kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
+                 dout: np.ndarray, gate_c: Optional[np.ndarray] = None,
+                 gate_f: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of the whole layer (raster in, raster out) for the upstream
+    gradient dout (raster), the LUT held fixed (R17): the forward's steps
+    taken backwards -- reorder dout, combine, fine attention (through the
+    LSE), coarse attention, pooling, reorder back.  Q, K and V each collect
+    their fine-stage gradient plus the pooled coarse-stage gradient.
+    Returns dict(dq, dk, dv, dgate_c, dgate_f) in raster order (absent gates
+    give None)."""
+    f = vsa_forward(q, k, v, grid, cube, 0, gate_c=gate_c, gate_f=gate_f,
+                    kv_block_idx=kv_block_idx, valid_block_num=valid_block_num)
+    pi = f["pi"]
+    vol = cube[0] * cube[1] * cube[2]
+    scale = f["scale"]
+    doutp = permute(np.asarray(dout, np.float64), pi)
+    gcp = None if gate_c is None else permute(np.asarray(gate_c, np.float64), pi)
+    gfp = None if gate_f is None else permute(np.asarray(gate_f, np.float64), pi)
+    dof, doc, dgcp, dgfp = combine_bwd(doutp, f["o_fine"], f["oc"], vol, gcp, gfp)
+    dqf, dkf, dvf = fine_attention_bwd(f["qp"], f["kp"], f["vp"], kv_block_idx, valid_block_num,
+                                       scale, vol, f["o_fine"], f["lse"], dof)
+    dqc, dkc, dvc = coarse_attention_bwd(f["qc"], f["kc"], f["vc"], scale, doc)
+    return dict(dq=unpermute(dqf + pool_bwd(dqc, vol), pi),
+                dk=unpermute(dkf + pool_bwd(dkc, vol), pi),
+                dv=unpermute(dvf + pool_bwd(dvc, vol), pi),
+                dgate_c=None if dgcp is None else unpermute(dgcp, pi),
+                dgate_f=None if dgfp is None else unpermute(dgfp, pi))

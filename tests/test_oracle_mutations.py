@@ -12,13 +12,14 @@ from oracle import vsa_oracle as vo
 import test_oracle_coarse as tc
 import test_oracle_fine as tf
 import test_oracle_bwd as tb
+import test_oracle_full_bwd as tfb
 import test_oracle_mask as tm
 import test_oracle_reorder as tr
 from block_sparse_video_major_amd import workloads as wl
 
 
 _ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut",
-                                     "fine_attention_bwd")}
+                                     "fine_attention_bwd", "coarse_attention_bwd", "pool_bwd", "combine_bwd")}
 
 
 def _raster_perm(T, H, W, ct, ch, cw):
@@ -99,6 +100,20 @@ def _bwd_dv_from_q(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
     return dq, dk, dq
 
 
+def _coarse_bwd_dk_no_scale(qc, kc, vc, scale, doc):
+    dq, dk, dv = _ORIG["coarse_attention_bwd"](qc, kc, vc, scale, doc)
+    return dq, dk / scale, dv
+
+
+def _pool_bwd_no_divisor(dxc, vol):
+    return _ORIG["pool_bwd"](dxc, vol) * vol
+
+
+def _combine_bwd_dgc_from_of(dout, of, oc, vol, gate_c=None, gate_f=None):
+    dof, doc, dgc, dgf = _ORIG["combine_bwd"](dout, of, oc, vol, gate_c, gate_f)
+    return dof, doc, (None if dgc is None else np.asarray(dout) * np.asarray(of)), dgf
+
+
 def _pins():
     """The pin checks, called directly (each raises AssertionError on failure)."""
     yield lambda: tr.test_each_block_is_one_cube_in_raster_cube_order((4, 8, 8), (4, 4, 4))
@@ -118,6 +133,10 @@ def _pins():
     yield lambda: tm.test_relation_matrix_of_a_topk_lut_gives_the_lut_back()
     yield lambda: tm.test_masked_fine_attention_is_dense_masked_softmax()
     yield lambda: tm.test_overflow_rows_are_counted_and_keep_their_first_blocks()
+    yield lambda: tfb.test_coarse_attention_bwd_matches_autograd()
+    yield lambda: tfb.test_pool_bwd_is_the_adjoint_of_pool()
+    yield lambda: tfb.test_combine_bwd_matches_autograd()
+    yield lambda: tfb.test_whole_layer_backward_matches_autograd()
 
 
 MUTATIONS = {
@@ -136,6 +155,9 @@ MUTATIONS = {
     "backward dV taken from dQ": ("fine_attention_bwd", _bwd_dv_from_q),
     "mask read transposed": ("mask_to_lut", _mask_transposed),
     "mask overflow keeps the last blocks": ("mask_to_lut", _mask_last_blocks_on_overflow),
+    "coarse backward dKc without the scale": ("coarse_attention_bwd", _coarse_bwd_dk_no_scale),
+    "pool backward without 1/vol": ("pool_bwd", _pool_bwd_no_divisor),
+    "combine backward dg_c taken from O_f": ("combine_bwd", _combine_bwd_dgc_from_of),
 }
 
 
