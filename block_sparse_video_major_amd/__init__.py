@@ -11,8 +11,9 @@ from ._lib import (  # noqa: F401
     vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
     vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size,
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
+    vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
 )
-from .pipeline import VsaForward, vsa_forward  # noqa: F401
+from .pipeline import VsaBackward, VsaForward, vsa_forward  # noqa: F401
 
 __all__ = [
     "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
@@ -20,4 +21,6 @@ __all__ = [
     "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
     "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size",
     "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
+    "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
+    "VsaBackward",
 ]

@@ -98,6 +98,10 @@ def load() -> ctypes.CDLL:
         "vsa_mask_to_lut": [P, vp, i32, vp, vp, vp, vp],
         "vsa_sparse_attn_bwd_workspace_size": [P, i32, ctypes.POINTER(ctypes.c_size_t)],
         "vsa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "vsa_combine_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "vsa_coarse_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
+        "vsa_coarse_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "vsa_pool_unpermute_bwd": [P, vp, vp, vp, vp],
         "vsa_perm_index": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
@@ -328,3 +332,61 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
                                       _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
                                       _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       int(workspace.numel()), _stream(stream, dev)), "vsa_sparse_attn_bwd")
+
+
+def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: torch.Tensor,
+                    o_f: Optional[torch.Tensor] = None, oc: Optional[torch.Tensor] = None,
+                    gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                    d_gate_c: Optional[torch.Tensor] = None, d_gate_f: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """Gradients of the gated combination (cube-major token tensors)."""
+    dev = dout.device
+    ts, cs = _tok_shape(p), _cube_shape(p)
+    for name, t in (("dout", dout), ("d_of", d_of), ("o_f", o_f), ("gate_c", gate_c), ("gate_f", gate_f)):
+        if t is not None:
+            _need(t, name, ts, torch.bfloat16, dev)
+    for name, t in (("d_gate_c", d_gate_c), ("d_gate_f", d_gate_f)):
+        if t is not None:
+            _need(t, name, ts, torch.float32, dev)
+    for name, t in (("oc", oc), ("d_oc", d_oc)):
+        if t is not None:
+            _need(t, name, cs, torch.float32, dev)
+    _check(load().vsa_combine_bwd(ctypes.byref(p.c_struct()), _ptr(dout), _ptr(o_f), _ptr(oc), _ptr(gate_c),
+                                  _ptr(gate_f), _ptr(d_of), _ptr(d_oc), _ptr(d_gate_c), _ptr(d_gate_f),
+                                  _stream(stream, dev)), "vsa_combine_bwd")
+
+
+def vsa_coarse_bwd_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().vsa_coarse_bwd_workspace_size(ctypes.byref(p.c_struct()), ctypes.byref(n)),
+           "vsa_coarse_bwd_workspace_size")
+    return int(n.value)
+
+
+def vsa_coarse_bwd(p: Problem, qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, oc: torch.Tensor,
+                   d_oc: torch.Tensor, dqc: torch.Tensor, dkc: torch.Tensor, dvc: torch.Tensor,
+                   workspace: torch.Tensor, stream=None) -> None:
+    """Gradients of the coarse attention (float32 cube tensors)."""
+    dev = qc.device
+    cs = _cube_shape(p)
+    for name, t in (("qc", qc), ("kc", kc), ("vc", vc), ("oc", oc), ("d_oc", d_oc), ("dqc", dqc),
+                    ("dkc", dkc), ("dvc", dvc)):
+        _need(t, name, cs, torch.float32, dev)
+    if workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D byte tensor")
+    _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    _check(load().vsa_coarse_bwd(ctypes.byref(p.c_struct()), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(oc), _ptr(d_oc),
+                                 _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(workspace), int(workspace.numel()),
+                                 _stream(stream, dev)), "vsa_coarse_bwd")
+
+
+def vsa_pool_unpermute_bwd(p: Problem, dx_cube: torch.Tensor, dxc: Optional[torch.Tensor], dx_raster: torch.Tensor,
+                           stream=None) -> None:
+    """dx_raster = unpermute(dx_cube + dxc broadcast over each cube / vol), float32."""
+    dev = dx_cube.device
+    _need(dx_cube, "dx_cube", _tok_shape(p), torch.float32, dev)
+    _need(dx_raster, "dx_raster", _tok_shape(p), torch.float32, dev)
+    if dxc is not None:
+        _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
+    _check(load().vsa_pool_unpermute_bwd(ctypes.byref(p.c_struct()), _ptr(dx_cube), _ptr(dxc), _ptr(dx_raster),
+                                         _stream(stream, dev)), "vsa_pool_unpermute_bwd")

@@ -17,6 +17,10 @@
 // d = 128).  All index arithmetic is 32-bit within a (batch, head) and done
 // once per row, so the kernels stay HBM-bound.
 //
+// The gradient pass (float32 only) runs the reorder back and the adjoint of
+// the pool at once: every token of cube c leaves with its own gradient plus
+// xc[c] / vol, the gradient that reaches it through the cube mean.
+//
 // Pooling sums a thread's rows in increasing order in float32, then the RG
 // partial rows in phase order through LDS, then divides by vol: the order
 // never depends on timing, so results are bit-reproducible, and the fused
@@ -31,7 +35,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int64_t kMaxGrid = 1 << 20;   // larger problems loop over cubes
 
-enum Mode { kToCube = 0, kToRaster = 1, kPool = 2, kToCubePool = 3 };
+enum Mode { kToCube = 0, kToRaster = 1, kPool = 2, kToCubePool = 3, kToRasterAddPooled = 4 };
 
 template <typename T>
 __device__ __forceinline__ void widen(const uint4& raw, float* out);
@@ -101,6 +105,8 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
   constexpr bool kCopy = MODE != kPool;
   constexpr bool kFromRaster = MODE == kToCube || MODE == kToCubePool;
   constexpr bool kStreamLoads = MODE != kToCubePool;
+  constexpr bool kAddPooled = MODE == kToRasterAddPooled;
+  static_assert(!kAddPooled || std::is_same<T, float>::value, "the gradient pass is float32");
   __shared__ float part[kPooling ? RG : 1][kPooling ? D + 1 : 1];
   const int col = threadIdx.x % CPR;
   const int phase = threadIdx.x / CPR;
@@ -117,6 +123,12 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
     float acc[kPooling ? E : 1];
 #pragma unroll
     for (int e = 0; e < (kPooling ? E : 1); ++e) acc[e] = 0.f;
+    float4 add = make_float4(0.f, 0.f, 0.f, 0.f);   // xc[c] / vol of this thread's columns
+    if (kAddPooled) {
+      const float4 x = reinterpret_cast<const float4*>(xc + unit * D)[col];
+      const float inv = 1.0f / (float)a.vol;
+      add = make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv);
+    }
 
     // Batches of KB rows per thread.  A full batch issues all its loads
     // before the first store; only a cube's ragged last batch is guarded.
@@ -135,7 +147,14 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
       for (int b = 0; b < KB; ++b) {
         const int32_t l = l0 + b * RG;
         if (!guarded.value || l < a.vol) {
-          if (kCopy) dst[(kFromRaster ? cube0 + l : rrow[b]) * CPR + col] = buf[b];
+          if (kAddPooled) {
+            float4 f = make_float4(__uint_as_float(buf[b].x) + add.x, __uint_as_float(buf[b].y) + add.y,
+                                   __uint_as_float(buf[b].z) + add.z, __uint_as_float(buf[b].w) + add.w);
+            dst[rrow[b] * CPR + col] = make_uint4(__float_as_uint(f.x), __float_as_uint(f.y),
+                                                  __float_as_uint(f.z), __float_as_uint(f.w));
+          } else if (kCopy) {
+            dst[(kFromRaster ? cube0 + l : rrow[b]) * CPR + col] = buf[b];
+          }
           if (kPooling) {
             float v[E];
             widen<T>(buf[b], v);
@@ -212,6 +231,12 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, 
 hipError_t launch_permute_pool(const Geom& g, int dtype, const void* x_raster, void* x_cube, float* xc,
                                hipStream_t s) {
   return launch_dtype<kToCubePool>(g, dtype, x_raster, x_cube, xc, s);
+}
+
+hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const float* dxc, float* dx_raster,
+                                     hipStream_t s) {
+  if (dxc == nullptr) return launch_mode<float, kToRaster>(g, dx_cube, dx_raster, nullptr, s);
+  return launch_mode<float, kToRasterAddPooled>(g, dx_cube, dx_raster, const_cast<float*>(dxc), s);
 }
 
 }  // namespace vsa

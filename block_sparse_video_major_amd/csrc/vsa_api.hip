@@ -39,7 +39,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (1 << 16) | 1; }
+int vsa_abi_version(void) { return (1 << 16) | 2; }
 
 const char* vsa_status_str(int status) {
   switch (status) {
@@ -195,6 +195,51 @@ int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k, cons
   if (workspace_bytes < vsa::sparse_attn_bwd_workspace(g, max_kv_blocks)) return VSA_ERR_WORKSPACE;
   return hip_status(vsa::launch_sparse_attn_bwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, o, lse,
                                                 d_o, dq, dk, dv, workspace, (hipStream_t)stream));
+}
+
+int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f, const float* oc, const void* gate_c,
+                    const void* gate_f, void* d_of, float* d_oc, float* d_gate_c, float* d_gate_f, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (dout == nullptr || d_of == nullptr || d_oc == nullptr) return VSA_ERR_NULL;
+  if (gate_f != nullptr && (o_f == nullptr || d_gate_f == nullptr)) return VSA_ERR_NULL;
+  if (gate_c != nullptr && (oc == nullptr || d_gate_c == nullptr)) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_combine_bwd(g, dout, o_f, oc, gate_c, gate_f, d_of, d_oc, d_gate_c, d_gate_f,
+                                            (hipStream_t)stream));
+}
+
+int vsa_coarse_bwd_workspace_size(const vsa_problem* p, size_t* bytes) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (bytes == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (g.Nc > vsa::kMaxCoarseCubes) return VSA_ERR_UNSUPPORTED;
+  *bytes = vsa::coarse_bwd_workspace(g);
+  return VSA_OK;
+}
+
+int vsa_coarse_bwd(const vsa_problem* p, const float* qc, const float* kc, const float* vc, const float* oc,
+                   const float* d_oc, float* dqc, float* dkc, float* dvc, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (qc == nullptr || kc == nullptr || vc == nullptr || oc == nullptr || d_oc == nullptr || dqc == nullptr ||
+      dkc == nullptr || dvc == nullptr || workspace == nullptr)
+    return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (g.Nc > vsa::kMaxCoarseCubes) return VSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < vsa::coarse_bwd_workspace(g)) return VSA_ERR_WORKSPACE;
+  return hip_status(vsa::launch_coarse_bwd(g, qc, kc, vc, oc, d_oc, dqc, dkc, dvc, workspace, (hipStream_t)stream));
+}
+
+int vsa_pool_unpermute_bwd(const vsa_problem* p, const float* dx_cube, const float* dxc, float* dx_raster,
+                           void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (dx_cube == nullptr || dx_raster == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_pool_unpermute_bwd(g, dx_cube, dxc, dx_raster, (hipStream_t)stream));
 }
 
 int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32_t* valid_block_num,

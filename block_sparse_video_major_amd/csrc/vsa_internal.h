@@ -64,6 +64,18 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, c
                                   const void* dout, float* dq, float* dk, float* dv, void* workspace,
                                   hipStream_t s);
 
+// Backward of the other steps: the gated combination (cube-major), the coarse
+// attention (workspace: P and dS, 2 * BH * Nc^2 floats) and the reorder back
+// with the pooled gradient added (float32).
+hipError_t launch_combine_bwd(const Geom& g, const void* dout, const void* of, const float* oc, const void* gate_c,
+                              const void* gate_f, void* d_of, float* d_oc, float* d_gate_c, float* d_gate_f,
+                              hipStream_t s);
+size_t coarse_bwd_workspace(const Geom& g);
+hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
+                             const float* doc, float* dqc, float* dkc, float* dvc, void* workspace, hipStream_t s);
+hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const float* dxc, float* dx_raster,
+                                     hipStream_t s);
+
 // Largest number of cubes per (batch, head) the coarse stage handles.
 constexpr int64_t kMaxCoarseCubes = 4096;
 // ... and the backward (one LDS counter per key cube in the list build).

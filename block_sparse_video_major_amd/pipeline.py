@@ -1,4 +1,4 @@
-"""The whole VSA forward pass as a sequence of C-ABI calls.
+"""The whole VSA forward pass, and its backward, as sequences of C-ABI calls.
 
 Order of the steps ("VSA: Accelerating Video Diffusion Inference with Sparse
 Attention on AMD GPUs", §Two-Stage Architecture): reorder tokens into cubes
@@ -6,8 +6,11 @@ and mean-pool them (one fused pass per tensor), coarse cube attention with
 Top-K selection, fine block-sparse attention over the selected cubes combined
 with the coarse output through the gates, written straight back in the
 model's token order (the reorder back runs in the fine kernel's epilogue).
-This module only allocates the intermediate buffers (through torch) and calls
-the library; every step runs in the HIP kernels of libvsa.so.
+The backward ("VSA: Faster Video Diffusion with Trainable Sparse
+Attention", Abstract: trained end to end) takes those steps in reverse with
+the index list held fixed.  This module only allocates the intermediate
+buffers (through torch) and calls the library; every step runs in the HIP
+kernels of libvsa.so.
 """
 from __future__ import annotations
 
@@ -68,3 +71,58 @@ def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, t
     f = VsaForward(p, top_k, q.device, with_gates=gate_c is not None or gate_f is not None)
     out = torch.empty_like(q)
     return f(q, k, v, out, gate_c, gate_f, stream)
+
+
+class VsaBackward:
+    """Buffers for the backward of one layer; call() runs it.
+
+    Inputs are the forward's cube-major intermediates (qp, kp, vp, qc, kc, vc,
+    oc, the LUT and counts), O_f and its LSE (cube-major: vsa_sparse_attn_fwd
+    without gates), and the raster-order upstream gradient dout and gates.
+    Outputs are the raster-order float32 gradients of q, k, v and the gates.
+    Steps: reorder dout and the gates into cubes, combine backward, fine
+    backward, coarse backward, then the reorder back with each pooled
+    gradient added."""
+
+    def __init__(self, p: Problem, max_kv: int, device="cuda"):
+        self.p = p
+        ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
+        cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
+        bf, f32 = torch.bfloat16, torch.float32
+        self.doutp, self.gcp, self.gfp, self.d_of = (torch.empty(ts, dtype=bf, device=device) for _ in range(4))
+        self.dgcp, self.dgfp = (torch.empty(ts, dtype=f32, device=device) for _ in range(2))
+        self.dqf, self.dkf, self.dvf = (torch.empty(ts, dtype=f32, device=device) for _ in range(3))
+        self.d_oc, self.dqc, self.dkc, self.dvc = (torch.empty(cs, dtype=f32, device=device) for _ in range(4))
+        self.ws_fine = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, max_kv), dtype=torch.uint8,
+                                   device=device)
+        self.ws_coarse = torch.empty(L.vsa_coarse_bwd_workspace_size(p), dtype=torch.uint8, device=device)
+
+    def __call__(self, saved: Dict[str, torch.Tensor], o_f: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                 dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                 gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                 dgate_c: Optional[torch.Tensor] = None, dgate_f: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+        p, B = self.p, L.VSA_BF16
+        L.vsa_permute(p, B, dout, self.doutp, stream)
+        gcp = gfp = None
+        if gate_c is not None:
+            L.vsa_permute(p, B, gate_c, self.gcp, stream)
+            gcp = self.gcp
+        if gate_f is not None:
+            L.vsa_permute(p, B, gate_f, self.gfp, stream)
+            gfp = self.gfp
+        L.vsa_combine_bwd(p, self.doutp, self.d_of, self.d_oc, o_f=o_f, oc=saved["oc"], gate_c=gcp, gate_f=gfp,
+                          d_gate_c=self.dgcp if gcp is not None else None,
+                          d_gate_f=self.dgfp if gfp is not None else None, stream=stream)
+        L.vsa_sparse_attn_bwd(p, saved["qp"], saved["kp"], saved["vp"], saved["kv_block_idx"],
+                              saved["valid_block_num"], o_f, lse, self.d_of, self.dqf, self.dkf, self.dvf,
+                              self.ws_fine, stream)
+        L.vsa_coarse_bwd(p, saved["qc"], saved["kc"], saved["vc"], saved["oc"], self.d_oc, self.dqc, self.dkc,
+                         self.dvc, self.ws_coarse, stream)
+        L.vsa_pool_unpermute_bwd(p, self.dqf, self.dqc, dq, stream)
+        L.vsa_pool_unpermute_bwd(p, self.dkf, self.dkc, dk, stream)
+        L.vsa_pool_unpermute_bwd(p, self.dvf, self.dvc, dv, stream)
+        if gcp is not None and dgate_c is not None:
+            L.vsa_pool_unpermute_bwd(p, self.dgcp, None, dgate_c, stream)
+        if gfp is not None and dgate_f is not None:
+            L.vsa_pool_unpermute_bwd(p, self.dgfp, None, dgate_f, stream)

@@ -15,7 +15,9 @@
  *   4. vsa_sparse_attn_fwd  fine attention over the listed cubes, combined
  *                       with O_c through the gates
  *   5. vsa_unpermute    cube-major -> raster order
- * and the backward of step 4's attention (vsa_sparse_attn_bwd), for training.
+ * and, for training a layer end to end, the backward of each step:
+ *   vsa_combine_bwd, vsa_sparse_attn_bwd, vsa_coarse_bwd and
+ *   vsa_pool_unpermute_bwd (the index list held fixed).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -236,6 +238,54 @@ int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k,
                         const void* o, const float* lse, const void* d_o,
                         float* dq, float* dk, float* dv, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Backward of the gated combination ([VSA-ROCm] §Two-Stage Architecture:
+ * gates between the coarse and fine outputs; [VSA-arXiv] Abstract: trained
+ * end to end).  For out[p] = g_f[p] * O_f[p] + g_c[p] * oc[c(p)], c(p) the cube
+ * of token p, and the upstream gradient dout:
+ *   d_of[p]     = g_f[p] * dout[p]                   (bf16, RNE)
+ *   d_oc[c]     = sum over the cube's tokens of g_c * dout   (float32,
+ *                 fixed summation order; 0 when gate_c == NULL)
+ *   d_gate_f[p] = dout[p] * O_f[p],  d_gate_c[p] = dout[p] * oc[c(p)]  (float32)
+ * gate_f == NULL means g_f = 1 (then o_f and d_gate_f may be NULL);
+ * gate_c == NULL means g_c = 0 (then oc and d_gate_c may be NULL).
+ * dout, o_f, gate_c, gate_f, d_of: [batch, heads, N, head_dim] bf16;
+ * d_gate_c, d_gate_f: same shape float32; oc, d_oc: [batch, heads, Nc,
+ * head_dim] float32.  All token tensors cube-major (vsa_permute them). */
+int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f,
+                    const float* oc, const void* gate_c, const void* gate_f,
+                    void* d_of, float* d_oc, float* d_gate_c, float* d_gate_f,
+                    void* stream);
+
+/* Workspace of vsa_coarse_bwd in bytes (2 * batch * heads * Nc^2 * 4: the
+ * coarse probabilities P and dS).  Host only; Nc > 4096 gives
+ * VSA_ERR_UNSUPPORTED. */
+int vsa_coarse_bwd_workspace_size(const vsa_problem* p, size_t* bytes);
+
+/* Backward of the coarse attention ([VSA-ROCm] §Two-Stage Architecture,
+ * Stage 1; [VSA-arXiv] Abstract).  With S = qc kc^T / sqrt(head_dim) over all
+ * cubes, P = softmax(S) (recomputed), Dc = rowsum(d_oc * oc):
+ *   dvc = P^T d_oc,  dS = P * (d_oc vc^T - Dc),
+ *   dqc = dS kc / sqrt(head_dim),  dkc = dS^T qc / sqrt(head_dim).
+ * qc, kc, vc, oc (the forward's O_c), d_oc, dqc, dkc, dvc: [batch, heads, Nc,
+ * head_dim] float32, computed in float32.  workspace of workspace_bytes >=
+ * vsa_coarse_bwd_workspace_size, else VSA_ERR_WORKSPACE; clobbered.
+ * Nc <= 4096. */
+int vsa_coarse_bwd(const vsa_problem* p, const float* qc, const float* kc,
+                   const float* vc, const float* oc, const float* d_oc,
+                   float* dqc, float* dkc, float* dvc, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Backward of the reorder and the cube pool ([VSA-ROCm] §Two-Stage
+ * Architecture: pre-stage reordering and Stage 1 mean-pooling): the gradient
+ * of the raster input collects the cube-major gradient of its token plus,
+ * through the mean, 1/vol of its cube's pooled gradient:
+ *   dx_raster[b, h, pi(p), :] = dx_cube[b, h, p, :] + dxc[b, h, c(p), :] / vol
+ * dx_cube, dx_raster: [batch, heads, N, head_dim] float32; dxc: [batch,
+ * heads, Nc, head_dim] float32 or NULL (then a plain float32 unpermute).
+ * Buffers must not overlap. */
+int vsa_pool_unpermute_bwd(const vsa_problem* p, const float* dx_cube,
+                           const float* dxc, float* dx_raster, void* stream);
 
 /* Host helper: perm_host[p] = pi(p) for p < N (the order vsa_permute
  * applies).  perm_host is a host array of N int32.  No device work. */
