@@ -260,7 +260,46 @@ def main() -> int:
             e[1].record(stream)
             torch.cuda.synchronize()
             t_bwd += e[0].elapsed_time(e[1]) / reps
-        del grads, ws, d_o, o_f, lse_f
+        # the whole layer's backward (VsaBackward) with seeded gates: reorder
+        # dout and gates, combine backward, fine backward, coarse backward,
+        # reorder back with the pooled gradients added
+        bw = vsa.VsaBackward(p, w.top_k, dev)
+        gate_c = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+        gate_f = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+        lgrads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(5)]
+
+        def layer_bwd(ev=None):
+            def mark(i):
+                if ev is not None:
+                    ev[i].record(stream)
+            mark(0)
+            for src, dst in ((d_o, bw.doutp), (gate_c, bw.gcp), (gate_f, bw.gfp)):
+                L.vsa_permute(p, B, src, dst, stream)
+            mark(1)
+            L.vsa_combine_bwd(p, bw.doutp, bw.d_of, bw.d_oc, o_f=o_f, oc=f.oc, gate_c=bw.gcp, gate_f=bw.gfp,
+                              d_gate_c=bw.dgcp, d_gate_f=bw.dgfp, stream=stream)
+            mark(2)
+            L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, bw.d_of, bw.dqf, bw.dkf,
+                                  bw.dvf, bw.ws_fine, stream)
+            mark(3)
+            L.vsa_coarse_bwd(p, f.qc, f.kc, f.vc, f.oc, bw.d_oc, bw.dqc, bw.dkc, bw.dvc, bw.ws_coarse, stream)
+            mark(4)
+            for src, sc, dst in ((bw.dqf, bw.dqc, lgrads[0]), (bw.dkf, bw.dkc, lgrads[1]),
+                                 (bw.dvf, bw.dvc, lgrads[2]), (bw.dgcp, None, lgrads[3]),
+                                 (bw.dgfp, None, lgrads[4])):
+                L.vsa_pool_unpermute_bwd(p, src, sc, dst, stream)
+            mark(5)
+        layer_bwd()
+        torch.cuda.synchronize()
+        lnames = ["reorder_dout_gates", "combine_bwd", "sparse_attn_bwd", "coarse_bwd", "pool_unpermute_bwd"]
+        lt = {n: 0.0 for n in lnames}
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            layer_bwd(e)
+            torch.cuda.synchronize()
+            for i, n in enumerate(lnames):
+                lt[n] += e[i].elapsed_time(e[i + 1]) / reps
+        del grads, ws, d_o, o_f, lse_f, bw, lgrads, gate_c, gate_f
     torch.cuda.synchronize()
 
     flops = w.selected_flops()
@@ -307,7 +346,10 @@ def main() -> int:
         "backward": {"ms_per_call": round(t_bwd, 4),
                      "tflops": round(2.5 * flops / (t_bwd * 1e-3) / 1e12, 2),
                      "pct_bf16_peak": round(100 * 2.5 * flops / (t_bwd * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2),
-                     "flop_accounting": "5 products of 2*64*64*d per selected pair (S, dP, dQ, dK, dV)"},
+                     "flop_accounting": "5 products of 2*64*64*d per selected pair (S, dP, dQ, dK, dV)",
+                     "layer_ms": round(sum(lt.values()), 4),
+                     "layer_stages_ms": {n: round(t, 4) for n, t in lt.items()},
+                     "layer_note": "whole-layer backward with gates (VsaBackward steps), LUT fixed"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},
