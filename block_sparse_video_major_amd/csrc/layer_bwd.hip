@@ -15,18 +15,16 @@
 //
 // Combine: one workgroup per cube, thread t owns column chunk t % CPR of rows
 // t / CPR + RG k; the per-cube sum for dO_c is reduced through LDS in a fixed
-// order (bit-reproducible).  Coarse, fp32 throughout: the rows kernel takes R
-// query cubes per workgroup, forms their score and dP rows against key chunks
-// staged in LDS, the row softmax, P and dS (written to the workspace) and dQc;
-// the columns kernel takes R key cubes and sums dKc and dVc over query chunks
-// staged the same way.
+// order (bit-reproducible).  Coarse, float32 throughout: five batched
+// products over the heads (S and dP, then dQc, dKc and dVc) with
+// register-blocked 64 x 64 tiles, and one row pass for the softmax and dS;
+// S / P and dP / dS live in the caller's workspace.
 #include "vsa_internal.h"
 
 namespace vsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 32;   // key (or query) cubes staged in LDS at a time
 
 __device__ __forceinline__ void unpack8(const uint4& raw, float* f) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -108,226 +106,116 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   }
 }
 
-// ---- coarse: rows ----------------------------------------------------------------
-// Query cubes i0 .. i0 + R - 1 of one (batch, head).  LDS: their Qc and dO_c
-// rows, their score / P rows and dP / dS rows over all Nc key cubes, and one
-// staged chunk of Kc and Vc rows.
-template <int D, int R>
-__global__ __launch_bounds__(kThreads) void coarse_bwd_rows_kernel(
-    const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
-    const float* __restrict__ oc, const float* __restrict__ doc, float* __restrict__ dqc,
-    float* __restrict__ pmat, float* __restrict__ dsmat, int Nc, float scale) {
-  constexpr int KS = D + 1;   // padded row stride of staged chunks
-  extern __shared__ float sm[];
-  float* qr = sm;                      // [R][D]
-  float* dr = qr + R * D;              // [R][D]
-  float* sr = dr + R * D;              // [R][Nc]  scores, then P
-  float* pr = sr + R * Nc;             // [R][Nc]  dP, then dS
-  float* kch = pr + R * Nc;            // [kChunk][KS]
-  float* vch = kch + kChunk * KS;      // [kChunk][KS]
+// ---- coarse: batched float32 products -------------------------------------------
+// C[h] = alpha * op(A[h]) op(B[h]) for every (batch, head) h (grid z), with
+// op(X) = X or X^T as stored row-major.  64 x 64 output tiles per workgroup,
+// k in steps of 16 staged in LDS (A as [k][m], B as [k][n], rows padded to
+// 68 floats), each thread a 4 x 4 block from two 16-byte LDS reads per k.
+// Global loads run along whichever dimension is contiguous, 16 bytes at a
+// time when the dimension and the row stride allow it.
+constexpr int kTM = 64, kTN = 64, kTK = 16, kPad = 68;
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                           float* __restrict__ C, int M, int N, int K, int lda,
+                                                           int ldb, int ldc, int64_t sa, int64_t sb, int64_t sc,
+                                                           float alpha) {
+  __shared__ __attribute__((aligned(16))) float As[kTK][kPad];
+  __shared__ __attribute__((aligned(16))) float Bs[kTK][kPad];
   const int tid = threadIdx.x;
-  const int blocks = (Nc + R - 1) / R;
-  const int64_t bh = blockIdx.x / blocks;
-  const int i0 = (int)(blockIdx.x - bh * blocks) * R;
-  const int64_t base = bh * (int64_t)Nc * D;
-  for (int e = tid; e < R * D; e += kThreads) {
-    const int r = e / D, i = i0 + r;
-    qr[e] = i < Nc ? qc[base + (int64_t)i * D + e % D] : 0.f;
-    dr[e] = i < Nc ? doc[base + (int64_t)i * D + e % D] : 0.f;
-  }
-  // scores and dP against key chunks
-  for (int j0 = 0; j0 < Nc; j0 += kChunk) {
-    __syncthreads();
-    for (int e = tid; e < kChunk * D; e += kThreads) {
-      const int jj = e / D, j = j0 + jj;
-      kch[jj * KS + e % D] = j < Nc ? kc[base + (int64_t)j * D + e % D] : 0.f;
-      vch[jj * KS + e % D] = j < Nc ? vc[base + (int64_t)j * D + e % D] : 0.f;
-    }
-    __syncthreads();
-    for (int pair = tid; pair < R * kChunk; pair += kThreads) {
-      const int r = pair / kChunk, jj = pair % kChunk, j = j0 + jj;
-      float s = 0.f, p = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(qr[r * D + d], kch[jj * KS + d], s);
-        p = fmaf(dr[r * D + d], vch[jj * KS + d], p);
-      }
-      if (j < Nc) {
-        sr[r * Nc + j] = scale * s;
-        pr[r * Nc + j] = p;
-      }
-    }
-  }
-  __syncthreads();
-  // row softmax, Dc, dS; one wavefront per row
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int r = wave; r < R; r += kThreads / 64) {
-    const int i = i0 + r;
-    if (i >= Nc) continue;
-    float m = -INFINITY;
-    for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[r * Nc + j]);
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float sum = 0.f;
-    for (int j = lane; j < Nc; j += 64) sum += __expf(sr[r * Nc + j] - m);
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-    float dc = 0.f;
-    for (int d = lane; d < D; d += 64) dc = fmaf(dr[r * D + d], oc[base + (int64_t)i * D + d], dc);
-    for (int o = 32; o >= 1; o >>= 1) dc += __shfl_xor(dc, o);
-    const float inv = 1.f / sum;
-    float* prow = pmat + (bh * (int64_t)Nc + i) * Nc;
-    float* dsrow = dsmat + (bh * (int64_t)Nc + i) * Nc;
-    for (int j = lane; j < Nc; j += 64) {
-      const float p = __expf(sr[r * Nc + j] - m) * inv;
-      const float ds = p * (pr[r * Nc + j] - dc);
-      sr[r * Nc + j] = p;
-      pr[r * Nc + j] = ds;
-      prow[j] = p;
-      dsrow[j] = ds;
-    }
-  }
-  // dQc = scale * dS Kc over key chunks
-  constexpr int OUT = R * D / kThreads > 0 ? R * D / kThreads : 1;   // outputs per thread
-  float acc[OUT];
+  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+  A += blockIdx.z * sa;
+  B += blockIdx.z * sb;
+  C += blockIdx.z * sc;
+  const int tm = tid / 16, tn = tid % 16;   // 4 x 4 block (4 tm.., 4 tn..)
+  float acc[4][4];
 #pragma unroll
-  for (int u = 0; u < OUT; ++u) acc[u] = 0.f;
-  for (int j0 = 0; j0 < Nc; j0 += kChunk) {
-    __syncthreads();
-    for (int e = tid; e < kChunk * D; e += kThreads) {
-      const int jj = e / D, j = j0 + jj;
-      kch[jj * KS + e % D] = j < Nc ? kc[base + (int64_t)j * D + e % D] : 0.f;
-    }
-    __syncthreads();
-    const int jn = Nc - j0 < kChunk ? Nc - j0 : kChunk;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int u = 0; u < OUT; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < R * D) {
-        const int r = e / D, d = e % D;
-        float a = acc[u];
-        for (int jj = 0; jj < jn; ++jj) a = fmaf(pr[r * Nc + j0 + jj], kch[jj * KS + d], a);
-        acc[u] = a;
-      }
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  // element (m, k) of op(A) is A[m * lda + k] (TA: A[k * lda + m]); (k, n) of
+  // op(B) is B[k * ldb + n] (TB: B[n * ldb + k])
+  for (int k0 = 0; k0 < K; k0 += kTK) {
+    // 64 x 16 = 1024 elements of each tile, 4 per thread
+    if (!TA) {   // contiguous along k: thread -> (m = tid / 4, k = 4 * (tid % 4) ..)
+      const int m = m0 + tid / 4, k = k0 + 4 * (tid % 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[4 * (tid % 4) + e][tid / 4] = (m < M && k + e < K) ? A[(int64_t)m * lda + k + e] : 0.f;
+    } else {     // contiguous along m: thread -> (k = tid / 16, m = 4 * (tid % 16) ..)
+      const int k = k0 + tid / 16, m = m0 + 4 * (tid % 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[tid / 16][4 * (tid % 16) + e] = (k < K && m + e < M) ? A[(int64_t)k * lda + m + e] : 0.f;
     }
+    if (!TB) {   // contiguous along n
+      const int k = k0 + tid / 16, n = n0 + 4 * (tid % 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[tid / 16][4 * (tid % 16) + e] = (k < K && n + e < N) ? B[(int64_t)k * ldb + n + e] : 0.f;
+    } else {     // contiguous along k
+      const int n = n0 + tid / 4, k = k0 + 4 * (tid % 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[4 * (tid % 4) + e][tid / 4] = (n < N && k + e < K) ? B[(int64_t)n * ldb + k + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kTK; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[kk][4 * tm]);
+      const float4 b = *reinterpret_cast<const float4*>(&Bs[kk][4 * tn]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
   }
 #pragma unroll
-  for (int u = 0; u < OUT; ++u) {
-    const int e = tid + u * kThreads;
-    if (e < R * D) {
-      const int r = e / D, d = e % D, i = i0 + r;
-      if (i < Nc) dqc[base + (int64_t)i * D + d] = scale * acc[u];
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * tm + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 4 * tn + j;
+      if (n < N) C[(int64_t)m * ldc + n] = alpha * acc[i][j];
     }
   }
 }
 
-// ---- coarse: columns --------------------------------------------------------------
-// Key cubes j0 .. j0 + R - 1: dKc = scale * dS^T Qc and dVc = P^T dO_c, summed
-// over chunks of query cubes staged in LDS.
-template <int D, int R>
-__global__ __launch_bounds__(kThreads) void coarse_bwd_cols_kernel(
-    const float* __restrict__ qc, const float* __restrict__ doc, const float* __restrict__ pmat,
-    const float* __restrict__ dsmat, float* __restrict__ dkc, float* __restrict__ dvc, int Nc, float scale) {
-  constexpr int KS = D + 1;
-  __shared__ float qch[kChunk * KS];
-  __shared__ float dch[kChunk * KS];
-  __shared__ float pch[kChunk * R];
-  __shared__ float sch[kChunk * R];
-  const int tid = threadIdx.x;
-  const int blocks = (Nc + R - 1) / R;
-  const int64_t bh = blockIdx.x / blocks;
-  const int j0 = (int)(blockIdx.x - bh * blocks) * R;
-  const int64_t base = bh * (int64_t)Nc * D;
-  const int64_t mbase = bh * (int64_t)Nc * Nc;
-  constexpr int OUT = R * D / kThreads > 0 ? R * D / kThreads : 1;
-  float ak[OUT], av[OUT];
-#pragma unroll
-  for (int u = 0; u < OUT; ++u) { ak[u] = 0.f; av[u] = 0.f; }
-  for (int i0 = 0; i0 < Nc; i0 += kChunk) {
-    __syncthreads();
-    for (int e = tid; e < kChunk * D; e += kThreads) {
-      const int ii = e / D, i = i0 + ii;
-      qch[ii * KS + e % D] = i < Nc ? qc[base + (int64_t)i * D + e % D] : 0.f;
-      dch[ii * KS + e % D] = i < Nc ? doc[base + (int64_t)i * D + e % D] : 0.f;
-    }
-    for (int e = tid; e < kChunk * R; e += kThreads) {
-      const int ii = e / R, jr = e % R, i = i0 + ii, j = j0 + jr;
-      const bool in = i < Nc && j < Nc;
-      pch[e] = in ? pmat[mbase + (int64_t)i * Nc + j] : 0.f;
-      sch[e] = in ? dsmat[mbase + (int64_t)i * Nc + j] : 0.f;
-    }
-    __syncthreads();
-    const int in_n = Nc - i0 < kChunk ? Nc - i0 : kChunk;
-#pragma unroll
-    for (int u = 0; u < OUT; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < R * D) {
-        const int jr = e / D, d = e % D;
-        float a = ak[u], b = av[u];
-        for (int ii = 0; ii < in_n; ++ii) {
-          a = fmaf(sch[ii * R + jr], qch[ii * KS + d], a);
-          b = fmaf(pch[ii * R + jr], dch[ii * KS + d], b);
-        }
-        ak[u] = a;
-        av[u] = b;
-      }
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < OUT; ++u) {
-    const int e = tid + u * kThreads;
-    if (e < R * D) {
-      const int jr = e / D, d = e % D, j = j0 + jr;
-      if (j < Nc) {
-        dkc[base + (int64_t)j * D + d] = scale * ak[u];
-        dvc[base + (int64_t)j * D + d] = av[u];
-      }
-    }
+// Row i of one head: P = softmax(S) in place of S, and, with
+// Dc = rowsum(dO_c * O_c), dS = P * (dP - Dc) in place of dP.  One wavefront
+// per row.
+__global__ __launch_bounds__(kThreads) void coarse_softmax_ds_kernel(float* __restrict__ smat, float* __restrict__ dpmat,
+                                                                    const float* __restrict__ oc,
+                                                                    const float* __restrict__ doc, int Nc, int D,
+                                                                    int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float* srow = smat + row * Nc;
+  float* drow = dpmat + row * Nc;
+  float m = -INFINITY;
+  for (int j = lane; j < Nc; j += 64) m = fmaxf(m, srow[j]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float sum = 0.f;
+  for (int j = lane; j < Nc; j += 64) sum += __expf(srow[j] - m);
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  float dc = 0.f;
+  for (int d = lane; d < D; d += 64) dc = fmaf(doc[row * D + d], oc[row * D + d], dc);
+  for (int o = 32; o >= 1; o >>= 1) dc += __shfl_xor(dc, o);
+  const float inv = 1.f / sum;
+  for (int j = lane; j < Nc; j += 64) {
+    const float p = __expf(srow[j] - m) * inv;
+    srow[j] = p;
+    drow[j] = p * (drow[j] - dc);
   }
 }
 
-constexpr int kLdsMax = 160 * 1024;
-
-template <int D, int R>
-size_t rows_lds(int Nc) {
-  return sizeof(float) * ((size_t)2 * R * D + (size_t)2 * R * Nc + (size_t)2 * kChunk * (D + 1));
-}
-
-template <int D, int R>
-hipError_t launch_coarse_r(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
-                           const float* doc, float* dqc, float* dkc, float* dvc, float* pmat, float* dsmat,
-                           hipStream_t s) {
-  static int granted[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const int Nc = (int)g.Nc;
-  const size_t lds = rows_lds<D, R>(Nc);
-  if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
-  auto kr = coarse_bwd_rows_kernel<D, R>;
-  if (granted[dev] < (int)lds) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    granted[dev] = (int)lds;
-  }
-  const float scale = 1.0f / sqrtf((float)D);
-  const unsigned blocks = (unsigned)(g.BH * ((Nc + R - 1) / R));
-  hipLaunchKernelGGL(kr, dim3(blocks), dim3(kThreads), lds, s, qc, kc, vc, oc, doc, dqc, pmat, dsmat, Nc, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((coarse_bwd_cols_kernel<D, R>), dim3(blocks), dim3(kThreads), 0, s, qc, doc,
-                     (const float*)pmat, (const float*)dsmat, dkc, dvc, Nc, scale);
+template <bool TA, bool TB>
+hipError_t gemm(int heads, const float* A, const float* B, float* C, int M, int N, int K, int lda, int ldb, int ldc,
+                int64_t sa, int64_t sb, int64_t sc, float alpha, hipStream_t s) {
+  const dim3 grid((unsigned)((N + kTN - 1) / kTN), (unsigned)((M + kTM - 1) / kTM), (unsigned)heads);
+  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, dim3(kThreads), 0, s, A, B, C, M, N, K, lda, ldb, ldc, sa,
+                     sb, sc, alpha);
   return hipGetLastError();
-}
-
-// R = query (key) cubes per workgroup: as many as let the score rows fit in LDS.
-template <int D>
-hipError_t launch_coarse_d(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
-                           const float* doc, float* dqc, float* dkc, float* dvc, float* pmat, float* dsmat,
-                           hipStream_t s) {
-  const int Nc = (int)g.Nc;
-  if (rows_lds<D, 8>(Nc) <= (size_t)kLdsMax)
-    return launch_coarse_r<D, 8>(g, qc, kc, vc, oc, doc, dqc, dkc, dvc, pmat, dsmat, s);
-  if (rows_lds<D, 4>(Nc) <= (size_t)kLdsMax)
-    return launch_coarse_r<D, 4>(g, qc, kc, vc, oc, doc, dqc, dkc, dvc, pmat, dsmat, s);
-  return launch_coarse_r<D, 2>(g, qc, kc, vc, oc, doc, dqc, dkc, dvc, pmat, dsmat, s);
 }
 
 }  // namespace
@@ -354,14 +242,26 @@ size_t coarse_bwd_workspace(const Geom& g) {
   return 2 * sizeof(float) * (size_t)g.BH * (size_t)g.Nc * (size_t)g.Nc;
 }
 
+// S = scale Qc Kc^T and dP = dO_c Vc^T, then P and dS in place, then
+// dQc = scale dS Kc, dKc = scale dS^T Qc, dVc = P^T dO_c.
 hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
                              const float* doc, float* dqc, float* dkc, float* dvc, void* workspace,
                              hipStream_t s) {
-  float* pmat = static_cast<float*>(workspace);
-  float* dsmat = pmat + (size_t)g.BH * g.Nc * g.Nc;
-  if (g.D == 128) return launch_coarse_d<128>(g, qc, kc, vc, oc, doc, dqc, dkc, dvc, pmat, dsmat, s);
-  if (g.D == 64) return launch_coarse_d<64>(g, qc, kc, vc, oc, doc, dqc, dkc, dvc, pmat, dsmat, s);
-  return hipErrorInvalidValue;
+  const int Nc = (int)g.Nc, D = g.D, H = (int)g.BH;
+  const int64_t sm = (int64_t)Nc * Nc, sx = (int64_t)Nc * D;
+  float* smat = static_cast<float*>(workspace);
+  float* dpmat = smat + (size_t)g.BH * sm;
+  const float scale = 1.0f / sqrtf((float)D);
+  hipError_t e;
+  if ((e = gemm<false, true>(H, qc, kc, smat, Nc, Nc, D, D, D, Nc, sx, sx, sm, scale, s)) != hipSuccess) return e;
+  if ((e = gemm<false, true>(H, doc, vc, dpmat, Nc, Nc, D, D, D, Nc, sx, sx, sm, 1.0f, s)) != hipSuccess) return e;
+  const int64_t rows = g.BH * g.Nc;
+  hipLaunchKernelGGL(coarse_softmax_ds_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, smat, dpmat,
+                     oc, doc, Nc, D, rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = gemm<false, false>(H, dpmat, kc, dqc, Nc, D, Nc, Nc, D, D, sm, sx, sx, scale, s)) != hipSuccess) return e;
+  if ((e = gemm<true, false>(H, dpmat, qc, dkc, Nc, D, Nc, Nc, D, D, sm, sx, sx, scale, s)) != hipSuccess) return e;
+  return gemm<true, false>(H, smat, doc, dvc, Nc, D, Nc, Nc, D, D, sm, sx, sx, 1.0f, s);
 }
 
 }  // namespace vsa
