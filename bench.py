@@ -104,6 +104,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the warm-up and timed steps (for counter runs on the step's kernels)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -166,140 +168,143 @@ def main() -> int:
         ms_total = t_start.elapsed_time(t_end)
         fine_ms = [a.elapsed_time(b) for a, b in ev]
 
-        # per-stage breakdown (separate, untimed pass); the step runs the
-        # fused permute_pool, the separate permute and pool are timed too
-        names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute",
-                 "sparse_attn_fwd_raster"]
-        reps = max(3, min(10, args.steps))
-        acc = {n: 0.0 for n in names}
-        for _ in range(reps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-            e[0].record(stream)
-            for t, dst in ((q, f.qp), (k, f.kp), (v, f.vp)):
-                L.vsa_permute(p, B, t, dst, stream)
-            e[1].record(stream)
-            for src, dst in ((f.qp, f.qc), (f.kp, f.kc), (f.vp, f.vc)):
-                L.vsa_pool(p, B, src, dst, stream)
-            e[2].record(stream)
-            for t, dst, dc in ((q, f.qp, f.qc), (k, f.kp, f.kc), (v, f.vp, f.vc)):
-                L.vsa_permute_pool(p, B, t, dst, dc, stream)
-            e[3].record(stream)
-            L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
-            e[4].record(stream)
-            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, out_cube, oc=f.oc, stream=stream)
-            e[5].record(stream)
-            L.vsa_unpermute(p, B, out_cube, out, stream)
-            e[6].record(stream)
-            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
-            e[7].record(stream)
-            torch.cuda.synchronize()
-            for i, n in enumerate(names):
-                acc[n] += e[i].elapsed_time(e[i + 1]) / reps
-        # second workload: a block relation matrix (union of importance,
-        # condition and adjacency masks; a different count per row) converted
-        # by vsa_mask_to_lut and run through the fine kernel
-        mask = wl.block_relation_mask(w, 48, 4)
-        maxk = int(mask.astype(np.int64).sum(axis=-1).max())
-        mask_d = torch.from_numpy(mask).to(dev)
-        lut_m = torch.zeros((w.batch, w.heads, w.n_cubes, maxk), dtype=torch.int32, device=dev)
-        valid_m = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
-        over_m = torch.empty((1,), dtype=torch.int32, device=dev)
-        mt = {"mask_to_lut": 0.0, "fine": 0.0}
-        for _ in range(reps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record(stream)
-            L.vsa_mask_to_lut(p, mask_d, lut_m, valid_m, over_m, stream)
-            e[1].record(stream)
-            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, lut_m, valid_m, out_cube, oc=f.oc, stream=stream)
-            e[2].record(stream)
-            torch.cuda.synchronize()
-            mt["mask_to_lut"] += e[0].elapsed_time(e[1]) / reps
-            mt["fine"] += e[1].elapsed_time(e[2]) / reps
-        pairs_m = int(valid_m.sum().item())
+        def extras():
+            # per-stage breakdown (separate, untimed pass); the step runs the
+            # fused permute_pool, the separate permute and pool are timed too
+            names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute",
+                     "sparse_attn_fwd_raster"]
+            reps = max(3, min(10, args.steps))
+            acc = {n: 0.0 for n in names}
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                e[0].record(stream)
+                for t, dst in ((q, f.qp), (k, f.kp), (v, f.vp)):
+                    L.vsa_permute(p, B, t, dst, stream)
+                e[1].record(stream)
+                for src, dst in ((f.qp, f.qc), (f.kp, f.kc), (f.vp, f.vc)):
+                    L.vsa_pool(p, B, src, dst, stream)
+                e[2].record(stream)
+                for t, dst, dc in ((q, f.qp, f.qc), (k, f.kp, f.kc), (v, f.vp, f.vc)):
+                    L.vsa_permute_pool(p, B, t, dst, dc, stream)
+                e[3].record(stream)
+                L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
+                e[4].record(stream)
+                L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, out_cube, oc=f.oc, stream=stream)
+                e[5].record(stream)
+                L.vsa_unpermute(p, B, out_cube, out, stream)
+                e[6].record(stream)
+                L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
+                e[7].record(stream)
+                torch.cuda.synchronize()
+                for i, n in enumerate(names):
+                    acc[n] += e[i].elapsed_time(e[i + 1]) / reps
+            # second workload: a block relation matrix (union of importance,
+            # condition and adjacency masks; a different count per row) converted
+            # by vsa_mask_to_lut and run through the fine kernel
+            mask = wl.block_relation_mask(w, 48, 4)
+            maxk = int(mask.astype(np.int64).sum(axis=-1).max())
+            mask_d = torch.from_numpy(mask).to(dev)
+            lut_m = torch.zeros((w.batch, w.heads, w.n_cubes, maxk), dtype=torch.int32, device=dev)
+            valid_m = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
+            over_m = torch.empty((1,), dtype=torch.int32, device=dev)
+            mt = {"mask_to_lut": 0.0, "fine": 0.0}
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                L.vsa_mask_to_lut(p, mask_d, lut_m, valid_m, over_m, stream)
+                e[1].record(stream)
+                L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, lut_m, valid_m, out_cube, oc=f.oc, stream=stream)
+                e[2].record(stream)
+                torch.cuda.synchronize()
+                mt["mask_to_lut"] += e[0].elapsed_time(e[1]) / reps
+                mt["fine"] += e[1].elapsed_time(e[2]) / reps
+            pairs_m = int(valid_m.sum().item())
 
-        # sparsity sweep (a diffusion run changes the sparsity from step to
-        # step): coarse stage + fine kernel at each Top-K on the same inputs
-        sweep = {}
-        for kk in wl.SWEEP_TOPK:
-            lut_s = torch.empty((w.batch, w.heads, w.n_cubes, kk), dtype=torch.int32, device=dev)
-            valid_s = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
-            L.vsa_coarse_topk(p, kk, f.qc, f.kc, f.vc, lut_s, valid_s, f.oc, stream)
-            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
-            tsum = 0.0
+            # sparsity sweep (a diffusion run changes the sparsity from step to
+            # step): coarse stage + fine kernel at each Top-K on the same inputs
+            sweep = {}
+            for kk in wl.SWEEP_TOPK:
+                lut_s = torch.empty((w.batch, w.heads, w.n_cubes, kk), dtype=torch.int32, device=dev)
+                valid_s = torch.empty((w.batch, w.heads, w.n_cubes), dtype=torch.int32, device=dev)
+                L.vsa_coarse_topk(p, kk, f.qc, f.kc, f.vc, lut_s, valid_s, f.oc, stream)
+                L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
+                tsum = 0.0
+                for _ in range(reps):
+                    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    e[0].record(stream)
+                    L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
+                    e[1].record(stream)
+                    torch.cuda.synchronize()
+                    tsum += e[0].elapsed_time(e[1]) / reps
+                fl = w.selected_flops(kk)
+                sweep[str(kk)] = {"sparsity": round(1 - kk / w.n_cubes, 3), "fine_ms": round(tsum, 4),
+                                  "fine_tflops": round(fl / (tsum * 1e-3) / 1e12, 2)}
+            flops_m = 4 * 64 * 64 * w.head_dim * pairs_m   # per selected (query cube, key cube) pair
+
+            # backward of the fine stage (training): dQ, dK, dV from the forward's
+            # O_f and log-sum-exp on the same LUT, with a seeded output gradient
+            o_f = torch.empty_like(q)
+            lse_f = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device=dev)
+            L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse_f, stream=stream)
+            gen = torch.Generator(device=dev).manual_seed(5)
+            d_o = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+            ws = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, w.top_k), dtype=torch.uint8, device=dev)
+
+            def bwd():
+                L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, d_o, *grads, ws, stream)
+            bwd()
+            torch.cuda.synchronize()
+            t_bwd = 0.0
             for _ in range(reps):
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
                 e[0].record(stream)
-                L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, lut_s, valid_s, out, oc=f.oc, stream=stream)
+                bwd()
                 e[1].record(stream)
                 torch.cuda.synchronize()
-                tsum += e[0].elapsed_time(e[1]) / reps
-            fl = w.selected_flops(kk)
-            sweep[str(kk)] = {"sparsity": round(1 - kk / w.n_cubes, 3), "fine_ms": round(tsum, 4),
-                              "fine_tflops": round(fl / (tsum * 1e-3) / 1e12, 2)}
-        flops_m = 4 * 64 * 64 * w.head_dim * pairs_m   # per selected (query cube, key cube) pair
+                t_bwd += e[0].elapsed_time(e[1]) / reps
+            # the whole layer's backward (VsaBackward) with seeded gates: reorder
+            # dout and gates, combine backward, fine backward, coarse backward,
+            # reorder back with the pooled gradients added
+            bw = vsa.VsaBackward(p, w.top_k, dev)
+            gate_c = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+            gate_f = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+            lgrads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(5)]
 
-        # backward of the fine stage (training): dQ, dK, dV from the forward's
-        # O_f and log-sum-exp on the same LUT, with a seeded output gradient
-        o_f = torch.empty_like(q)
-        lse_f = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device=dev)
-        L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse_f, stream=stream)
-        gen = torch.Generator(device=dev).manual_seed(5)
-        d_o = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
-        ws = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, w.top_k), dtype=torch.uint8, device=dev)
-
-        def bwd():
-            L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, d_o, *grads, ws, stream)
-        bwd()
-        torch.cuda.synchronize()
-        t_bwd = 0.0
-        for _ in range(reps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(stream)
-            bwd()
-            e[1].record(stream)
+            def layer_bwd(ev=None):
+                def mark(i):
+                    if ev is not None:
+                        ev[i].record(stream)
+                mark(0)
+                for src, dst in ((d_o, bw.doutp), (gate_c, bw.gcp), (gate_f, bw.gfp)):
+                    L.vsa_permute(p, B, src, dst, stream)
+                mark(1)
+                L.vsa_combine_bwd(p, bw.doutp, bw.d_of, bw.d_oc, o_f=o_f, oc=f.oc, gate_c=bw.gcp, gate_f=bw.gfp,
+                                  d_gate_c=bw.dgcp, d_gate_f=bw.dgfp, stream=stream)
+                mark(2)
+                L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, bw.d_of, bw.dqf, bw.dkf,
+                                      bw.dvf, bw.ws_fine, stream)
+                mark(3)
+                L.vsa_coarse_bwd(p, f.qc, f.kc, f.vc, f.oc, bw.d_oc, bw.dqc, bw.dkc, bw.dvc, bw.ws_coarse, stream)
+                mark(4)
+                for src, sc, dst in ((bw.dqf, bw.dqc, lgrads[0]), (bw.dkf, bw.dkc, lgrads[1]),
+                                     (bw.dvf, bw.dvc, lgrads[2]), (bw.dgcp, None, lgrads[3]),
+                                     (bw.dgfp, None, lgrads[4])):
+                    L.vsa_pool_unpermute_bwd(p, src, sc, dst, stream)
+                mark(5)
+            layer_bwd()
             torch.cuda.synchronize()
-            t_bwd += e[0].elapsed_time(e[1]) / reps
-        # the whole layer's backward (VsaBackward) with seeded gates: reorder
-        # dout and gates, combine backward, fine backward, coarse backward,
-        # reorder back with the pooled gradients added
-        bw = vsa.VsaBackward(p, w.top_k, dev)
-        gate_c = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
-        gate_f = torch.rand(q.shape, generator=gen, device=dev).to(torch.bfloat16)
-        lgrads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(5)]
-
-        def layer_bwd(ev=None):
-            def mark(i):
-                if ev is not None:
-                    ev[i].record(stream)
-            mark(0)
-            for src, dst in ((d_o, bw.doutp), (gate_c, bw.gcp), (gate_f, bw.gfp)):
-                L.vsa_permute(p, B, src, dst, stream)
-            mark(1)
-            L.vsa_combine_bwd(p, bw.doutp, bw.d_of, bw.d_oc, o_f=o_f, oc=f.oc, gate_c=bw.gcp, gate_f=bw.gfp,
-                              d_gate_c=bw.dgcp, d_gate_f=bw.dgfp, stream=stream)
-            mark(2)
-            L.vsa_sparse_attn_bwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse_f, bw.d_of, bw.dqf, bw.dkf,
-                                  bw.dvf, bw.ws_fine, stream)
-            mark(3)
-            L.vsa_coarse_bwd(p, f.qc, f.kc, f.vc, f.oc, bw.d_oc, bw.dqc, bw.dkc, bw.dvc, bw.ws_coarse, stream)
-            mark(4)
-            for src, sc, dst in ((bw.dqf, bw.dqc, lgrads[0]), (bw.dkf, bw.dkc, lgrads[1]),
-                                 (bw.dvf, bw.dvc, lgrads[2]), (bw.dgcp, None, lgrads[3]),
-                                 (bw.dgfp, None, lgrads[4])):
-                L.vsa_pool_unpermute_bwd(p, src, sc, dst, stream)
-            mark(5)
-        layer_bwd()
-        torch.cuda.synchronize()
-        lnames = ["reorder_dout_gates", "combine_bwd", "sparse_attn_bwd", "coarse_bwd", "pool_unpermute_bwd"]
-        lt = {n: 0.0 for n in lnames}
-        for _ in range(reps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-            layer_bwd(e)
-            torch.cuda.synchronize()
-            for i, n in enumerate(lnames):
-                lt[n] += e[i].elapsed_time(e[i + 1]) / reps
-        del grads, ws, d_o, o_f, lse_f, bw, lgrads, gate_c, gate_f
+            lnames = ["reorder_dout_gates", "combine_bwd", "sparse_attn_bwd", "coarse_bwd", "pool_unpermute_bwd"]
+            lt = {n: 0.0 for n in lnames}
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+                layer_bwd(e)
+                torch.cuda.synchronize()
+                for i, n in enumerate(lnames):
+                    lt[n] += e[i].elapsed_time(e[i + 1]) / reps
+            del grads, ws, d_o, o_f, lse_f, bw, lgrads, gate_c, gate_f
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt
+        ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
     flops = w.selected_flops()
@@ -332,28 +337,34 @@ def main() -> int:
         "fine_ms_per_call": round(fine_avg, 4),
         "fine_tflops": round(achieved, 2),
         "fine_pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
-        "stages_ms": {n: round(t, 4) for n, t in acc.items()},
-        "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
-                        "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
-                        "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9, 1),
-                        "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
-        "topk_sweep": sweep,
-        "mask_workload": {"pattern": "union of 48 random + 4 fixed + 3x3x3-neighbour key cubes per query cube",
-                          "mean_key_cubes_per_query_cube": round(pairs_m / (w.batch * w.heads * w.n_cubes), 1),
-                          "overflow_rows": int(over_m.item()),
-                          "mask_to_lut_ms": round(mt["mask_to_lut"], 4), "fine_ms": round(mt["fine"], 4),
-                          "fine_tflops": round(flops_m / (mt["fine"] * 1e-3) / 1e12, 2)},
-        "backward": {"ms_per_call": round(t_bwd, 4),
-                     "tflops": round(2.5 * flops / (t_bwd * 1e-3) / 1e12, 2),
-                     "pct_bf16_peak": round(100 * 2.5 * flops / (t_bwd * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2),
-                     "flop_accounting": "5 products of 2*64*64*d per selected pair (S, dP, dQ, dK, dV)",
-                     "layer_ms": round(sum(lt.values()), 4),
-                     "layer_stages_ms": {n: round(t, 4) for n, t in lt.items()},
-                     "layer_note": "whole-layer backward with gates (VsaBackward steps), LUT fixed"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},
     }
+    if ex is not None:
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt = ex
+        rec.update({
+            "stages_ms": {n: round(t, 4) for n, t in acc.items()},
+            "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
+                            "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
+                            "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9,
+                                                      1),
+                            "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
+            "topk_sweep": sweep,
+            "mask_workload": {"pattern": "union of 48 random + 4 fixed + 3x3x3-neighbour key cubes per query cube",
+                              "mean_key_cubes_per_query_cube": round(pairs_m / (w.batch * w.heads * w.n_cubes), 1),
+                              "overflow_rows": int(over_m.item()),
+                              "mask_to_lut_ms": round(mt["mask_to_lut"], 4), "fine_ms": round(mt["fine"], 4),
+                              "fine_tflops": round(flops_m / (mt["fine"] * 1e-3) / 1e12, 2)},
+            "backward": {"ms_per_call": round(t_bwd, 4),
+                         "tflops": round(2.5 * flops / (t_bwd * 1e-3) / 1e12, 2),
+                         "pct_bf16_peak": round(100 * 2.5 * flops / (t_bwd * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS,
+                                                2),
+                         "flop_accounting": "5 products of 2*64*64*d per selected pair (S, dP, dQ, dK, dV)",
+                         "layer_ms": round(sum(lt.values()), 4),
+                         "layer_stages_ms": {n: round(t, 4) for n, t in lt.items()},
+                         "layer_note": "whole-layer backward with gates (VsaBackward steps), LUT fixed"},
+        })
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(rec))
