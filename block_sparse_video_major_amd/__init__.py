@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size,
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
     vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
+    vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
 )
 from .pipeline import VsaBackward, VsaForward, vsa_forward  # noqa: F401
 
@@ -23,4 +24,5 @@ __all__ = [
     "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
     "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",
+    "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
 ]

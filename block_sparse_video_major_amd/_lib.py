@@ -102,6 +102,10 @@ def load() -> ctypes.CDLL:
         "vsa_coarse_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "vsa_coarse_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "vsa_pool_unpermute_bwd": [P, vp, vp, vp, vp],
+        "vsa_permute_bnhd": [P, i32, vp, vp, vp],
+        "vsa_permute_pool_bnhd": [P, i32, vp, vp, vp, vp],
+        "vsa_sparse_attn_fwd_bnhd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
+        "vsa_pool_unpermute_bwd_bnhd": [P, vp, vp, vp, vp],
         "vsa_perm_index": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
@@ -164,6 +168,10 @@ def _token_dtype(dtype: int):
 
 def _tok_shape(p: Problem):
     return (p.batch, p.heads, p.n_tokens, p.head_dim)
+
+
+def _bnhd_shape(p: Problem):
+    return (p.batch, p.n_tokens, p.heads, p.head_dim)
 
 
 def _cube_shape(p: Problem):
@@ -246,11 +254,22 @@ def vsa_sparse_attn_fwd_raster(p: Problem, q: torch.Tensor, k: torch.Tensor, v: 
     _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, True)
 
 
+def vsa_sparse_attn_fwd_bnhd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                             out: torch.Tensor, oc: Optional[torch.Tensor] = None,
+                             gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """As vsa_sparse_attn_fwd_raster with gate_c, gate_f and out as [batch, N, heads, d]."""
+    _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, "bnhd")
+
+
 def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, raster):
     dev = q.device
     ts = _tok_shape(p)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+    os_ = _bnhd_shape(p) if raster == "bnhd" else ts
+    for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, ts, torch.bfloat16, dev)
+    _need(out, "out", os_, torch.bfloat16, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
     max_kv = kv_block_idx.shape[-1]
@@ -260,10 +279,11 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
         _need(oc, "oc", _cube_shape(p), torch.float32, dev)
     for name, t in (("gate_c", gate_c), ("gate_f", gate_f)):
         if t is not None:
-            _need(t, name, ts, torch.bfloat16, dev)
+            _need(t, name, os_, torch.bfloat16, dev)
     if lse is not None:
         _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
-    name = "vsa_sparse_attn_fwd_raster" if raster else "vsa_sparse_attn_fwd"
+    name = {"bnhd": "vsa_sparse_attn_fwd_bnhd", True: "vsa_sparse_attn_fwd_raster",
+            False: "vsa_sparse_attn_fwd"}[raster]
     _check(getattr(load(), name)(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
                                  _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
@@ -390,3 +410,35 @@ def vsa_pool_unpermute_bwd(p: Problem, dx_cube: torch.Tensor, dxc: Optional[torc
         _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
     _check(load().vsa_pool_unpermute_bwd(ctypes.byref(p.c_struct()), _ptr(dx_cube), _ptr(dxc), _ptr(dx_raster),
                                          _stream(stream, dev)), "vsa_pool_unpermute_bwd")
+
+
+def vsa_permute_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch.Tensor, stream=None) -> None:
+    """vsa_permute reading the model layout [batch, N, heads, d]."""
+    td = _token_dtype(dtype)
+    _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
+    _need(x_cube, "x_cube", _tok_shape(p), td, x_bnhd.device)
+    _check(load().vsa_permute_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube),
+                                   _stream(stream, x_bnhd.device)), "vsa_permute_bnhd")
+
+
+def vsa_permute_pool_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch.Tensor, xc: torch.Tensor,
+                          stream=None) -> None:
+    """vsa_permute_pool reading the model layout [batch, N, heads, d]."""
+    td = _token_dtype(dtype)
+    _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
+    _need(x_cube, "x_cube", _tok_shape(p), td, x_bnhd.device)
+    _need(xc, "xc", _cube_shape(p), torch.float32, x_bnhd.device)
+    _check(load().vsa_permute_pool_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube), _ptr(xc),
+                                        _stream(stream, x_bnhd.device)), "vsa_permute_pool_bnhd")
+
+
+def vsa_pool_unpermute_bwd_bnhd(p: Problem, dx_cube: torch.Tensor, dxc: Optional[torch.Tensor],
+                                dx_bnhd: torch.Tensor, stream=None) -> None:
+    """vsa_pool_unpermute_bwd writing the model layout [batch, N, heads, d]."""
+    dev = dx_cube.device
+    _need(dx_cube, "dx_cube", _tok_shape(p), torch.float32, dev)
+    _need(dx_bnhd, "dx_bnhd", _bnhd_shape(p), torch.float32, dev)
+    if dxc is not None:
+        _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
+    _check(load().vsa_pool_unpermute_bwd_bnhd(ctypes.byref(p.c_struct()), _ptr(dx_cube), _ptr(dxc), _ptr(dx_bnhd),
+                                              _stream(stream, dev)), "vsa_pool_unpermute_bwd_bnhd")

@@ -17,6 +17,10 @@
 // d = 128).  All index arithmetic is 32-bit within a (batch, head) and done
 // once per row, so the kernels stay HBM-bound.
 //
+// The raster side is either [batch, heads, N, d] or the model's own
+// [batch, N, heads, d] (a DiT's attention projections produce that order), so
+// no separate transpose pass is needed on either side of the path.
+//
 // The gradient pass (float32 only) runs the reorder back and the adjoint of
 // the pool at once: every token of cube c leaves with its own gradient plus
 // xc[c] / vol, the gradient that reaches it through the cube mean.
@@ -78,6 +82,8 @@ struct CubeArgs {
   int32_t vol;            // tokens per cube
   int32_t N;              // tokens per (batch, head)
   int32_t Nc;             // cubes per (batch, head)
+  int32_t heads;          // heads per batch entry
+  int32_t bnhd;           // raster side is [batch, N, heads, d] (else [batch, heads, N, d])
   int64_t units;          // batch * heads * Nc
 };
 
@@ -118,7 +124,14 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
     const int32_t ch_i = (c / a.gW) % a.gH;
     const int32_t ct_i = c / (a.gW * a.gH);
     const int64_t head_rows = bh * (int64_t)a.N;
-    const int64_t raster0 = head_rows + (ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw;
+    // raster side: row of token n of this (batch, head) is rbase + n * tstride
+    int64_t rbase = head_rows, tstride = 1;
+    if (a.bnhd) {
+      const int64_t b = bh / a.heads;
+      rbase = b * a.N * (int64_t)a.heads + (bh - b * a.heads);
+      tstride = a.heads;
+    }
+    const int64_t raster0 = rbase + (int64_t)((ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw) * tstride;
     const int64_t cube0 = head_rows + (int64_t)c * a.vol;
     float acc[kPooling ? E : 1];
 #pragma unroll
@@ -139,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
       for (int b = 0; b < KB; ++b) {
         const int32_t l = l0 + b * RG;
         if (!guarded.value || l < a.vol) {
-          rrow[b] = raster0 + row_offset(l, a);
+          rrow[b] = raster0 + (int64_t)row_offset(l, a) * tstride;
           buf[b] = load16<kStreamLoads>(src + (kFromRaster ? rrow[b] : cube0 + l) * CPR + col);
         }
       }
@@ -183,8 +196,10 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
   }
 }
 
-CubeArgs cube_args(const Geom& g) {
+CubeArgs cube_args(const Geom& g, RasterLayout layout) {
   CubeArgs a;
+  a.heads = g.heads;
+  a.bnhd = layout == kBNHD ? 1 : 0;
   a.H = g.H; a.W = g.W;
   a.ct = g.ct; a.ch = g.ch; a.cw = g.cw;
   a.gH = g.gH; a.gW = g.gW;
@@ -196,8 +211,9 @@ CubeArgs cube_args(const Geom& g) {
 }
 
 template <typename T, int MODE>
-hipError_t launch_mode(const Geom& g, const void* src, void* dst, float* xc, hipStream_t s) {
-  const CubeArgs a = cube_args(g);
+hipError_t launch_mode(const Geom& g, const void* src, void* dst, float* xc, hipStream_t s,
+                       RasterLayout layout = kBHND) {
+  const CubeArgs a = cube_args(g, layout);
   const dim3 grid((unsigned)(a.units < kMaxGrid ? a.units : kMaxGrid));
   if (g.D == 64)
     hipLaunchKernelGGL((cube_pass_kernel<T, 64, MODE>), grid, dim3(kThreads), 0, s, (const uint4*)src,
@@ -211,17 +227,18 @@ hipError_t launch_mode(const Geom& g, const void* src, void* dst, float* xc, hip
 }
 
 template <int MODE>
-hipError_t launch_dtype(const Geom& g, int dtype, const void* src, void* dst, float* xc, hipStream_t s) {
-  return dtype == VSA_BF16 ? launch_mode<__bf16, MODE>(g, src, dst, xc, s)
-                           : launch_mode<float, MODE>(g, src, dst, xc, s);
+hipError_t launch_dtype(const Geom& g, int dtype, const void* src, void* dst, float* xc, hipStream_t s,
+                        RasterLayout layout = kBHND) {
+  return dtype == VSA_BF16 ? launch_mode<__bf16, MODE>(g, src, dst, xc, s, layout)
+                           : launch_mode<float, MODE>(g, src, dst, xc, s, layout);
 }
 
 }  // namespace
 
 hipError_t launch_reorder(const Geom& g, int dtype, const void* src, void* dst, bool to_cube,
-                          hipStream_t s) {
-  return to_cube ? launch_dtype<kToCube>(g, dtype, src, dst, nullptr, s)
-                 : launch_dtype<kToRaster>(g, dtype, src, dst, nullptr, s);
+                          hipStream_t s, RasterLayout layout) {
+  return to_cube ? launch_dtype<kToCube>(g, dtype, src, dst, nullptr, s, layout)
+                 : launch_dtype<kToRaster>(g, dtype, src, dst, nullptr, s, layout);
 }
 
 hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, hipStream_t s) {
@@ -229,14 +246,14 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, 
 }
 
 hipError_t launch_permute_pool(const Geom& g, int dtype, const void* x_raster, void* x_cube, float* xc,
-                               hipStream_t s) {
-  return launch_dtype<kToCubePool>(g, dtype, x_raster, x_cube, xc, s);
+                               hipStream_t s, RasterLayout layout) {
+  return launch_dtype<kToCubePool>(g, dtype, x_raster, x_cube, xc, s, layout);
 }
 
 hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const float* dxc, float* dx_raster,
-                                     hipStream_t s) {
-  if (dxc == nullptr) return launch_mode<float, kToRaster>(g, dx_cube, dx_raster, nullptr, s);
-  return launch_mode<float, kToRasterAddPooled>(g, dx_cube, dx_raster, const_cast<float*>(dxc), s);
+                                     hipStream_t s, RasterLayout layout) {
+  if (dxc == nullptr) return launch_mode<float, kToRaster>(g, dx_cube, dx_raster, nullptr, s, layout);
+  return launch_mode<float, kToRasterAddPooled>(g, dx_cube, dx_raster, const_cast<float*>(dxc), s, layout);
 }
 
 }  // namespace vsa

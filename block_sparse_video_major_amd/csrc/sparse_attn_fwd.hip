@@ -133,12 +133,17 @@ __device__ __forceinline__ void wait_parts(int parts) {
 
 // RK / RV: positions of the K and V tile rings.
 // Token order of out, gate_c, gate_f and lse: cube-major (on == 0) or raster
-// (t, h, w) order (on == 1; the reorder back fused into the epilogue).
+// (t, h, w) order (on == 1; the reorder back fused into the epilogue).  With
+// bnhd == 1 (raster only) out and the gates are the model's [batch, N, heads,
+// d] rows instead of [batch, heads, N, d]; lse stays [batch, heads, N].
 struct TokenMap {
   int32_t on;
+  int32_t bnhd;
   int32_t H, W;         // token grid (rows and columns of a frame)
   int32_t ct, ch, cw;   // cube edges
   int32_t gH, gW;       // cube grid
+  int32_t heads;        // heads per batch entry
+  int32_t N;            // tokens per (batch, head)
 };
 
 // Position of token l (< 64) of cube c within its (batch, head) in the
@@ -150,6 +155,14 @@ __device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, int32
   const int32_t lt = l / plane, rem = l - lt * plane;
   const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
   return ((ct_i * m.ct + lt) * m.H + ch_i * m.ch + lh) * m.W + cw_i * m.cw + lw;
+}
+
+// Element offset of token l of cube c of (batch, head) bh in out and the gates.
+__device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int32_t c, int32_t l, int D) {
+  const int64_t n = token_pos(m, c, l);
+  if (!m.bnhd) return (bh * m.N + n) * D;
+  const int64_t b = bh / m.heads, h = bh - b * m.heads;
+  return ((b * m.N + n) * m.heads + h) * D;
 }
 
 template <int D, int RK, int RV>
@@ -684,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;
         const int row = c / C::CPR, col = c % C::CPR;
-        const int64_t gidx = head_off + (int64_t)token_pos(tmap, my_cube, row) * D + col * 8;
+        const int64_t gidx = token_elem(tmap, bh, my_cube, row, D) + col * 8;
         float val[8];
         const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
         const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
@@ -811,9 +824,12 @@ bool sparse_attn_fwd_fits(const Geom& g, int max_kv) {
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, bool raster_out, hipStream_t s) {
+                                  void* out, float* lse, int out_order, hipStream_t s) {
   TokenMap m;
-  m.on = raster_out ? 1 : 0;
+  m.on = out_order != 0 ? 1 : 0;
+  m.bnhd = out_order == 2 ? 1 : 0;
+  m.heads = g.heads;
+  m.N = (int32_t)g.N;
   m.H = g.H; m.W = g.W;
   m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
   m.gH = g.gH; m.gW = g.gW;

@@ -39,7 +39,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (1 << 16) | 2; }
+int vsa_abi_version(void) { return (1 << 16) | 3; }
 
 const char* vsa_status_str(int status) {
   switch (status) {
@@ -129,7 +129,7 @@ namespace {
 int sparse_attn_fwd_common(const vsa_problem* p, const void* q, const void* k, const void* v,
                            const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
                            const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
-                           bool raster_out, void* stream) {
+                           int out_order, void* stream) {
   int st = check_problem(p);
   if (st != VSA_OK) return st;
   if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
@@ -141,7 +141,7 @@ int sparse_attn_fwd_common(const vsa_problem* p, const void* q, const void* k, c
   if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
   if (!vsa::sparse_attn_fwd_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
   return hip_status(vsa::launch_sparse_attn_fwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc,
-                                                gate_c, gate_f, out, lse, raster_out, (hipStream_t)stream));
+                                                gate_c, gate_f, out, lse, out_order, (hipStream_t)stream));
 }
 }  // namespace
 
@@ -150,7 +150,7 @@ int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k, cons
                         const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
                         void* stream) {
   return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
-                                out, lse, false, stream);
+                                out, lse, 0, stream);
 }
 
 int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q, const void* k, const void* v,
@@ -158,7 +158,34 @@ int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q, const void* 
                                int32_t max_kv_blocks, const float* oc, const void* gate_c, const void* gate_f,
                                void* out, float* lse, void* stream) {
   return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
-                                out, lse, true, stream);
+                                out, lse, 1, stream);
+}
+
+int vsa_sparse_attn_fwd_bnhd(const vsa_problem* p, const void* q, const void* k, const void* v,
+                             const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
+                             const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
+                             void* stream) {
+  return sparse_attn_fwd_common(p, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc, gate_c, gate_f,
+                                out, lse, 2, stream);
+}
+
+int vsa_permute_bnhd(const vsa_problem* p, int32_t dtype, const void* x_bnhd, void* x_cube, void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_bnhd == nullptr || x_cube == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_reorder(g, dtype, x_bnhd, x_cube, true, (hipStream_t)stream, vsa::kBNHD));
+}
+
+int vsa_permute_pool_bnhd(const vsa_problem* p, int32_t dtype, const void* x_bnhd, void* x_cube, float* xc,
+                          void* stream) {
+  int st = check_problem(p);
+  if (st == VSA_OK) st = check_dtype(dtype);
+  if (st != VSA_OK) return st;
+  if (x_bnhd == nullptr || x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_permute_pool(g, dtype, x_bnhd, x_cube, xc, (hipStream_t)stream, vsa::kBNHD));
 }
 
 namespace {
@@ -240,6 +267,15 @@ int vsa_pool_unpermute_bwd(const vsa_problem* p, const float* dx_cube, const flo
   if (dx_cube == nullptr || dx_raster == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
   return hip_status(vsa::launch_pool_unpermute_bwd(g, dx_cube, dxc, dx_raster, (hipStream_t)stream));
+}
+
+int vsa_pool_unpermute_bwd_bnhd(const vsa_problem* p, const float* dx_cube, const float* dxc, float* dx_bnhd,
+                                void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (dx_cube == nullptr || dx_bnhd == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_pool_unpermute_bwd(g, dx_cube, dxc, dx_bnhd, (hipStream_t)stream, vsa::kBNHD));
 }
 
 int vsa_check_lut(const vsa_problem* p, const int32_t* kv_block_idx, const int32_t* valid_block_num,

@@ -18,6 +18,7 @@ struct Geom {
   int64_t N;              // tokens per (batch, head)
   int64_t Nc;             // cubes per (batch, head)
   int64_t BH;             // batch * heads
+  int32_t heads;          // heads per batch entry
   int32_t D;              // head_dim
 };
 
@@ -30,16 +31,20 @@ inline Geom make_geom(const vsa_problem& p) {
   g.N = (int64_t)p.T * p.H * p.W;
   g.Nc = g.N / g.vol;
   g.BH = (int64_t)p.batch * p.heads;
+  g.heads = p.heads;
   g.D = p.head_dim;
   return g;
 }
 
 // Launchers (each returns the hipGetLastError() of its launch).
+// Raster-side row order of the reorder kernels: [batch, heads, N, d] or the
+// model's [batch, N, heads, d].
+enum RasterLayout { kBHND = 0, kBNHD = 1 };
 hipError_t launch_reorder(const Geom& g, int dtype, const void* src, void* dst, bool to_cube,
-                          hipStream_t s);
+                          hipStream_t s, RasterLayout layout = kBHND);
 hipError_t launch_pool(const Geom& g, int dtype, const void* x_cube, float* xc, hipStream_t s);
 hipError_t launch_permute_pool(const Geom& g, int dtype, const void* x_raster, void* x_cube, float* xc,
-                               hipStream_t s);
+                               hipStream_t s, RasterLayout layout = kBHND);
 hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
                               const float* vc, int32_t* lut, int32_t* valid, float* oc,
                               hipStream_t s);
@@ -48,7 +53,7 @@ bool sparse_attn_fwd_fits(const Geom& g, int max_kv);
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, bool raster_out, hipStream_t s);
+                                  void* out, float* lse, int out_order, hipStream_t s);   // 0 cube, 1 raster, 2 raster bnhd
 hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* valid, int max_kv,
                             int32_t* bad_rows, hipStream_t s);
 hipError_t launch_mask_to_lut(const Geom& g, const uint8_t* mask, int max_kv, int32_t* lut, int32_t* valid,
@@ -74,7 +79,7 @@ size_t coarse_bwd_workspace(const Geom& g);
 hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
                              const float* doc, float* dqc, float* dkc, float* dvc, void* workspace, hipStream_t s);
 hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const float* dxc, float* dx_raster,
-                                     hipStream_t s);
+                                     hipStream_t s, RasterLayout layout = kBHND);
 
 // Largest number of cubes per (batch, head) the coarse stage handles.
 constexpr int64_t kMaxCoarseCubes = 4096;

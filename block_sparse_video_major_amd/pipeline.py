@@ -26,13 +26,16 @@ class VsaForward:
     """Preallocated buffers for one problem size; call() runs one forward pass."""
 
     def __init__(self, p: Problem, top_k: int, device="cuda", with_gates: bool = False,
-                 with_lse: bool = False):
+                 with_lse: bool = False, layout: str = "bhnd"):
         # with_gates is accepted for callers that pass gates; the raster-order
         # gates are read directly, so no buffer is needed for them.  lse (if
-        # kept) is in raster token order.
+        # kept) is in raster token order.  layout "bnhd" takes q, k, v, the
+        # gates and out in the model's [batch, N, heads, d] order.
         if not 1 <= top_k <= p.n_cubes:
             raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
-        self.p, self.top_k = p, top_k
+        if layout not in ("bhnd", "bnhd"):
+            raise ValueError(f"layout {layout!r} is not 'bhnd' or 'bnhd'")
+        self.p, self.top_k, self.layout = p, top_k, layout
         ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
@@ -46,14 +49,17 @@ class VsaForward:
                  gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
         p, B = self.p, L.VSA_BF16
-        L.vsa_permute_pool(p, B, q, self.qp, self.qc, stream)
-        L.vsa_permute_pool(p, B, k, self.kp, self.kc, stream)
-        L.vsa_permute_pool(p, B, v, self.vp, self.vc, stream)
+        bnhd = self.layout == "bnhd"
+        permute_pool = L.vsa_permute_pool_bnhd if bnhd else L.vsa_permute_pool
+        permute_pool(p, B, q, self.qp, self.qc, stream)
+        permute_pool(p, B, k, self.kp, self.kc, stream)
+        permute_pool(p, B, v, self.vp, self.vc, stream)
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
         # fine attention reading the raster-order gates and writing the
         # raster-order output directly (the reorder back is in its epilogue)
-        L.vsa_sparse_attn_fwd_raster(p, self.qp, self.kp, self.vp, self.lut, self.valid, out,
-                                     oc=self.oc, gate_c=gate_c, gate_f=gate_f, lse=self.lse, stream=stream)
+        fine = L.vsa_sparse_attn_fwd_bnhd if bnhd else L.vsa_sparse_attn_fwd_raster
+        fine(p, self.qp, self.kp, self.vp, self.lut, self.valid, out,
+             oc=self.oc, gate_c=gate_c, gate_f=gate_f, lse=self.lse, stream=stream)
         return out
 
     def intermediates(self) -> Dict[str, torch.Tensor]:

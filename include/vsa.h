@@ -170,6 +170,40 @@ int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q,
                                const void* gate_c, const void* gate_f,
                                void* out, float* lse, void* stream);
 
+/* The model's own token layout ([VSA-ROCm] §Two-Stage Architecture: the
+ * pre-stage reordering reads the sequence as the DiT produces it, and the
+ * output is handed back in the model's order).  These take the raster-side
+ * token tensors as [batch, N, heads, head_dim] (token-major, heads
+ * interleaved, what a DiT's projections produce) instead of [batch, heads,
+ * N, head_dim]; everything else is as for the entry point named in each.
+ * Cube-major tensors keep the [batch, heads, N, head_dim] layout. */
+
+/* vsa_permute with x_bnhd [batch, N, heads, head_dim]. */
+int vsa_permute_bnhd(const vsa_problem* p, int32_t dtype, const void* x_bnhd,
+                     void* x_cube, void* stream);
+
+/* vsa_permute_pool with x_bnhd [batch, N, heads, head_dim]. */
+int vsa_permute_pool_bnhd(const vsa_problem* p, int32_t dtype,
+                          const void* x_bnhd, void* x_cube, float* xc,
+                          void* stream);
+
+/* vsa_sparse_attn_fwd_raster with gate_c, gate_f and out as [batch, N,
+ * heads, head_dim] bf16 (raster token order); lse stays [batch, heads, N]
+ * float32 in raster order.  out holds exactly the bits of the raster entry
+ * point's out, transposed. */
+int vsa_sparse_attn_fwd_bnhd(const vsa_problem* p, const void* q,
+                             const void* k, const void* v,
+                             const int32_t* kv_block_idx,
+                             const int32_t* valid_block_num,
+                             int32_t max_kv_blocks, const float* oc,
+                             const void* gate_c, const void* gate_f,
+                             void* out, float* lse, void* stream);
+
+/* vsa_pool_unpermute_bwd with dx_bnhd [batch, N, heads, head_dim] float32. */
+int vsa_pool_unpermute_bwd_bnhd(const vsa_problem* p, const float* dx_cube,
+                                const float* dxc, float* dx_bnhd,
+                                void* stream);
+
 /* Device-side LUT validator (optional, asynchronous).  Writes to
  * *bad_rows (one device int32) the number of LUT rows whose count is
  * outside [0, max_kv_blocks] or which list a cube outside [0, Nc).

@@ -148,6 +148,22 @@ def test_sparse_attn_bwd_workspace_and_errors():
     assert call(prob=None) == L.VSA_ERR_NULL
 
 
+def test_model_layout_entry_points_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob())
+    assert lib.vsa_permute_bnhd(pr, L.VSA_BF16, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_bnhd(pr, 7, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_permute_pool_bnhd(pr, L.VSA_BF16, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool_bnhd(ctypes.byref(_prob(H=10)), L.VSA_BF16, DUMMY, DUMMY, DUMMY, None) == \
+        L.VSA_ERR_SHAPE
+    assert lib.vsa_pool_unpermute_bwd_bnhd(pr, None, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_pool_unpermute_bwd_bnhd(pr, DUMMY, None, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd_bnhd(pr, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 0, None, None, None, DUMMY, None,
+                                        None) == L.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd_bnhd(pr, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, None, DUMMY, None, DUMMY, None,
+                                        None) == L.VSA_ERR_NULL
+
+
 def test_coarse_topk_errors():
     lib = _raw()
     pr = ctypes.byref(_prob())          # Nc = 8*16*16/64 = 32
