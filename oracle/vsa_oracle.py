@@ -36,6 +36,10 @@ DESIGN.md):
   counted as overflows.
 * R17 the backward differentiates the layer with its LUT held fixed (Top-K
   selection has no gradient); P is recomputed from the forward's LSE.
+* R19 grouped heads (K and V with fewer heads than Q, the head counts of the
+  CK kernel interface in [VSA-ROCm]): query head h uses key/value head
+  h // G with G = heads / kv_heads; equivalently every key/value head is
+  repeated G times, and its gradient is the sum over its G copies.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, invariants, brute force, library special cases); none is
@@ -317,6 +321,31 @@ def combine(of: np.ndarray, oc: np.ndarray, vol: int,
 
 
 # ---------------------------------------------------------------------------
+# Grouped heads (R19).
+# ---------------------------------------------------------------------------
+
+def kv_group(q: np.ndarray, k: np.ndarray) -> int:
+    """G = heads of q per head of k (axis 1); k's head count must divide q's."""
+    hq, hk = q.shape[1], k.shape[1]
+    if hk < 1 or hq % hk:
+        raise ValueError(f"{hk} key/value heads do not divide {hq} query heads")
+    return hq // hk
+
+
+def expand_kv_heads(x: np.ndarray, group: int) -> np.ndarray:
+    """Repeat every head (axis 1) `group` times: head h of the result is head
+    h // group of x."""
+    return np.repeat(np.asarray(x), group, axis=1)
+
+
+def reduce_kv_heads(dx: np.ndarray, group: int) -> np.ndarray:
+    """Adjoint of expand_kv_heads: sum each run of `group` heads."""
+    dx = np.asarray(dx, np.float64)
+    B, h = dx.shape[:2]
+    return dx.reshape((B, h // group, group) + dx.shape[2:]).sum(axis=2)
+
+
+# ---------------------------------------------------------------------------
 # The whole forward pass, steps in the pages' order.
 # ---------------------------------------------------------------------------
 
@@ -328,13 +357,16 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 valid_block_num: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """VSA forward on raster inputs [B, heads, N, d]; returns every
     intermediate.  If a LUT is given it replaces the Top-K selection (used to
-    score a kernel on exactly the LUT it was handed)."""
+    score a kernel on exactly the LUT it was handed).  k and v may have fewer
+    heads than q (R19); their intermediates are then returned expanded to
+    the query heads."""
     T, H, W = grid
     ct, ch, cw = cube
     vol = ct * ch * cw
     q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    group = kv_group(q, np.asarray(k))
+    k = expand_kv_heads(np.asarray(k, np.float64), group)
+    v = expand_kv_heads(np.asarray(v, np.float64), group)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d)
     pi = perm_index(T, H, W, ct, ch, cw)
@@ -419,9 +451,11 @@ def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
     gradient dout (raster), the LUT held fixed (R17): the forward's steps
     taken backwards -- reorder dout, combine, fine attention (through the
     LSE), coarse attention, pooling, reorder back.  Q, K and V each collect
-    their fine-stage gradient plus the pooled coarse-stage gradient.
+    their fine-stage gradient plus the pooled coarse-stage gradient; with
+    grouped heads (R19) dK and dV sum over each key/value head's query heads.
     Returns dict(dq, dk, dv, dgate_c, dgate_f) in raster order (absent gates
     give None)."""
+    group = kv_group(np.asarray(q), np.asarray(k))
     f = vsa_forward(q, k, v, grid, cube, 0, gate_c=gate_c, gate_f=gate_f,
                     kv_block_idx=kv_block_idx, valid_block_num=valid_block_num)
     pi = f["pi"]
@@ -435,7 +469,7 @@ def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
                                        scale, vol, f["o_fine"], f["lse"], dof)
     dqc, dkc, dvc = coarse_attention_bwd(f["qc"], f["kc"], f["vc"], scale, doc)
     return dict(dq=unpermute(dqf + pool_bwd(dqc, vol), pi),
-                dk=unpermute(dkf + pool_bwd(dkc, vol), pi),
-                dv=unpermute(dvf + pool_bwd(dvc, vol), pi),
+                dk=reduce_kv_heads(unpermute(dkf + pool_bwd(dkc, vol), pi), group),
+                dv=reduce_kv_heads(unpermute(dvf + pool_bwd(dvc, vol), pi), group),
                 dgate_c=None if dgcp is None else unpermute(dgcp, pi),
                 dgate_f=None if dgfp is None else unpermute(dgfp, pi))

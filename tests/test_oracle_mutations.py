@@ -13,6 +13,7 @@ import test_oracle_coarse as tc
 import test_oracle_fine as tf
 import test_oracle_bwd as tb
 import test_oracle_full_bwd as tfb
+import test_oracle_gqa as tg
 import test_oracle_mask as tm
 import test_oracle_reorder as tr
 from block_sparse_video_major_amd import workloads as wl
@@ -114,6 +115,11 @@ def _combine_bwd_dgc_from_of(dout, of, oc, vol, gate_c=None, gate_f=None):
     return dof, doc, (None if dgc is None else np.asarray(dout) * np.asarray(of)), dgf
 
 
+def _expand_interleaved(x, group):
+    # head h takes key/value head h % kv_heads instead of h // group
+    return np.tile(np.asarray(x), (1, group) + (1,) * (np.asarray(x).ndim - 2))
+
+
 def _pins():
     """The pin checks, called directly (each raises AssertionError on failure)."""
     yield lambda: tr.test_each_block_is_one_cube_in_raster_cube_order((4, 8, 8), (4, 4, 4))
@@ -137,6 +143,7 @@ def _pins():
     yield lambda: tfb.test_pool_bwd_is_the_adjoint_of_pool()
     yield lambda: tfb.test_combine_bwd_matches_autograd()
     yield lambda: tfb.test_whole_layer_backward_matches_autograd()
+    yield lambda: tg.test_dense_layer_equals_gqa_sdpa(4, 2)
 
 
 MUTATIONS = {
@@ -158,6 +165,7 @@ MUTATIONS = {
     "coarse backward dKc without the scale": ("coarse_attention_bwd", _coarse_bwd_dk_no_scale),
     "pool backward without 1/vol": ("pool_bwd", _pool_bwd_no_divisor),
     "combine backward dg_c taken from O_f": ("combine_bwd", _combine_bwd_dgc_from_of),
+    "grouped heads interleaved instead of repeated": ("expand_kv_heads", _expand_interleaved),
 }
 
 
