@@ -39,7 +39,7 @@ class VsaError(RuntimeError):
 
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim")]
+                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim", "heads_kv")]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -54,6 +54,7 @@ class Problem:
     ch: int = 4
     cw: int = 4
     head_dim: int = 128
+    heads_kv: int = 0          # key/value heads (grouped heads); 0 means heads
 
     @property
     def n_tokens(self) -> int:
@@ -67,9 +68,18 @@ class Problem:
     def n_cubes(self) -> int:
         return self.n_tokens // self.cube_volume
 
+    @property
+    def kv_heads(self) -> int:
+        return self.heads_kv if self.heads_kv else self.heads
+
+    def kv_problem(self) -> "Problem":
+        """The problem of a key/value tensor alone (for the single-tensor
+        reorders and pools)."""
+        return dataclasses.replace(self, heads=self.kv_heads, heads_kv=0)
+
     def c_struct(self) -> _Problem:
         return _Problem(self.batch, self.heads, self.T, self.H, self.W,
-                        self.ct, self.ch, self.cw, self.head_dim)
+                        self.ct, self.ch, self.cw, self.head_dim, self.heads_kv)
 
 
 _lib = None
@@ -178,6 +188,14 @@ def _cube_shape(p: Problem):
     return (p.batch, p.heads, p.n_cubes, p.head_dim)
 
 
+def _kv_tok_shape(p: Problem):
+    return (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
+
+
+def _kv_cube_shape(p: Problem):
+    return (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
+
+
 # ---------------------------------------------------------------- entry points
 
 def vsa_perm_index(p: Problem) -> torch.Tensor:
@@ -225,9 +243,9 @@ def vsa_coarse_topk(p: Problem, top_k: int, qc: torch.Tensor, kc: torch.Tensor, 
                     stream=None) -> None:
     dev = qc.device
     _need(qc, "qc", _cube_shape(p), torch.float32)
-    _need(kc, "kc", _cube_shape(p), torch.float32, dev)
+    _need(kc, "kc", _kv_cube_shape(p), torch.float32, dev)
     if vc is not None:
-        _need(vc, "vc", _cube_shape(p), torch.float32, dev)
+        _need(vc, "vc", _kv_cube_shape(p), torch.float32, dev)
     if oc is not None:
         _need(oc, "oc", _cube_shape(p), torch.float32, dev)
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, top_k), torch.int32, dev)
@@ -267,8 +285,9 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
     dev = q.device
     ts = _tok_shape(p)
     os_ = _bnhd_shape(p) if raster == "bnhd" else ts
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, ts, torch.bfloat16, dev)
+    _need(q, "q", ts, torch.bfloat16, dev)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, _kv_tok_shape(p), torch.bfloat16, dev)
     _need(out, "out", os_, torch.bfloat16, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
@@ -334,11 +353,14 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
                         workspace: torch.Tensor, stream=None) -> None:
     """Gradients of the fine attention (all tensors cube-major; dq, dk, dv float32)."""
     dev = q.device
-    ts = _tok_shape(p)
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+    ts, ks = _tok_shape(p), _kv_tok_shape(p)
+    for name, t in (("q", q), ("o", o), ("d_o", d_o)):
         _need(t, name, ts, torch.bfloat16, dev)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(t, name, ts, torch.float32, dev)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, ks, torch.bfloat16, dev)
+    _need(dq, "dq", ts, torch.float32, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _need(t, name, ks, torch.float32, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
     max_kv = kv_block_idx.shape[-1]
@@ -388,10 +410,11 @@ def vsa_coarse_bwd(p: Problem, qc: torch.Tensor, kc: torch.Tensor, vc: torch.Ten
                    workspace: torch.Tensor, stream=None) -> None:
     """Gradients of the coarse attention (float32 cube tensors)."""
     dev = qc.device
-    cs = _cube_shape(p)
-    for name, t in (("qc", qc), ("kc", kc), ("vc", vc), ("oc", oc), ("d_oc", d_oc), ("dqc", dqc),
-                    ("dkc", dkc), ("dvc", dvc)):
+    cs, kcs = _cube_shape(p), _kv_cube_shape(p)
+    for name, t in (("qc", qc), ("oc", oc), ("d_oc", d_oc), ("dqc", dqc)):
         _need(t, name, cs, torch.float32, dev)
+    for name, t in (("kc", kc), ("vc", vc), ("dkc", dkc), ("dvc", dvc)):
+        _need(t, name, kcs, torch.float32, dev)
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D byte tensor")
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)

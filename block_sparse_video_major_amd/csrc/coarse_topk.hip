@@ -92,7 +92,7 @@ template <int D, int R, int NS, int kThreads>
 __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
     int32_t* __restrict__ lut, int32_t* __restrict__ valid, float* __restrict__ oc, int Nc, int top_k,
-    int tiles_per_head, float scale) {
+    int tiles_per_head, float scale, int group) {
   constexpr int kWaves = kThreads / 64;
   static_assert(R % kWaves == 0, "rows per workgroup");
   extern __shared__ float smem[];
@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   const int64_t bh = blockIdx.x / tiles_per_head;
   const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * R;
   const int rows = min(R, Nc - i0);
-  const float* kh = kc + bh * (int64_t)Nc * D;
+  const int64_t kvh = bh / group;   // key/value head of this query head
+  const float* kh = kc + kvh * (int64_t)Nc * D;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     }
   }
   // The first value chunk is in flight during the selection.
-  const float* vh = vc + bh * (int64_t)Nc * D;
+  const float* vh = vc + kvh * (int64_t)Nc * D;
   if (oc != nullptr) st.load(vh, 0, Nc, tid);
   __syncthreads();
 
@@ -300,7 +301,7 @@ static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const fl
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(T), lds, s, qc, kc, vc, lut, valid, oc, Nc, top_k,
-                     tiles, scale);
+                     tiles, scale, g.group);
   return hipGetLastError();
 }
 

@@ -243,25 +243,28 @@ size_t coarse_bwd_workspace(const Geom& g) {
 }
 
 // S = scale Qc Kc^T and dP = dO_c Vc^T, then P and dS in place, then
-// dQc = scale dS Kc, dKc = scale dS^T Qc, dVc = P^T dO_c.
+// dQc = scale dS Kc, dKc = scale dS^T Qc, dVc = P^T dO_c.  Each product is
+// batched over key/value heads: the `group` query heads sharing one are
+// contiguous, so their Qc, dO_c, S and dS rows stack into one M = group * Nc
+// operand and dKc, dVc sum over the group inside the product.
 hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
                              const float* doc, float* dqc, float* dkc, float* dvc, void* workspace,
                              hipStream_t s) {
-  const int Nc = (int)g.Nc, D = g.D, H = (int)g.BH;
-  const int64_t sm = (int64_t)Nc * Nc, sx = (int64_t)Nc * D;
+  const int Nc = (int)g.Nc, D = g.D, Hk = (int)g.BHkv, Mq = g.group * Nc;
+  const int64_t sq = (int64_t)Mq * D, sk = (int64_t)Nc * D, sm = (int64_t)Mq * Nc;
   float* smat = static_cast<float*>(workspace);
-  float* dpmat = smat + (size_t)g.BH * sm;
+  float* dpmat = smat + (size_t)g.BH * g.Nc * g.Nc;
   const float scale = 1.0f / sqrtf((float)D);
   hipError_t e;
-  if ((e = gemm<false, true>(H, qc, kc, smat, Nc, Nc, D, D, D, Nc, sx, sx, sm, scale, s)) != hipSuccess) return e;
-  if ((e = gemm<false, true>(H, doc, vc, dpmat, Nc, Nc, D, D, D, Nc, sx, sx, sm, 1.0f, s)) != hipSuccess) return e;
+  if ((e = gemm<false, true>(Hk, qc, kc, smat, Mq, Nc, D, D, D, Nc, sq, sk, sm, scale, s)) != hipSuccess) return e;
+  if ((e = gemm<false, true>(Hk, doc, vc, dpmat, Mq, Nc, D, D, D, Nc, sq, sk, sm, 1.0f, s)) != hipSuccess) return e;
   const int64_t rows = g.BH * g.Nc;
   hipLaunchKernelGGL(coarse_softmax_ds_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, smat, dpmat,
                      oc, doc, Nc, D, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = gemm<false, false>(H, dpmat, kc, dqc, Nc, D, Nc, Nc, D, D, sm, sx, sx, scale, s)) != hipSuccess) return e;
-  if ((e = gemm<true, false>(H, dpmat, qc, dkc, Nc, D, Nc, Nc, D, D, sm, sx, sx, scale, s)) != hipSuccess) return e;
-  return gemm<true, false>(H, smat, doc, dvc, Nc, D, Nc, Nc, D, D, sm, sx, sx, 1.0f, s);
+  if ((e = gemm<false, false>(Hk, dpmat, kc, dqc, Mq, D, Nc, Nc, D, D, sm, sk, sq, scale, s)) != hipSuccess) return e;
+  if ((e = gemm<true, false>(Hk, dpmat, qc, dkc, Nc, D, Mq, Nc, D, D, sm, sq, sk, scale, s)) != hipSuccess) return e;
+  return gemm<true, false>(Hk, smat, doc, dvc, Nc, D, Mq, Nc, D, D, sm, sq, sk, 1.0f, s);
 }
 
 }  // namespace vsa

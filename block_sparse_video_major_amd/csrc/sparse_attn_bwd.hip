@@ -18,7 +18,10 @@
 //   * prep: one pass over O and dO writes, per token, the 8-byte record
 //     (LSE * log2 e, Drow), which both gradient kernels read.
 //   * transposed index list: for every key cube, the query cubes whose rows
-//     list it, ascending (a cube listed twice by one row appears twice).  Built
+//     list it, ascending (a cube listed twice by one row appears twice).  With
+//     grouped key/value heads the list of a key cube runs over the query cubes
+//     of all the query heads that share its key/value head (their LUT rows
+//     are contiguous), so dK and dV sum over the group as well.  Built
 //     without ordering races in three passes: per block of 16 rows the count
 //     of each key cube, one scan per (batch, head) that turns counts into
 //     list offsets, and a scatter in which one wavefront walks its block's
@@ -269,18 +272,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
 }
 
 // ---- transposed index list ----------------------------------------------------
-// blkcnt[bh][rb][j] = how often rows 16*rb .. 16*rb + 15 of (b, h) list key cube j.
+// Rows: the Nr = group * Nc LUT rows of the query heads that share one
+// key/value head (grp), contiguous in the LUT.  blkcnt[grp][rb][j] = how often
+// rows 16*rb .. 16*rb + 15 of the group list key cube j.
 __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ lut,
-                                                        const int32_t* __restrict__ valid, int max_kv, int Nc,
-                                                        int nrb, int32_t* __restrict__ blkcnt) {
+                                                        const int32_t* __restrict__ valid, int max_kv, int Nr,
+                                                        int Nc, int nrb, int32_t* __restrict__ blkcnt) {
   extern __shared__ int cnt[];
-  const int64_t bh = blockIdx.x / nrb;
+  const int64_t bh = blockIdx.x / nrb;   // the group
   const int rb = (int)(blockIdx.x - bh * nrb);
   for (int j = threadIdx.x; j < Nc; j += 256) cnt[j] = 0;
   __syncthreads();
-  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nc ? r0 + kRowsPerBlk : Nc;
+  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nr ? r0 + kRowsPerBlk : Nr;
   for (int i = r0; i < r1; ++i) {
-    const int64_t row = bh * Nc + i;
+    const int64_t row = bh * Nr + i;
     const int n = clamp_count(valid[row], max_kv);
     for (int e = threadIdx.x; e < n; e += 256) atomicAdd(&cnt[clamp_cube(lut[row * max_kv + e], Nc)], 1);
   }
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restric
   for (int j = threadIdx.x; j < Nc; j += 256) out[j] = cnt[j];
 }
 
-// Per (b, h): blkcnt becomes the exclusive prefix over row blocks, and
+// Per group: blkcnt becomes the exclusive prefix over row blocks, and
 // coloff[j] the start of key cube j's list (coloff[Nc] = total entries).
 __global__ __launch_bounds__(256) void csr_scan_kernel(int32_t* __restrict__ blkcnt, int Nc, int nrb,
                                                        int32_t* __restrict__ coloff) {
@@ -336,8 +341,8 @@ __global__ __launch_bounds__(256) void csr_scan_kernel(int32_t* __restrict__ blk
 // One wavefront per row block writes the query cube of every listing into its
 // key cube's list, rows in ascending order.
 __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ lut,
-                                                         const int32_t* __restrict__ valid, int max_kv, int Nc,
-                                                         int nrb, const int32_t* __restrict__ blkcnt,
+                                                         const int32_t* __restrict__ valid, int max_kv, int Nr,
+                                                         int Nc, int nrb, const int32_t* __restrict__ blkcnt,
                                                          const int32_t* __restrict__ coloff,
                                                          int32_t* __restrict__ csr) {
   extern __shared__ int cur[];
@@ -348,10 +353,10 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
   const int32_t* co = coloff + bh * (int64_t)(Nc + 1);
   for (int j = lane; j < Nc; j += 64) cur[j] = co[j] + bc[j];
   __syncthreads();
-  int32_t* out = csr + bh * (int64_t)Nc * max_kv;
-  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nc ? r0 + kRowsPerBlk : Nc;
+  int32_t* out = csr + bh * (int64_t)Nr * max_kv;
+  const int r0 = rb * kRowsPerBlk, r1 = r0 + kRowsPerBlk < Nr ? r0 + kRowsPerBlk : Nr;
   for (int i = r0; i < r1; ++i) {
-    const int64_t row = bh * Nc + i;
+    const int64_t row = bh * Nr + i;
     const int n = clamp_count(valid[row], max_kv);
     for (int e0 = 0; e0 < n; e0 += 64) {
       const int e = e0 + lane;
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const int32_t* __restrict__ lut, const int32_t* __restrict__ valid,
     int max_kv, const float2* __restrict__ ld, float* __restrict__ dq, int Nc, int64_t total_cubes,
-    float c_log2, float scale) {
+    float c_log2, float scale, int group) {
   using C = BCfg<D>;
   constexpr int SLOT = 2 * C::TILE;   // K tile, then V tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -382,8 +387,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
   const int64_t bh = cube / Nc;
   const int ci = (int)(cube - bh * Nc);
   const int64_t head_off = bh * (int64_t)Nc * kBlk * D;
-  const char* k_head = reinterpret_cast<const char*>(k + head_off);
-  const char* v_head = reinterpret_cast<const char*>(v + head_off);
+  const int64_t kv_off = (bh / group) * (int64_t)Nc * kBlk * D;   // its key/value head
+  const char* k_head = reinterpret_cast<const char*>(k + kv_off);
+  const char* v_head = reinterpret_cast<const char*>(v + kv_off);
   const int n = clamp_count(valid[cube], max_kv);
   ListWindow lw(lut + cube * (int64_t)max_kv, n, Nc, lane);
 
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const int32_t* __restrict__ coloff, const int32_t* __restrict__ csr,
     int max_kv, const float2* __restrict__ ld, float* __restrict__ dk, float* __restrict__ dv, int Nc,
-    int64_t total_cubes, float c_log2, float scale) {
+    int64_t total_cubes, float c_log2, float scale, int group) {
   using C = BCfg<D>;
   constexpr int SLOT = 2 * C::TILE + 1024;   // Q tile, dO tile, (LSE log2 e, Drow) of 64 queries
   constexpr int NST = 4;                     // ring stages
@@ -484,17 +490,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_bwd_dkdv_kernel(
   const int qh = wave & 1, kh = wave >> 1;
   const int g = lane >> 5;
 
+  // cube = key cube cj of key/value head bh; its list indexes the Nr query
+  // cubes of the `group` query heads that share that head (contiguous)
   const int64_t cube = xcd_remap(blockIdx.x, total_cubes);
   const int64_t bh = cube / Nc;
   const int cj = (int)(cube - bh * Nc);
-  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;
-  const char* q_head = reinterpret_cast<const char*>(q + head_off);
-  const char* d_head = reinterpret_cast<const char*>(dout + head_off);
-  const char* ld_head = reinterpret_cast<const char*>(ld + bh * (int64_t)Nc * kBlk);
+  const int Nr = group * Nc;
+  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;        // K, V, dK, dV
+  const int64_t qgrp_off = bh * (int64_t)Nr * kBlk * D;        // Q, dO of the group
+  const char* q_head = reinterpret_cast<const char*>(q + qgrp_off);
+  const char* d_head = reinterpret_cast<const char*>(dout + qgrp_off);
+  const char* ld_head = reinterpret_cast<const char*>(ld + bh * (int64_t)Nr * kBlk);
   const int32_t* co = coloff + bh * (int64_t)(Nc + 1);
   const int b0 = co[cj];
   const int n = co[cj + 1] - b0;
-  ListWindow lw(csr + bh * (int64_t)Nc * max_kv + b0, n, Nc, lane);
+  ListWindow lw(csr + bh * (int64_t)Nr * max_kv + b0, n, Nr, lane);
 
   const LaneOffsets<D> off(wave, lane, qh);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -719,14 +729,16 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Lists are per key/value head: Nr = group * Nc query rows each.
 WsLayout ws_layout(const Geom& g, int max_kv) {
-  const size_t nrb = (size_t)(g.Nc + kRowsPerBlk - 1) / kRowsPerBlk;
+  const size_t Nr = (size_t)g.group * g.Nc;
+  const size_t nrb = (Nr + kRowsPerBlk - 1) / kRowsPerBlk;
   WsLayout w;
   w.ld = 0;
   w.blkcnt = w.ld + align256((size_t)g.BH * g.N * 8);
-  w.coloff = w.blkcnt + align256((size_t)g.BH * nrb * g.Nc * 4);
-  w.csr = w.coloff + align256((size_t)g.BH * (g.Nc + 1) * 4);
-  w.total = w.csr + align256((size_t)g.BH * g.Nc * max_kv * 4);
+  w.coloff = w.blkcnt + align256((size_t)g.BHkv * nrb * g.Nc * 4);
+  w.csr = w.coloff + align256((size_t)g.BHkv * (g.Nc + 1) * 4);
+  w.total = w.csr + align256((size_t)g.BHkv * Nr * max_kv * 4);
   return w;
 }
 
@@ -743,9 +755,11 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   int32_t* coloff = reinterpret_cast<int32_t*>(ws + w.coloff);
   int32_t* csr = reinterpret_cast<int32_t*>(ws + w.csr);
   const int Nc = (int)g.Nc;
-  const int nrb = (Nc + kRowsPerBlk - 1) / kRowsPerBlk;
+  const int Nr = g.group * Nc;   // query rows per key/value head
+  const int nrb = (Nr + kRowsPerBlk - 1) / kRowsPerBlk;
   const int64_t total_tok = g.BH * g.N;
-  const int64_t total_cubes = g.BH * g.Nc;
+  const int64_t total_cubes = g.BH * g.Nc;       // query cubes
+  const int64_t total_kv_cubes = g.BHkv * g.Nc;  // key cubes
 
   constexpr int TOK_PER_BLOCK = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((total_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK)),
@@ -753,13 +767,13 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t cnt_lds = (size_t)Nc * 4;
-  hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)(g.BH * nrb)), dim3(256), cnt_lds, s, lut, valid, max_kv,
-                     Nc, nrb, blkcnt);
+  hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)(g.BHkv * nrb)), dim3(256), cnt_lds, s, lut, valid, max_kv,
+                     Nr, Nc, nrb, blkcnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)g.BH), dim3(256), cnt_lds, s, blkcnt, Nc, nrb, coloff);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)g.BHkv), dim3(256), cnt_lds, s, blkcnt, Nc, nrb, coloff);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)(g.BH * nrb)), dim3(64), cnt_lds, s, lut, valid, max_kv,
-                     Nc, nrb, blkcnt, coloff, csr);
+  hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)(g.BHkv * nrb)), dim3(64), cnt_lds, s, lut, valid, max_kv,
+                     Nr, Nc, nrb, blkcnt, coloff, csr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const float c_log2 = kLog2e / sqrtf((float)D);
@@ -770,11 +784,12 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   if ((e = grant_lds(kkv, dkdv_lds<D>(), granted[dev][1])) != hipSuccess) return e;
   hipLaunchKernelGGL(kq, dim3((unsigned)total_cubes), dim3(kThreads), dq_lds<D>(), s, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lut, valid, max_kv,
-                     (const float2*)ld, dq, Nc, total_cubes, c_log2, scale);
+                     (const float2*)ld, dq, Nc, total_cubes, c_log2, scale, g.group);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kkv, dim3((unsigned)total_cubes), dim3(kThreads), dkdv_lds<D>(), s, (const __bf16*)q,
+  hipLaunchKernelGGL(kkv, dim3((unsigned)total_kv_cubes), dim3(kThreads), dkdv_lds<D>(), s, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const int32_t*)coloff,
-                     (const int32_t*)csr, max_kv, (const float2*)ld, dk, dv, Nc, total_cubes, c_log2, scale);
+                     (const int32_t*)csr, max_kv, (const float2*)ld, dk, dv, Nc, total_kv_cubes, c_log2, scale,
+                     g.group);
   return hipGetLastError();
 }
 
@@ -784,10 +799,12 @@ static_assert(dq_lds<128>() <= kLdsMax && dkdv_lds<128>() <= kLdsMax, "LDS budge
 
 size_t sparse_attn_bwd_workspace(const Geom& g, int max_kv) { return ws_layout(g, max_kv).total; }
 
-bool sparse_attn_bwd_fits(const Geom& g) {
+bool sparse_attn_bwd_fits(const Geom& g, int max_kv) {
   // LDS counters of the transposed-list build hold one int per key cube;
-  // every launch grid stays below 2^31 workgroups.
-  return g.Nc >= 1 && g.Nc <= kMaxBwdCubes && g.BH * g.Nc < ((int64_t)1 << 31);
+  // every launch grid stays below 2^31 workgroups, and a key/value head's
+  // list offsets (group * Nc * max_kv entries) fit in int32.
+  return g.Nc >= 1 && g.Nc <= kMaxBwdCubes && g.BH * g.Nc < ((int64_t)1 << 31) &&
+         (int64_t)g.group * g.Nc * max_kv < ((int64_t)1 << 31);
 }
 
 hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
     const float* __restrict__ oc, const __bf16* __restrict__ gate_c, const __bf16* __restrict__ gate_f,
     __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2,
-    TokenMap tmap) {
+    TokenMap tmap, int group) {
   using C = Cfg<D>;
   constexpr int V_BASE = RK * C::TILE;           // V ring after the K ring
   constexpr int RING = (RK + RV) * C::TILE;
@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const bool hasB = cubeA + 1 < Nc;
     const int64_t rowA = bh * Nc + cubeA;
     const int64_t head_off = bh * (int64_t)Nc * kBlk * D;   // element offset of this (b, h)
-    const char* k_head = reinterpret_cast<const char*>(k + head_off);
-    const char* v_head = reinterpret_cast<const char*>(v + head_off);
+    const int64_t kv_off = (bh / group) * (int64_t)Nc * kBlk * D;   // its key/value head
+    const char* k_head = reinterpret_cast<const char*>(k + kv_off);
+    const char* v_head = reinterpret_cast<const char*>(v + kv_off);
     auto count_of = [&](int64_t row) {
       const int n = valid[row];
       return n < 0 ? 0 : (n > max_kv ? max_kv : n);
@@ -773,7 +774,7 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, lut, valid, max_kv, oc, (const __bf16*)gate_c, (const __bf16*)gate_f,
-                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2, tmap);
+                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2, tmap, g.group);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ int check_problem(const vsa_problem* p) {
       p->ch <= 0 || p->cw <= 0 || p->head_dim <= 0)
     return VSA_ERR_SHAPE;
   if (p->T % p->ct || p->H % p->ch || p->W % p->cw) return VSA_ERR_SHAPE;
+  if (p->heads_kv < 0 || (p->heads_kv > 0 && p->heads % p->heads_kv)) return VSA_ERR_SHAPE;
   const int64_t n = (int64_t)p->T * p->H * p->W;
   const int64_t vol = (int64_t)p->ct * p->ch * p->cw;
   const int64_t bh = (int64_t)p->batch * p->heads;
@@ -39,13 +40,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (1 << 16) | 3; }
+int vsa_abi_version(void) { return (2 << 16) | 0; }
 
 const char* vsa_status_str(int status) {
   switch (status) {
     case VSA_OK: return "ok";
     case VSA_ERR_NULL: return "required pointer is NULL";
-    case VSA_ERR_SHAPE: return "invalid shape (non-positive size, grid not a multiple of the cube, or too large)";
+    case VSA_ERR_SHAPE:
+      return "invalid shape (non-positive size, grid not a multiple of the cube, heads_kv not dividing heads, or too "
+             "large)";
     case VSA_ERR_TOPK: return "top_k / max_kv_blocks outside [1, Nc]";
     case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume or cube count";
     case VSA_ERR_HIP: return "HIP runtime error at launch";
@@ -195,7 +198,7 @@ int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks) {
   const Geom g = vsa::make_geom(*p);
   if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
   if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
-  if (!vsa::sparse_attn_bwd_fits(g)) return VSA_ERR_UNSUPPORTED;
+  if (!vsa::sparse_attn_bwd_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
   return VSA_OK;
 }
 }  // namespace

@@ -19,6 +19,8 @@ struct Geom {
   int64_t Nc;             // cubes per (batch, head)
   int64_t BH;             // batch * heads
   int32_t heads;          // heads per batch entry
+  int32_t group;          // query heads per key/value head; key/value head of bh is bh / group
+  int64_t BHkv;           // batch * key/value heads
   int32_t D;              // head_dim
 };
 
@@ -32,6 +34,8 @@ inline Geom make_geom(const vsa_problem& p) {
   g.Nc = g.N / g.vol;
   g.BH = (int64_t)p.batch * p.heads;
   g.heads = p.heads;
+  g.group = p.heads_kv > 0 ? p.heads / p.heads_kv : 1;
+  g.BHkv = g.BH / g.group;
   g.D = p.head_dim;
   return g;
 }
@@ -63,7 +67,7 @@ hipError_t launch_mask_to_lut(const Geom& g, const uint8_t* mask, int max_kv, in
 // handles this geometry, and the launcher (prep, transposed index list, dQ,
 // then dK/dV, all on stream s).
 size_t sparse_attn_bwd_workspace(const Geom& g, int max_kv);
-bool sparse_attn_bwd_fits(const Geom& g);
+bool sparse_attn_bwd_fits(const Geom& g, int max_kv);
 hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                                   const int32_t* valid, int max_kv, const void* o, const float* lse,
                                   const void* dout, float* dq, float* dk, float* dv, void* workspace,

@@ -38,9 +38,13 @@ class VsaForward:
         self.p, self.top_k, self.layout = p, top_k, layout
         ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
+        kts = (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
+        kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
-        self.qp, self.kp, self.vp = (torch.empty(ts, dtype=bf, device=device) for _ in range(3))
-        self.qc, self.kc, self.vc, self.oc = (torch.empty(cs, dtype=f32, device=device) for _ in range(4))
+        self.qp = torch.empty(ts, dtype=bf, device=device)
+        self.kp, self.vp = (torch.empty(kts, dtype=bf, device=device) for _ in range(2))
+        self.qc, self.oc = (torch.empty(cs, dtype=f32, device=device) for _ in range(2))
+        self.kc, self.vc = (torch.empty(kcs, dtype=f32, device=device) for _ in range(2))
         self.lut = torch.empty((p.batch, p.heads, p.n_cubes, top_k), dtype=torch.int32, device=device)
         self.valid = torch.empty((p.batch, p.heads, p.n_cubes), dtype=torch.int32, device=device)
         self.lse = torch.empty((p.batch, p.heads, p.n_tokens), dtype=f32, device=device) if with_lse else None
@@ -51,9 +55,10 @@ class VsaForward:
         p, B = self.p, L.VSA_BF16
         bnhd = self.layout == "bnhd"
         permute_pool = L.vsa_permute_pool_bnhd if bnhd else L.vsa_permute_pool
+        pkv = p.kv_problem()   # K and V may have fewer (grouped) heads
         permute_pool(p, B, q, self.qp, self.qc, stream)
-        permute_pool(p, B, k, self.kp, self.kc, stream)
-        permute_pool(p, B, v, self.vp, self.vc, stream)
+        permute_pool(pkv, B, k, self.kp, self.kc, stream)
+        permute_pool(pkv, B, v, self.vp, self.vc, stream)
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
         # fine attention reading the raster-order gates and writing the
         # raster-order output directly (the reorder back is in its epilogue)
@@ -94,11 +99,15 @@ class VsaBackward:
         self.p = p
         ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
+        kts = (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
+        kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
         self.doutp, self.gcp, self.gfp, self.d_of = (torch.empty(ts, dtype=bf, device=device) for _ in range(4))
         self.dgcp, self.dgfp = (torch.empty(ts, dtype=f32, device=device) for _ in range(2))
-        self.dqf, self.dkf, self.dvf = (torch.empty(ts, dtype=f32, device=device) for _ in range(3))
-        self.d_oc, self.dqc, self.dkc, self.dvc = (torch.empty(cs, dtype=f32, device=device) for _ in range(4))
+        self.dqf = torch.empty(ts, dtype=f32, device=device)
+        self.dkf, self.dvf = (torch.empty(kts, dtype=f32, device=device) for _ in range(2))
+        self.d_oc, self.dqc = (torch.empty(cs, dtype=f32, device=device) for _ in range(2))
+        self.dkc, self.dvc = (torch.empty(kcs, dtype=f32, device=device) for _ in range(2))
         self.ws_fine = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, max_kv), dtype=torch.uint8,
                                    device=device)
         self.ws_coarse = torch.empty(L.vsa_coarse_bwd_workspace_size(p), dtype=torch.uint8, device=device)
@@ -125,9 +134,10 @@ class VsaBackward:
                               self.ws_fine, stream)
         L.vsa_coarse_bwd(p, saved["qc"], saved["kc"], saved["vc"], saved["oc"], self.d_oc, self.dqc, self.dkc,
                          self.dvc, self.ws_coarse, stream)
+        pkv = p.kv_problem()
         L.vsa_pool_unpermute_bwd(p, self.dqf, self.dqc, dq, stream)
-        L.vsa_pool_unpermute_bwd(p, self.dkf, self.dkc, dk, stream)
-        L.vsa_pool_unpermute_bwd(p, self.dvf, self.dvc, dv, stream)
+        L.vsa_pool_unpermute_bwd(pkv, self.dkf, self.dkc, dk, stream)
+        L.vsa_pool_unpermute_bwd(pkv, self.dvf, self.dvc, dv, stream)
         if gcp is not None and dgate_c is not None:
             L.vsa_pool_unpermute_bwd(p, self.dgcp, None, dgate_c, stream)
         if gfp is not None and dgate_f is not None:

@@ -59,6 +59,14 @@ typedef struct vsa_problem {
   int32_t T, H, W;      /* token grid */
   int32_t ct, ch, cw;   /* cube edges; each grid edge must be a multiple */
   int32_t head_dim;     /* 64 or 128 */
+  int32_t heads_kv;     /* key/value heads (grouped heads, the nhead_k of the
+                           CK interface in [VSA-ROCm]); 0 means heads.  Must
+                           divide heads: query head h uses key/value head
+                           h / (heads / heads_kv).  K, V, Kc, Vc and their
+                           gradients have heads_kv heads; everything else
+                           has heads.  The single-tensor reorders and pools
+                           work on p->heads heads: for a grouped K or V pass a
+                           problem whose heads is heads_kv. */
 } vsa_problem;
 
 /* Element type of token tensors. */
@@ -68,7 +76,8 @@ enum { VSA_BF16 = 0, VSA_F32 = 1 };
 enum {
   VSA_OK = 0,
   VSA_ERR_NULL = -1,        /* a required pointer is NULL (or gate_c without oc) */
-  VSA_ERR_SHAPE = -2,       /* a size <= 0, grid not a multiple of the cube, or sizes overflow */
+  VSA_ERR_SHAPE = -2,       /* a size <= 0, grid not a multiple of the cube, heads_kv not
+                               dividing heads, or sizes overflow */
   VSA_ERR_TOPK = -3,        /* top_k / max_kv_blocks outside [1, Nc] */
   VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume this build does not handle */
   VSA_ERR_HIP = -5,         /* the HIP runtime refused a launch */

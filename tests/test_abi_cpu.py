@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert L.vsa_abi_version() >> 16 == 1
+    assert L.vsa_abi_version() >> 16 == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.vsa_status_str(code) and L.vsa_status_str(code) != "unknown status"
     assert L.vsa_status_str(42) == "unknown status"
@@ -146,6 +146,21 @@ def test_sparse_attn_bwd_workspace_and_errors():
     assert call(maxkv=33) == L.VSA_ERR_TOPK
     assert call(prob=ctypes.byref(_prob(head_dim=96))) == L.VSA_ERR_UNSUPPORTED
     assert call(prob=None) == L.VSA_ERR_NULL
+
+
+def test_grouped_heads_must_divide():
+    lib = _raw()
+    ok = L.Problem(1, 4, 8, 16, 16, 4, 4, 4, 64, heads_kv=2)
+    bad = L.Problem(1, 4, 8, 16, 16, 4, 4, 4, 64, heads_kv=3)
+    neg = L.Problem(1, 4, 8, 16, 16, 4, 4, 4, 64, heads_kv=-1)
+    n = ctypes.c_size_t(0)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(ok.c_struct()), 4, ctypes.byref(n)) == L.VSA_OK
+    for p in (bad, neg):
+        assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(p.c_struct()), 4, ctypes.byref(n)) == \
+            L.VSA_ERR_SHAPE
+        assert lib.vsa_coarse_topk(ctypes.byref(p.c_struct()), 4, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None,
+                                   None) == L.VSA_ERR_SHAPE
+    assert ok.kv_heads == 2 and ok.kv_problem().heads == 2 and ok.kv_problem().heads_kv == 0
 
 
 def test_model_layout_entry_points_errors():
