@@ -36,6 +36,10 @@ DESIGN.md):
   counted as overflows.
 * R17 the backward differentiates the layer with its LUT held fixed (Top-K
   selection has no gradient); P is recomputed from the forward's LSE.
+* R20 a grid that does not divide into cubes is padded up to whole cubes;
+  padded positions hold no token: they are never attended as keys, pooling
+  averages the real tokens of a cube only, and only real tokens have
+  outputs and gradients.
 * R19 grouped heads (K and V with fewer heads than Q, the head counts of the
   CK kernel interface in [VSA-ROCm]): query head h uses key/value head
   h // G with G = heads / kv_heads; equivalently every key/value head is
@@ -87,6 +91,60 @@ def perm_index(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> np.ndarray:
                             w = cube_w * cw + lw
                             order.append((t * H + h) * W + w)
     return np.asarray(order, dtype=np.int64)
+
+
+def token_layout(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> np.ndarray:
+    """Cube-major layout of a grid that need not divide into cubes (R20):
+    the grid is padded to whole cubes (ceil(T/ct)*ct, ...), cubes and tokens
+    are visited as in perm_index, and pi[p] is the raster index (in the
+    unpadded T x H x W grid) of the token at position p, or -1 where p is
+    padding.  Equals perm_index when the grid divides."""
+    for name, n, c in (("T", T, ct), ("H", H, ch), ("W", W, cw)):
+        if n <= 0 or c <= 0:
+            raise ValueError(f"{name}={n}, cube={c}: sizes must be positive")
+    order = []
+    for cube_t in range(-(-T // ct)):
+        for cube_h in range(-(-H // ch)):
+            for cube_w in range(-(-W // cw)):
+                for lt in range(ct):
+                    for lh in range(ch):
+                        for lw in range(cw):
+                            t = cube_t * ct + lt
+                            h = cube_h * ch + lh
+                            w = cube_w * cw + lw
+                            real = t < T and h < H and w < W
+                            order.append((t * H + h) * W + w if real else -1)
+    return np.asarray(order, dtype=np.int64)
+
+
+def gather_padded(x: np.ndarray, pi: np.ndarray) -> np.ndarray:
+    """x'[..., p, :] = x[..., pi[p], :] for real positions, 0 for padding."""
+    x = np.asarray(x)
+    out = np.zeros(x.shape[:-2] + (len(pi), x.shape[-1]), dtype=np.float64)
+    real = pi >= 0
+    out[..., real, :] = x[..., pi[real], :]
+    return out
+
+
+def scatter_padded(xp: np.ndarray, pi: np.ndarray, n: int) -> np.ndarray:
+    """out[..., pi[p], :] = x'[..., p, :] for real positions (n raster tokens)."""
+    xp = np.asarray(xp, np.float64)
+    out = np.zeros(xp.shape[:-2] + (n, xp.shape[-1]), dtype=np.float64)
+    real = pi >= 0
+    out[..., pi[real], :] = xp[..., real, :]
+    return out
+
+
+def pool_real(xp: np.ndarray, vol: int, real: np.ndarray) -> np.ndarray:
+    """Cube mean over the real tokens of each cube only (R20); pool when
+    every position is real."""
+    xp = np.asarray(xp, np.float64)
+    nc = xp.shape[-2] // vol
+    out = np.zeros(xp.shape[:-2] + (nc, xp.shape[-1]), dtype=np.float64)
+    for c in range(nc):
+        sel = np.nonzero(real[c * vol:(c + 1) * vol])[0] + c * vol
+        out[..., c, :] = xp[..., sel, :].sum(axis=-2) / len(sel)
+    return out
 
 
 def permute(x: np.ndarray, pi: np.ndarray) -> np.ndarray:
@@ -167,7 +225,7 @@ def topk_lut(s: np.ndarray, k: int):
 
 def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
                    kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
-                   scale: float, vol: int, query_cubes=None):
+                   scale: float, vol: int, query_cubes=None, key_valid=None):
     """Token-level attention of every query cube over its listed key cubes.
 
     qp/kp/vp: cube-major [B, heads, N, d].  For query cube i the key set is
@@ -177,6 +235,8 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     LSE = log(sum_q exp(scale * q.k)) in natural-log units (R7 for empty rows).
     ``query_cubes`` (optional iterable of (b, h, i)) limits the work to those
     query cubes, for spot checks at full size; other rows stay 0 / -inf.
+    ``key_valid`` (optional bool per cube-major position) drops padded key
+    positions (R20).
     """
     qp = np.asarray(qp, np.float64)
     kp = np.asarray(kp, np.float64)
@@ -193,6 +253,8 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
             continue
         blocks = kv_block_idx[b, h, i, :cnt]
         rows = np.concatenate([np.arange(j * vol, j * vol + vol) for j in blocks])
+        if key_valid is not None:
+            rows = rows[key_valid[rows]]
         q = qp[b, h, i * vol:(i + 1) * vol]
         s = scale * (q @ kp[b, h, rows].T)
         m = s.max(axis=1, keepdims=True)
@@ -206,7 +268,7 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
 def fine_attention_bwd(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
                        kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
                        scale: float, vol: int, of: np.ndarray, lse: np.ndarray,
-                       dof: np.ndarray):
+                       dof: np.ndarray, key_valid=None):
     """Gradients of the fine stage ([VSA-arXiv] Abstract: the method is
     trained end to end; the forward is the block-sparse softmax attention of
     fine_attention).  For query cube i with key rows R (the listed cubes'
@@ -214,7 +276,8 @@ def fine_attention_bwd(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     attention matrix of the forward; with D = rowsum(dO_i * O_i):
         dV_R += P^T dO_i,   dP = dO_i V_R^T,   dS = P * (dP - D),
         dQ_i  = scale * dS K_R,   dK_R += scale * dS^T Q_i.
-    A cube listed twice receives both contributions.  Returns (dq, dk, dv),
+    A cube listed twice receives both contributions; ``key_valid`` drops
+    padded key positions as in fine_attention.  Returns (dq, dk, dv),
     cube-major like the inputs."""
     qp = np.asarray(qp, np.float64)
     kp = np.asarray(kp, np.float64)
@@ -234,6 +297,8 @@ def fine_attention_bwd(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
                     continue
                 rows = np.concatenate([np.arange(j * vol, j * vol + vol)
                                        for j in kv_block_idx[b, h, i, :cnt]])
+                if key_valid is not None:
+                    rows = rows[key_valid[rows]]
                 qs = slice(i * vol, (i + 1) * vol)
                 q, do, o = qp[b, h, qs], dof[b, h, qs], of[b, h, qs]
                 p = np.exp(scale * (q @ kp[b, h, rows].T) - lse[b, h, qs][:, None])
@@ -359,7 +424,8 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     intermediate.  If a LUT is given it replaces the Top-K selection (used to
     score a kernel on exactly the LUT it was handed).  k and v may have fewer
     heads than q (R19); their intermediates are then returned expanded to
-    the query heads."""
+    the query heads.  A grid that does not divide into cubes is padded (R20):
+    pi holds -1 at padded cube-major positions."""
     T, H, W = grid
     ct, ch, cw = cube
     vol = ct * ch * cw
@@ -369,17 +435,20 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     v = expand_kv_heads(np.asarray(v, np.float64), group)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d)
-    pi = perm_index(T, H, W, ct, ch, cw)
-    qp, kp, vp = permute(q, pi), permute(k, pi), permute(v, pi)
-    qc, kc, vc = pool(qp, vol), pool(kp, vol), pool(vp, vol)
+    pi = token_layout(T, H, W, ct, ch, cw)   # = perm_index when the grid divides
+    real = pi >= 0
+    n = T * H * W
+    qp, kp, vp = gather_padded(q, pi), gather_padded(k, pi), gather_padded(v, pi)
+    qc, kc, vc = pool_real(qp, vol, real), pool_real(kp, vol, real), pool_real(vp, vol, real)
     s, pc, oc = coarse_attention(qc, kc, vc, scale)
     if kv_block_idx is None:
         kv_block_idx, valid_block_num = topk_lut(s, top_k)
-    of, lse = fine_attention(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol)
-    gcp = None if gate_c is None else permute(np.asarray(gate_c, np.float64), pi)
-    gfp = None if gate_f is None else permute(np.asarray(gate_f, np.float64), pi)
+    of, lse = fine_attention(qp, kp, vp, kv_block_idx, valid_block_num, scale, vol,
+                             key_valid=None if real.all() else real)
+    gcp = None if gate_c is None else gather_padded(gate_c, pi)
+    gfp = None if gate_f is None else gather_padded(gate_f, pi)
     outp = combine(of, oc, vol, gcp, gfp)
-    out = unpermute(outp, pi)
+    out = scatter_padded(outp, pi, n)
     return dict(pi=pi, qp=qp, kp=kp, vp=vp, qc=qc, kc=kc, vc=vc, scores=s,
                 p_coarse=pc, oc=oc, kv_block_idx=kv_block_idx,
                 valid_block_num=valid_block_num, o_fine=of, lse=lse,
@@ -443,6 +512,18 @@ def pool_bwd(dxc: np.ndarray, vol: int) -> np.ndarray:
     return np.repeat(np.asarray(dxc, np.float64), vol, axis=-2) / vol
 
 
+def pool_real_bwd(dxc: np.ndarray, vol: int, real: np.ndarray) -> np.ndarray:
+    """Gradient of pool_real: each real token of cube c receives dxc[c] / (the
+    cube's real-token count); padded positions receive 0.  pool_bwd when every
+    position is real."""
+    dxc = np.asarray(dxc, np.float64)
+    nc = dxc.shape[-2]
+    counts = real.reshape(nc, vol).sum(axis=1).astype(np.float64)
+    out = np.repeat(dxc / counts[:, None], vol, axis=-2)
+    out[..., ~real, :] = 0.0
+    return out
+
+
 def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
                  kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
                  dout: np.ndarray, gate_c: Optional[np.ndarray] = None,
@@ -459,17 +540,20 @@ def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
     f = vsa_forward(q, k, v, grid, cube, 0, gate_c=gate_c, gate_f=gate_f,
                     kv_block_idx=kv_block_idx, valid_block_num=valid_block_num)
     pi = f["pi"]
+    real = pi >= 0
+    kv = None if real.all() else real
+    n = grid[0] * grid[1] * grid[2]
     vol = cube[0] * cube[1] * cube[2]
     scale = f["scale"]
-    doutp = permute(np.asarray(dout, np.float64), pi)
-    gcp = None if gate_c is None else permute(np.asarray(gate_c, np.float64), pi)
-    gfp = None if gate_f is None else permute(np.asarray(gate_f, np.float64), pi)
+    doutp = gather_padded(dout, pi)
+    gcp = None if gate_c is None else gather_padded(gate_c, pi)
+    gfp = None if gate_f is None else gather_padded(gate_f, pi)
     dof, doc, dgcp, dgfp = combine_bwd(doutp, f["o_fine"], f["oc"], vol, gcp, gfp)
     dqf, dkf, dvf = fine_attention_bwd(f["qp"], f["kp"], f["vp"], kv_block_idx, valid_block_num,
-                                       scale, vol, f["o_fine"], f["lse"], dof)
+                                       scale, vol, f["o_fine"], f["lse"], dof, key_valid=kv)
     dqc, dkc, dvc = coarse_attention_bwd(f["qc"], f["kc"], f["vc"], scale, doc)
-    return dict(dq=unpermute(dqf + pool_bwd(dqc, vol), pi),
-                dk=reduce_kv_heads(unpermute(dkf + pool_bwd(dkc, vol), pi), group),
-                dv=reduce_kv_heads(unpermute(dvf + pool_bwd(dvc, vol), pi), group),
-                dgate_c=None if dgcp is None else unpermute(dgcp, pi),
-                dgate_f=None if dgfp is None else unpermute(dgfp, pi))
+    return dict(dq=scatter_padded(dqf + pool_real_bwd(dqc, vol, real), pi, n),
+                dk=reduce_kv_heads(scatter_padded(dkf + pool_real_bwd(dkc, vol, real), pi, n), group),
+                dv=reduce_kv_heads(scatter_padded(dvf + pool_real_bwd(dvc, vol, real), pi, n), group),
+                dgate_c=None if dgcp is None else scatter_padded(dgcp, pi, n),
+                dgate_f=None if dgfp is None else scatter_padded(dgfp, pi, n))

@@ -14,13 +14,15 @@ import test_oracle_fine as tf
 import test_oracle_bwd as tb
 import test_oracle_full_bwd as tfb
 import test_oracle_gqa as tg
+import test_oracle_padding as tpad
 import test_oracle_mask as tm
 import test_oracle_reorder as tr
 from block_sparse_video_major_amd import workloads as wl
 
 
 _ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut",
-                                     "fine_attention_bwd", "coarse_attention_bwd", "pool_bwd", "combine_bwd")}
+                                     "fine_attention_bwd", "coarse_attention_bwd", "pool_bwd", "combine_bwd",
+                                     "pool_real")}
 
 
 def _raster_perm(T, H, W, ct, ch, cw):
@@ -45,17 +47,17 @@ def _topk_smallest(s, k):
     return _ORIG["topk_lut"](-s, k)
 
 
-def _fine_no_scale(qp, kp, vp, lut, valid, scale, vol):
-    return _ORIG["fine_attention"](qp, kp, vp, lut, valid, 1.0, vol)
+def _fine_no_scale(qp, kp, vp, lut, valid, scale, vol, **kw):
+    return _ORIG["fine_attention"](qp, kp, vp, lut, valid, 1.0, vol, **kw)
 
 
-def _fine_q_for_k(qp, kp, vp, lut, valid, scale, vol):
-    return _ORIG["fine_attention"](qp, qp, vp, lut, valid, scale, vol)
+def _fine_q_for_k(qp, kp, vp, lut, valid, scale, vol, **kw):
+    return _ORIG["fine_attention"](qp, qp, vp, lut, valid, scale, vol, **kw)
 
 
-def _fine_shifted_block(qp, kp, vp, lut, valid, scale, vol):
+def _fine_shifted_block(qp, kp, vp, lut, valid, scale, vol, **kw):
     nc = qp.shape[-2] // vol
-    return _ORIG["fine_attention"](qp, kp, vp, (lut + 1) % nc, valid, scale, vol)
+    return _ORIG["fine_attention"](qp, kp, vp, (lut + 1) % nc, valid, scale, vol, **kw)
 
 
 def _combine_swapped(of, oc, vol, gate_c=None, gate_f=None):
@@ -86,18 +88,18 @@ def _mask_last_blocks_on_overflow(mask, max_kv):
     return out, valid, over
 
 
-def _bwd_dk_no_scale(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
-    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof)
+def _bwd_dk_no_scale(qp, kp, vp, lut, valid, scale, vol, of, lse, dof, **kw):
+    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof, **kw)
     return dq, dk / scale, dv
 
 
-def _bwd_no_rowsum_term(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
+def _bwd_no_rowsum_term(qp, kp, vp, lut, valid, scale, vol, of, lse, dof, **kw):
     # D = rowsum(dO * O) dropped: equivalent to passing O = 0
-    return _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, np.zeros_like(of), lse, dof)
+    return _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, np.zeros_like(of), lse, dof, **kw)
 
 
-def _bwd_dv_from_q(qp, kp, vp, lut, valid, scale, vol, of, lse, dof):
-    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof)
+def _bwd_dv_from_q(qp, kp, vp, lut, valid, scale, vol, of, lse, dof, **kw):
+    dq, dk, dv = _ORIG["fine_attention_bwd"](qp, kp, vp, lut, valid, scale, vol, of, lse, dof, **kw)
     return dq, dk, dq
 
 
@@ -118,6 +120,16 @@ def _combine_bwd_dgc_from_of(dout, of, oc, vol, gate_c=None, gate_f=None):
 def _expand_interleaved(x, group):
     # head h takes key/value head h % kv_heads instead of h // group
     return np.tile(np.asarray(x), (1, group) + (1,) * (np.asarray(x).ndim - 2))
+
+
+def _fine_attends_padding(qp, kp, vp, lut, valid, scale, vol, **kw):
+    kw.pop("key_valid", None)
+    return _ORIG["fine_attention"](qp, kp, vp, lut, valid, scale, vol, **kw)
+
+
+def _pool_real_full_volume(xp, vol, real):
+    # divides by the cube volume instead of the real-token count
+    return _ORIG["pool_real"](xp, vol, real) * real.reshape(-1, vol).sum(axis=1)[:, None] / vol
 
 
 def _pins():
@@ -144,6 +156,8 @@ def _pins():
     yield lambda: tfb.test_combine_bwd_matches_autograd()
     yield lambda: tfb.test_whole_layer_backward_matches_autograd()
     yield lambda: tg.test_dense_layer_equals_gqa_sdpa(4, 2)
+    yield lambda: tpad.test_padded_dense_layer_equals_sdpa_on_real_tokens((5, 6, 7), (2, 2, 2))
+    yield lambda: tpad.test_pool_averages_the_real_tokens_only()
 
 
 MUTATIONS = {
@@ -166,6 +180,8 @@ MUTATIONS = {
     "pool backward without 1/vol": ("pool_bwd", _pool_bwd_no_divisor),
     "combine backward dg_c taken from O_f": ("combine_bwd", _combine_bwd_dgc_from_of),
     "grouped heads interleaved instead of repeated": ("expand_kv_heads", _expand_interleaved),
+    "padded positions attended as keys": ("fine_attention", _fine_attends_padding),
+    "padded cubes averaged over the full volume": ("pool_real", _pool_real_full_volume),
 }
 
 
