@@ -65,8 +65,24 @@ class Problem:
         return self.ct * self.ch * self.cw
 
     @property
+    def cube_grid(self) -> tuple:
+        """Cubes along t, h, w (a grid that does not divide is padded up)."""
+        return (-(-self.T // self.ct), -(-self.H // self.ch), -(-self.W // self.cw))
+
+    @property
     def n_cubes(self) -> int:
-        return self.n_tokens // self.cube_volume
+        gt, gh, gw = self.cube_grid
+        return gt * gh * gw
+
+    @property
+    def n_positions(self) -> int:
+        """Rows of a cube-major token tensor: n_cubes * cube_volume (N when
+        the grid divides into cubes, more when it is padded)."""
+        return self.n_cubes * self.cube_volume
+
+    @property
+    def padded(self) -> bool:
+        return self.n_positions != self.n_tokens
 
     @property
     def kv_heads(self) -> int:
@@ -184,12 +200,17 @@ def _bnhd_shape(p: Problem):
     return (p.batch, p.n_tokens, p.heads, p.head_dim)
 
 
+def _pos_shape(p: Problem):
+    """Cube-major token tensor: Np = n_cubes * vol rows."""
+    return (p.batch, p.heads, p.n_positions, p.head_dim)
+
+
+def _kv_pos_shape(p: Problem):
+    return (p.batch, p.kv_heads, p.n_positions, p.head_dim)
+
+
 def _cube_shape(p: Problem):
     return (p.batch, p.heads, p.n_cubes, p.head_dim)
-
-
-def _kv_tok_shape(p: Problem):
-    return (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
 
 
 def _kv_cube_shape(p: Problem):
@@ -199,8 +220,9 @@ def _kv_cube_shape(p: Problem):
 # ---------------------------------------------------------------- entry points
 
 def vsa_perm_index(p: Problem) -> torch.Tensor:
-    """pi[p] = raster index of cube-major position p (host int32 tensor)."""
-    out = torch.empty(p.n_tokens, dtype=torch.int32)
+    """pi[p] = raster index of cube-major position p, -1 at a padded
+    position (host int32 tensor of n_positions)."""
+    out = torch.empty(p.n_positions, dtype=torch.int32)
     _check(load().vsa_perm_index(ctypes.byref(p.c_struct()), out.data_ptr()), "vsa_perm_index")
     return out
 
@@ -208,21 +230,21 @@ def vsa_perm_index(p: Problem) -> torch.Tensor:
 def vsa_permute(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: torch.Tensor, stream=None) -> None:
     td = _token_dtype(dtype)
     _need(x_raster, "x_raster", _tok_shape(p), td)
-    _need(x_cube, "x_cube", _tok_shape(p), td, x_raster.device)
+    _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
     _check(load().vsa_permute(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube),
                               _stream(stream, x_raster.device)), "vsa_permute")
 
 
 def vsa_unpermute(p: Problem, dtype: int, x_cube: torch.Tensor, x_raster: torch.Tensor, stream=None) -> None:
     td = _token_dtype(dtype)
-    _need(x_cube, "x_cube", _tok_shape(p), td)
+    _need(x_cube, "x_cube", _pos_shape(p), td)
     _need(x_raster, "x_raster", _tok_shape(p), td, x_cube.device)
     _check(load().vsa_unpermute(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(x_raster),
                                 _stream(stream, x_cube.device)), "vsa_unpermute")
 
 
 def vsa_pool(p: Problem, dtype: int, x_cube: torch.Tensor, xc: torch.Tensor, stream=None) -> None:
-    _need(x_cube, "x_cube", _tok_shape(p), _token_dtype(dtype))
+    _need(x_cube, "x_cube", _pos_shape(p), _token_dtype(dtype))
     _need(xc, "xc", _cube_shape(p), torch.float32, x_cube.device)
     _check(load().vsa_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(xc),
                            _stream(stream, x_cube.device)), "vsa_pool")
@@ -232,7 +254,7 @@ def vsa_permute_pool(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: tor
                      stream=None) -> None:
     td = _token_dtype(dtype)
     _need(x_raster, "x_raster", _tok_shape(p), td)
-    _need(x_cube, "x_cube", _tok_shape(p), td, x_raster.device)
+    _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_raster.device)
     _check(load().vsa_permute_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube), _ptr(xc),
                                    _stream(stream, x_raster.device)), "vsa_permute_pool")
@@ -283,11 +305,11 @@ def vsa_sparse_attn_fwd_bnhd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: to
 
 def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, raster):
     dev = q.device
-    ts = _tok_shape(p)
-    os_ = _bnhd_shape(p) if raster == "bnhd" else ts
+    ts = _pos_shape(p)
+    os_ = {"bnhd": _bnhd_shape(p), True: _tok_shape(p), False: ts}[raster]
     _need(q, "q", ts, torch.bfloat16, dev)
     for name, t in (("k", k), ("v", v)):
-        _need(t, name, _kv_tok_shape(p), torch.bfloat16, dev)
+        _need(t, name, _kv_pos_shape(p), torch.bfloat16, dev)
     _need(out, "out", os_, torch.bfloat16, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
@@ -300,7 +322,7 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
         if t is not None:
             _need(t, name, os_, torch.bfloat16, dev)
     if lse is not None:
-        _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
+        _need(lse, "lse", (p.batch, p.heads, p.n_positions if raster is False else p.n_tokens), torch.float32, dev)
     name = {"bnhd": "vsa_sparse_attn_fwd_bnhd", True: "vsa_sparse_attn_fwd_raster",
             False: "vsa_sparse_attn_fwd"}[raster]
     _check(getattr(load(), name)(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
@@ -353,7 +375,7 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
                         workspace: torch.Tensor, stream=None) -> None:
     """Gradients of the fine attention (all tensors cube-major; dq, dk, dv float32)."""
     dev = q.device
-    ts, ks = _tok_shape(p), _kv_tok_shape(p)
+    ts, ks = _pos_shape(p), _kv_pos_shape(p)
     for name, t in (("q", q), ("o", o), ("d_o", d_o)):
         _need(t, name, ts, torch.bfloat16, dev)
     for name, t in (("k", k), ("v", v)):
@@ -366,7 +388,7 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
     max_kv = kv_block_idx.shape[-1]
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
-    _need(lse, "lse", (p.batch, p.heads, p.n_tokens), torch.float32, dev)
+    _need(lse, "lse", (p.batch, p.heads, p.n_positions), torch.float32, dev)
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D byte tensor")
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
@@ -383,7 +405,7 @@ def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: to
                     stream=None) -> None:
     """Gradients of the gated combination (cube-major token tensors)."""
     dev = dout.device
-    ts, cs = _tok_shape(p), _cube_shape(p)
+    ts, cs = _pos_shape(p), _cube_shape(p)
     for name, t in (("dout", dout), ("d_of", d_of), ("o_f", o_f), ("gate_c", gate_c), ("gate_f", gate_f)):
         if t is not None:
             _need(t, name, ts, torch.bfloat16, dev)
@@ -427,7 +449,7 @@ def vsa_pool_unpermute_bwd(p: Problem, dx_cube: torch.Tensor, dxc: Optional[torc
                            stream=None) -> None:
     """dx_raster = unpermute(dx_cube + dxc broadcast over each cube / vol), float32."""
     dev = dx_cube.device
-    _need(dx_cube, "dx_cube", _tok_shape(p), torch.float32, dev)
+    _need(dx_cube, "dx_cube", _pos_shape(p), torch.float32, dev)
     _need(dx_raster, "dx_raster", _tok_shape(p), torch.float32, dev)
     if dxc is not None:
         _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
@@ -439,7 +461,7 @@ def vsa_permute_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch
     """vsa_permute reading the model layout [batch, N, heads, d]."""
     td = _token_dtype(dtype)
     _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
-    _need(x_cube, "x_cube", _tok_shape(p), td, x_bnhd.device)
+    _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
     _check(load().vsa_permute_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube),
                                    _stream(stream, x_bnhd.device)), "vsa_permute_bnhd")
 
@@ -449,7 +471,7 @@ def vsa_permute_pool_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: 
     """vsa_permute_pool reading the model layout [batch, N, heads, d]."""
     td = _token_dtype(dtype)
     _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
-    _need(x_cube, "x_cube", _tok_shape(p), td, x_bnhd.device)
+    _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_bnhd.device)
     _check(load().vsa_permute_pool_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube), _ptr(xc),
                                         _stream(stream, x_bnhd.device)), "vsa_permute_pool_bnhd")
@@ -459,7 +481,7 @@ def vsa_pool_unpermute_bwd_bnhd(p: Problem, dx_cube: torch.Tensor, dxc: Optional
                                 dx_bnhd: torch.Tensor, stream=None) -> None:
     """vsa_pool_unpermute_bwd writing the model layout [batch, N, heads, d]."""
     dev = dx_cube.device
-    _need(dx_cube, "dx_cube", _tok_shape(p), torch.float32, dev)
+    _need(dx_cube, "dx_cube", _pos_shape(p), torch.float32, dev)
     _need(dx_bnhd, "dx_bnhd", _bnhd_shape(p), torch.float32, dev)
     if dxc is not None:
         _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)

@@ -17,6 +17,10 @@
 // d = 128).  All index arithmetic is 32-bit within a (batch, head) and done
 // once per row, so the kernels stay HBM-bound.
 //
+// A grid that does not divide into cubes is padded up to whole cubes: padded
+// positions are written as zeros on the cube-major side, have no raster row,
+// and are left out of the cube mean (which divides by the real-token count).
+//
 // The raster side is either [batch, heads, N, d] or the model's own
 // [batch, N, heads, d] (a DiT's attention projections produce that order), so
 // no separate transpose pass is needed on either side of the path.
@@ -76,12 +80,14 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 
 // Geometry of one launch, all sizes that the row mapping needs.
 struct CubeArgs {
-  int32_t H, W;           // token grid (T is implied by the cube count)
+  int32_t T, H, W;        // token grid
   int32_t ct, ch, cw;     // cube edges
   int32_t gH, gW;         // cube grid
-  int32_t vol;            // tokens per cube
-  int32_t N;              // tokens per (batch, head)
+  int32_t vol;            // positions per cube
+  int32_t N;              // real tokens per (batch, head): raster rows
+  int32_t Np;             // cube-major positions per (batch, head)
   int32_t Nc;             // cubes per (batch, head)
+  int32_t padded;         // the grid was padded up to whole cubes
   int32_t heads;          // heads per batch entry
   int32_t bnhd;           // raster side is [batch, N, heads, d] (else [batch, heads, N, d])
   int64_t units;          // batch * heads * Nc
@@ -99,7 +105,7 @@ __device__ __forceinline__ int32_t row_offset(int32_t l, const CubeArgs& a) {
 
 // T = element type (pool modes), D = head_dim; CPR = 16-byte chunks per row.
 // Grid-stride over units = (batch*head) * Nc + cube.
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool PAD>
 __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __restrict__ src,
                                                              uint4* __restrict__ dst,
                                                              float* __restrict__ xc, CubeArgs a) {
@@ -123,23 +129,33 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
     const int32_t cw_i = c % a.gW;
     const int32_t ch_i = (c / a.gW) % a.gH;
     const int32_t ct_i = c / (a.gW * a.gH);
-    const int64_t head_rows = bh * (int64_t)a.N;
     // raster side: row of token n of this (batch, head) is rbase + n * tstride
-    int64_t rbase = head_rows, tstride = 1;
+    int64_t rbase = bh * (int64_t)a.N, tstride = 1;
     if (a.bnhd) {
       const int64_t b = bh / a.heads;
       rbase = b * a.N * (int64_t)a.heads + (bh - b * a.heads);
       tstride = a.heads;
     }
     const int64_t raster0 = rbase + (int64_t)((ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw) * tstride;
-    const int64_t cube0 = head_rows + (int64_t)c * a.vol;
+    const int64_t cube0 = bh * (int64_t)a.Np + (int64_t)c * a.vol;
+    // real extent of this cube along each axis (the edge unless padded)
+    const int32_t rem_t = min(a.ct, a.T - ct_i * a.ct), rem_h = min(a.ch, a.H - ch_i * a.ch),
+                  rem_w = min(a.cw, a.W - cw_i * a.cw);
+    auto real = [&](int32_t l) {
+      if constexpr (!PAD) return true;
+      const int32_t plane = a.ch * a.cw;
+      const int32_t lt = l / plane, rem = l - lt * plane;
+      const int32_t lh = rem / a.cw;
+      return lt < rem_t && lh < rem_h && rem - lh * a.cw < rem_w;
+    };
     float acc[kPooling ? E : 1];
 #pragma unroll
     for (int e = 0; e < (kPooling ? E : 1); ++e) acc[e] = 0.f;
-    float4 add = make_float4(0.f, 0.f, 0.f, 0.f);   // xc[c] / vol of this thread's columns
+    const int32_t n_real = PAD ? rem_t * rem_h * rem_w : a.vol;
+    float4 add = make_float4(0.f, 0.f, 0.f, 0.f);   // xc[c] / n_real of this thread's columns
     if (kAddPooled) {
       const float4 x = reinterpret_cast<const float4*>(xc + unit * D)[col];
-      const float inv = 1.0f / (float)a.vol;
+      const float inv = 1.0f / (float)n_real;
       add = make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv);
     }
 
@@ -148,18 +164,24 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
     auto batch = [&](int32_t l0, auto guarded) {
       uint4 buf[KB];
       int64_t rrow[KB];   // raster row of token l0 + b*RG
+      bool isreal[KB];    // a real token (not padding)
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
         const int32_t l = l0 + b * RG;
         if (!guarded.value || l < a.vol) {
+          isreal[b] = real(l);
           rrow[b] = raster0 + (int64_t)row_offset(l, a) * tstride;
-          buf[b] = load16<kStreamLoads>(src + (kFromRaster ? rrow[b] : cube0 + l) * CPR + col);
+          if (PAD && !isreal[b])
+            buf[b] = make_uint4(0u, 0u, 0u, 0u);
+          else
+            buf[b] = load16<kStreamLoads>(src + (kFromRaster ? rrow[b] : cube0 + l) * CPR + col);
         }
       }
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
         const int32_t l = l0 + b * RG;
         if (!guarded.value || l < a.vol) {
+          if (PAD && !kFromRaster && !isreal[b]) continue;   // padding has no raster row
           if (kAddPooled) {
             float4 f = make_float4(__uint_as_float(buf[b].x) + add.x, __uint_as_float(buf[b].y) + add.y,
                                    __uint_as_float(buf[b].z) + add.z, __uint_as_float(buf[b].w) + add.w);
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
 #pragma unroll
       for (int e = 0; e < E; ++e) part[phase][col * E + e] = acc[e];
       __syncthreads();
-      const float fvol = (float)a.vol;
+      const float fvol = (float)n_real;
       for (int d = threadIdx.x; d < D; d += kThreads) {
         float s = 0.f;
 #pragma unroll
@@ -200,12 +222,14 @@ CubeArgs cube_args(const Geom& g, RasterLayout layout) {
   CubeArgs a;
   a.heads = g.heads;
   a.bnhd = layout == kBNHD ? 1 : 0;
-  a.H = g.H; a.W = g.W;
+  a.T = g.T; a.H = g.H; a.W = g.W;
   a.ct = g.ct; a.ch = g.ch; a.cw = g.cw;
   a.gH = g.gH; a.gW = g.gW;
   a.vol = g.vol;
   a.N = (int32_t)g.N;
+  a.Np = (int32_t)g.Np;
   a.Nc = (int32_t)g.Nc;
+  a.padded = g.padded;
   a.units = g.BH * g.Nc;
   return a;
 }
@@ -215,11 +239,17 @@ hipError_t launch_mode(const Geom& g, const void* src, void* dst, float* xc, hip
                        RasterLayout layout = kBHND) {
   const CubeArgs a = cube_args(g, layout);
   const dim3 grid((unsigned)(a.units < kMaxGrid ? a.units : kMaxGrid));
-  if (g.D == 64)
-    hipLaunchKernelGGL((cube_pass_kernel<T, 64, MODE>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+  if (g.D == 64 && g.padded)
+    hipLaunchKernelGGL((cube_pass_kernel<T, 64, MODE, true>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+                       (uint4*)dst, xc, a);
+  else if (g.D == 64)
+    hipLaunchKernelGGL((cube_pass_kernel<T, 64, MODE, false>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+                       (uint4*)dst, xc, a);
+  else if (g.D == 128 && g.padded)
+    hipLaunchKernelGGL((cube_pass_kernel<T, 128, MODE, true>), grid, dim3(kThreads), 0, s, (const uint4*)src,
                        (uint4*)dst, xc, a);
   else if (g.D == 128)
-    hipLaunchKernelGGL((cube_pass_kernel<T, 128, MODE>), grid, dim3(kThreads), 0, s, (const uint4*)src,
+    hipLaunchKernelGGL((cube_pass_kernel<T, 128, MODE, false>), grid, dim3(kThreads), 0, s, (const uint4*)src,
                        (uint4*)dst, xc, a);
   else
     return hipErrorInvalidValue;

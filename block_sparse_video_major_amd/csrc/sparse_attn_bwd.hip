@@ -735,7 +735,7 @@ WsLayout ws_layout(const Geom& g, int max_kv) {
   const size_t nrb = (Nr + kRowsPerBlk - 1) / kRowsPerBlk;
   WsLayout w;
   w.ld = 0;
-  w.blkcnt = w.ld + align256((size_t)g.BH * g.N * 8);
+  w.blkcnt = w.ld + align256((size_t)g.BH * g.Np * 8);
   w.coloff = w.blkcnt + align256((size_t)g.BHkv * nrb * g.Nc * 4);
   w.csr = w.coloff + align256((size_t)g.BHkv * (g.Nc + 1) * 4);
   w.total = w.csr + align256((size_t)g.BHkv * Nr * max_kv * 4);
@@ -757,7 +757,7 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   const int Nc = (int)g.Nc;
   const int Nr = g.group * Nc;   // query rows per key/value head
   const int nrb = (Nr + kRowsPerBlk - 1) / kRowsPerBlk;
-  const int64_t total_tok = g.BH * g.N;
+  const int64_t total_tok = g.BH * g.Np;
   const int64_t total_cubes = g.BH * g.Nc;       // query cubes
   const int64_t total_kv_cubes = g.BHkv * g.Nc;  // key cubes
 

@@ -133,18 +133,49 @@ __device__ __forceinline__ void wait_parts(int parts) {
 
 // RK / RV: positions of the K and V tile rings.
 // Token order of out, gate_c, gate_f and lse: cube-major (on == 0) or raster
-// (t, h, w) order (on == 1; the reorder back fused into the epilogue).  With
+// (t, h, w) order (on == 1; the reorder back fused into the epilogue).  A
+// grid padded up to whole cubes has positions with no token: they are never
+// keys and, in raster order, have no output row.  With
 // bnhd == 1 (raster only) out and the gates are the model's [batch, N, heads,
 // d] rows instead of [batch, heads, N, d]; lse stays [batch, heads, N].
 struct TokenMap {
   int32_t on;
   int32_t bnhd;
-  int32_t H, W;         // token grid (rows and columns of a frame)
+  int32_t T, H, W;      // token grid (frames, rows and columns of a frame)
   int32_t ct, ch, cw;   // cube edges
   int32_t gH, gW;       // cube grid
   int32_t heads;        // heads per batch entry
-  int32_t N;            // tokens per (batch, head)
+  int32_t N;            // real tokens per (batch, head): raster rows
+  int32_t Np;           // cube-major positions per (batch, head)
+  int32_t padded;       // the grid was padded up to whole cubes
 };
+
+// Whether position l of cube c holds a real token (not padding).
+__device__ __forceinline__ bool token_real(const TokenMap& m, int32_t c, int32_t l) {
+  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
+  const int32_t plane = m.ch * m.cw;
+  const int32_t lt = l / plane, rem = l - lt * plane;
+  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
+  return ct_i * m.ct + lt < m.T && ch_i * m.ch + lh < m.H && cw_i * m.cw + lw < m.W;
+}
+
+// Bit l set when position l of cube c holds a real token.  The cube edges
+// multiply to 64 positions; tokens run w fastest, then h, then t.
+__device__ __forceinline__ uint64_t cube_mask(const TokenMap& m, int32_t c) {
+  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
+  const int32_t rt = min(m.ct, m.T - ct_i * m.ct), rh = min(m.ch, m.H - ch_i * m.ch), rw = min(m.cw, m.W - cw_i * m.cw);
+  const uint64_t row = rw >= 64 ? ~0ull : ((1ull << rw) - 1);
+  uint64_t plane = 0, all = 0;
+  for (int32_t h = 0; h < rh; ++h) plane |= row << (h * m.cw);
+  for (int32_t t = 0; t < rt; ++t) all |= plane << (t * m.ch * m.cw);
+  return all;
+}
+
+// Whether cube c reaches past the grid (holds padded positions).
+__device__ __forceinline__ bool cube_partial(const TokenMap& m, int32_t c) {
+  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
+  return (ct_i + 1) * m.ct > m.T || (ch_i + 1) * m.ch > m.H || (cw_i + 1) * m.cw > m.W;
+}
 
 // Position of token l (< 64) of cube c within its (batch, head) in the
 // order the map selects.
@@ -160,6 +191,7 @@ __device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, int32
 // Element offset of token l of cube c of (batch, head) bh in out and the gates.
 __device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int32_t c, int32_t l, int D) {
   const int64_t n = token_pos(m, c, l);
+  if (!m.on) return (bh * m.Np + n) * D;
   if (!m.bnhd) return (bh * m.N + n) * D;
   const int64_t b = bh / m.heads, h = bh - b * m.heads;
   return ((b * m.N + n) * m.heads + h) * D;
@@ -433,6 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     //   bits 18 / 19      half A / half B had a tile in step p - 1
     //   bits 20-24        tiles to leave in flight at barrier p
     //   bits 25-29        tiles to issue after barrier p
+    //   bits 30 / 31      half A's / half B's tile of step p holds padded positions
     {
       auto kpos = [&](int st) { return st < 0 ? 0 : (int)(plan[st] & 0xffffu); };
       auto fr = [&](int st) { return (int)(plan[st] >> 16); };
@@ -446,6 +479,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           const int kb = k0 + ((a != 0xffffu && b != a) ? 1 : 0);
           d |= (uint32_t)(k0 % RK) | ((uint32_t)(kb % RK) << 4);
           d |= (a != 0xffffu ? 1u << 16 : 0u) | (b != 0xffffu ? 1u << 17 : 0u);
+          if (tmap.padded) {
+            if (a != 0xffffu && cube_partial(tmap, (int)a)) d |= 1u << 30;
+            if (b != 0xffffu && cube_partial(tmap, (int)b)) d |= 1u << 31;
+          }
         }
         if (pp > 0) {
           const uint32_t e = sched[pp - 1];
@@ -627,6 +664,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // A key tile that reaches past the grid: its padded positions are not
+      // keys (score -inf, so they add nothing to the row max or the sum).
+      if ((d_c >> (30 + grp)) & 1u) {
+        const uint32_t e = sched[p];
+        const int32_t cube = __builtin_amdgcn_readfirstlane((int32_t)(grp == 0 ? (e & 0xffffu) : (e >> 16)));
+        const uint64_t real = cube_mask(tmap, cube);   // bit l: position l is a real token
+        // this lane's keys 32*kh + 4*g + 8*q + j (q, j < 4) are bits 8*q + j of m
+        const uint64_t m = real >> (32 * kh + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((m >> (8 * (r >> 2) + (r & 3))) & 1ull)) sn[r] = -INFINITY;
+      }
       // PV(p-1) with the row max of step p.
       float mx = kNegBig;
 #pragma unroll
@@ -683,9 +732,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           // d = 32*t + 8*rq + 4*g + 0..3
           *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
         }
-      if (lse != nullptr && g == 0 && my_valid) {
+      const int32_t my_tok = 32 * qh + n32;
+      if (lse != nullptr && g == 0 && my_valid && (!tmap.on || !tmap.padded || token_real(tmap, my_cube, my_tok))) {
         const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-        lse[bh * (int64_t)Nc * kBlk + token_pos(tmap, my_cube, 32 * qh + n32)] = val;
+        lse[bh * (int64_t)(tmap.on ? tmap.N : tmap.Np) + token_pos(tmap, my_cube, my_tok)] = val;
       }
     }
     __syncthreads();
@@ -698,6 +748,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;
         const int row = c / C::CPR, col = c % C::CPR;
+        if (tmap.on && tmap.padded && !token_real(tmap, my_cube, row)) continue;   // padding: no raster row
         const int64_t gidx = token_elem(tmap, bh, my_cube, row, D) + col * 8;
         float val[8];
         const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
@@ -831,7 +882,9 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
   m.bnhd = out_order == 2 ? 1 : 0;
   m.heads = g.heads;
   m.N = (int32_t)g.N;
-  m.H = g.H; m.W = g.W;
+  m.Np = (int32_t)g.Np;
+  m.padded = g.padded;
+  m.T = g.T; m.H = g.H; m.W = g.W;
   m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
   m.gH = g.gH; m.gW = g.gW;
   if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);

@@ -18,9 +18,10 @@ int check_problem(const vsa_problem* p) {
   if (p->batch <= 0 || p->heads <= 0 || p->T <= 0 || p->H <= 0 || p->W <= 0 || p->ct <= 0 ||
       p->ch <= 0 || p->cw <= 0 || p->head_dim <= 0)
     return VSA_ERR_SHAPE;
-  if (p->T % p->ct || p->H % p->ch || p->W % p->cw) return VSA_ERR_SHAPE;
   if (p->heads_kv < 0 || (p->heads_kv > 0 && p->heads % p->heads_kv)) return VSA_ERR_SHAPE;
-  const int64_t n = (int64_t)p->T * p->H * p->W;
+  // a grid that does not divide into cubes is padded up to whole cubes
+  const auto up = [](int64_t x, int64_t c) { return (x + c - 1) / c * c; };
+  const int64_t n = up(p->T, p->ct) * up(p->H, p->ch) * up(p->W, p->cw);
   const int64_t vol = (int64_t)p->ct * p->ch * p->cw;
   const int64_t bh = (int64_t)p->batch * p->heads;
   if (n > INT32_MAX || vol > INT32_MAX || bh > INT32_MAX) return VSA_ERR_SHAPE;
@@ -46,9 +47,7 @@ const char* vsa_status_str(int status) {
   switch (status) {
     case VSA_OK: return "ok";
     case VSA_ERR_NULL: return "required pointer is NULL";
-    case VSA_ERR_SHAPE:
-      return "invalid shape (non-positive size, grid not a multiple of the cube, heads_kv not dividing heads, or too "
-             "large)";
+    case VSA_ERR_SHAPE: return "invalid shape (non-positive size, heads_kv not dividing heads, or too large)";
     case VSA_ERR_TOPK: return "top_k / max_kv_blocks outside [1, Nc]";
     case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume or cube count";
     case VSA_ERR_HIP: return "HIP runtime error at launch";
@@ -72,7 +71,8 @@ int vsa_perm_index(const vsa_problem* p, int32_t* perm_host) {
             for (int lw = 0; lw < g.cw; ++lw) {
               const int64_t t = (int64_t)ct_i * g.ct + lt, h = (int64_t)ch_i * g.ch + lh,
                             w = (int64_t)cw_i * g.cw + lw;
-              perm_host[pos++] = (int32_t)((t * g.H + h) * g.W + w);
+              const bool real = t < g.T && h < g.H && w < g.W;
+              perm_host[pos++] = real ? (int32_t)((t * g.H + h) * g.W + w) : -1;
             }
   return VSA_OK;
 }

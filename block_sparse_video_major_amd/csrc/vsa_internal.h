@@ -10,13 +10,18 @@
 namespace vsa {
 
 // Token grid and cube geometry with the derived sizes every kernel needs.
+// A grid that does not divide into cubes is padded up to whole cubes: the
+// cube-major tensors have Np = Nc * vol rows per (batch, head), the raster
+// tensors the N real tokens.
 struct Geom {
   int32_t T, H, W;        // token grid
   int32_t ct, ch, cw;     // cube edges
-  int32_t gT, gH, gW;     // cube grid = grid / cube
+  int32_t gT, gH, gW;     // cube grid = grid / cube, rounded up
   int32_t vol;            // ct * ch * cw
-  int64_t N;              // tokens per (batch, head)
+  int64_t N;              // real tokens per (batch, head): raster rows
+  int64_t Np;             // cube-major positions per (batch, head): Nc * vol
   int64_t Nc;             // cubes per (batch, head)
+  int32_t padded;         // Np != N
   int64_t BH;             // batch * heads
   int32_t heads;          // heads per batch entry
   int32_t group;          // query heads per key/value head; key/value head of bh is bh / group
@@ -28,10 +33,14 @@ inline Geom make_geom(const vsa_problem& p) {
   Geom g;
   g.T = p.T; g.H = p.H; g.W = p.W;
   g.ct = p.ct; g.ch = p.ch; g.cw = p.cw;
-  g.gT = p.T / p.ct; g.gH = p.H / p.ch; g.gW = p.W / p.cw;
+  g.gT = (int32_t)(((int64_t)p.T + p.ct - 1) / p.ct);
+  g.gH = (int32_t)(((int64_t)p.H + p.ch - 1) / p.ch);
+  g.gW = (int32_t)(((int64_t)p.W + p.cw - 1) / p.cw);
   g.vol = p.ct * p.ch * p.cw;
   g.N = (int64_t)p.T * p.H * p.W;
-  g.Nc = g.N / g.vol;
+  g.Nc = (int64_t)g.gT * g.gH * g.gW;
+  g.Np = g.Nc * g.vol;
+  g.padded = g.Np != g.N ? 1 : 0;
   g.BH = (int64_t)p.batch * p.heads;
   g.heads = p.heads;
   g.group = p.heads_kv > 0 ? p.heads / p.heads_kv : 1;

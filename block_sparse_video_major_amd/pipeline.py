@@ -36,9 +36,9 @@ class VsaForward:
         if layout not in ("bhnd", "bnhd"):
             raise ValueError(f"layout {layout!r} is not 'bhnd' or 'bnhd'")
         self.p, self.top_k, self.layout = p, top_k, layout
-        ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
+        ts = (p.batch, p.heads, p.n_positions, p.head_dim)   # cube-major (padded) rows
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
-        kts = (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
+        kts = (p.batch, p.kv_heads, p.n_positions, p.head_dim)
         kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
         self.qp = torch.empty(ts, dtype=bf, device=device)
@@ -97,9 +97,9 @@ class VsaBackward:
 
     def __init__(self, p: Problem, max_kv: int, device="cuda"):
         self.p = p
-        ts = (p.batch, p.heads, p.n_tokens, p.head_dim)
+        ts = (p.batch, p.heads, p.n_positions, p.head_dim)   # cube-major (padded) rows
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
-        kts = (p.batch, p.kv_heads, p.n_tokens, p.head_dim)
+        kts = (p.batch, p.kv_heads, p.n_positions, p.head_dim)
         kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
         self.doutp, self.gcp, self.gfp, self.d_of = (torch.empty(ts, dtype=bf, device=device) for _ in range(4))

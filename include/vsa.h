@@ -21,12 +21,18 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Tensors are dense, row-major, caller-allocated device buffers.  Token
- *   tensors are [batch, heads, N, head_dim] with N = T*H*W; cube tensors are
- *   [batch, heads, Nc, head_dim] with Nc = N / (ct*ch*cw).  Raster token index
- *   is (t*H + h)*W + w.  Cube-major position p = c*vol + l, where cube c runs
- *   in raster order over the (T/ct, H/ch, W/cw) cube grid and l in raster
- *   order over (ct, ch, cw) inside the cube.
+ * - Tensors are dense, row-major, caller-allocated device buffers.  Raster
+ *   token tensors are [batch, heads, N, head_dim] with N = T*H*W and raster
+ *   token index (t*H + h)*W + w.  The cube grid is (ceil(T/ct), ceil(H/ch),
+ *   ceil(W/cw)) with Nc cubes: a grid that does not divide into cubes is
+ *   padded up to whole cubes ([VSA-ROCm] shows no other handling; reading:
+ *   padded positions hold no token).  Cube-major token tensors are [batch,
+ *   heads, Np, head_dim] with Np = Nc*vol rows; position p = c*vol + l, where
+ *   cube c runs in raster order over the cube grid and l in raster order
+ *   over (ct, ch, cw) inside the cube.  Padded positions hold zeros after a
+ *   reorder, are never attended as keys, are left out of the cube means, and
+ *   have no raster row (their cube-major outputs are unspecified).  Cube
+ *   tensors are [batch, heads, Nc, head_dim].  When the grid divides, Np = N.
  * - The library never allocates, frees or synchronises.  Every call only
  *   queues work on `stream` (a hipStream_t; NULL is the default stream) and
  *   returns.  Calls are stateless and re-entrant; two calls may run
@@ -57,7 +63,7 @@ typedef struct vsa_problem {
   int32_t batch;
   int32_t heads;
   int32_t T, H, W;      /* token grid */
-  int32_t ct, ch, cw;   /* cube edges; each grid edge must be a multiple */
+  int32_t ct, ch, cw;   /* cube edges (a grid that does not divide is padded) */
   int32_t head_dim;     /* 64 or 128 */
   int32_t heads_kv;     /* key/value heads (grouped heads, the nhead_k of the
                            CK interface in [VSA-ROCm]); 0 means heads.  Must
@@ -76,8 +82,7 @@ enum { VSA_BF16 = 0, VSA_F32 = 1 };
 enum {
   VSA_OK = 0,
   VSA_ERR_NULL = -1,        /* a required pointer is NULL (or gate_c without oc) */
-  VSA_ERR_SHAPE = -2,       /* a size <= 0, grid not a multiple of the cube, heads_kv not
-                               dividing heads, or sizes overflow */
+  VSA_ERR_SHAPE = -2,       /* a size <= 0, heads_kv not dividing heads, or sizes overflow */
   VSA_ERR_TOPK = -3,        /* top_k / max_kv_blocks outside [1, Nc] */
   VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume this build does not handle */
   VSA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
@@ -102,7 +107,8 @@ int vsa_unpermute(const vsa_problem* p, int32_t dtype, const void* x_cube,
                   void* x_raster, void* stream);
 
 /* Cube mean-pool ([VSA-ROCm] §Two-Stage Architecture, Stage 1):
- *   xc[b, h, c, :] = (1/vol) * sum_{l < vol} x_cube[b, h, c*vol + l, :]
+ *   xc[b, h, c, :] = (1/n_c) * sum over the n_c real positions l of cube c
+ *                    of x_cube[b, h, c*vol + l, :]   (n_c = vol unless padded)
  * x_cube: [batch, heads, N, head_dim] of `dtype`, cube-major.
  * xc:     [batch, heads, Nc, head_dim] float32, accumulated in float32 in a
  *         fixed order (deterministic). */
@@ -330,8 +336,9 @@ int vsa_coarse_bwd(const vsa_problem* p, const float* qc, const float* kc,
 int vsa_pool_unpermute_bwd(const vsa_problem* p, const float* dx_cube,
                            const float* dxc, float* dx_raster, void* stream);
 
-/* Host helper: perm_host[p] = pi(p) for p < N (the order vsa_permute
- * applies).  perm_host is a host array of N int32.  No device work. */
+/* Host helper: perm_host[p] = pi(p) for p < Np (the order vsa_permute
+ * applies), -1 at padded positions.  perm_host is a host array of Np int32.
+ * No device work. */
 int vsa_perm_index(const vsa_problem* p, int32_t* perm_host);
 
 /* Static description of a status code (never NULL). */

@@ -50,6 +50,20 @@ def test_host_perm_index_matches_oracle(grid, cube):
     assert np.array_equal(got, oracle.perm_index(*grid, *cube))
 
 
+@pytest.mark.parametrize("grid,cube", [((6, 8, 8), (4, 4, 4)), ((5, 7, 9), (4, 4, 4)),
+                                       ((1, 1, 1), (4, 4, 4)), ((3, 5, 2), (2, 2, 2)),
+                                       ((21, 30, 52), (4, 4, 4))])
+def test_host_perm_index_padded_grid(grid, cube):
+    """A grid that does not divide into cubes: Np = ceil-cube count * vol
+    positions, -1 at padding, as the oracle's padded layout."""
+    p = L.Problem(1, 1, *grid, *cube, 64)
+    want = oracle.token_layout(*grid, *cube)
+    assert p.padded and p.n_positions == len(want)
+    assert p.n_cubes * p.cube_volume == len(want)
+    got = L.vsa_perm_index(p).numpy()
+    assert np.array_equal(got, want)
+
+
 # ----------------------------------------------------------------- errors
 DUMMY = 0x1000   # never dereferenced: each call fails validation first
 
@@ -70,14 +84,14 @@ def _perm(prob, dtype=L.VSA_BF16, src=DUMMY, dst=DUMMY):
 
 def test_permute_errors():
     assert _perm(None) == L.VSA_ERR_NULL
-    assert _perm(_prob(T=6)) == L.VSA_ERR_SHAPE            # 6 is not a multiple of 4
+    assert _perm(_prob(ct=0)) == L.VSA_ERR_SHAPE
     assert _perm(_prob(W=0)) == L.VSA_ERR_SHAPE
     assert _perm(_prob(batch=-1)) == L.VSA_ERR_SHAPE
     assert _perm(_prob(head_dim=96)) == L.VSA_ERR_UNSUPPORTED
     assert _perm(_prob(), dtype=7) == L.VSA_ERR_UNSUPPORTED
     assert _perm(_prob(), src=None) == L.VSA_ERR_NULL
     assert _perm(_prob(), dst=None) == L.VSA_ERR_NULL
-    assert _raw().vsa_unpermute(ctypes.byref(_prob(H=10)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert _raw().vsa_unpermute(ctypes.byref(_prob(ch=-1)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
     assert _raw().vsa_unpermute(ctypes.byref(_prob()), 0, None, DUMMY, None) == L.VSA_ERR_NULL
     assert _perm(_prob(T=1 << 14, H=1 << 14, W=1 << 14, ct=1, ch=1, cw=1)) == L.VSA_ERR_SHAPE
 
@@ -86,7 +100,7 @@ def test_pool_errors():
     lib = _raw()
     assert lib.vsa_pool(ctypes.byref(_prob()), 0, None, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_pool(ctypes.byref(_prob()), 0, DUMMY, None, None) == L.VSA_ERR_NULL
-    assert lib.vsa_pool(ctypes.byref(_prob(cw=3)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_pool(ctypes.byref(_prob(cw=0)), 0, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
     assert lib.vsa_pool(ctypes.byref(_prob()), 3, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
 
 
@@ -96,7 +110,7 @@ def test_permute_pool_errors():
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, None, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
     assert lib.vsa_permute_pool(None, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
-    assert lib.vsa_permute_pool(ctypes.byref(_prob(W=10)), 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_permute_pool(ctypes.byref(_prob(T=0)), 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 2, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
 
 
@@ -109,7 +123,7 @@ def test_mask_to_lut_errors():
     assert lib.vsa_mask_to_lut(pr, DUMMY, 4, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
     assert lib.vsa_mask_to_lut(pr, DUMMY, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
     assert lib.vsa_mask_to_lut(pr, DUMMY, 33, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_TOPK
-    assert lib.vsa_mask_to_lut(ctypes.byref(_prob(H=10)), DUMMY, 4, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_mask_to_lut(ctypes.byref(_prob(heads=0)), DUMMY, 4, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
 
 
 def test_sparse_attn_bwd_workspace_and_errors():
@@ -121,6 +135,10 @@ def test_sparse_attn_bwd_workspace_and_errors():
     al = lambda x: (x + 255) // 256 * 256
     bh, nc, ntok = 2, 32, 2048
     assert n.value == al(bh * ntok * 8) + al(bh * 2 * nc * 4) + al(bh * (nc + 1) * 4) + al(bh * nc * 8 * 4)
+    # a padded 6 x 8 x 8 grid: 8 cubes, per-token records over the 512 padded positions
+    pp = ctypes.byref(_prob(T=6, H=8, W=8, head_dim=128))
+    assert lib.vsa_sparse_attn_bwd_workspace_size(pp, 4, ctypes.byref(n)) == L.VSA_OK
+    assert n.value == al(bh * 512 * 8) + al(bh * 1 * 8 * 4) + al(bh * 9 * 4) + al(bh * 8 * 4 * 4)
     assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 8, None) == L.VSA_ERR_NULL
     assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 0, ctypes.byref(n)) == L.VSA_ERR_TOPK
     assert lib.vsa_sparse_attn_bwd_workspace_size(pr, 33, ctypes.byref(n)) == L.VSA_ERR_TOPK
@@ -169,7 +187,7 @@ def test_model_layout_entry_points_errors():
     assert lib.vsa_permute_bnhd(pr, L.VSA_BF16, None, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_permute_bnhd(pr, 7, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
     assert lib.vsa_permute_pool_bnhd(pr, L.VSA_BF16, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
-    assert lib.vsa_permute_pool_bnhd(ctypes.byref(_prob(H=10)), L.VSA_BF16, DUMMY, DUMMY, DUMMY, None) == \
+    assert lib.vsa_permute_pool_bnhd(ctypes.byref(_prob(W=-1)), L.VSA_BF16, DUMMY, DUMMY, DUMMY, None) == \
         L.VSA_ERR_SHAPE
     assert lib.vsa_pool_unpermute_bwd_bnhd(pr, None, None, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_pool_unpermute_bwd_bnhd(pr, DUMMY, None, None, None) == L.VSA_ERR_NULL
@@ -218,7 +236,7 @@ def test_sparse_attn_errors():
     assert call(maxkv=33) == L.VSA_ERR_TOPK
     assert call(prob=_prob(ct=2, ch=2, cw=2)) == L.VSA_ERR_UNSUPPORTED   # cube volume 8
     assert call(prob=_prob(head_dim=32)) == L.VSA_ERR_UNSUPPORTED
-    assert call(prob=_prob(T=5)) == L.VSA_ERR_SHAPE
+    assert call(prob=_prob(H=-4)) == L.VSA_ERR_SHAPE
     # 16-bit cube ids: Nc = 65536 is beyond the fine kernel
     assert call(prob=_prob(T=4, H=4, W=4 * 65536)) == L.VSA_ERR_UNSUPPORTED
     # the per-row schedule must fit beside the tile ring in LDS (Nc = 4096)
