@@ -197,7 +197,10 @@ __device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int
   return ((b * m.N + n) * m.heads + h) * D;
 }
 
-template <int D, int RK, int RV>
+// PAD: the grid was padded up to whole cubes (the key masking of partial
+// tiles is compiled only into this variant, so the divisible case keeps its
+// loop as it is).
+template <int D, int RK, int RV, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           const int kb = k0 + ((a != 0xffffu && b != a) ? 1 : 0);
           d |= (uint32_t)(k0 % RK) | ((uint32_t)(kb % RK) << 4);
           d |= (a != 0xffffu ? 1u << 16 : 0u) | (b != 0xffffu ? 1u << 17 : 0u);
-          if (tmap.padded) {
+          if constexpr (PAD) {
             if (a != 0xffffu && cube_partial(tmap, (int)a)) d |= 1u << 30;
             if (b != 0xffffu && cube_partial(tmap, (int)b)) d |= 1u << 31;
           }
@@ -666,7 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       }
       // A key tile that reaches past the grid: its padded positions are not
       // keys (score -inf, so they add nothing to the row max or the sum).
-      if ((d_c >> (30 + grp)) & 1u) {
+      if (PAD && ((d_c >> (30 + grp)) & 1u)) {
         const uint32_t e = sched[p];
         const int32_t cube = __builtin_amdgcn_readfirstlane((int32_t)(grp == 0 ? (e & 0xffffu) : (e >> 16)));
         const uint64_t real = cube_mask(tmap, cube);   // bit l: position l is a real token
@@ -733,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
         }
       const int32_t my_tok = 32 * qh + n32;
-      if (lse != nullptr && g == 0 && my_valid && (!tmap.on || !tmap.padded || token_real(tmap, my_cube, my_tok))) {
+      if (lse != nullptr && g == 0 && my_valid && (!PAD || !tmap.on || token_real(tmap, my_cube, my_tok))) {
         const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
         lse[bh * (int64_t)(tmap.on ? tmap.N : tmap.Np) + token_pos(tmap, my_cube, my_tok)] = val;
       }
@@ -748,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;
         const int row = c / C::CPR, col = c % C::CPR;
-        if (tmap.on && tmap.padded && !token_real(tmap, my_cube, row)) continue;   // padding: no raster row
+        if (PAD && tmap.on && !token_real(tmap, my_cube, row)) continue;   // padding: no raster row
         const int64_t gidx = token_elem(tmap, bh, my_cube, row, D) + col * 8;
         float val[8];
         const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
@@ -786,12 +789,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
 // granted to each instantiation.
 struct DevState {
   int cus = 0;
-  int lds_granted[4] = {0, 0, 0, 0};
+  int lds_granted[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 };
 
 constexpr int kLdsMax = 160 * 1024;
 
-template <int D, int RK, int RV>
+template <int D, int RK, int RV, bool PAD>
 hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                        const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                        const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot,
@@ -801,7 +804,7 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   DevState& st = dev_state[dev];
-  auto kern = sparse_attn_fwd_kernel<D, RK, RV>;
+  auto kern = sparse_attn_fwd_kernel<D, RK, RV, PAD>;
   size_t lds = (size_t)(RK + RV) * C::TILE + sched_bytes;
   if (lds < (size_t)C::EPI_BYTES) lds = C::EPI_BYTES;
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
@@ -841,7 +844,7 @@ constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8
 
 // The deeper ring is used whenever the schedule (and the schedule build's
 // scratch, which lives in the ring) fits beside it in LDS.
-template <int D>
+template <int D, bool PAD>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                     const void* gate_f, void* out, float* lse, hipStream_t s, const TokenMap& tmap) {
@@ -852,13 +855,13 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   if (!sparse_attn_fwd_fits(g, max_kv)) return hipErrorInvalidValue;
   const size_t sched = sched_bytes(g, max_kv);
   const size_t build_scratch = 16 * (size_t)max_kv;   // SH, EXA, EXB, PK
-  const int base_slot = D == 128 ? 2 : 0;
+  const int base_slot = (D == 128 ? 2 : 0) + (PAD ? 4 : 0);
   if ((size_t)(RK_DEEP + RV_DEEP) * C::TILE + sched <= (size_t)kLdsMax &&
       build_scratch <= (size_t)(RK_DEEP + RV_DEEP) * C::TILE)
-    return launch_ring<D, RK_DEEP, RV_DEEP>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
+    return launch_ring<D, RK_DEEP, RV_DEEP, PAD>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
                                             sched, base_slot, tmap);
   if (build_scratch > (size_t)(2 * R_BASE) * C::TILE) return hipErrorInvalidValue;
-  return launch_ring<D, R_BASE, R_BASE>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, sched,
+  return launch_ring<D, R_BASE, R_BASE, PAD>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, sched,
                                         base_slot + 1, tmap);
 }
 
@@ -887,8 +890,10 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
   m.T = g.T; m.H = g.H; m.W = g.W;
   m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
   m.gH = g.gH; m.gW = g.gW;
-  if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
-  if (g.D == 64) return launch_d<64>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 128 && g.padded) return launch_d<128, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 128) return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 64 && g.padded) return launch_d<64, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 64) return launch_d<64, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   return hipErrorInvalidValue;
 }
 
