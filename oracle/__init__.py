@@ -9,5 +9,5 @@ from .vsa_oracle import (  # noqa: F401
     fine_attention_masked, fine_attention_bwd, combine, vsa_forward, mask_to_lut,
     combine_bwd, coarse_attention_bwd, pool_bwd, vsa_backward,
     kv_group, expand_kv_heads, reduce_kv_heads,
-    token_layout, gather_padded, scatter_padded, pool_real, pool_real_bwd,
+    token_layout, hilbert_index, cube_sequence, gather_padded, scatter_padded, pool_real, pool_real_bwd,
 )

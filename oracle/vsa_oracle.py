@@ -22,7 +22,7 @@ DESIGN.md):
 
 * R1 the "3D space-filling curve" order is cube-major: cubes in raster order
   over the cube grid, tokens in raster order inside a cube.
-* R2 grids must divide into whole cubes.
+* R2 a grid that does not divide into whole cubes is padded (R20).
 * R3 coarse attention is softmax(scale * Qc Kc^T) over all cubes with
   scale = 1/sqrt(d), and O_c = P_c Vc; Top-K ranks the same scores.
 * R4 each token of cube i receives O_c[i] (broadcast).
@@ -40,6 +40,10 @@ DESIGN.md):
   padded positions hold no token: they are never attended as keys, pooling
   averages the real tokens of a cube only, and only real tokens have
   outputs and gradients.
+* R21 optional Hilbert cube order: cubes follow the 3D Hilbert curve of
+  Skilling's transform over the smallest power-of-two cube that covers the
+  cube grid (axis t first), cells outside the grid skipped; tokens inside a
+  cube stay in raster order.  R1's raster cube order stays the default.
 * R19 grouped heads (K and V with fewer heads than Q, the head counts of the
   CK kernel interface in [VSA-ROCm]): query head h uses key/value head
   h // G with G = heads / kv_heads; equivalently every key/value head is
@@ -93,27 +97,82 @@ def perm_index(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> np.ndarray:
     return np.asarray(order, dtype=np.int64)
 
 
-def token_layout(T: int, H: int, W: int, ct: int, ch: int, cw: int) -> np.ndarray:
+def hilbert_index(t: int, h: int, w: int, bits: int) -> int:
+    """Distance of cell (t, h, w) along the 3D Hilbert curve that fills the
+    cube of side 2**bits (R21), by Skilling's transform ("Programming the
+    Hilbert curve", AIP Conference Proceedings 707, 2004).
+
+    Going down the levels from the coarsest, a coordinate whose bit is set
+    at the current level reflects the lower bits of the first coordinate,
+    otherwise the two exchange their lower bits; this undoes the rotations
+    and reflections of the sub-cubes.  The three coordinates are then
+    Gray-encoded together, and the distance reads their bits level by
+    level, most significant level first, t before h before w."""
+    x = [t, h, w]
+    level = 1 << (bits - 1)
+    while level > 1:
+        low = level - 1
+        for i in range(3):
+            if x[i] & level:
+                x[0] ^= low
+            else:
+                swap = (x[0] ^ x[i]) & low
+                x[0] ^= swap
+                x[i] ^= swap
+        level >>= 1
+    x[1] ^= x[0]
+    x[2] ^= x[1]
+    flip = 0
+    level = 1 << (bits - 1)
+    while level > 1:
+        if x[2] & level:
+            flip ^= level - 1
+        level >>= 1
+    x = [c ^ flip for c in x]
+    dist = 0
+    for b in range(bits - 1, -1, -1):
+        for i in range(3):
+            dist = (dist << 1) | ((x[i] >> b) & 1)
+    return dist
+
+
+def cube_sequence(gT: int, gH: int, gW: int, cube_order: str = "raster"):
+    """Grid coordinates (ct_i, ch_i, cw_i) of the cubes in cube-major order:
+    raster order over the cube grid (R1), or along the Hilbert curve of the
+    smallest power-of-two cube that covers it, skipping cells outside the
+    grid (R21)."""
+    cells = [(a, b, c) for a in range(gT) for b in range(gH) for c in range(gW)]
+    if cube_order == "raster":
+        return cells
+    if cube_order != "hilbert":
+        raise ValueError(f"cube_order {cube_order!r} is not 'raster' or 'hilbert'")
+    bits = 1
+    while (1 << bits) < max(gT, gH, gW):
+        bits += 1
+    return sorted(cells, key=lambda c: hilbert_index(*c, bits))
+
+
+def token_layout(T: int, H: int, W: int, ct: int, ch: int, cw: int,
+                 cube_order: str = "raster") -> np.ndarray:
     """Cube-major layout of a grid that need not divide into cubes (R20):
-    the grid is padded to whole cubes (ceil(T/ct)*ct, ...), cubes and tokens
-    are visited as in perm_index, and pi[p] is the raster index (in the
-    unpadded T x H x W grid) of the token at position p, or -1 where p is
-    padding.  Equals perm_index when the grid divides."""
+    the grid is padded to whole cubes (ceil(T/ct)*ct, ...), cubes are
+    visited in cube_sequence's order and tokens in raster order inside each
+    cube, and pi[p] is the raster index (in the unpadded T x H x W grid) of
+    the token at position p, or -1 where p is padding.  Equals perm_index
+    when the grid divides and the cube order is raster."""
     for name, n, c in (("T", T, ct), ("H", H, ch), ("W", W, cw)):
         if n <= 0 or c <= 0:
             raise ValueError(f"{name}={n}, cube={c}: sizes must be positive")
     order = []
-    for cube_t in range(-(-T // ct)):
-        for cube_h in range(-(-H // ch)):
-            for cube_w in range(-(-W // cw)):
-                for lt in range(ct):
-                    for lh in range(ch):
-                        for lw in range(cw):
-                            t = cube_t * ct + lt
-                            h = cube_h * ch + lh
-                            w = cube_w * cw + lw
-                            real = t < T and h < H and w < W
-                            order.append((t * H + h) * W + w if real else -1)
+    for cube_t, cube_h, cube_w in cube_sequence(-(-T // ct), -(-H // ch), -(-W // cw), cube_order):
+        for lt in range(ct):
+            for lh in range(ch):
+                for lw in range(cw):
+                    t = cube_t * ct + lt
+                    h = cube_h * ch + lh
+                    w = cube_w * cw + lw
+                    real = t < T and h < H and w < W
+                    order.append((t * H + h) * W + w if real else -1)
     return np.asarray(order, dtype=np.int64)
 
 
@@ -419,13 +478,16 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 gate_c: Optional[np.ndarray] = None,
                 gate_f: Optional[np.ndarray] = None,
                 kv_block_idx: Optional[np.ndarray] = None,
-                valid_block_num: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                valid_block_num: Optional[np.ndarray] = None,
+                cube_order: str = "raster") -> Dict[str, np.ndarray]:
     """VSA forward on raster inputs [B, heads, N, d]; returns every
     intermediate.  If a LUT is given it replaces the Top-K selection (used to
     score a kernel on exactly the LUT it was handed).  k and v may have fewer
     heads than q (R19); their intermediates are then returned expanded to
     the query heads.  A grid that does not divide into cubes is padded (R20):
-    pi holds -1 at padded cube-major positions."""
+    pi holds -1 at padded cube-major positions.  cube_order picks the order
+    of the cubes (R1 raster, or R21 Hilbert); cube indices in a given LUT
+    refer to that order."""
     T, H, W = grid
     ct, ch, cw = cube
     vol = ct * ch * cw
@@ -435,7 +497,7 @@ def vsa_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     v = expand_kv_heads(np.asarray(v, np.float64), group)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d)
-    pi = token_layout(T, H, W, ct, ch, cw)   # = perm_index when the grid divides
+    pi = token_layout(T, H, W, ct, ch, cw, cube_order)   # = perm_index for a divisible raster layout
     real = pi >= 0
     n = T * H * W
     qp, kp, vp = gather_padded(q, pi), gather_padded(k, pi), gather_padded(v, pi)
@@ -527,7 +589,7 @@ def pool_real_bwd(dxc: np.ndarray, vol: int, real: np.ndarray) -> np.ndarray:
 def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
                  kv_block_idx: np.ndarray, valid_block_num: np.ndarray,
                  dout: np.ndarray, gate_c: Optional[np.ndarray] = None,
-                 gate_f: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                 gate_f: Optional[np.ndarray] = None, cube_order: str = "raster") -> Dict[str, np.ndarray]:
     """Gradients of the whole layer (raster in, raster out) for the upstream
     gradient dout (raster), the LUT held fixed (R17): the forward's steps
     taken backwards -- reorder dout, combine, fine attention (through the
@@ -538,7 +600,7 @@ def vsa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, cube,
     give None)."""
     group = kv_group(np.asarray(q), np.asarray(k))
     f = vsa_forward(q, k, v, grid, cube, 0, gate_c=gate_c, gate_f=gate_f,
-                    kv_block_idx=kv_block_idx, valid_block_num=valid_block_num)
+                    kv_block_idx=kv_block_idx, valid_block_num=valid_block_num, cube_order=cube_order)
     pi = f["pi"]
     real = pi >= 0
     kv = None if real.all() else real

@@ -10,6 +10,7 @@ import pytest
 import oracle
 from oracle import vsa_oracle as vo
 import test_oracle_coarse as tc
+import test_oracle_curve as tcv
 import test_oracle_fine as tf
 import test_oracle_bwd as tb
 import test_oracle_full_bwd as tfb
@@ -23,6 +24,50 @@ from block_sparse_video_major_amd import workloads as wl
 _ORIG = {n: getattr(vo, n) for n in ("pool", "topk_lut", "fine_attention", "combine", "mask_to_lut",
                                      "fine_attention_bwd", "coarse_attention_bwd", "pool_bwd", "combine_bwd",
                                      "pool_real")}
+
+
+def _hilbert_variant(t, h, w, bits, gray=True, reflect_on_set=True, t_first=True):
+    """The oracle's transform with one planted change (see the callers)."""
+    x = [t, h, w]
+    level = 1 << (bits - 1)
+    while level > 1:
+        low = level - 1
+        for i in range(3):
+            if bool(x[i] & level) == reflect_on_set:
+                x[0] ^= low
+            else:
+                swap = (x[0] ^ x[i]) & low
+                x[0] ^= swap
+                x[i] ^= swap
+        level >>= 1
+    if gray:
+        x[1] ^= x[0]
+        x[2] ^= x[1]
+        flip = 0
+        level = 1 << (bits - 1)
+        while level > 1:
+            if x[2] & level:
+                flip ^= level - 1
+            level >>= 1
+        x = [c ^ flip for c in x]
+    order = (0, 1, 2) if t_first else (2, 1, 0)
+    dist = 0
+    for b in range(bits - 1, -1, -1):
+        for i in order:
+            dist = (dist << 1) | ((x[i] >> b) & 1)
+    return dist
+
+
+def _hilbert_no_gray(t, h, w, bits):
+    return _hilbert_variant(t, h, w, bits, gray=False)
+
+
+def _hilbert_branches_swapped(t, h, w, bits):
+    return _hilbert_variant(t, h, w, bits, reflect_on_set=False)
+
+
+def _hilbert_w_first(t, h, w, bits):
+    return _hilbert_variant(t, h, w, bits, t_first=False)
 
 
 def _raster_perm(T, H, W, ct, ch, cw):
@@ -158,6 +203,9 @@ def _pins():
     yield lambda: tg.test_dense_layer_equals_gqa_sdpa(4, 2)
     yield lambda: tpad.test_padded_dense_layer_equals_sdpa_on_real_tokens((5, 6, 7), (2, 2, 2))
     yield lambda: tpad.test_pool_averages_the_real_tokens_only()
+    yield lambda: tcv.test_hilbert_curve_is_a_unit_step_walk_through_the_cube(3)
+    yield lambda: tcv.test_aligned_subcubes_are_contiguous(3)
+    yield lambda: tcv.test_hilbert_token_layout_is_cube_major_along_the_curve((6, 7, 9), (4, 4, 4))
 
 
 MUTATIONS = {
@@ -182,6 +230,9 @@ MUTATIONS = {
     "grouped heads interleaved instead of repeated": ("expand_kv_heads", _expand_interleaved),
     "padded positions attended as keys": ("fine_attention", _fine_attends_padding),
     "padded cubes averaged over the full volume": ("pool_real", _pool_real_full_volume),
+    "Hilbert transform without the Gray encoding": ("hilbert_index", _hilbert_no_gray),
+    "Hilbert transform with reflect and exchange swapped": ("hilbert_index", _hilbert_branches_swapped),
+    "Hilbert bits interleaved w first": ("hilbert_index", _hilbert_w_first),
 }
 
 
