@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--top-k K]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -104,6 +105,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--cube-order", choices=("raster", "hilbert"), default="raster",
+                    help="order of the cubes in the timed step (the extras also time the Hilbert order)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the warm-up and timed steps (for counter runs on the step's kernels)")
     args = ap.parse_args()
@@ -128,7 +131,7 @@ def main() -> int:
     L.load()
 
     w = wl.WAN if args.top_k is None else wl.WAN.with_top_k(args.top_k)
-    p = vsa.Problem(w.batch, w.heads, w.T, w.H, w.W, *w.cube, w.head_dim)
+    p = vsa.Problem(w.batch, w.heads, w.T, w.H, w.W, *w.cube, w.head_dim, cube_order=args.cube_order)
     x = wl.make_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
@@ -139,7 +142,7 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
     B = L.VSA_BF16
 
-    def step(ev0=None, ev1=None):
+    def step(ev0=None, ev1=None, p=p, f=f):
         L.vsa_permute_pool(p, B, q, f.qp, f.qc, stream)
         L.vsa_permute_pool(p, B, k, f.kp, f.kc, stream)
         L.vsa_permute_pool(p, B, v, f.vp, f.vc, stream)
@@ -302,8 +305,42 @@ def main() -> int:
                 torch.cuda.synchronize()
                 for i, n in enumerate(lnames):
                     lt[n] += e[i].elapsed_time(e[i + 1]) / reps
-            del grads, ws, d_o, o_f, lse_f, bw, lgrads, gate_c, gate_f
-            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt
+            del bw, lgrads, gate_c, gate_f
+
+            # the same step and fine backward with the cubes in Hilbert order
+            # (same inputs; the LUT is the Hilbert-order coarse stage's own)
+            ph = dataclasses.replace(p, cube_order="hilbert")
+            fh = vsa.VsaForward(ph, w.top_k, dev)
+            for _ in range(2):
+                step(p=ph, f=fh)
+            torch.cuda.synchronize()
+            hs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            h0.record(stream)
+            for i in range(reps):
+                step(*hs[i], p=ph, f=fh)
+            h1.record(stream)
+            torch.cuda.synchronize()
+            h_step = h0.elapsed_time(h1) / reps
+            h_fine = float(np.mean([a.elapsed_time(b) for a, b in hs]))
+            L.vsa_sparse_attn_fwd(ph, fh.qp, fh.kp, fh.vp, fh.lut, fh.valid, o_f, lse=lse_f, stream=stream)
+
+            def hbwd():
+                L.vsa_sparse_attn_bwd(ph, fh.qp, fh.kp, fh.vp, fh.lut, fh.valid, o_f, lse_f, d_o, *grads, ws, stream)
+            hbwd()
+            torch.cuda.synchronize()
+            h_bwd = 0.0
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                hbwd()
+                e[1].record(stream)
+                torch.cuda.synchronize()
+                h_bwd += e[0].elapsed_time(e[1]) / reps
+            hil = {"step_ms": h_step, "fine_ms": h_fine, "bwd_ms": h_bwd,
+                   "pairs": int(fh.valid.sum().item())}
+            del grads, ws, d_o, o_f, lse_f, fh
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
@@ -332,7 +369,7 @@ def main() -> int:
         "config": {"workload": f"wan2.1-scale layer: grid 16x32x64 (32768 tokens), cube 4x4x4, 12 heads, "
                                f"d=128, Top-K {w.top_k} of 512 cubes ({w.sparsity:.1%} sparsity)",
                    "batch": w.batch, "heads": w.heads, "tokens": w.n_tokens, "head_dim": w.head_dim,
-                   "top_k": w.top_k, "n_cubes": w.n_cubes},
+                   "top_k": w.top_k, "n_cubes": w.n_cubes, "cube_order": args.cube_order},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "fine_ms_per_call": round(fine_avg, 4),
         "fine_tflops": round(achieved, 2),
@@ -342,7 +379,7 @@ def main() -> int:
                      "traffic": _measured_traffic()},
     }
     if ex is not None:
-        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt = ex
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil = ex
         rec.update({
             "stages_ms": {n: round(t, 4) for n, t in acc.items()},
             "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
@@ -364,6 +401,13 @@ def main() -> int:
                          "layer_ms": round(sum(lt.values()), 4),
                          "layer_stages_ms": {n: round(t, 4) for n, t in lt.items()},
                          "layer_note": "whole-layer backward with gates (VsaBackward steps), LUT fixed"},
+            "hilbert_order": {"note": "the same step and fine backward with the cubes in 3D Hilbert order",
+                              "ms_per_step": round(hil["step_ms"], 4),
+                              "tflops_per_step": round(flops / (hil["step_ms"] * 1e-3) / 1e12, 2),
+                              "fine_ms_per_call": round(hil["fine_ms"], 4),
+                              "fine_tflops": round(flops / (hil["fine_ms"] * 1e-3) / 1e12, 2),
+                              "bwd_ms_per_call": round(hil["bwd_ms"], 4),
+                              "bwd_tflops": round(2.5 * flops / (hil["bwd_ms"] * 1e-3) / 1e12, 2)},
         })
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -39,7 +39,13 @@ class VsaError(RuntimeError):
 
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim", "heads_kv")]
+                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim", "heads_kv", "cube_order")] + \
+               [("cube_coords", ctypes.c_void_p)]
+
+
+VSA_CUBES_RASTER, VSA_CUBES_HILBERT = 0, 1
+_CUBE_ORDERS = {"raster": VSA_CUBES_RASTER, "hilbert": VSA_CUBES_HILBERT}
+_tables: dict = {}   # (grid, cube, order, device) -> device table of packed cube coordinates
 
 
 @dataclasses.dataclass(frozen=True)
@@ -55,6 +61,7 @@ class Problem:
     cw: int = 4
     head_dim: int = 128
     heads_kv: int = 0          # key/value heads (grouped heads); 0 means heads
+    cube_order: str = "raster"   # "raster" or "hilbert": the order of the cubes
 
     @property
     def n_tokens(self) -> int:
@@ -93,9 +100,19 @@ class Problem:
         reorders and pools)."""
         return dataclasses.replace(self, heads=self.kv_heads, heads_kv=0)
 
-    def c_struct(self) -> _Problem:
-        return _Problem(self.batch, self.heads, self.T, self.H, self.W,
-                        self.ct, self.ch, self.cw, self.head_dim, self.heads_kv)
+    def c_struct(self, device=None) -> _Problem:
+        """The C struct; with the Hilbert order and a device, cube_coords
+        points at that device's copy of vsa_cube_table's table (made once
+        per grid and device, then kept)."""
+        if self.cube_order not in _CUBE_ORDERS:
+            raise ValueError(f"cube_order {self.cube_order!r} is not one of {sorted(_CUBE_ORDERS)}")
+        order = _CUBE_ORDERS[self.cube_order]
+        st = _Problem(self.batch, self.heads, self.T, self.H, self.W,
+                      self.ct, self.ch, self.cw, self.head_dim, self.heads_kv, order, None)
+        if order != VSA_CUBES_RASTER and device is not None and torch.device(device).type == "cuda":
+            st.cube_coords = _cube_table(self, torch.device(device)).data_ptr()
+        return st
+
 
 
 _lib = None
@@ -133,6 +150,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd_bnhd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_pool_unpermute_bwd_bnhd": [P, vp, vp, vp, vp],
         "vsa_perm_index": [P, vp],
+        "vsa_cube_table": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
     }
@@ -142,6 +160,26 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_char_p if name == "vsa_status_str" else ctypes.c_int
     _lib = lib
     return lib
+
+
+def vsa_cube_table(p: "Problem") -> torch.Tensor:
+    """Packed grid coordinates (t << 20 | h << 10 | w) of the cubes in p's
+    cube order (host int32 tensor of n_cubes)."""
+    out = torch.empty(p.n_cubes, dtype=torch.int32)
+    _check(load().vsa_cube_table(ctypes.byref(p.c_struct()), out.data_ptr()), "vsa_cube_table")
+    return out
+
+
+def _cube_table(p: "Problem", device: torch.device) -> torch.Tensor:
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    key = (p.T, p.H, p.W, p.ct, p.ch, p.cw, p.cube_order, str(device))
+    t = _tables.get(key)
+    if t is None:
+        t = vsa_cube_table(p).to(device)
+        torch.cuda.synchronize(device)
+        _tables[key] = t
+    return t
 
 
 def vsa_status_str(status: int) -> str:
@@ -231,7 +269,7 @@ def vsa_permute(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: torch.Te
     td = _token_dtype(dtype)
     _need(x_raster, "x_raster", _tok_shape(p), td)
     _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
-    _check(load().vsa_permute(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube),
+    _check(load().vsa_permute(ctypes.byref(p.c_struct(x_raster.device)), dtype, _ptr(x_raster), _ptr(x_cube),
                               _stream(stream, x_raster.device)), "vsa_permute")
 
 
@@ -239,14 +277,14 @@ def vsa_unpermute(p: Problem, dtype: int, x_cube: torch.Tensor, x_raster: torch.
     td = _token_dtype(dtype)
     _need(x_cube, "x_cube", _pos_shape(p), td)
     _need(x_raster, "x_raster", _tok_shape(p), td, x_cube.device)
-    _check(load().vsa_unpermute(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(x_raster),
+    _check(load().vsa_unpermute(ctypes.byref(p.c_struct(x_cube.device)), dtype, _ptr(x_cube), _ptr(x_raster),
                                 _stream(stream, x_cube.device)), "vsa_unpermute")
 
 
 def vsa_pool(p: Problem, dtype: int, x_cube: torch.Tensor, xc: torch.Tensor, stream=None) -> None:
     _need(x_cube, "x_cube", _pos_shape(p), _token_dtype(dtype))
     _need(xc, "xc", _cube_shape(p), torch.float32, x_cube.device)
-    _check(load().vsa_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_cube), _ptr(xc),
+    _check(load().vsa_pool(ctypes.byref(p.c_struct(x_cube.device)), dtype, _ptr(x_cube), _ptr(xc),
                            _stream(stream, x_cube.device)), "vsa_pool")
 
 
@@ -256,7 +294,7 @@ def vsa_permute_pool(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: tor
     _need(x_raster, "x_raster", _tok_shape(p), td)
     _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_raster.device)
-    _check(load().vsa_permute_pool(ctypes.byref(p.c_struct()), dtype, _ptr(x_raster), _ptr(x_cube), _ptr(xc),
+    _check(load().vsa_permute_pool(ctypes.byref(p.c_struct(x_raster.device)), dtype, _ptr(x_raster), _ptr(x_cube), _ptr(xc),
                                    _stream(stream, x_raster.device)), "vsa_permute_pool")
 
 
@@ -272,7 +310,7 @@ def vsa_coarse_topk(p: Problem, top_k: int, qc: torch.Tensor, kc: torch.Tensor, 
         _need(oc, "oc", _cube_shape(p), torch.float32, dev)
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, top_k), torch.int32, dev)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
-    _check(load().vsa_coarse_topk(ctypes.byref(p.c_struct()), int(top_k), _ptr(qc), _ptr(kc), _ptr(vc),
+    _check(load().vsa_coarse_topk(ctypes.byref(p.c_struct(dev)), int(top_k), _ptr(qc), _ptr(kc), _ptr(vc),
                                   _ptr(kv_block_idx), _ptr(valid_block_num), _ptr(oc),
                                   _stream(stream, dev)), "vsa_coarse_topk")
 
@@ -325,7 +363,7 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
         _need(lse, "lse", (p.batch, p.heads, p.n_positions if raster is False else p.n_tokens), torch.float32, dev)
     name = {"bnhd": "vsa_sparse_attn_fwd_bnhd", True: "vsa_sparse_attn_fwd_raster",
             False: "vsa_sparse_attn_fwd"}[raster]
-    _check(getattr(load(), name)(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
+    _check(getattr(load(), name)(ctypes.byref(p.c_struct(dev)), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
                                  _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
                                  _stream(stream, dev)), name)
@@ -340,7 +378,7 @@ def vsa_check_lut(p: Problem, kv_block_idx: torch.Tensor, valid_block_num: torch
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
     _need(bad_rows, "bad_rows", (1,), torch.int32, dev)
-    _check(load().vsa_check_lut(ctypes.byref(p.c_struct()), _ptr(kv_block_idx), _ptr(valid_block_num),
+    _check(load().vsa_check_lut(ctypes.byref(p.c_struct(dev)), _ptr(kv_block_idx), _ptr(valid_block_num),
                                 int(max_kv), _ptr(bad_rows), _stream(stream, dev)), "vsa_check_lut")
 
 
@@ -355,7 +393,7 @@ def vsa_mask_to_lut(p: Problem, mask: torch.Tensor, kv_block_idx: torch.Tensor, 
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
     _need(overflow_rows, "overflow_rows", (1,), torch.int32, dev)
-    _check(load().vsa_mask_to_lut(ctypes.byref(p.c_struct()), _ptr(mask), int(max_kv), _ptr(kv_block_idx),
+    _check(load().vsa_mask_to_lut(ctypes.byref(p.c_struct(dev)), _ptr(mask), int(max_kv), _ptr(kv_block_idx),
                                   _ptr(valid_block_num), _ptr(overflow_rows), _stream(stream, dev)),
            "vsa_mask_to_lut")
 
@@ -392,7 +430,7 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D byte tensor")
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
-    _check(load().vsa_sparse_attn_bwd(ctypes.byref(p.c_struct()), _ptr(q), _ptr(k), _ptr(v),
+    _check(load().vsa_sparse_attn_bwd(ctypes.byref(p.c_struct(dev)), _ptr(q), _ptr(k), _ptr(v),
                                       _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
                                       _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       int(workspace.numel()), _stream(stream, dev)), "vsa_sparse_attn_bwd")
@@ -415,7 +453,7 @@ def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: to
     for name, t in (("oc", oc), ("d_oc", d_oc)):
         if t is not None:
             _need(t, name, cs, torch.float32, dev)
-    _check(load().vsa_combine_bwd(ctypes.byref(p.c_struct()), _ptr(dout), _ptr(o_f), _ptr(oc), _ptr(gate_c),
+    _check(load().vsa_combine_bwd(ctypes.byref(p.c_struct(dev)), _ptr(dout), _ptr(o_f), _ptr(oc), _ptr(gate_c),
                                   _ptr(gate_f), _ptr(d_of), _ptr(d_oc), _ptr(d_gate_c), _ptr(d_gate_f),
                                   _stream(stream, dev)), "vsa_combine_bwd")
 
@@ -440,7 +478,7 @@ def vsa_coarse_bwd(p: Problem, qc: torch.Tensor, kc: torch.Tensor, vc: torch.Ten
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D byte tensor")
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
-    _check(load().vsa_coarse_bwd(ctypes.byref(p.c_struct()), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(oc), _ptr(d_oc),
+    _check(load().vsa_coarse_bwd(ctypes.byref(p.c_struct(dev)), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(oc), _ptr(d_oc),
                                  _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(workspace), int(workspace.numel()),
                                  _stream(stream, dev)), "vsa_coarse_bwd")
 
@@ -453,7 +491,7 @@ def vsa_pool_unpermute_bwd(p: Problem, dx_cube: torch.Tensor, dxc: Optional[torc
     _need(dx_raster, "dx_raster", _tok_shape(p), torch.float32, dev)
     if dxc is not None:
         _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
-    _check(load().vsa_pool_unpermute_bwd(ctypes.byref(p.c_struct()), _ptr(dx_cube), _ptr(dxc), _ptr(dx_raster),
+    _check(load().vsa_pool_unpermute_bwd(ctypes.byref(p.c_struct(dev)), _ptr(dx_cube), _ptr(dxc), _ptr(dx_raster),
                                          _stream(stream, dev)), "vsa_pool_unpermute_bwd")
 
 
@@ -462,7 +500,7 @@ def vsa_permute_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch
     td = _token_dtype(dtype)
     _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
     _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
-    _check(load().vsa_permute_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube),
+    _check(load().vsa_permute_bnhd(ctypes.byref(p.c_struct(x_bnhd.device)), dtype, _ptr(x_bnhd), _ptr(x_cube),
                                    _stream(stream, x_bnhd.device)), "vsa_permute_bnhd")
 
 
@@ -473,7 +511,7 @@ def vsa_permute_pool_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: 
     _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
     _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_bnhd.device)
-    _check(load().vsa_permute_pool_bnhd(ctypes.byref(p.c_struct()), dtype, _ptr(x_bnhd), _ptr(x_cube), _ptr(xc),
+    _check(load().vsa_permute_pool_bnhd(ctypes.byref(p.c_struct(x_bnhd.device)), dtype, _ptr(x_bnhd), _ptr(x_cube), _ptr(xc),
                                         _stream(stream, x_bnhd.device)), "vsa_permute_pool_bnhd")
 
 
@@ -485,5 +523,5 @@ def vsa_pool_unpermute_bwd_bnhd(p: Problem, dx_cube: torch.Tensor, dxc: Optional
     _need(dx_bnhd, "dx_bnhd", _bnhd_shape(p), torch.float32, dev)
     if dxc is not None:
         _need(dxc, "dxc", _cube_shape(p), torch.float32, dev)
-    _check(load().vsa_pool_unpermute_bwd_bnhd(ctypes.byref(p.c_struct()), _ptr(dx_cube), _ptr(dxc), _ptr(dx_bnhd),
+    _check(load().vsa_pool_unpermute_bwd_bnhd(ctypes.byref(p.c_struct(dev)), _ptr(dx_cube), _ptr(dxc), _ptr(dx_bnhd),
                                               _stream(stream, dev)), "vsa_pool_unpermute_bwd_bnhd")

@@ -17,6 +17,9 @@
 // d = 128).  All index arithmetic is 32-bit within a (batch, head) and done
 // once per row, so the kernels stay HBM-bound.
 //
+// Cubes are numbered in the problem's cube order: raster over the cube grid,
+// or a table of packed grid coordinates (one read per cube).
+//
 // A grid that does not divide into cubes is padded up to whole cubes: padded
 // positions are written as zeros on the cube-major side, have no raster row,
 // and are left out of the cube mean (which divides by the real-token count).
@@ -82,7 +85,8 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 struct CubeArgs {
   int32_t T, H, W;        // token grid
   int32_t ct, ch, cw;     // cube edges
-  int32_t gH, gW;         // cube grid
+  int32_t gT, gH, gW;     // cube grid
+  const int32_t* coords;  // packed coordinates of each cube (Hilbert order), or null (raster order)
   int32_t vol;            // positions per cube
   int32_t N;              // real tokens per (batch, head): raster rows
   int32_t Np;             // cube-major positions per (batch, head)
@@ -126,9 +130,18 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
   for (int64_t unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
     const int64_t bh = unit / a.Nc;
     const int32_t c = (int32_t)(unit - bh * a.Nc);
-    const int32_t cw_i = c % a.gW;
-    const int32_t ch_i = (c / a.gW) % a.gH;
-    const int32_t ct_i = c / (a.gW * a.gH);
+    int32_t ct_i, ch_i, cw_i;
+    if (a.coords != nullptr) {
+      const int32_t e = a.coords[c];   // the same for the whole workgroup
+      ct_i = (e >> 20) & 1023;
+      ch_i = (e >> 10) & 1023;
+      cw_i = e & 1023;
+      if (ct_i >= a.gT || ch_i >= a.gH || cw_i >= a.gW) continue;   // not a table for this grid
+    } else {
+      cw_i = c % a.gW;
+      ch_i = (c / a.gW) % a.gH;
+      ct_i = c / (a.gW * a.gH);
+    }
     // raster side: row of token n of this (batch, head) is rbase + n * tstride
     int64_t rbase = bh * (int64_t)a.N, tstride = 1;
     if (a.bnhd) {
@@ -224,7 +237,8 @@ CubeArgs cube_args(const Geom& g, RasterLayout layout) {
   a.bnhd = layout == kBNHD ? 1 : 0;
   a.T = g.T; a.H = g.H; a.W = g.W;
   a.ct = g.ct; a.ch = g.ch; a.cw = g.cw;
-  a.gH = g.gH; a.gW = g.gW;
+  a.gT = g.gT; a.gH = g.gH; a.gW = g.gW;
+  a.coords = g.coords;
   a.vol = g.vol;
   a.N = (int32_t)g.N;
   a.Np = (int32_t)g.Np;

@@ -143,27 +143,53 @@ struct TokenMap {
   int32_t bnhd;
   int32_t T, H, W;      // token grid (frames, rows and columns of a frame)
   int32_t ct, ch, cw;   // cube edges
-  int32_t gH, gW;       // cube grid
+  int32_t gT, gH, gW;   // cube grid
+  const int32_t* coords;  // packed grid coordinates of each cube (Hilbert order), or null (raster)
   int32_t heads;        // heads per batch entry
   int32_t N;            // real tokens per (batch, head): raster rows
   int32_t Np;           // cube-major positions per (batch, head)
   int32_t padded;       // the grid was padded up to whole cubes
 };
 
-// Whether position l of cube c holds a real token (not padding).
-__device__ __forceinline__ bool token_real(const TokenMap& m, int32_t c, int32_t l) {
-  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
+// Grid coordinates of cube c: raster order over the cube grid, or the
+// problem's table of packed coordinates.  A table entry outside the grid
+// (a table written for another problem) marks the cube invalid: it then has
+// no real token, so it is never read as keys or written in raster order.
+struct CubeAt {
+  int32_t t, h, w;
+  bool ok;
+};
+
+__device__ __forceinline__ CubeAt cube_at(const TokenMap& m, int32_t c) {
+  CubeAt r;
+  if (m.coords != nullptr) {
+    const int32_t e = m.coords[c];
+    r.t = (e >> 20) & 1023;
+    r.h = (e >> 10) & 1023;
+    r.w = e & 1023;
+    r.ok = r.t < m.gT && r.h < m.gH && r.w < m.gW;
+  } else {
+    r.w = c % m.gW;
+    r.h = (c / m.gW) % m.gH;
+    r.t = c / (m.gW * m.gH);
+    r.ok = true;
+  }
+  return r;
+}
+
+// Whether position l of cube q holds a real token (not padding).
+__device__ __forceinline__ bool token_real(const TokenMap& m, const CubeAt& q, int32_t l) {
   const int32_t plane = m.ch * m.cw;
   const int32_t lt = l / plane, rem = l - lt * plane;
   const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
-  return ct_i * m.ct + lt < m.T && ch_i * m.ch + lh < m.H && cw_i * m.cw + lw < m.W;
+  return q.ok && q.t * m.ct + lt < m.T && q.h * m.ch + lh < m.H && q.w * m.cw + lw < m.W;
 }
 
-// Bit l set when position l of cube c holds a real token.  The cube edges
+// Bit l set when position l of cube q holds a real token.  The cube edges
 // multiply to 64 positions; tokens run w fastest, then h, then t.
-__device__ __forceinline__ uint64_t cube_mask(const TokenMap& m, int32_t c) {
-  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
-  const int32_t rt = min(m.ct, m.T - ct_i * m.ct), rh = min(m.ch, m.H - ch_i * m.ch), rw = min(m.cw, m.W - cw_i * m.cw);
+__device__ __forceinline__ uint64_t cube_mask(const TokenMap& m, const CubeAt& q) {
+  if (!q.ok) return 0;
+  const int32_t rt = min(m.ct, m.T - q.t * m.ct), rh = min(m.ch, m.H - q.h * m.ch), rw = min(m.cw, m.W - q.w * m.cw);
   const uint64_t row = rw >= 64 ? ~0ull : ((1ull << rw) - 1);
   uint64_t plane = 0, all = 0;
   for (int32_t h = 0; h < rh; ++h) plane |= row << (h * m.cw);
@@ -171,26 +197,26 @@ __device__ __forceinline__ uint64_t cube_mask(const TokenMap& m, int32_t c) {
   return all;
 }
 
-// Whether cube c reaches past the grid (holds padded positions).
-__device__ __forceinline__ bool cube_partial(const TokenMap& m, int32_t c) {
-  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
-  return (ct_i + 1) * m.ct > m.T || (ch_i + 1) * m.ch > m.H || (cw_i + 1) * m.cw > m.W;
+// Whether cube q reaches past the grid (holds padded positions).
+__device__ __forceinline__ bool cube_partial(const TokenMap& m, const CubeAt& q) {
+  return !q.ok || (q.t + 1) * m.ct > m.T || (q.h + 1) * m.ch > m.H || (q.w + 1) * m.cw > m.W;
 }
 
-// Position of token l (< 64) of cube c within its (batch, head) in the
-// order the map selects.
-__device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, int32_t l) {
+// Position of token l (< 64) of cube c (coordinates q) within its (batch,
+// head) in the order the map selects.
+__device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, const CubeAt& q, int32_t l) {
   if (!m.on) return c * kBlk + l;
-  const int32_t cw_i = c % m.gW, ch_i = (c / m.gW) % m.gH, ct_i = c / (m.gW * m.gH);
   const int32_t plane = m.ch * m.cw;
   const int32_t lt = l / plane, rem = l - lt * plane;
   const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
-  return ((ct_i * m.ct + lt) * m.H + ch_i * m.ch + lh) * m.W + cw_i * m.cw + lw;
+  return ((q.t * m.ct + lt) * m.H + q.h * m.ch + lh) * m.W + q.w * m.cw + lw;
 }
 
-// Element offset of token l of cube c of (batch, head) bh in out and the gates.
-__device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int32_t c, int32_t l, int D) {
-  const int64_t n = token_pos(m, c, l);
+// Element offset of token l of cube c (coordinates q) of (batch, head) bh in
+// out and the gates.
+__device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int32_t c, const CubeAt& q, int32_t l,
+                                              int D) {
+  const int64_t n = token_pos(m, c, q, l);
   if (!m.on) return (bh * m.Np + n) * D;
   if (!m.bnhd) return (bh * m.N + n) * D;
   const int64_t b = bh / m.heads, h = bh - b * m.heads;
@@ -483,8 +509,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           d |= (uint32_t)(k0 % RK) | ((uint32_t)(kb % RK) << 4);
           d |= (a != 0xffffu ? 1u << 16 : 0u) | (b != 0xffffu ? 1u << 17 : 0u);
           if constexpr (PAD) {
-            if (a != 0xffffu && cube_partial(tmap, (int)a)) d |= 1u << 30;
-            if (b != 0xffffu && cube_partial(tmap, (int)b)) d |= 1u << 31;
+            if (a != 0xffffu && cube_partial(tmap, cube_at(tmap, (int)a))) d |= 1u << 30;
+            if (b != 0xffffu && cube_partial(tmap, cube_at(tmap, (int)b))) d |= 1u << 31;
           }
         }
         if (pp > 0) {
@@ -672,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       if (PAD && ((d_c >> (30 + grp)) & 1u)) {
         const uint32_t e = sched[p];
         const int32_t cube = __builtin_amdgcn_readfirstlane((int32_t)(grp == 0 ? (e & 0xffffu) : (e >> 16)));
-        const uint64_t real = cube_mask(tmap, cube);   // bit l: position l is a real token
+        const uint64_t real = cube_mask(tmap, cube_at(tmap, cube));   // bit l: position l is a real token
         // this lane's keys 32*kh + 4*g + 8*q + j (q, j < 4) are bits 8*q + j of m
         const uint64_t m = real >> (32 * kh + 4 * g);
 #pragma unroll
@@ -736,14 +762,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
         }
       const int32_t my_tok = 32 * qh + n32;
-      if (lse != nullptr && g == 0 && my_valid && (!PAD || !tmap.on || token_real(tmap, my_cube, my_tok))) {
+      const CubeAt mq = tmap.on ? cube_at(tmap, my_cube) : CubeAt{0, 0, 0, true};
+      if (lse != nullptr && g == 0 && my_valid && mq.ok && (!PAD || !tmap.on || token_real(tmap, mq, my_tok))) {
         const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-        lse[bh * (int64_t)(tmap.on ? tmap.N : tmap.Np) + token_pos(tmap, my_cube, my_tok)] = val;
+        lse[bh * (int64_t)(tmap.on ? tmap.N : tmap.Np) + token_pos(tmap, my_cube, mq, my_tok)] = val;
       }
     }
     __syncthreads();
 
-    if (my_valid) {
+    const CubeAt mq = tmap.on ? cube_at(tmap, my_cube) : CubeAt{0, 0, 0, true};
+    if (my_valid && mq.ok) {
       const int64_t my_row = rowA + grp;
       const float* ocrow = oc ? oc + my_row * (int64_t)D : nullptr;
       const int gt = tid & 255;   // thread index within the half
@@ -751,8 +779,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;
         const int row = c / C::CPR, col = c % C::CPR;
-        if (PAD && tmap.on && !token_real(tmap, my_cube, row)) continue;   // padding: no raster row
-        const int64_t gidx = token_elem(tmap, bh, my_cube, row, D) + col * 8;
+        if (PAD && tmap.on && !token_real(tmap, mq, row)) continue;   // padding: no raster row
+        const int64_t gidx = token_elem(tmap, bh, my_cube, mq, row, D) + col * 8;
         float val[8];
         const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
         const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
@@ -889,7 +917,8 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
   m.padded = g.padded;
   m.T = g.T; m.H = g.H; m.W = g.W;
   m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
-  m.gH = g.gH; m.gW = g.gW;
+  m.gT = g.gT; m.gH = g.gH; m.gW = g.gW;
+  m.coords = g.coords;
   if (g.D == 128 && g.padded) return launch_d<128, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   if (g.D == 128) return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   if (g.D == 64 && g.padded) return launch_d<64, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);

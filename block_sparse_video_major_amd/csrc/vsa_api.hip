@@ -7,13 +7,15 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "vsa_internal.h"
 
 namespace {
 
 using vsa::Geom;
 
-int check_problem(const vsa_problem* p) {
+int check_problem(const vsa_problem* p, bool need_table = true) {
   if (p == nullptr) return VSA_ERR_NULL;
   if (p->batch <= 0 || p->heads <= 0 || p->T <= 0 || p->H <= 0 || p->W <= 0 || p->ct <= 0 ||
       p->ch <= 0 || p->cw <= 0 || p->head_dim <= 0)
@@ -28,7 +30,65 @@ int check_problem(const vsa_problem* p) {
   // every element index must fit comfortably in int64 and every launch grid in 2^31 blocks
   if (bh * n > ((int64_t)1 << 40)) return VSA_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return VSA_ERR_UNSUPPORTED;
+  if (p->cube_order != VSA_CUBES_RASTER && p->cube_order != VSA_CUBES_HILBERT) return VSA_ERR_UNSUPPORTED;
+  if (p->cube_order == VSA_CUBES_HILBERT) {
+    const int64_t sides[3] = {(p->T + (int64_t)p->ct - 1) / p->ct, (p->H + (int64_t)p->ch - 1) / p->ch,
+                              (p->W + (int64_t)p->cw - 1) / p->cw};
+    for (int64_t s : sides)
+      if (s > 1024) return VSA_ERR_UNSUPPORTED;   // 10 bits per packed coordinate
+    if (need_table && p->cube_coords == nullptr) return VSA_ERR_NULL;
+  }
   return VSA_OK;
+}
+
+// Distance of cell (t, h, w) along the 3D Hilbert curve that fills the cube
+// of side 2^bits (Skilling, "Programming the Hilbert curve", 2004).  From
+// the coarsest level down, a coordinate whose bit is set at that level
+// reflects the lower bits of t, otherwise t and that coordinate exchange
+// their lower bits (undoing the sub-cubes' rotations and reflections); the
+// three are then Gray-encoded together, and the distance takes their bits
+// level by level from the top, t before h before w.
+uint32_t hilbert_distance(uint32_t t, uint32_t h, uint32_t w, int bits) {
+  uint32_t x[3] = {t, h, w};
+  for (uint32_t level = 1u << (bits - 1); level > 1; level >>= 1) {
+    const uint32_t low = level - 1;
+    for (int i = 0; i < 3; ++i) {
+      if (x[i] & level) {
+        x[0] ^= low;
+      } else {
+        const uint32_t swap = (x[0] ^ x[i]) & low;
+        x[0] ^= swap;
+        x[i] ^= swap;
+      }
+    }
+  }
+  x[1] ^= x[0];
+  x[2] ^= x[1];
+  uint32_t flip = 0;
+  for (uint32_t level = 1u << (bits - 1); level > 1; level >>= 1)
+    if (x[2] & level) flip ^= level - 1;
+  for (uint32_t& c : x) c ^= flip;
+  uint32_t dist = 0;
+  for (int b = bits - 1; b >= 0; --b)
+    for (int i = 0; i < 3; ++i) dist = (dist << 1) | ((x[i] >> b) & 1u);
+  return dist;
+}
+
+// out[c] = packed grid coordinates (t << 20 | h << 10 | w) of the c-th cube
+// in the problem's cube order; every side at most 1024 (checked by the
+// caller).  Sorted in place by curve distance: no allocation.
+void fill_cube_table(const Geom& g, int order, int32_t* out) {
+  int32_t c = 0;
+  for (int32_t t = 0; t < g.gT; ++t)
+    for (int32_t h = 0; h < g.gH; ++h)
+      for (int32_t w = 0; w < g.gW; ++w) out[c++] = (t << 20) | (h << 10) | w;
+  if (order == VSA_CUBES_RASTER) return;
+  int bits = 1;
+  while ((1 << bits) < std::max(g.gT, std::max(g.gH, g.gW))) ++bits;
+  const auto dist = [bits](int32_t e) {
+    return hilbert_distance((uint32_t)(e >> 20) & 1023u, (uint32_t)(e >> 10) & 1023u, (uint32_t)e & 1023u, bits);
+  };
+  std::sort(out, out + c, [&](int32_t a, int32_t b) { return dist(a) < dist(b); });
 }
 
 int check_dtype(int32_t dtype) {
@@ -41,7 +101,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (2 << 16) | 0; }
+int vsa_abi_version(void) { return (3 << 16) | 0; }
 
 const char* vsa_status_str(int status) {
   switch (status) {
@@ -49,7 +109,7 @@ const char* vsa_status_str(int status) {
     case VSA_ERR_NULL: return "required pointer is NULL";
     case VSA_ERR_SHAPE: return "invalid shape (non-positive size, heads_kv not dividing heads, or too large)";
     case VSA_ERR_TOPK: return "top_k / max_kv_blocks outside [1, Nc]";
-    case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume or cube count";
+    case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume, cube count or cube order";
     case VSA_ERR_HIP: return "HIP runtime error at launch";
     case VSA_ERR_LUT: return "invalid LUT";
     case VSA_ERR_WORKSPACE: return "workspace smaller than vsa_sparse_attn_bwd_workspace_size reports";
@@ -58,22 +118,51 @@ const char* vsa_status_str(int status) {
 }
 
 int vsa_perm_index(const vsa_problem* p, int32_t* perm_host) {
-  int st = check_problem(p);
+  int st = check_problem(p, false);
   if (st != VSA_OK) return st;
   if (perm_host == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  int64_t pos = 0;
-  for (int ct_i = 0; ct_i < g.gT; ++ct_i)
-    for (int ch_i = 0; ch_i < g.gH; ++ch_i)
-      for (int cw_i = 0; cw_i < g.gW; ++cw_i)
-        for (int lt = 0; lt < g.ct; ++lt)
-          for (int lh = 0; lh < g.ch; ++lh)
-            for (int lw = 0; lw < g.cw; ++lw) {
-              const int64_t t = (int64_t)ct_i * g.ct + lt, h = (int64_t)ch_i * g.ch + lh,
-                            w = (int64_t)cw_i * g.cw + lw;
-              const bool real = t < g.T && h < g.H && w < g.W;
-              perm_host[pos++] = real ? (int32_t)((t * g.H + h) * g.W + w) : -1;
-            }
+  if (p->cube_order == VSA_CUBES_RASTER) {
+    int64_t pos = 0;
+    for (int ct_i = 0; ct_i < g.gT; ++ct_i)
+      for (int ch_i = 0; ch_i < g.gH; ++ch_i)
+        for (int cw_i = 0; cw_i < g.gW; ++cw_i)
+          for (int lt = 0; lt < g.ct; ++lt)
+            for (int lh = 0; lh < g.ch; ++lh)
+              for (int lw = 0; lw < g.cw; ++lw) {
+                const int64_t t = (int64_t)ct_i * g.ct + lt, h = (int64_t)ch_i * g.ch + lh,
+                              w = (int64_t)cw_i * g.cw + lw;
+                const bool real = t < g.T && h < g.H && w < g.W;
+                perm_host[pos++] = real ? (int32_t)((t * g.H + h) * g.W + w) : -1;
+              }
+    return VSA_OK;
+  }
+  // The cube table goes into the first Nc entries; cubes are then expanded
+  // from the last one down.  Cube c's vol positions start at c*vol >= c, so
+  // entries of cubes not yet expanded are never overwritten first.
+  fill_cube_table(g, p->cube_order, perm_host);
+  for (int64_t c = g.Nc - 1; c >= 0; --c) {
+    const int32_t e = perm_host[c];
+    const int64_t ct_i = (e >> 20) & 1023, ch_i = (e >> 10) & 1023, cw_i = e & 1023;
+    int64_t pos = c * g.vol;
+    for (int lt = 0; lt < g.ct; ++lt)
+      for (int lh = 0; lh < g.ch; ++lh)
+        for (int lw = 0; lw < g.cw; ++lw) {
+          const int64_t t = ct_i * g.ct + lt, h = ch_i * g.ch + lh, w = cw_i * g.cw + lw;
+          const bool real = t < g.T && h < g.H && w < g.W;
+          perm_host[pos++] = real ? (int32_t)((t * g.H + h) * g.W + w) : -1;
+        }
+  }
+  return VSA_OK;
+}
+
+int vsa_cube_table(const vsa_problem* p, int32_t* coords_host) {
+  int st = check_problem(p, false);
+  if (st != VSA_OK) return st;
+  if (coords_host == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (g.gT > 1024 || g.gH > 1024 || g.gW > 1024) return VSA_ERR_UNSUPPORTED;
+  fill_cube_table(g, p->cube_order, coords_host);
   return VSA_OK;
 }
 
@@ -192,8 +281,8 @@ int vsa_permute_pool_bnhd(const vsa_problem* p, int32_t dtype, const void* x_bnh
 }
 
 namespace {
-int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks) {
-  int st = check_problem(p);
+int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks, bool need_table = true) {
+  int st = check_problem(p, need_table);
   if (st != VSA_OK) return st;
   const Geom g = vsa::make_geom(*p);
   if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
@@ -205,7 +294,7 @@ int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks) {
 
 int vsa_sparse_attn_bwd_workspace_size(const vsa_problem* p, int32_t max_kv_blocks, size_t* bytes) {
   if (bytes == nullptr) return VSA_ERR_NULL;
-  const int st = sparse_attn_bwd_check(p, max_kv_blocks);
+  const int st = sparse_attn_bwd_check(p, max_kv_blocks, false);
   if (st != VSA_OK) return st;
   *bytes = vsa::sparse_attn_bwd_workspace(vsa::make_geom(*p), max_kv_blocks);
   return VSA_OK;
@@ -240,7 +329,7 @@ int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f, con
 }
 
 int vsa_coarse_bwd_workspace_size(const vsa_problem* p, size_t* bytes) {
-  int st = check_problem(p);
+  int st = check_problem(p, false);
   if (st != VSA_OK) return st;
   if (bytes == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);

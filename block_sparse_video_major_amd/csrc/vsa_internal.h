@@ -22,6 +22,7 @@ struct Geom {
   int64_t Np;             // cube-major positions per (batch, head): Nc * vol
   int64_t Nc;             // cubes per (batch, head)
   int32_t padded;         // Np != N
+  const int32_t* coords;  // device table of packed cube coordinates (Hilbert order), or null (raster)
   int64_t BH;             // batch * heads
   int32_t heads;          // heads per batch entry
   int32_t group;          // query heads per key/value head; key/value head of bh is bh / group
@@ -41,6 +42,7 @@ inline Geom make_geom(const vsa_problem& p) {
   g.Nc = (int64_t)g.gT * g.gH * g.gW;
   g.Np = g.Nc * g.vol;
   g.padded = g.Np != g.N ? 1 : 0;
+  g.coords = p.cube_order == VSA_CUBES_RASTER ? nullptr : p.cube_coords;
   g.BH = (int64_t)p.batch * p.heads;
   g.heads = p.heads;
   g.group = p.heads_kv > 0 ? p.heads / p.heads_kv : 1;

@@ -28,8 +28,9 @@
  *   padded up to whole cubes ([VSA-ROCm] shows no other handling; reading:
  *   padded positions hold no token).  Cube-major token tensors are [batch,
  *   heads, Np, head_dim] with Np = Nc*vol rows; position p = c*vol + l, where
- *   cube c runs in raster order over the cube grid and l in raster order
- *   over (ct, ch, cw) inside the cube.  Padded positions hold zeros after a
+ *   cube c runs over the cube grid in the problem's cube order (raster by
+ *   default, or along a 3D Hilbert curve) and l in raster order over
+ *   (ct, ch, cw) inside the cube.  Padded positions hold zeros after a
  *   reorder, are never attended as keys, are left out of the cube means, and
  *   have no raster row (their cube-major outputs are unspecified).  Cube
  *   tensors are [batch, heads, Nc, head_dim].  When the grid divides, Np = N.
@@ -73,7 +74,32 @@ typedef struct vsa_problem {
                            has heads.  The single-tensor reorders and pools
                            work on p->heads heads: for a grouped K or V pass a
                            problem whose heads is heads_kv. */
+  int32_t cube_order;   /* VSA_CUBES_RASTER or VSA_CUBES_HILBERT: the order
+                           of the cubes in every cube-major tensor, in the
+                           LUT and in the cube tensors ([VSA-ROCm]
+                           §Two-Stage Architecture, Pre-stage: a 3D
+                           space-filling curve; the raster order of the cube
+                           grid is the default reading, the Hilbert order
+                           keeps consecutive cubes adjacent in 3D). */
+  const int32_t* cube_coords;  /* device array of Nc packed cube coordinates
+                           written by vsa_cube_table for this problem and
+                           copied to the device by the caller.  Required
+                           (VSA_ERR_NULL otherwise) by every device entry
+                           point when cube_order is VSA_CUBES_HILBERT;
+                           ignored for VSA_CUBES_RASTER.  A table that was
+                           not written for this problem gives unspecified
+                           results, but kernels skip entries that lie outside
+                           the cube grid, so it never causes an
+                           out-of-bounds access. */
 } vsa_problem;
+
+/* Cube orders.  VSA_CUBES_HILBERT: the cubes follow the 3D Hilbert curve
+ * of Skilling's transform ("Programming the Hilbert curve", AIP Conference
+ * Proceedings 707, 2004) over the smallest power-of-two cube covering the
+ * cube grid, t taking the first bit of each level; cells outside the grid
+ * are skipped.  Each side of the cube grid must be at most 1024 cubes
+ * (VSA_ERR_UNSUPPORTED otherwise). */
+enum { VSA_CUBES_RASTER = 0, VSA_CUBES_HILBERT = 1 };
 
 /* Element type of token tensors. */
 enum { VSA_BF16 = 0, VSA_F32 = 1 };
@@ -337,9 +363,16 @@ int vsa_pool_unpermute_bwd(const vsa_problem* p, const float* dx_cube,
                            const float* dxc, float* dx_raster, void* stream);
 
 /* Host helper: perm_host[p] = pi(p) for p < Np (the order vsa_permute
- * applies), -1 at padded positions.  perm_host is a host array of Np int32.
- * No device work. */
+ * applies, in p->cube_order), -1 at padded positions.  perm_host is a host
+ * array of Np int32.  No device work; cube_coords is not read. */
 int vsa_perm_index(const vsa_problem* p, int32_t* perm_host);
+
+/* Host helper: coords_host[c] = (ct_c << 20) | (ch_c << 10) | cw_c, the
+ * grid coordinates of the c-th cube in p->cube_order, for c < Nc.  Copy
+ * the array to the device and pass it as p->cube_coords.  coords_host is a
+ * host array of Nc int32.  Each side of the cube grid must be at most 1024
+ * cubes (VSA_ERR_UNSUPPORTED).  No device work, no allocation. */
+int vsa_cube_table(const vsa_problem* p, int32_t* coords_host);
 
 /* Static description of a status code (never NULL). */
 const char* vsa_status_str(int status);

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert L.vsa_abi_version() >> 16 == 2
+    assert L.vsa_abi_version() >> 16 == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.vsa_status_str(code) and L.vsa_status_str(code) != "unknown status"
     assert L.vsa_status_str(42) == "unknown status"
@@ -62,6 +62,45 @@ def test_host_perm_index_padded_grid(grid, cube):
     assert p.n_cubes * p.cube_volume == len(want)
     got = L.vsa_perm_index(p).numpy()
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("grid,cube", [((16, 32, 64), (4, 4, 4)), ((32, 48, 80), (4, 4, 4)),
+                                       ((21, 30, 52), (4, 4, 4)), ((3, 5, 2), (2, 2, 2)), ((4, 4, 4), (4, 4, 4)),
+                                       ((2, 9, 3), (1, 1, 1))])
+def test_host_hilbert_order_matches_oracle(grid, cube):
+    """The library's Hilbert cube table and token order, written in C from
+    the same published transform, equal the oracle's."""
+    p = L.Problem(1, 1, *grid, *cube, 64, cube_order="hilbert")
+    seq = oracle.cube_sequence(*p.cube_grid, "hilbert")
+    table = L.vsa_cube_table(p).numpy()
+    assert table.tolist() == [(t << 20) | (h << 10) | w for t, h, w in seq]
+    assert np.array_equal(L.vsa_perm_index(p).numpy(), oracle.token_layout(*grid, *cube, "hilbert"))
+    raster = L.Problem(1, 1, *grid, *cube, 64)
+    assert L.vsa_cube_table(raster).tolist() == [(t << 20) | (h << 10) | w
+                                                 for t, h, w in oracle.cube_sequence(*p.cube_grid, "raster")]
+
+
+def test_hilbert_order_needs_its_device_table():
+    lib = _raw()
+    hp = L.Problem(1, 2, 8, 16, 16, 4, 4, 4, 64, cube_order="hilbert").c_struct()
+    assert hp.cube_coords is None
+    assert lib.vsa_permute(ctypes.byref(hp), 0, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd(ctypes.byref(hp), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, None, None, None,
+                                   DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_coarse_topk(ctypes.byref(hp), 4, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, None) == \
+        L.VSA_ERR_NULL
+    # host helpers and size queries do not read the table
+    n = ctypes.c_size_t(0)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(hp), 4, ctypes.byref(n)) == L.VSA_OK
+    assert lib.vsa_coarse_bwd_workspace_size(ctypes.byref(hp), ctypes.byref(n)) == L.VSA_OK
+    bad = L.Problem(1, 2, 8, 16, 16, 4, 4, 4, 64).c_struct()
+    bad.cube_order = 7
+    assert lib.vsa_perm_index(ctypes.byref(bad), DUMMY) == L.VSA_ERR_UNSUPPORTED
+    wide = L.Problem(1, 1, 4, 4, 4 * 1025, 4, 4, 4, 64, cube_order="hilbert")
+    out = np.zeros(wide.n_cubes, np.int32)
+    assert lib.vsa_cube_table(ctypes.byref(wide.c_struct()), out.ctypes.data) == L.VSA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        L.Problem(1, 1, 4, 4, 4, cube_order="morton").c_struct()
 
 
 # ----------------------------------------------------------------- errors
