@@ -44,6 +44,11 @@ DESIGN.md):
   Skilling's transform over the smallest power-of-two cube that covers the
   cube grid (axis t first), cells outside the grid skipped; tokens inside a
   cube stay in raster order.  R1's raster cube order stays the default.
+* R22 values may be narrower or wider than queries and keys (the separate
+  hdim_v of the CK interface in [VSA-ROCm]): O_f, O_c, the gates and the
+  output take V's width d_v; the softmax scale stays 1/sqrt(d) of the
+  query/key width (the d_k of the SDPA formula, [VSA-ROCm] §The Attention
+  Bottleneck in Video Diffusion).
 * R19 grouped heads (K and V with fewer heads than Q, the head counts of the
   CK kernel interface in [VSA-ROCm]): query head h uses key/value head
   h // G with G = heads / kv_heads; equivalently every key/value head is
@@ -287,7 +292,7 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
                    scale: float, vol: int, query_cubes=None, key_valid=None):
     """Token-level attention of every query cube over its listed key cubes.
 
-    qp/kp/vp: cube-major [B, heads, N, d].  For query cube i the key set is
+    qp/kp/vp: cube-major [B, heads, N, d] (vp may be d_v wide, R22).  For query cube i the key set is
     the concatenation of token ranges [vol*j, vol*j + vol) for the first
     valid_block_num[i] entries j of row i of the LUT (R8: in LUT order).
     Returns (O_f [B, heads, N, d], LSE [B, heads, N]) with
@@ -302,7 +307,7 @@ def fine_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray,
     vp = np.asarray(vp, np.float64)
     B, nh, N, d = qp.shape
     nc = N // vol
-    of = np.zeros((B, nh, N, d), dtype=np.float64)
+    of = np.zeros((B, nh, N, vp.shape[-1]), dtype=np.float64)   # V's width (R22)
     lse = np.full((B, nh, N), -np.inf, dtype=np.float64)
     todo = ((b, h, i) for b in range(B) for h in range(nh) for i in range(nc)) \
         if query_cubes is None else query_cubes
