@@ -340,7 +340,30 @@ def main() -> int:
             hil = {"step_ms": h_step, "fine_ms": h_fine, "bwd_ms": h_bwd,
                    "pairs": int(fh.valid.sum().item())}
             del grads, ws, d_o, o_f, lse_f, fh
-            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil
+
+            # a value head size different from the query/key head size (its
+            # own four-wavefront kernel): the step's cube-major tensors cut to
+            # the widths, the step's Top-K LUT, raster output with O_c
+            dvres = {}
+            for dq_, dv_ in ((128, 64), (64, 128)):
+                pv = dataclasses.replace(p, head_dim=dq_, head_dim_v=dv_)
+                qx, kx = f.qp[..., :dq_].contiguous(), f.kp[..., :dq_].contiguous()
+                vx, ocx = f.vp[..., :dv_].contiguous(), f.oc[..., :dv_].contiguous()
+                ox = torch.empty(q.shape[:-1] + (dv_,), dtype=torch.bfloat16, device=dev)
+
+                def run_dv():
+                    L.vsa_sparse_attn_fwd_raster(pv, qx, kx, vx, f.lut, f.valid, ox, oc=ocx, stream=stream)
+                run_dv()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    run_dv()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                dvres[(dq_, dv_)] = e0.elapsed_time(e1) / reps
+                del qx, kx, vx, ocx, ox
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
@@ -379,7 +402,7 @@ def main() -> int:
                      "traffic": _measured_traffic()},
     }
     if ex is not None:
-        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil = ex
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres = ex
         rec.update({
             "stages_ms": {n: round(t, 4) for n, t in acc.items()},
             "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
@@ -408,6 +431,12 @@ def main() -> int:
                               "fine_tflops": round(flops / (hil["fine_ms"] * 1e-3) / 1e12, 2),
                               "bwd_ms_per_call": round(hil["bwd_ms"], 4),
                               "bwd_tflops": round(2.5 * flops / (hil["bwd_ms"] * 1e-3) / 1e12, 2)},
+            "value_head_size": {
+                "note": "fine stage with d_v != d (its own kernel), the step's Top-K LUT, raster output with O_c; "
+                        "FLOPs 2*64*64*(d + d_v) per selected pair",
+                **{f"d{a}_dv{b}": {"fine_ms_per_call": round(t, 4),
+                                   "tflops": round(flops * (a + b) / 256 / (t * 1e-3) / 1e12, 2)}
+                   for (a, b), t in dvres.items()}},
         })
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -39,7 +39,8 @@ class VsaError(RuntimeError):
 
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim", "heads_kv", "cube_order")] + \
+                ("batch", "heads", "T", "H", "W", "ct", "ch", "cw", "head_dim", "heads_kv", "cube_order",
+                 "head_dim_v")] + \
                [("cube_coords", ctypes.c_void_p)]
 
 
@@ -62,6 +63,7 @@ class Problem:
     head_dim: int = 128
     heads_kv: int = 0          # key/value heads (grouped heads); 0 means heads
     cube_order: str = "raster"   # "raster" or "hilbert": the order of the cubes
+    head_dim_v: int = 0        # value head size; 0 means head_dim
 
     @property
     def n_tokens(self) -> int:
@@ -95,10 +97,18 @@ class Problem:
     def kv_heads(self) -> int:
         return self.heads_kv if self.heads_kv else self.heads
 
+    @property
+    def v_dim(self) -> int:
+        return self.head_dim_v if self.head_dim_v else self.head_dim
+
     def kv_problem(self) -> "Problem":
-        """The problem of a key/value tensor alone (for the single-tensor
-        reorders and pools)."""
-        return dataclasses.replace(self, heads=self.kv_heads, heads_kv=0)
+        """The problem of a key tensor alone (for the single-tensor reorders
+        and pools); also a value tensor's when the head sizes agree."""
+        return dataclasses.replace(self, heads=self.kv_heads, heads_kv=0, head_dim_v=0)
+
+    def v_problem(self) -> "Problem":
+        """The problem of a value tensor alone: key/value heads, value head size."""
+        return dataclasses.replace(self, heads=self.kv_heads, heads_kv=0, head_dim=self.v_dim, head_dim_v=0)
 
     def c_struct(self, device=None) -> _Problem:
         """The C struct; with the Hilbert order and a device, cube_coords
@@ -108,7 +118,7 @@ class Problem:
             raise ValueError(f"cube_order {self.cube_order!r} is not one of {sorted(_CUBE_ORDERS)}")
         order = _CUBE_ORDERS[self.cube_order]
         st = _Problem(self.batch, self.heads, self.T, self.H, self.W,
-                      self.ct, self.ch, self.cw, self.head_dim, self.heads_kv, order, None)
+                      self.ct, self.ch, self.cw, self.head_dim, self.heads_kv, order, self.head_dim_v, None)
         if order != VSA_CUBES_RASTER and device is not None and torch.device(device).type == "cuda":
             st.cube_coords = _cube_table(self, torch.device(device)).data_ptr()
         return st
@@ -230,29 +240,29 @@ def _token_dtype(dtype: int):
     raise ValueError(f"dtype code {dtype} is not VSA_BF16 or VSA_F32")
 
 
-def _tok_shape(p: Problem):
-    return (p.batch, p.heads, p.n_tokens, p.head_dim)
+def _tok_shape(p: Problem, d: Optional[int] = None):
+    return (p.batch, p.heads, p.n_tokens, d or p.head_dim)
 
 
-def _bnhd_shape(p: Problem):
-    return (p.batch, p.n_tokens, p.heads, p.head_dim)
+def _bnhd_shape(p: Problem, d: Optional[int] = None):
+    return (p.batch, p.n_tokens, p.heads, d or p.head_dim)
 
 
-def _pos_shape(p: Problem):
+def _pos_shape(p: Problem, d: Optional[int] = None):
     """Cube-major token tensor: Np = n_cubes * vol rows."""
-    return (p.batch, p.heads, p.n_positions, p.head_dim)
+    return (p.batch, p.heads, p.n_positions, d or p.head_dim)
 
 
-def _kv_pos_shape(p: Problem):
-    return (p.batch, p.kv_heads, p.n_positions, p.head_dim)
+def _kv_pos_shape(p: Problem, d: Optional[int] = None):
+    return (p.batch, p.kv_heads, p.n_positions, d or p.head_dim)
 
 
-def _cube_shape(p: Problem):
-    return (p.batch, p.heads, p.n_cubes, p.head_dim)
+def _cube_shape(p: Problem, d: Optional[int] = None):
+    return (p.batch, p.heads, p.n_cubes, d or p.head_dim)
 
 
-def _kv_cube_shape(p: Problem):
-    return (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
+def _kv_cube_shape(p: Problem, d: Optional[int] = None):
+    return (p.batch, p.kv_heads, p.n_cubes, d or p.head_dim)
 
 
 # ---------------------------------------------------------------- entry points
@@ -305,9 +315,9 @@ def vsa_coarse_topk(p: Problem, top_k: int, qc: torch.Tensor, kc: torch.Tensor, 
     _need(qc, "qc", _cube_shape(p), torch.float32)
     _need(kc, "kc", _kv_cube_shape(p), torch.float32, dev)
     if vc is not None:
-        _need(vc, "vc", _kv_cube_shape(p), torch.float32, dev)
+        _need(vc, "vc", _kv_cube_shape(p, p.v_dim), torch.float32, dev)
     if oc is not None:
-        _need(oc, "oc", _cube_shape(p), torch.float32, dev)
+        _need(oc, "oc", _cube_shape(p, p.v_dim), torch.float32, dev)
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, top_k), torch.int32, dev)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
     _check(load().vsa_coarse_topk(ctypes.byref(p.c_struct(dev)), int(top_k), _ptr(qc), _ptr(kc), _ptr(vc),
@@ -344,10 +354,11 @@ def vsa_sparse_attn_fwd_bnhd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: to
 def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, raster):
     dev = q.device
     ts = _pos_shape(p)
-    os_ = {"bnhd": _bnhd_shape(p), True: _tok_shape(p), False: ts}[raster]
+    dv = p.v_dim
+    os_ = {"bnhd": _bnhd_shape(p, dv), True: _tok_shape(p, dv), False: _pos_shape(p, dv)}[raster]
     _need(q, "q", ts, torch.bfloat16, dev)
-    for name, t in (("k", k), ("v", v)):
-        _need(t, name, _kv_pos_shape(p), torch.bfloat16, dev)
+    _need(k, "k", _kv_pos_shape(p), torch.bfloat16, dev)
+    _need(v, "v", _kv_pos_shape(p, dv), torch.bfloat16, dev)
     _need(out, "out", os_, torch.bfloat16, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
@@ -355,7 +366,7 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
     _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
     _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
     if oc is not None:
-        _need(oc, "oc", _cube_shape(p), torch.float32, dev)
+        _need(oc, "oc", _cube_shape(p, dv), torch.float32, dev)
     for name, t in (("gate_c", gate_c), ("gate_f", gate_f)):
         if t is not None:
             _need(t, name, os_, torch.bfloat16, dev)

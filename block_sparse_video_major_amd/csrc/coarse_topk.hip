@@ -88,7 +88,8 @@ struct ChunkStage {
   }
 };
 
-template <int D, int R, int NS, int kThreads>
+// DQ: query/key head size (scores); DV: value head size (O_c).
+template <int DQ, int DV, int R, int NS, int kThreads>
 __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
     int32_t* __restrict__ lut, int32_t* __restrict__ valid, float* __restrict__ oc, int Nc, int top_k,
@@ -97,15 +98,16 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   static_assert(R % kWaves == 0, "rows per workgroup");
   extern __shared__ float smem[];
   const int NcP = padded_cols(Nc);
-  float* chunk = smem;                       // [kChunk][D + 4]
-  float* srow = chunk + kChunk * (D + 4);    // [R][NcP]
+  constexpr int DM = DQ > DV ? DQ : DV;
+  float* chunk = smem;                       // [kChunk][DQ + 4] keys, then [kChunk][DV + 4] values
+  float* srow = chunk + kChunk * (DM + 4);   // [R][NcP]
   float* inv_sum = srow + (int64_t)R * NcP;  // [R]
 
   const int64_t bh = blockIdx.x / tiles_per_head;
   const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * R;
   const int rows = min(R, Nc - i0);
   const int64_t kvh = bh / group;   // key/value head of this query head
-  const float* kh = kc + kvh * (int64_t)Nc * D;
+  const float* kh = kc + kvh * (int64_t)Nc * DQ;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   const float* qrow[RW];
 #pragma unroll
   for (int u = 0; u < RW; ++u)
-    qrow[u] = qc + (bh * Nc + min(i0 + wave + kWaves * u, Nc - 1)) * (int64_t)D;
-  ChunkStage<D, kThreads> st;
+    qrow[u] = qc + (bh * Nc + min(i0 + wave + kWaves * u, Nc - 1)) * (int64_t)DQ;
+  ChunkStage<DQ, kThreads> st;
   st.load(kh, 0, Nc, tid);
   for (int c0 = 0; c0 < Nc; c0 += kChunk) {
     __syncthreads();   // previous chunk fully read
@@ -128,9 +130,9 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     float acc[RW];
 #pragma unroll
     for (int u = 0; u < RW; ++u) acc[u] = 0.f;
-    const float* kr = chunk + lane * (D + 4);
+    const float* kr = chunk + lane * (DQ + 4);
 #pragma unroll 8
-    for (int d4 = 0; d4 < D / 4; ++d4) {
+    for (int d4 = 0; d4 < DQ / 4; ++d4) {
       const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * d4);
 #pragma unroll
       for (int u = 0; u < RW; ++u) {
@@ -147,8 +149,9 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     }
   }
   // The first value chunk is in flight during the selection.
-  const float* vh = vc + kvh * (int64_t)Nc * D;
-  if (oc != nullptr) st.load(vh, 0, Nc, tid);
+  const float* vh = vc + kvh * (int64_t)Nc * DV;
+  ChunkStage<DV, kThreads> sv;
+  if (oc != nullptr) sv.load(vh, 0, Nc, tid);
   __syncthreads();
 
   // phase 2: per-row Top-K and softmax weights, one wavefront per row
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   if (oc == nullptr) return;
 
   // phase 3: O_c rows
-  constexpr int C4 = D / 4;                     // 16-byte column groups
+  constexpr int C4 = DV / 4;                    // 16-byte column groups
   constexpr int NRG = kThreads / C4;            // row groups
   constexpr int RPT = R >= NRG ? R / NRG : 1;   // rows per thread
   constexpr int KS = R >= NRG ? 1 : NRG / R;    // key splits
@@ -227,15 +230,15 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   for (int u = 0; u < RPT; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < Nc; c0 += kChunk) {
     __syncthreads();   // phase 2 done / previous chunk fully read
-    st.store(chunk, tid);
+    sv.store(chunk, tid);
     __syncthreads();
-    if (c0 + kChunk < Nc) st.load(vh, c0 + kChunk, Nc, tid);
+    if (c0 + kChunk < Nc) sv.load(vh, c0 + kChunk, Nc, tid);
     const int jend = min(kChunk, NcP - c0);   // multiple of 4; pad columns carry p = 0
     for (int j = 4 * ks; j < jend; j += 4 * KS) {
-      const float4 v0 = *reinterpret_cast<const float4*>(chunk + (j + 0) * (D + 4) + 4 * c4);
-      const float4 v1 = *reinterpret_cast<const float4*>(chunk + (j + 1) * (D + 4) + 4 * c4);
-      const float4 v2 = *reinterpret_cast<const float4*>(chunk + (j + 2) * (D + 4) + 4 * c4);
-      const float4 v3 = *reinterpret_cast<const float4*>(chunk + (j + 3) * (D + 4) + 4 * c4);
+      const float4 v0 = *reinterpret_cast<const float4*>(chunk + (j + 0) * (DV + 4) + 4 * c4);
+      const float4 v1 = *reinterpret_cast<const float4*>(chunk + (j + 1) * (DV + 4) + 4 * c4);
+      const float4 v2 = *reinterpret_cast<const float4*>(chunk + (j + 2) * (DV + 4) + 4 * c4);
+      const float4 v3 = *reinterpret_cast<const float4*>(chunk + (j + 3) * (DV + 4) + 4 * c4);
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
         const int r = r_first + NRG * u;
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
     if (r < rows) {
       const float is = inv_sum[r];
       const float4 a = acc[u];
-      reinterpret_cast<float4*>(oc + (bh * Nc + i0 + r) * D)[c4] =
+      reinterpret_cast<float4*>(oc + (bh * Nc + i0 + r) * DV)[c4] =
           make_float4(a.x * is, a.y * is, a.z * is, a.w * is);
     }
   }
@@ -281,21 +284,21 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
 
 }  // namespace
 
-static size_t coarse_lds_bytes(int R, int Nc, int D) {
+static size_t coarse_lds_bytes(int R, int Nc, int D) {   // D: the wider of the two head sizes
   return sizeof(float) * ((size_t)kChunk * (D + 4) + (size_t)R * padded_cols(Nc) + R);
 }
 
 constexpr size_t kCoarseLdsMax = 160 * 1024;
 
-template <int D, int R, int NS, int T>
+template <int DQ, int DV, int R, int NS, int T>
 static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                              int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
   const int Nc = (int)g.Nc;
   const int tiles = (Nc + R - 1) / R;
   const int64_t blocks = g.BH * tiles;
-  const size_t lds = coarse_lds_bytes(R, Nc, D);
-  const float scale = 1.0f / sqrtf((float)D);
-  auto k = coarse_topk_kernel<D, R, NS, T>;
+  const size_t lds = coarse_lds_bytes(R, Nc, DQ > DV ? DQ : DV);
+  const float scale = 1.0f / sqrtf((float)DQ);
+  auto k = coarse_topk_kernel<DQ, DV, R, NS, T>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -305,33 +308,35 @@ static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const fl
   return hipGetLastError();
 }
 
-template <int D, int R, int T>
+template <int DQ, int DV, int R, int T>
 static hipError_t launch_r(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                            int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
   const int slots = (int)((g.Nc + 63) / 64);
-  if (slots <= 8) return launch_rns<D, R, 8, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
-  if (slots <= 16) return launch_rns<D, R, 16, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
-  if (slots <= 32) return launch_rns<D, R, 32, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
-  return launch_rns<D, R, 64, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 8) return launch_rns<DQ, DV, R, 8, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 16) return launch_rns<DQ, DV, R, 16, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 32) return launch_rns<DQ, DV, R, 32, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return launch_rns<DQ, DV, R, 64, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
 }
 
 // Eight query cubes per 512-thread workgroup where their score rows fit in
 // LDS, else four per 256 threads: measured on 12 heads x 512 cubes, more,
 // smaller workgroups hide the staging latency better than larger ones.
-template <int D>
+template <int DQ, int DV>
 static hipError_t launch_d(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                            int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
-  if (coarse_lds_bytes(8, (int)g.Nc, D) <= kCoarseLdsMax)
-    return launch_r<D, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);
-  return launch_r<D, 4, 256>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (coarse_lds_bytes(8, (int)g.Nc, DQ > DV ? DQ : DV) <= kCoarseLdsMax)
+    return launch_r<DQ, DV, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return launch_r<DQ, DV, 4, 256>(g, top_k, qc, kc, vc, lut, valid, oc, s);
 }
 
 hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const float* kc,
                               const float* vc, int32_t* lut, int32_t* valid, float* oc,
                               hipStream_t s) {
   if (g.Nc < 1 || g.Nc > kMaxCoarseCubes) return hipErrorInvalidValue;
-  if (g.D == 64) return launch_d<64>(g, top_k, qc, kc, vc, lut, valid, oc, s);
-  if (g.D == 128) return launch_d<128>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (g.D == 64 && g.Dv == 64) return launch_d<64, 64>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (g.D == 128 && g.Dv == 128) return launch_d<128, 128>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (g.D == 128 && g.Dv == 64) return launch_d<128, 64>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (g.D == 64 && g.Dv == 128) return launch_d<64, 128>(g, top_k, qc, kc, vc, lut, valid, oc, s);
   return hipErrorInvalidValue;
 }
 

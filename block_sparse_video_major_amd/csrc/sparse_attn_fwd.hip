@@ -64,6 +64,7 @@
 //     schedule (slot, offset and wait arithmetic) cost more, because every
 //     wave issues them between its MFMAs.
 #include "mfma_util.h"
+#include "token_map.h"
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -132,97 +133,6 @@ __device__ __forceinline__ void wait_parts(int parts) {
 }
 
 // RK / RV: positions of the K and V tile rings.
-// Token order of out, gate_c, gate_f and lse: cube-major (on == 0) or raster
-// (t, h, w) order (on == 1; the reorder back fused into the epilogue).  A
-// grid padded up to whole cubes has positions with no token: they are never
-// keys and, in raster order, have no output row.  With
-// bnhd == 1 (raster only) out and the gates are the model's [batch, N, heads,
-// d] rows instead of [batch, heads, N, d]; lse stays [batch, heads, N].
-struct TokenMap {
-  int32_t on;
-  int32_t bnhd;
-  int32_t T, H, W;      // token grid (frames, rows and columns of a frame)
-  int32_t ct, ch, cw;   // cube edges
-  int32_t gT, gH, gW;   // cube grid
-  const int32_t* coords;  // packed grid coordinates of each cube (Hilbert order), or null (raster)
-  int32_t heads;        // heads per batch entry
-  int32_t N;            // real tokens per (batch, head): raster rows
-  int32_t Np;           // cube-major positions per (batch, head)
-  int32_t padded;       // the grid was padded up to whole cubes
-};
-
-// Grid coordinates of cube c: raster order over the cube grid, or the
-// problem's table of packed coordinates.  A table entry outside the grid
-// (a table written for another problem) marks the cube invalid: it then has
-// no real token, so it is never read as keys or written in raster order.
-struct CubeAt {
-  int32_t t, h, w;
-  bool ok;
-};
-
-__device__ __forceinline__ CubeAt cube_at(const TokenMap& m, int32_t c) {
-  CubeAt r;
-  if (m.coords != nullptr) {
-    const int32_t e = m.coords[c];
-    r.t = (e >> 20) & 1023;
-    r.h = (e >> 10) & 1023;
-    r.w = e & 1023;
-    r.ok = r.t < m.gT && r.h < m.gH && r.w < m.gW;
-  } else {
-    r.w = c % m.gW;
-    r.h = (c / m.gW) % m.gH;
-    r.t = c / (m.gW * m.gH);
-    r.ok = true;
-  }
-  return r;
-}
-
-// Whether position l of cube q holds a real token (not padding).
-__device__ __forceinline__ bool token_real(const TokenMap& m, const CubeAt& q, int32_t l) {
-  const int32_t plane = m.ch * m.cw;
-  const int32_t lt = l / plane, rem = l - lt * plane;
-  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
-  return q.ok && q.t * m.ct + lt < m.T && q.h * m.ch + lh < m.H && q.w * m.cw + lw < m.W;
-}
-
-// Bit l set when position l of cube q holds a real token.  The cube edges
-// multiply to 64 positions; tokens run w fastest, then h, then t.
-__device__ __forceinline__ uint64_t cube_mask(const TokenMap& m, const CubeAt& q) {
-  if (!q.ok) return 0;
-  const int32_t rt = min(m.ct, m.T - q.t * m.ct), rh = min(m.ch, m.H - q.h * m.ch), rw = min(m.cw, m.W - q.w * m.cw);
-  const uint64_t row = rw >= 64 ? ~0ull : ((1ull << rw) - 1);
-  uint64_t plane = 0, all = 0;
-  for (int32_t h = 0; h < rh; ++h) plane |= row << (h * m.cw);
-  for (int32_t t = 0; t < rt; ++t) all |= plane << (t * m.ch * m.cw);
-  return all;
-}
-
-// Whether cube q reaches past the grid (holds padded positions).
-__device__ __forceinline__ bool cube_partial(const TokenMap& m, const CubeAt& q) {
-  return !q.ok || (q.t + 1) * m.ct > m.T || (q.h + 1) * m.ch > m.H || (q.w + 1) * m.cw > m.W;
-}
-
-// Position of token l (< 64) of cube c (coordinates q) within its (batch,
-// head) in the order the map selects.
-__device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, const CubeAt& q, int32_t l) {
-  if (!m.on) return c * kBlk + l;
-  const int32_t plane = m.ch * m.cw;
-  const int32_t lt = l / plane, rem = l - lt * plane;
-  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
-  return ((q.t * m.ct + lt) * m.H + q.h * m.ch + lh) * m.W + q.w * m.cw + lw;
-}
-
-// Element offset of token l of cube c (coordinates q) of (batch, head) bh in
-// out and the gates.
-__device__ __forceinline__ int64_t token_elem(const TokenMap& m, int64_t bh, int32_t c, const CubeAt& q, int32_t l,
-                                              int D) {
-  const int64_t n = token_pos(m, c, q, l);
-  if (!m.on) return (bh * m.Np + n) * D;
-  if (!m.bnhd) return (bh * m.N + n) * D;
-  const int64_t b = bh / m.heads, h = bh - b * m.heads;
-  return ((b * m.N + n) * m.heads + h) * D;
-}
-
 // PAD: the grid was padded up to whole cubes (the key masking of partial
 // tiles is compiled only into this variant, so the divisible case keeps its
 // loop as it is).
@@ -908,17 +818,7 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
                                   void* out, float* lse, int out_order, hipStream_t s) {
-  TokenMap m;
-  m.on = out_order != 0 ? 1 : 0;
-  m.bnhd = out_order == 2 ? 1 : 0;
-  m.heads = g.heads;
-  m.N = (int32_t)g.N;
-  m.Np = (int32_t)g.Np;
-  m.padded = g.padded;
-  m.T = g.T; m.H = g.H; m.W = g.W;
-  m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
-  m.gT = g.gT; m.gH = g.gH; m.gW = g.gW;
-  m.coords = g.coords;
+  const TokenMap m = make_token_map(g, out_order);
   if (g.D == 128 && g.padded) return launch_d<128, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   if (g.D == 128) return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
   if (g.D == 64 && g.padded) return launch_d<64, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);

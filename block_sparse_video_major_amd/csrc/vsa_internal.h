@@ -27,7 +27,8 @@ struct Geom {
   int32_t heads;          // heads per batch entry
   int32_t group;          // query heads per key/value head; key/value head of bh is bh / group
   int64_t BHkv;           // batch * key/value heads
-  int32_t D;              // head_dim
+  int32_t D;              // head_dim (queries and keys)
+  int32_t Dv;             // value head size (head_dim_v, or head_dim)
 };
 
 inline Geom make_geom(const vsa_problem& p) {
@@ -48,6 +49,7 @@ inline Geom make_geom(const vsa_problem& p) {
   g.group = p.heads_kv > 0 ? p.heads / p.heads_kv : 1;
   g.BHkv = g.BH / g.group;
   g.D = p.head_dim;
+  g.Dv = p.head_dim_v > 0 ? p.head_dim_v : p.head_dim;
   return g;
 }
 
@@ -65,6 +67,14 @@ hipError_t launch_coarse_topk(const Geom& g, int top_k, const float* qc, const f
                               hipStream_t s);
 // Whether the fine kernel handles this cube count and LUT row length.
 bool sparse_attn_fwd_fits(const Geom& g, int max_kv);
+// Fine forward when the value head size differs from the query/key head
+// size (d_qk, d_v) in {(128, 64), (64, 128)}; same arguments and output
+// orders as launch_sparse_attn_fwd, with v, out, the gates and oc d_v wide.
+bool sparse_attn_fwd_dv_fits(const Geom& g, int max_kv);
+hipError_t launch_sparse_attn_fwd_dv(const Geom& g, const void* q, const void* k, const void* v,
+                                     const int32_t* lut, const int32_t* valid, int max_kv, const float* oc,
+                                     const void* gate_c, const void* gate_f, void* out, float* lse, int out_order,
+                                     hipStream_t s);
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,

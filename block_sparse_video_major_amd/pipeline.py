@@ -40,11 +40,16 @@ class VsaForward:
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
         kts = (p.batch, p.kv_heads, p.n_positions, p.head_dim)
         kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
+        vts = (p.batch, p.kv_heads, p.n_positions, p.v_dim)   # values may be narrower or wider
+        vcs = (p.batch, p.kv_heads, p.n_cubes, p.v_dim)
         bf, f32 = torch.bfloat16, torch.float32
         self.qp = torch.empty(ts, dtype=bf, device=device)
-        self.kp, self.vp = (torch.empty(kts, dtype=bf, device=device) for _ in range(2))
-        self.qc, self.oc = (torch.empty(cs, dtype=f32, device=device) for _ in range(2))
-        self.kc, self.vc = (torch.empty(kcs, dtype=f32, device=device) for _ in range(2))
+        self.kp = torch.empty(kts, dtype=bf, device=device)
+        self.vp = torch.empty(vts, dtype=bf, device=device)
+        self.qc = torch.empty(cs, dtype=f32, device=device)
+        self.oc = torch.empty((p.batch, p.heads, p.n_cubes, p.v_dim), dtype=f32, device=device)
+        self.kc = torch.empty(kcs, dtype=f32, device=device)
+        self.vc = torch.empty(vcs, dtype=f32, device=device)
         self.lut = torch.empty((p.batch, p.heads, p.n_cubes, top_k), dtype=torch.int32, device=device)
         self.valid = torch.empty((p.batch, p.heads, p.n_cubes), dtype=torch.int32, device=device)
         self.lse = torch.empty((p.batch, p.heads, p.n_tokens), dtype=f32, device=device) if with_lse else None
@@ -55,10 +60,10 @@ class VsaForward:
         p, B = self.p, L.VSA_BF16
         bnhd = self.layout == "bnhd"
         permute_pool = L.vsa_permute_pool_bnhd if bnhd else L.vsa_permute_pool
-        pkv = p.kv_problem()   # K and V may have fewer (grouped) heads
+        # K and V may have fewer (grouped) heads, and V its own head size
         permute_pool(p, B, q, self.qp, self.qc, stream)
-        permute_pool(pkv, B, k, self.kp, self.kc, stream)
-        permute_pool(pkv, B, v, self.vp, self.vc, stream)
+        permute_pool(p.kv_problem(), B, k, self.kp, self.kc, stream)
+        permute_pool(p.v_problem(), B, v, self.vp, self.vc, stream)
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
         # fine attention reading the raster-order gates and writing the
         # raster-order output directly (the reorder back is in its epilogue)
@@ -80,7 +85,7 @@ def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, t
                 stream=None) -> torch.Tensor:
     """One VSA forward pass on raster bf16 inputs [B, heads, N, d]."""
     f = VsaForward(p, top_k, q.device, with_gates=gate_c is not None or gate_f is not None)
-    out = torch.empty_like(q)
+    out = q.new_empty(q.shape[:-1] + (p.v_dim,))
     return f(q, k, v, out, gate_c, gate_f, stream)
 
 
@@ -96,6 +101,8 @@ class VsaBackward:
     gradient added."""
 
     def __init__(self, p: Problem, max_kv: int, device="cuda"):
+        if p.v_dim != p.head_dim:
+            raise ValueError("the backward needs head_dim_v == head_dim")
         self.p = p
         ts = (p.batch, p.heads, p.n_positions, p.head_dim)   # cube-major (padded) rows
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)

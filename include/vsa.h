@@ -81,6 +81,16 @@ typedef struct vsa_problem {
                            space-filling curve; the raster order of the cube
                            grid is the default reading, the Hilbert order
                            keeps consecutive cubes adjacent in 3D). */
+  int32_t head_dim_v;   /* value head size (the hdim_v of the CK interface in
+                           [VSA-ROCm]); 0 means head_dim.  64 or 128.  V, Vc,
+                           O_c, the gates and the attention output are this
+                           wide; Q, K, Qc and Kc are head_dim wide, and the
+                           softmax scale stays 1/sqrt(head_dim).  The
+                           single-tensor reorders and pools work on
+                           p->head_dim: for V pass a problem whose head_dim
+                           is head_dim_v.  The backward entry points require
+                           head_dim_v == head_dim (VSA_ERR_UNSUPPORTED
+                           otherwise). */
   const int32_t* cube_coords;  /* device array of Nc packed cube coordinates
                            written by vsa_cube_table for this problem and
                            copied to the device by the caller.  Required

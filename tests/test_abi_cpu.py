@@ -103,6 +103,29 @@ def test_hilbert_order_needs_its_device_table():
         L.Problem(1, 1, 4, 4, 4, cube_order="morton").c_struct()
 
 
+def test_value_head_size_errors():
+    lib = _raw()
+    bad = L.Problem(1, 2, 8, 16, 16, 4, 4, 4, 128, head_dim_v=96).c_struct()
+    assert lib.vsa_perm_index(ctypes.byref(bad), DUMMY) == L.VSA_ERR_UNSUPPORTED
+    hv = ctypes.byref(L.Problem(1, 2, 8, 16, 16, 4, 4, 4, 128, head_dim_v=64).c_struct())
+    n = ctypes.c_size_t(0)
+    # the backward of a layer whose value head size differs is not provided
+    assert lib.vsa_sparse_attn_bwd_workspace_size(hv, 4, ctypes.byref(n)) == L.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_sparse_attn_bwd(hv, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                   DUMMY, DUMMY, 1 << 30, None) == L.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_coarse_bwd_workspace_size(hv, ctypes.byref(n)) == L.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_combine_bwd(hv, DUMMY, None, None, None, None, DUMMY, DUMMY, None, None, None) == \
+        L.VSA_ERR_UNSUPPORTED
+    # the forward validates as usual before any launch
+    assert lib.vsa_sparse_attn_fwd(hv, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 0, None, None, None, DUMMY, None,
+                                   None) == L.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd(hv, DUMMY, DUMMY, None, DUMMY, DUMMY, 4, None, None, None, DUMMY, None,
+                                   None) == L.VSA_ERR_NULL
+    p = L.Problem(1, 4, 8, 16, 16, 4, 4, 4, 128, heads_kv=2, head_dim_v=64)
+    assert p.v_dim == 64 and p.v_problem().head_dim == 64 and p.v_problem().heads == 2
+    assert p.kv_problem().head_dim == 128 and p.kv_problem().head_dim_v == 0
+
+
 # ----------------------------------------------------------------- errors
 DUMMY = 0x1000   # never dereferenced: each call fails validation first
 
