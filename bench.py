@@ -361,8 +361,26 @@ def main() -> int:
                     run_dv()
                 e1.record(stream)
                 torch.cuda.synchronize()
-                dvres[(dq_, dv_)] = e0.elapsed_time(e1) / reps
-                del qx, kx, vx, ocx, ox
+                t_fwd = e0.elapsed_time(e1) / reps
+                # its fine backward on the same LUT (cube-major O_f and LSE of that forward)
+                of_x = torch.empty(q.shape[:-1] + (dv_,), dtype=torch.bfloat16, device=dev)
+                lse_x = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device=dev)
+                L.vsa_sparse_attn_fwd(pv, qx, kx, vx, f.lut, f.valid, of_x, lse=lse_x, stream=stream)
+                do_x = torch.randn(of_x.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                gx = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in (qx, kx, vx)]
+                wsx = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(pv, w.top_k), dtype=torch.uint8, device=dev)
+
+                def run_dv_bwd():
+                    L.vsa_sparse_attn_bwd(pv, qx, kx, vx, f.lut, f.valid, of_x, lse_x, do_x, *gx, wsx, stream)
+                run_dv_bwd()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(reps):
+                    run_dv_bwd()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                dvres[(dq_, dv_)] = (t_fwd, e0.elapsed_time(e1) / reps)
+                del qx, kx, vx, ocx, ox, of_x, lse_x, do_x, gx, wsx
             return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
@@ -432,10 +450,13 @@ def main() -> int:
                               "bwd_ms_per_call": round(hil["bwd_ms"], 4),
                               "bwd_tflops": round(2.5 * flops / (hil["bwd_ms"] * 1e-3) / 1e12, 2)},
             "value_head_size": {
-                "note": "fine stage with d_v != d (its own kernel), the step's Top-K LUT, raster output with O_c; "
-                        "FLOPs 2*64*64*(d + d_v) per selected pair",
-                **{f"d{a}_dv{b}": {"fine_ms_per_call": round(t, 4),
-                                   "tflops": round(flops * (a + b) / 256 / (t * 1e-3) / 1e12, 2)}
+                "note": "fine stage with d_v != d (its own forward kernel), the step's Top-K LUT, raster output "
+                        "with O_c; FLOPs 2*64*64*(d + d_v) per selected pair; fine backward on the same LUT, "
+                        "FLOPs 2*64*64*(3 d + 2 d_v) per pair (S, dP, dQ, dK, dV)",
+                **{f"d{a}_dv{b}": {"fine_ms_per_call": round(t[0], 4),
+                                   "tflops": round(flops * (a + b) / 256 / (t[0] * 1e-3) / 1e12, 2),
+                                   "bwd_ms_per_call": round(t[1], 4),
+                                   "bwd_tflops": round(flops * (3 * a + 2 * b) / 256 / (t[1] * 1e-3) / 1e12, 2)}
                    for (a, b), t in dvres.items()}},
         })
     if not args.no_cpu_baseline:

@@ -425,13 +425,15 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
     """Gradients of the fine attention (all tensors cube-major; dq, dk, dv float32)."""
     dev = q.device
     ts, ks = _pos_shape(p), _kv_pos_shape(p)
-    for name, t in (("q", q), ("o", o), ("d_o", d_o)):
-        _need(t, name, ts, torch.bfloat16, dev)
-    for name, t in (("k", k), ("v", v)):
-        _need(t, name, ks, torch.bfloat16, dev)
+    tv, kv = _pos_shape(p, p.v_dim), _kv_pos_shape(p, p.v_dim)   # O, dO and V, dV are d_v wide
+    _need(q, "q", ts, torch.bfloat16, dev)
+    for name, t in (("o", o), ("d_o", d_o)):
+        _need(t, name, tv, torch.bfloat16, dev)
+    _need(k, "k", ks, torch.bfloat16, dev)
+    _need(v, "v", kv, torch.bfloat16, dev)
     _need(dq, "dq", ts, torch.float32, dev)
-    for name, t in (("dk", dk), ("dv", dv)):
-        _need(t, name, ks, torch.float32, dev)
+    _need(dk, "dk", ks, torch.float32, dev)
+    _need(dv, "dv", kv, torch.float32, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
     max_kv = kv_block_idx.shape[-1]
@@ -454,7 +456,7 @@ def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: to
                     stream=None) -> None:
     """Gradients of the gated combination (cube-major token tensors)."""
     dev = dout.device
-    ts, cs = _pos_shape(p), _cube_shape(p)
+    ts, cs = _pos_shape(p, p.v_dim), _cube_shape(p, p.v_dim)   # all d_v wide
     for name, t in (("dout", dout), ("d_of", d_of), ("o_f", o_f), ("gate_c", gate_c), ("gate_f", gate_f)):
         if t is not None:
             _need(t, name, ts, torch.bfloat16, dev)
@@ -482,10 +484,10 @@ def vsa_coarse_bwd(p: Problem, qc: torch.Tensor, kc: torch.Tensor, vc: torch.Ten
     """Gradients of the coarse attention (float32 cube tensors)."""
     dev = qc.device
     cs, kcs = _cube_shape(p), _kv_cube_shape(p)
-    for name, t in (("qc", qc), ("oc", oc), ("d_oc", d_oc), ("dqc", dqc)):
-        _need(t, name, cs, torch.float32, dev)
-    for name, t in (("kc", kc), ("vc", vc), ("dkc", dkc), ("dvc", dvc)):
-        _need(t, name, kcs, torch.float32, dev)
+    for name, t, shape in (("qc", qc, cs), ("dqc", dqc, cs), ("oc", oc, _cube_shape(p, p.v_dim)),
+                           ("d_oc", d_oc, _cube_shape(p, p.v_dim)), ("kc", kc, kcs), ("dkc", dkc, kcs),
+                           ("vc", vc, _kv_cube_shape(p, p.v_dim)), ("dvc", dvc, _kv_cube_shape(p, p.v_dim))):
+        _need(t, name, shape, torch.float32, dev)
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D byte tensor")
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)

@@ -225,11 +225,11 @@ hipError_t launch_combine_bwd(const Geom& g, const void* dout, const void* of, c
                               hipStream_t s) {
   const int64_t units = g.BH * g.Nc;
   const unsigned grid = (unsigned)(units < (1 << 20) ? units : (1 << 20));
-  if (g.D == 128)
+  if (g.Dv == 128)   // every tensor here is as wide as V
     hipLaunchKernelGGL(combine_bwd_kernel<128>, dim3(grid), dim3(kThreads), 0, s, (const __bf16*)dout,
                        (const __bf16*)of, oc, (const __bf16*)gate_c, (const __bf16*)gate_f, (__bf16*)d_of, d_oc,
                        d_gate_c, d_gate_f, units, g.vol);
-  else if (g.D == 64)
+  else if (g.Dv == 64)
     hipLaunchKernelGGL(combine_bwd_kernel<64>, dim3(grid), dim3(kThreads), 0, s, (const __bf16*)dout,
                        (const __bf16*)of, oc, (const __bf16*)gate_c, (const __bf16*)gate_f, (__bf16*)d_of, d_oc,
                        d_gate_c, d_gate_f, units, g.vol);
@@ -250,21 +250,24 @@ size_t coarse_bwd_workspace(const Geom& g) {
 hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, const float* vc, const float* oc,
                              const float* doc, float* dqc, float* dkc, float* dvc, void* workspace,
                              hipStream_t s) {
-  const int Nc = (int)g.Nc, D = g.D, Hk = (int)g.BHkv, Mq = g.group * Nc;
+  // D: query/key width (Qc, Kc), DV: value width (Vc, O_c, dO_c)
+  const int Nc = (int)g.Nc, D = g.D, DV = g.Dv, Hk = (int)g.BHkv, Mq = g.group * Nc;
   const int64_t sq = (int64_t)Mq * D, sk = (int64_t)Nc * D, sm = (int64_t)Mq * Nc;
+  const int64_t sqv = (int64_t)Mq * DV, skv = (int64_t)Nc * DV;
   float* smat = static_cast<float*>(workspace);
   float* dpmat = smat + (size_t)g.BH * g.Nc * g.Nc;
   const float scale = 1.0f / sqrtf((float)D);
   hipError_t e;
   if ((e = gemm<false, true>(Hk, qc, kc, smat, Mq, Nc, D, D, D, Nc, sq, sk, sm, scale, s)) != hipSuccess) return e;
-  if ((e = gemm<false, true>(Hk, doc, vc, dpmat, Mq, Nc, D, D, D, Nc, sq, sk, sm, 1.0f, s)) != hipSuccess) return e;
+  if ((e = gemm<false, true>(Hk, doc, vc, dpmat, Mq, Nc, DV, DV, DV, Nc, sqv, skv, sm, 1.0f, s)) != hipSuccess)
+    return e;
   const int64_t rows = g.BH * g.Nc;
   hipLaunchKernelGGL(coarse_softmax_ds_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, smat, dpmat,
-                     oc, doc, Nc, D, rows);
+                     oc, doc, Nc, DV, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = gemm<false, false>(Hk, dpmat, kc, dqc, Mq, D, Nc, Nc, D, D, sm, sk, sq, scale, s)) != hipSuccess) return e;
   if ((e = gemm<true, false>(Hk, dpmat, qc, dkc, Nc, D, Mq, Nc, D, D, sm, sq, sk, scale, s)) != hipSuccess) return e;
-  return gemm<true, false>(Hk, smat, doc, dvc, Nc, D, Mq, Nc, D, D, sm, sq, sk, 1.0f, s);
+  return gemm<true, false>(Hk, smat, doc, dvc, Nc, DV, Mq, Nc, DV, DV, sm, sqv, skv, 1.0f, s);
 }
 
 }  // namespace vsa

@@ -184,14 +184,16 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
 }
 
 // ---- dQ -------------------------------------------------------------------------
-template <int D>
+// D: query/key head size, DV: value head size (dP^T contracts over DV).
+template <int D, int DV = D>
 __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const int32_t* __restrict__ lut, const int32_t* __restrict__ valid,
     int max_kv, const float2* __restrict__ ld, float* __restrict__ dq, int Nc, int64_t total_cubes,
     float c_log2, float scale, int group) {
   using C = BCfg<D>;
-  constexpr int SLOT = 2 * C::TILE;   // K tile, then V tile
+  using CV = BCfg<DV>;
+  constexpr int SLOT = C::TILE + CV::TILE;   // K tile, then V tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,27 +203,30 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
   const int64_t cube = xcd_remap(blockIdx.x, total_cubes);   // = LUT row
   const int64_t bh = cube / Nc;
   const int ci = (int)(cube - bh * Nc);
-  const int64_t head_off = bh * (int64_t)Nc * kBlk * D;
-  const int64_t kv_off = (bh / group) * (int64_t)Nc * kBlk * D;   // its key/value head
-  const char* k_head = reinterpret_cast<const char*>(k + kv_off);
-  const char* v_head = reinterpret_cast<const char*>(v + kv_off);
+  const int64_t rows_off = bh * (int64_t)Nc * kBlk;                  // this head's first row
+  const int64_t kv_rows = (bh / group) * (int64_t)Nc * kBlk;         // its key/value head's
+  const char* k_head = reinterpret_cast<const char*>(k + kv_rows * D);
+  const char* v_head = reinterpret_cast<const char*>(v + kv_rows * DV);
   const int n = clamp_count(valid[cube], max_kv);
   ListWindow lw(lut + cube * (int64_t)max_kv, n, Nc, lane);
 
   const LaneOffsets<D> off(wave, lane, kh);
+  const LaneOffsets<DV> offv(wave, lane, kh);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * C::LOADS * 1024));
+  const uint32_t lds0v =
+      __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(C::TILE + wave * CV::LOADS * 1024));
   auto issue = [&](int s, int stage) {
     const int cb = lw.at(s, lane);
     dma_tile(uniform_ptr(k_head + (int64_t)cb * C::TILE), off.g_off, lds0 + stage * SLOT);
-    dma_tile(uniform_ptr(v_head + (int64_t)cb * C::TILE), off.g_off, lds0 + stage * SLOT + C::TILE);
+    dma_tile(uniform_ptr(v_head + (int64_t)cb * CV::TILE), offv.g_off, lds0v + stage * SLOT);
   };
   if (n > 0) issue(0, 0);
 
   // Q and dO of this wave's 32 queries as B operands; this lane's query
   // 32*qh + n32 has its (LSE * log2 e, Drow) in registers.
-  bf16x8 qf[C::KS], df[C::KS];
-  load_b_operand<D>(q + head_off + (int64_t)ci * kBlk * D, qh, lane, qf);
-  load_b_operand<D>(dout + head_off + (int64_t)ci * kBlk * D, qh, lane, df);
+  bf16x8 qf[C::KS], df[CV::KS];
+  load_b_operand<D>(q + (rows_off + (int64_t)ci * kBlk) * D, qh, lane, qf);
+  load_b_operand<DV>(dout + (rows_off + (int64_t)ci * kBlk) * DV, qh, lane, df);
   const float2 ldv = ld[cube * kBlk + 32 * qh + (lane & 31)];
   f32x16 acc[C::OT];
 #pragma unroll
@@ -245,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
       sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sT, 0, 0, 0);
     }
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + off.row_off[ks]);
+    for (int ks = 0; ks < CV::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + offv.row_off[ks]);
       pT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[ks], pT, 0, 0, 0);
     }
     // dS^T = P^T * (dP^T - Drow) as the B operand of k-steps j = 0, 1
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_bwd_dq_kernel(
   __syncthreads();
   if (kh == 0) stage_add<D>(stg, acc, qh, lane, scale);
   __syncthreads();
-  stage_flush<D>(stg, dq + head_off + (int64_t)ci * kBlk * D, tid);
+  stage_flush<D>(stg, dq + (rows_off + (int64_t)ci * kBlk) * D, tid);
 }
 
 // ---- dK, dV ---------------------------------------------------------------------
@@ -517,12 +522,153 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_bwd_dkdv_kernel(
   stage_flush<D>(stg_k, dk + head_off + (int64_t)cj * kBlk * D, tid);
 }
 
+// ---- dK, dV when the value head size differs ------------------------------------
+// The plain form of the kernel above, for (D, DV) with D != DV: the same
+// products and layouts, K (D) and V (DV) in registers as B operands, one
+// step per barrier with the next step's Q and dO tiles and records loading
+// into the other of two stages, two workgroups per CU.
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads, 2) void sparse_attn_bwd_dkdv_dv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const int32_t* __restrict__ coloff, const int32_t* __restrict__ csr,
+    int max_kv, const float2* __restrict__ ld, float* __restrict__ dk, float* __restrict__ dv, int Nc,
+    int64_t total_cubes, float c_log2, float scale, int group) {
+  using C = BCfg<D>;
+  using CV = BCfg<DV>;
+  constexpr int SLOT = C::TILE + CV::TILE + 1024;   // Q tile, dO tile, (LSE log2 e, Drow) of 64 queries
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = wave & 1, kh = wave >> 1;
+  const int g = lane >> 5;
+
+  // cube = key cube cj of key/value head bh; its list indexes the Nr query
+  // cubes of the `group` query heads that share that head (contiguous)
+  const int64_t cube = xcd_remap(blockIdx.x, total_cubes);
+  const int64_t bh = cube / Nc;
+  const int cj = (int)(cube - bh * Nc);
+  const int Nr = group * Nc;
+  const int64_t kv_rows = bh * (int64_t)Nc * kBlk;    // K, V, dK, dV rows of this head
+  const int64_t q_rows = bh * (int64_t)Nr * kBlk;     // Q, dO rows of the group
+  const char* q_head = reinterpret_cast<const char*>(q + q_rows * D);
+  const char* d_head = reinterpret_cast<const char*>(dout + q_rows * DV);
+  const char* ld_head = reinterpret_cast<const char*>(ld + q_rows);
+  const int32_t* co = coloff + bh * (int64_t)(Nc + 1);
+  const int b0 = co[cj];
+  const int n = co[cj + 1] - b0;
+  ListWindow lw(csr + bh * (int64_t)Nr * max_kv + b0, n, Nr, lane);
+
+  const LaneOffsets<D> oq(wave, lane, qh);
+  const LaneOffsets<DV> od(wave, lane, qh);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t lds_q = lds_base + (uint32_t)(wave * C::LOADS * 1024);
+  const uint32_t lds_d = lds_base + (uint32_t)(C::TILE + wave * CV::LOADS * 1024);
+  const uint32_t ld_off = 16u * (uint32_t)(lane & 31);   // 512 bytes; lanes 32-63 repeat them
+  auto issue = [&](int s, int stage) {
+    const int ci = lw.at(s, lane);
+    dma_tile(uniform_ptr(q_head + (int64_t)ci * C::TILE), oq.g_off, lds_q + stage * SLOT);
+    dma_tile(uniform_ptr(d_head + (int64_t)ci * CV::TILE), od.g_off, lds_d + stage * SLOT);
+    if (wave == 0)
+      dma_piece(uniform_ptr(ld_head + (int64_t)ci * kBlk * 8), ld_off,
+                lds_base + stage * SLOT + C::TILE + CV::TILE);
+  };
+  if (n > 0) issue(0, 0);
+
+  bf16x8 kf[C::KS], vf[CV::KS];
+  load_b_operand<D>(k + (kv_rows + (int64_t)cj * kBlk) * D, kh, lane, kf);
+  load_b_operand<DV>(v + (kv_rows + (int64_t)cj * kBlk) * DV, kh, lane, vf);
+  f32x16 acc_v[CV::OT], acc_k[C::OT];   // dV^T, dK^T: rows = d, column = key 32*kh + n32
+#pragma unroll
+  for (int t = 0; t < CV::OT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_v[t][r] = 0.f;
+#pragma unroll
+  for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_k[t][r] = 0.f;
+  wait_vmem<0>();
+  __syncthreads();
+
+  for (int s = 0; s < n; ++s) {
+    const int st = s & 1;
+    if (s + 1 < n) issue(s + 1, st ^ 1);
+    const char* tq = smem + st * SLOT;
+    const char* td = tq + C::TILE;
+    // S and dP: rows = queries 32*qh + 8*(r/4) + 4*g + r%4, column = key
+    f32x16 sS, dP;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sS[r] = 0.f; dP[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      sS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(tq + oq.row_off[ks]), kf[ks],
+                                                   sS, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < CV::KS; ++ks)
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(td + od.row_off[ks]), vf[ks],
+                                                   dP, 0, 0, 0);
+    // (LSE log2 e, Drow) of the lane's 16 queries; P and dS as B operands
+    // (k-step j holds registers 8j..8j+7)
+    const float* rec = reinterpret_cast<const float*>(td + CV::TILE) + 2 * (32 * qh + 4 * g);
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float4 r01 = *reinterpret_cast<const float4*>(rec + 16 * rq);
+      const float4 r23 = *reinterpret_cast<const float4*>(rec + 16 * rq + 4);
+      const float lse_[4] = {r01.x, r01.z, r23.x, r23.z};
+      const float drw[4] = {r01.y, r01.w, r23.y, r23.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * rq + u;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sS[r], c_log2, -lse_[u]));
+        pb[r >> 3][r & 7] = (__bf16)p;
+        dsb[r >> 3][r & 7] = (__bf16)(p * (dP[r] - drw[u]));
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, transposing reads of the dO and Q tiles
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int t = 0; t < CV::OT; ++t)
+        acc_v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DV>(td, od, t, j), pb[j], acc_v[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < C::OT; ++t)
+        acc_k[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(tq, oq, t, j), dsb[j], acc_k[t], 0, 0, 0);
+    }
+    wait_vmem<0>();
+    __syncthreads();
+  }
+
+  // the two query halves summed through LDS; dK scaled
+  float* stg_v = reinterpret_cast<float*>(smem);
+  float* stg_k = reinterpret_cast<float*>(smem + CV::STAGE);
+  if (qh == 1) {
+    stage_store<DV>(stg_v, acc_v, kh, lane, 1.f);
+    stage_store<D>(stg_k, acc_k, kh, lane, 1.f);
+  }
+  __syncthreads();
+  if (qh == 0) {
+    stage_add<DV>(stg_v, acc_v, kh, lane, 1.f);
+    stage_add<D>(stg_k, acc_k, kh, lane, scale);
+  }
+  __syncthreads();
+  stage_flush<DV>(stg_v, dv + (kv_rows + (int64_t)cj * kBlk) * DV, tid);
+  stage_flush<D>(stg_k, dk + (kv_rows + (int64_t)cj * kBlk) * D, tid);
+}
+
 constexpr int kLdsMax = 160 * 1024;
 
-template <int D>
+template <int D, int DV = D>
 constexpr int dq_lds() {
   using C = BCfg<D>;
-  return 4 * C::TILE > C::STAGE ? 4 * C::TILE : C::STAGE;
+  constexpr int ring = 2 * (C::TILE + BCfg<DV>::TILE);
+  return ring > C::STAGE ? ring : C::STAGE;
+}
+template <int D, int DV>
+constexpr int dkdv_dv_lds() {
+  constexpr int ring = 2 * (BCfg<D>::TILE + BCfg<DV>::TILE + 1024);
+  constexpr int epi = BCfg<D>::STAGE + BCfg<DV>::STAGE;
+  return ring > epi ? ring : epi;
 }
 template <int D>
 constexpr int dkdv_lds() {
@@ -557,7 +703,8 @@ WsLayout ws_layout(const Geom& g, int max_kv) {
   return w;
 }
 
-template <int D>
+// D: query/key head size, DV: value head size.
+template <int D, int DV>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const void* o, const float* lse, const void* dout,
                     float* dq, float* dk, float* dv, char* ws, hipStream_t s) {
@@ -576,8 +723,8 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   const int64_t total_cubes = g.BH * g.Nc;       // query cubes
   const int64_t total_kv_cubes = g.BHkv * g.Nc;  // key cubes
 
-  constexpr int TOK_PER_BLOCK = 256 / (D / 8);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((total_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK)),
+  constexpr int TOK_PER_BLOCK = 256 / (DV / 8);   // O and dO rows are DV wide
+  hipLaunchKernelGGL(bwd_prep_kernel<DV>, dim3((unsigned)((total_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK)),
                      dim3(256), 0, s, (const __bf16*)o, (const __bf16*)dout, lse, ld, total_tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -593,15 +740,21 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
 
   const float c_log2 = kLog2e / sqrtf((float)D);
   const float scale = 1.0f / sqrtf((float)D);
-  auto kq = sparse_attn_bwd_dq_kernel<D>;
-  auto kkv = sparse_attn_bwd_dkdv_kernel<D>;
-  if ((e = grant_lds(kq, dq_lds<D>(), granted[dev][0])) != hipSuccess) return e;
-  if ((e = grant_lds(kkv, dkdv_lds<D>(), granted[dev][1])) != hipSuccess) return e;
-  hipLaunchKernelGGL(kq, dim3((unsigned)total_cubes), dim3(kThreads), dq_lds<D>(), s, (const __bf16*)q,
+  auto kq = sparse_attn_bwd_dq_kernel<D, DV>;
+  // equal head sizes: the pipelined dK/dV kernel; otherwise its plain form
+  auto kkv = [] {
+    if constexpr (D == DV) return sparse_attn_bwd_dkdv_kernel<D>;
+    else return sparse_attn_bwd_dkdv_dv_kernel<D, DV>;
+  }();
+  constexpr int kv_lds = D == DV ? dkdv_lds<D>() : dkdv_dv_lds<D, DV>();
+  constexpr int q_lds = dq_lds<D, DV>();
+  if ((e = grant_lds(kq, q_lds, granted[dev][0])) != hipSuccess) return e;
+  if ((e = grant_lds(kkv, kv_lds, granted[dev][1])) != hipSuccess) return e;
+  hipLaunchKernelGGL(kq, dim3((unsigned)total_cubes), dim3(kThreads), q_lds, s, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lut, valid, max_kv,
                      (const float2*)ld, dq, Nc, total_cubes, c_log2, scale, g.group);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kkv, dim3((unsigned)total_kv_cubes), dim3(kThreads), dkdv_lds<D>(), s, (const __bf16*)q,
+  hipLaunchKernelGGL(kkv, dim3((unsigned)total_kv_cubes), dim3(kThreads), kv_lds, s, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const int32_t*)coloff,
                      (const int32_t*)csr, max_kv, (const float2*)ld, dk, dv, Nc, total_kv_cubes, c_log2, scale,
                      g.group);
@@ -627,8 +780,14 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const void* q, const void* k, c
                                   const void* dout, float* dq, float* dk, float* dv, void* workspace,
                                   hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
-  if (g.D == 128) return launch_d<128>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
-  if (g.D == 64) return launch_d<64>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  if (g.D == 128 && g.Dv == 128)
+    return launch_d<128, 128>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  if (g.D == 64 && g.Dv == 64)
+    return launch_d<64, 64>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  if (g.D == 128 && g.Dv == 64)
+    return launch_d<128, 64>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
+  if (g.D == 64 && g.Dv == 128)
+    return launch_d<64, 128>(g, q, k, v, lut, valid, max_kv, o, lse, dout, dq, dk, dv, ws, s);
   return hipErrorInvalidValue;
 }
 

@@ -291,7 +291,7 @@ int sparse_attn_bwd_check(const vsa_problem* p, int32_t max_kv_blocks, bool need
   int st = check_problem(p, need_table);
   if (st != VSA_OK) return st;
   const Geom g = vsa::make_geom(*p);
-  if (g.vol != 64 || g.Dv != g.D) return VSA_ERR_UNSUPPORTED;
+  if (g.vol != 64) return VSA_ERR_UNSUPPORTED;
   if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
   if (!vsa::sparse_attn_bwd_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
   return VSA_OK;
@@ -330,7 +330,6 @@ int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f, con
   if (gate_f != nullptr && (o_f == nullptr || d_gate_f == nullptr)) return VSA_ERR_NULL;
   if (gate_c != nullptr && (oc == nullptr || d_gate_c == nullptr)) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  if (g.Dv != g.D) return VSA_ERR_UNSUPPORTED;
   return hip_status(vsa::launch_combine_bwd(g, dout, o_f, oc, gate_c, gate_f, d_of, d_oc, d_gate_c, d_gate_f,
                                             (hipStream_t)stream));
 }
@@ -340,7 +339,7 @@ int vsa_coarse_bwd_workspace_size(const vsa_problem* p, size_t* bytes) {
   if (st != VSA_OK) return st;
   if (bytes == nullptr) return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  if (g.Nc > vsa::kMaxCoarseCubes || g.Dv != g.D) return VSA_ERR_UNSUPPORTED;
+  if (g.Nc > vsa::kMaxCoarseCubes) return VSA_ERR_UNSUPPORTED;
   *bytes = vsa::coarse_bwd_workspace(g);
   return VSA_OK;
 }
@@ -354,7 +353,7 @@ int vsa_coarse_bwd(const vsa_problem* p, const float* qc, const float* kc, const
       dkc == nullptr || dvc == nullptr || workspace == nullptr)
     return VSA_ERR_NULL;
   const Geom g = vsa::make_geom(*p);
-  if (g.Nc > vsa::kMaxCoarseCubes || g.Dv != g.D) return VSA_ERR_UNSUPPORTED;
+  if (g.Nc > vsa::kMaxCoarseCubes) return VSA_ERR_UNSUPPORTED;
   if (workspace_bytes < vsa::coarse_bwd_workspace(g)) return VSA_ERR_WORKSPACE;
   return hip_status(vsa::launch_coarse_bwd(g, qc, kc, vc, oc, d_oc, dqc, dkc, dvc, workspace, (hipStream_t)stream));
 }

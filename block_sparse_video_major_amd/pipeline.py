@@ -14,6 +14,7 @@ kernels of libvsa.so.
 """
 from __future__ import annotations
 
+import dataclasses
 from typing import Dict, Optional
 
 import torch
@@ -101,20 +102,25 @@ class VsaBackward:
     gradient added."""
 
     def __init__(self, p: Problem, max_kv: int, device="cuda"):
-        if p.v_dim != p.head_dim:
-            raise ValueError("the backward needs head_dim_v == head_dim")
         self.p = p
+        # the output side (dout, the gates, O) is as wide as V
+        self.p_out = dataclasses.replace(p, head_dim=p.v_dim, head_dim_v=0)
+        dv_ = p.v_dim
         ts = (p.batch, p.heads, p.n_positions, p.head_dim)   # cube-major (padded) rows
+        tvs = (p.batch, p.heads, p.n_positions, dv_)
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
         kts = (p.batch, p.kv_heads, p.n_positions, p.head_dim)
         kcs = (p.batch, p.kv_heads, p.n_cubes, p.head_dim)
         bf, f32 = torch.bfloat16, torch.float32
-        self.doutp, self.gcp, self.gfp, self.d_of = (torch.empty(ts, dtype=bf, device=device) for _ in range(4))
-        self.dgcp, self.dgfp = (torch.empty(ts, dtype=f32, device=device) for _ in range(2))
+        self.doutp, self.gcp, self.gfp, self.d_of = (torch.empty(tvs, dtype=bf, device=device) for _ in range(4))
+        self.dgcp, self.dgfp = (torch.empty(tvs, dtype=f32, device=device) for _ in range(2))
         self.dqf = torch.empty(ts, dtype=f32, device=device)
-        self.dkf, self.dvf = (torch.empty(kts, dtype=f32, device=device) for _ in range(2))
-        self.d_oc, self.dqc = (torch.empty(cs, dtype=f32, device=device) for _ in range(2))
-        self.dkc, self.dvc = (torch.empty(kcs, dtype=f32, device=device) for _ in range(2))
+        self.dkf = torch.empty(kts, dtype=f32, device=device)
+        self.dvf = torch.empty((p.batch, p.kv_heads, p.n_positions, dv_), dtype=f32, device=device)
+        self.d_oc = torch.empty((p.batch, p.heads, p.n_cubes, dv_), dtype=f32, device=device)
+        self.dqc = torch.empty(cs, dtype=f32, device=device)
+        self.dkc = torch.empty(kcs, dtype=f32, device=device)
+        self.dvc = torch.empty((p.batch, p.kv_heads, p.n_cubes, dv_), dtype=f32, device=device)
         self.ws_fine = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(p, max_kv), dtype=torch.uint8,
                                    device=device)
         self.ws_coarse = torch.empty(L.vsa_coarse_bwd_workspace_size(p), dtype=torch.uint8, device=device)
@@ -124,14 +130,14 @@ class VsaBackward:
                  gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                  dgate_c: Optional[torch.Tensor] = None, dgate_f: Optional[torch.Tensor] = None,
                  stream=None) -> None:
-        p, B = self.p, L.VSA_BF16
-        L.vsa_permute(p, B, dout, self.doutp, stream)
+        p, po, B = self.p, self.p_out, L.VSA_BF16
+        L.vsa_permute(po, B, dout, self.doutp, stream)
         gcp = gfp = None
         if gate_c is not None:
-            L.vsa_permute(p, B, gate_c, self.gcp, stream)
+            L.vsa_permute(po, B, gate_c, self.gcp, stream)
             gcp = self.gcp
         if gate_f is not None:
-            L.vsa_permute(p, B, gate_f, self.gfp, stream)
+            L.vsa_permute(po, B, gate_f, self.gfp, stream)
             gfp = self.gfp
         L.vsa_combine_bwd(p, self.doutp, self.d_of, self.d_oc, o_f=o_f, oc=saved["oc"], gate_c=gcp, gate_f=gfp,
                           d_gate_c=self.dgcp if gcp is not None else None,
@@ -141,11 +147,10 @@ class VsaBackward:
                               self.ws_fine, stream)
         L.vsa_coarse_bwd(p, saved["qc"], saved["kc"], saved["vc"], saved["oc"], self.d_oc, self.dqc, self.dkc,
                          self.dvc, self.ws_coarse, stream)
-        pkv = p.kv_problem()
         L.vsa_pool_unpermute_bwd(p, self.dqf, self.dqc, dq, stream)
-        L.vsa_pool_unpermute_bwd(pkv, self.dkf, self.dkc, dk, stream)
-        L.vsa_pool_unpermute_bwd(pkv, self.dvf, self.dvc, dv, stream)
+        L.vsa_pool_unpermute_bwd(p.kv_problem(), self.dkf, self.dkc, dk, stream)
+        L.vsa_pool_unpermute_bwd(p.v_problem(), self.dvf, self.dvc, dv, stream)
         if gcp is not None and dgate_c is not None:
-            L.vsa_pool_unpermute_bwd(p, self.dgcp, None, dgate_c, stream)
+            L.vsa_pool_unpermute_bwd(po, self.dgcp, None, dgate_c, stream)
         if gfp is not None and dgate_f is not None:
-            L.vsa_pool_unpermute_bwd(p, self.dgfp, None, dgate_f, stream)
+            L.vsa_pool_unpermute_bwd(po, self.dgfp, None, dgate_f, stream)

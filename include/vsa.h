@@ -88,9 +88,9 @@ typedef struct vsa_problem {
                            softmax scale stays 1/sqrt(head_dim).  The
                            single-tensor reorders and pools work on
                            p->head_dim: for V pass a problem whose head_dim
-                           is head_dim_v.  The backward entry points require
-                           head_dim_v == head_dim (VSA_ERR_UNSUPPORTED
-                           otherwise). */
+                           is head_dim_v.  In the backward, O, dO, dV, dVc,
+                           dO_c and the gate gradients are head_dim_v wide
+                           as well. */
   const int32_t* cube_coords;  /* device array of Nc packed cube coordinates
                            written by vsa_cube_table for this problem and
                            copied to the device by the caller.  Required
@@ -301,13 +301,14 @@ int vsa_sparse_attn_bwd_workspace_size(const vsa_problem* p,
  * cubes no row lists get dk = dv = 0, rows with count 0 get dq = 0.
  * q, k, v, kv_block_idx, valid_block_num, max_kv_blocks: exactly as passed to
  *   vsa_sparse_attn_fwd (cube-major; every listed entry in [0, Nc)).
- * o:   [batch, heads, N, head_dim] bf16, cube-major: O_f, i.e. the out of
+ * o:   [batch, heads, N, head_dim_v] bf16, cube-major: O_f, i.e. the out of
  *      vsa_sparse_attn_fwd called with gate_c == NULL and gate_f == NULL.
  * lse: [batch, heads, N] float32, cube-major: the lse of that call.
- * d_o: [batch, heads, N, head_dim] bf16, cube-major: the gradient of the loss
+ * d_o: [batch, heads, N, head_dim_v] bf16, cube-major: the gradient of the loss
  *      with respect to O_f (the gates' own chain rule, elementwise, is the
  *      caller's).
- * dq, dk, dv: [batch, heads, N, head_dim] float32, cube-major, fully written
+ * dq, dk, dv: [batch, heads, N, head_dim] float32 (dv head_dim_v wide),
+ *      cube-major, fully written
  *      (no accumulation into prior contents); the products run on bf16 MFMA
  *      with float32 accumulation, P and dS rounded to bf16 as operands.
  * workspace: device memory of workspace_bytes >= the size
@@ -334,9 +335,9 @@ int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k,
  *   d_gate_f[p] = dout[p] * O_f[p],  d_gate_c[p] = dout[p] * oc[c(p)]  (float32)
  * gate_f == NULL means g_f = 1 (then o_f and d_gate_f may be NULL);
  * gate_c == NULL means g_c = 0 (then oc and d_gate_c may be NULL).
- * dout, o_f, gate_c, gate_f, d_of: [batch, heads, N, head_dim] bf16;
+ * dout, o_f, gate_c, gate_f, d_of: [batch, heads, N, head_dim_v] bf16;
  * d_gate_c, d_gate_f: same shape float32; oc, d_oc: [batch, heads, Nc,
- * head_dim] float32.  All token tensors cube-major (vsa_permute them). */
+ * head_dim_v] float32.  All token tensors cube-major (vsa_permute them). */
 int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f,
                     const float* oc, const void* gate_c, const void* gate_f,
                     void* d_of, float* d_oc, float* d_gate_c, float* d_gate_f,
@@ -353,7 +354,8 @@ int vsa_coarse_bwd_workspace_size(const vsa_problem* p, size_t* bytes);
  *   dvc = P^T d_oc,  dS = P * (d_oc vc^T - Dc),
  *   dqc = dS kc / sqrt(head_dim),  dkc = dS^T qc / sqrt(head_dim).
  * qc, kc, vc, oc (the forward's O_c), d_oc, dqc, dkc, dvc: [batch, heads, Nc,
- * head_dim] float32, computed in float32.  workspace of workspace_bytes >=
+ * head_dim] float32 (vc, oc, d_oc and dvc head_dim_v wide), computed in
+ * float32.  workspace of workspace_bytes >=
  * vsa_coarse_bwd_workspace_size, else VSA_ERR_WORKSPACE; clobbered.
  * Nc <= 4096. */
 int vsa_coarse_bwd(const vsa_problem* p, const float* qc, const float* kc,

@@ -109,13 +109,14 @@ def test_value_head_size_errors():
     assert lib.vsa_perm_index(ctypes.byref(bad), DUMMY) == L.VSA_ERR_UNSUPPORTED
     hv = ctypes.byref(L.Problem(1, 2, 8, 16, 16, 4, 4, 4, 128, head_dim_v=64).c_struct())
     n = ctypes.c_size_t(0)
-    # the backward of a layer whose value head size differs is not provided
-    assert lib.vsa_sparse_attn_bwd_workspace_size(hv, 4, ctypes.byref(n)) == L.VSA_ERR_UNSUPPORTED
+    # the backward sizes do not depend on the value head size
+    assert lib.vsa_sparse_attn_bwd_workspace_size(hv, 4, ctypes.byref(n)) == L.VSA_OK
+    same = ctypes.c_size_t(0)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(_prob(head_dim=128)), 4, ctypes.byref(same)) == \
+        L.VSA_OK and same.value == n.value
     assert lib.vsa_sparse_attn_bwd(hv, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
-                                   DUMMY, DUMMY, 1 << 30, None) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_coarse_bwd_workspace_size(hv, ctypes.byref(n)) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_combine_bwd(hv, DUMMY, None, None, None, None, DUMMY, DUMMY, None, None, None) == \
-        L.VSA_ERR_UNSUPPORTED
+                                   DUMMY, DUMMY, 1, None) == L.VSA_ERR_WORKSPACE
+    assert lib.vsa_coarse_bwd_workspace_size(hv, ctypes.byref(n)) == L.VSA_OK
     # the forward validates as usual before any launch
     assert lib.vsa_sparse_attn_fwd(hv, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 0, None, None, None, DUMMY, None,
                                    None) == L.VSA_ERR_TOPK

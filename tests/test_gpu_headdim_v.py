@@ -3,7 +3,8 @@
 scale is 1/sqrt of the query/key width).  (d, d_v) in {(128, 64), (64, 128)}.
 
 Bars as for equal head sizes: Top-K sets tie-tolerant, O_c within 1e-4,
-attention outputs max-abs 2e-2 and mean-abs 2e-3, LSE within 1e-3.  Every
+attention outputs max-abs 2e-2 and mean-abs 2e-3, LSE within 1e-3, gradients
+max 2% of max |grad| and mean 1% of mean |grad|.  Every
 input is a seeded draw; nothing the oracle sees comes from the GPU.
 """
 import math
@@ -15,7 +16,7 @@ import torch
 import oracle
 from block_sparse_video_major_amd import _lib as L
 from block_sparse_video_major_amd import workloads as wl
-from block_sparse_video_major_amd.pipeline import VsaForward
+from block_sparse_video_major_amd.pipeline import VsaBackward, VsaForward
 from gpu_helpers import (LSE_MAX_ABS, OC_MAX_ABS, assert_out_close, bits, check_lut_against_scores, dev, err,
                          host64)
 
@@ -161,3 +162,104 @@ def test_pipeline_other_value_width(d, dv):
                               gate_f=f64(gf), kv_block_idx=lut_g, valid_block_num=valid_g)
     mx, mean = assert_out_close(host64(out), want["out"], "pipeline out")
     print(f"tie-window rows {differ}; max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+def _grad_check(name, got, ref):
+    g, r = host64(got), np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite"
+    e = np.abs(g - r)
+    mx, mn = e.max() / max(np.abs(r).max(), 1e-30), e.mean() / max(np.abs(r).mean(), 1e-30)
+    print(f"{name}: max {mx:.2e} of max, mean {mn:.2e} of mean")
+    assert mx <= 2e-2 and mn <= 1e-2, name
+
+
+@pytest.mark.parametrize("d,dv,hk", [(128, 64, 2), (64, 128, 4), (64, 128, 1)])
+def test_sparse_attn_bwd_other_value_width(d, dv, hk):
+    """Fine-stage gradients (every element) against the oracle's, on the
+    oracle's O_f and LSE; rows with repeats, varying counts, one empty row.
+    Bars of the fine backward: max 2% of max |grad|, mean 1% of mean |grad|."""
+    B, nh, T, H, W = 1, 4, 8, 16, 16
+    _log(f"sparse_attn_bwd d={d} d_v={dv} kv heads {hk}")
+    p = L.Problem(B, nh, T, H, W, 4, 4, 4, d, heads_kv=hk if hk != nh else 0, head_dim_v=dv)
+    nc, g = p.n_cubes, nh // hk
+    rng = np.random.default_rng(124)
+    qp = _bf(rng.standard_normal((B, nh, p.n_positions, d)))
+    kp = _bf(rng.standard_normal((B, hk, p.n_positions, d)))
+    vp = _bf(rng.standard_normal((B, hk, p.n_positions, dv)))
+    maxk = 9
+    lut = rng.integers(0, nc, size=(B, nh, nc, maxk)).astype(np.int32)
+    valid = rng.integers(1, maxk + 1, size=(B, nh, nc)).astype(np.int32)
+    valid[0, 0, 2] = 0
+    lut[0, 1, 0, :3] = 5
+    f64 = wl.as_float64
+    q64, k64, v64 = f64(qp), oracle.expand_kv_heads(f64(kp), g), oracle.expand_kv_heads(f64(vp), g)
+    scale = 1 / math.sqrt(d)
+    of, lse = oracle.fine_attention(q64, k64, v64, lut, valid, scale, 64)
+    of_bits = _bf(of)
+    lse32 = lse.astype(np.float32)
+    dof_bits = _bf(rng.standard_normal(of.shape))
+    dq = torch.full((B, nh, p.n_positions, d), float("nan"), device="cuda")
+    dk = torch.full((B, hk, p.n_positions, d), float("nan"), device="cuda")
+    dvt = torch.full((B, hk, p.n_positions, dv), float("nan"), device="cuda")
+    ws = torch.full((L.vsa_sparse_attn_bwd_workspace_size(p, maxk),), 0xA5, dtype=torch.uint8, device="cuda")
+    L.vsa_sparse_attn_bwd(p, dev(qp), dev(kp), dev(vp), dev(lut), dev(valid), dev(of_bits), dev(lse32),
+                          dev(dof_bits), dq, dk, dvt, ws)
+    torch.cuda.synchronize()
+    ref = oracle.fine_attention_bwd(q64, k64, v64, lut, valid, scale, 64, f64(of_bits), lse32.astype(np.float64),
+                                    f64(dof_bits))
+    _grad_check("dq", dq, ref[0])
+    _grad_check("dk", dk, oracle.reduce_kv_heads(ref[1], g))
+    _grad_check("dv", dvt, oracle.reduce_kv_heads(ref[2], g))
+    assert np.all(host64(dq)[0, 0, 2 * 64:3 * 64] == 0.0)   # the empty row
+
+
+@pytest.mark.parametrize("dims,hk", [((1, 4, 8, 16, 16, 128, 64), 2), ((1, 2, 5, 7, 9, 64, 128), 0),
+                                     ((1, 4, 6, 8, 8, 64, 128), 1)], ids=["8x16x16-128-64-gqa",
+                                                                         "5x7x9-padded-64-128",
+                                                                         "6x8x8-padded-64-128-gqa"])
+def test_layer_backward_other_value_width(dims, hk):
+    """GPU forward (reorder + pool, coarse, fine without gates for O_f and
+    LSE) then VsaBackward, against the oracle's vsa_backward."""
+    B, nh, T, H, W, d, dv = dims
+    _log(f"layer backward {dims} kv heads {hk or nh}")
+    p = L.Problem(B, nh, T, H, W, 4, 4, 4, d, heads_kv=hk, head_dim_v=dv)
+    hkv = p.kv_heads
+    rng = np.random.default_rng(125)
+    q = _bf(rng.standard_normal((B, nh, p.n_tokens, d)))
+    k = _bf(rng.standard_normal((B, hkv, p.n_tokens, d)))
+    v = _bf(rng.standard_normal((B, hkv, p.n_tokens, dv)))
+    dout = _bf(rng.standard_normal((B, nh, p.n_tokens, dv)))
+    gc, gf = (_bf(rng.random((B, nh, p.n_tokens, dv))) for _ in range(2))
+    maxk = 6
+    lut = rng.integers(0, p.n_cubes, size=(B, nh, p.n_cubes, maxk)).astype(np.int32)
+    valid = rng.integers(1, maxk + 1, size=(B, nh, p.n_cubes)).astype(np.int32)
+    np_, nc = p.n_positions, p.n_cubes
+    bf = torch.bfloat16
+    saved = {"qp": torch.empty((B, nh, np_, d), dtype=bf, device="cuda"),
+             "kp": torch.empty((B, hkv, np_, d), dtype=bf, device="cuda"),
+             "vp": torch.empty((B, hkv, np_, dv), dtype=bf, device="cuda"),
+             "qc": torch.empty((B, nh, nc, d), device="cuda"), "oc": torch.empty((B, nh, nc, dv), device="cuda"),
+             "kc": torch.empty((B, hkv, nc, d), device="cuda"), "vc": torch.empty((B, hkv, nc, dv), device="cuda"),
+             "kv_block_idx": dev(lut), "valid_block_num": dev(valid)}
+    L.vsa_permute_pool(p, L.VSA_BF16, dev(q), saved["qp"], saved["qc"])
+    L.vsa_permute_pool(p.kv_problem(), L.VSA_BF16, dev(k), saved["kp"], saved["kc"])
+    L.vsa_permute_pool(p.v_problem(), L.VSA_BF16, dev(v), saved["vp"], saved["vc"])
+    tl = torch.empty((B, nh, nc, 1), dtype=torch.int32, device="cuda")
+    tv = torch.empty((B, nh, nc), dtype=torch.int32, device="cuda")
+    L.vsa_coarse_topk(p, 1, saved["qc"], saved["kc"], saved["vc"], tl, tv, saved["oc"])
+    o_f = torch.empty((B, nh, np_, dv), dtype=bf, device="cuda")
+    lse = torch.empty((B, nh, np_), device="cuda")
+    L.vsa_sparse_attn_fwd(p, saved["qp"], saved["kp"], saved["vp"], saved["kv_block_idx"],
+                          saved["valid_block_num"], o_f, lse=lse)
+    dq = torch.full((B, nh, p.n_tokens, d), float("nan"), device="cuda")
+    dk = torch.full((B, hkv, p.n_tokens, d), float("nan"), device="cuda")
+    dvt = torch.full((B, hkv, p.n_tokens, dv), float("nan"), device="cuda")
+    dgc, dgf = (torch.full((B, nh, p.n_tokens, dv), float("nan"), device="cuda") for _ in range(2))
+    VsaBackward(p, maxk)(saved, o_f, lse, dev(dout), dq, dk, dvt, gate_c=dev(gc), gate_f=dev(gf),
+                         dgate_c=dgc, dgate_f=dgf)
+    torch.cuda.synchronize()
+    f64 = wl.as_float64
+    ref = oracle.vsa_backward(f64(q), f64(k), f64(v), (T, H, W), (4, 4, 4), lut, valid, f64(dout),
+                              gate_c=f64(gc), gate_f=f64(gf))
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dvt), ("dgate_c", dgc), ("dgate_f", dgf)):
+        _grad_check(nm, t, ref[nm])
