@@ -34,13 +34,18 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, published
 MI355X_HBM_PEAK_GBPS = 8000.0        # HBM3E, published
-FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_major_amd", "csrc", "sparse_attn_fwd.hip")
+# the fine kernel's source and the headers it includes
+FINE_SOURCES = [os.path.join(ROOT, "block_sparse_video_major_amd", "csrc", n)
+                for n in ("sparse_attn_fwd.hip", "token_map.h", "mfma_util.h", "vsa_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_wan_traffic.md")
 
 
 def _fine_source_hash() -> str:
-    with open(FINE_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in FINE_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _measured_traffic():
