@@ -386,7 +386,63 @@ def main() -> int:
                 torch.cuda.synchronize()
                 dvres[(dq_, dv_)] = (t_fwd, e0.elapsed_time(e1) / reps)
                 del qx, kx, vx, ocx, ox, of_x, lse_x, do_x, gx, wsx
-            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres
+
+            # the latent grid of an 832 x 480, 81-frame video (21 x 30 x 52 =
+            # 32,760 tokens), which does not divide into 4 x 4 x 4 cubes: padded
+            # to 24 x 32 x 52 positions (624 cubes), Top-K 187 (70% sparsity)
+            pp = dataclasses.replace(p, T=21, H=30, W=52, cube_order="raster")
+            kp_ = int(0.3 * pp.n_cubes)
+            gpad = torch.Generator(device=dev).manual_seed(7)
+            xs = [torch.randn((w.batch, w.heads, pp.n_tokens, w.head_dim), generator=gpad, device=dev)
+                  .to(torch.bfloat16) for _ in range(3)]
+            fpad = vsa.VsaForward(pp, kp_, dev)
+            opad = torch.empty_like(xs[0])
+
+            def pstep(ev=None):
+                L.vsa_permute_pool(pp, B, xs[0], fpad.qp, fpad.qc, stream)
+                L.vsa_permute_pool(pp, B, xs[1], fpad.kp, fpad.kc, stream)
+                L.vsa_permute_pool(pp, B, xs[2], fpad.vp, fpad.vc, stream)
+                L.vsa_coarse_topk(pp, kp_, fpad.qc, fpad.kc, fpad.vc, fpad.lut, fpad.valid, fpad.oc, stream)
+                if ev is not None:
+                    ev[0].record(stream)
+                L.vsa_sparse_attn_fwd_raster(pp, fpad.qp, fpad.kp, fpad.vp, fpad.lut, fpad.valid, opad, oc=fpad.oc,
+                                             stream=stream)
+                if ev is not None:
+                    ev[1].record(stream)
+            pstep()
+            torch.cuda.synchronize()
+            pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            for i in range(reps):
+                pstep(pe[i])
+            p1.record(stream)
+            torch.cuda.synchronize()
+            pad_step = p0.elapsed_time(p1) / reps
+            pad_fine = float(np.mean([a.elapsed_time(b) for a, b in pe]))
+            of_p = torch.empty_like(fpad.qp)
+            lse_p = torch.empty((w.batch, w.heads, pp.n_positions), dtype=torch.float32, device=dev)
+            L.vsa_sparse_attn_fwd(pp, fpad.qp, fpad.kp, fpad.vp, fpad.lut, fpad.valid, of_p, lse=lse_p, stream=stream)
+            do_p = torch.randn(of_p.shape, generator=gpad, device=dev).to(torch.bfloat16)
+            gp = [torch.empty(of_p.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+            wsp = torch.empty(L.vsa_sparse_attn_bwd_workspace_size(pp, kp_), dtype=torch.uint8, device=dev)
+
+            def pbwd():
+                L.vsa_sparse_attn_bwd(pp, fpad.qp, fpad.kp, fpad.vp, fpad.lut, fpad.valid, of_p, lse_p, do_p, *gp, wsp,
+                                      stream)
+            pbwd()
+            torch.cuda.synchronize()
+            p0.record(stream)
+            for _ in range(reps):
+                pbwd()
+            p1.record(stream)
+            torch.cuda.synchronize()
+            pad_bwd = p0.elapsed_time(p1) / reps
+            pad = {"grid": "21x30x52", "tokens": pp.n_tokens, "positions": pp.n_positions, "cubes": pp.n_cubes,
+                   "top_k": kp_, "pairs": w.batch * w.heads * pp.n_cubes * kp_, "step_ms": pad_step,
+                   "fine_ms": pad_fine, "bwd_ms": pad_bwd}
+            del xs, fpad, opad, of_p, lse_p, do_p, gp, wsp
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
@@ -425,7 +481,8 @@ def main() -> int:
                      "traffic": _measured_traffic()},
     }
     if ex is not None:
-        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres = ex
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad = ex
+        pad_fl = 4 * 64 * 64 * w.head_dim * pad["pairs"]   # per selected pair, padded positions included
         rec.update({
             "stages_ms": {n: round(t, 4) for n, t in acc.items()},
             "stages_gbps": {"permute_qkv": round(permute_bytes / (acc["permute_qkv"] * 1e-3) / 1e9, 1),
@@ -454,6 +511,15 @@ def main() -> int:
                               "fine_tflops": round(flops / (hil["fine_ms"] * 1e-3) / 1e12, 2),
                               "bwd_ms_per_call": round(hil["bwd_ms"], 4),
                               "bwd_tflops": round(2.5 * flops / (hil["bwd_ms"] * 1e-3) / 1e12, 2)},
+            "padded_grid": {"note": "latent grid of an 832x480, 81-frame video: 21x30x52 tokens padded to whole "
+                                    "4x4x4 cubes; FLOPs per selected cube pair as for the main line",
+                            "grid": pad["grid"], "tokens": pad["tokens"], "positions": pad["positions"],
+                            "cubes": pad["cubes"], "top_k": pad["top_k"],
+                            "ms_per_step": round(pad["step_ms"], 4),
+                            "fine_ms_per_call": round(pad["fine_ms"], 4),
+                            "fine_tflops": round(pad_fl / (pad["fine_ms"] * 1e-3) / 1e12, 2),
+                            "bwd_ms_per_call": round(pad["bwd_ms"], 4),
+                            "bwd_tflops": round(2.5 * pad_fl / (pad["bwd_ms"] * 1e-3) / 1e12, 2)},
             "value_head_size": {
                 "note": "fine stage with d_v != d (its own forward kernel), the step's Top-K LUT, raster output "
                         "with O_c; FLOPs 2*64*64*(d + d_v) per selected pair; fine backward on the same LUT, "
