@@ -603,6 +603,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (PAD) {
+        // The masking branch below would otherwise let the compiler sink the
+        // exponentials past it, next to the PV products that consume them,
+        // where nothing overlaps them: keep them with the QK products.
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        asm volatile("" ::"v"(__builtin_bit_cast(i32x4, pb[0])), "v"(__builtin_bit_cast(i32x4, pb[1])),
+                     "v"(l_part));
+      }
       // A key tile that reaches past the grid: its padded positions are not
       // keys (score -inf, so they add nothing to the row max or the sum).
       if (PAD && ((d_c >> (30 + grp)) & 1u)) {
