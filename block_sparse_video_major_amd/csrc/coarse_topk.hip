@@ -27,6 +27,8 @@
 //            row groups and the partial sums are added in a fixed order.
 // The scale 1/sqrt(d) > 0 does not change the ranking, so ranking uses the
 // raw scores.
+#include <mutex>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -300,8 +302,17 @@ static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const fl
   const float scale = 1.0f / sqrtf((float)DQ);
   auto k = coarse_topk_kernel<DQ, DV, R, NS, T>;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // the granted size only grows, under a lock: host threads may launch concurrently
+    static std::mutex mu;
+    static int granted[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (granted[dev] < (int)lds) {
+      const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      granted[dev] = (int)lds;
+    }
   }
   hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(T), lds, s, qc, kc, vc, lut, valid, oc, Nc, top_k,
                      tiles, scale, g.group);

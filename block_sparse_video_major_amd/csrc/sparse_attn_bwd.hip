@@ -57,6 +57,8 @@
 //     ~700 cycles of vector issue, and barrier plus load wait ~300.
 //   * Workgroups are mapped to XCDs in contiguous ranges of cubes, so the
 //     workgroups sharing an L2 walk overlapping lists.
+#include <mutex>
+
 #include "tile_ops.h"
 
 namespace vsa {
@@ -678,6 +680,8 @@ constexpr int dkdv_lds() {
 
 template <typename K>
 hipError_t grant_lds(K kern, int bytes, int& granted) {
+  static std::mutex mu;   // host threads may launch concurrently
+  std::lock_guard<std::mutex> lock(mu);
   if (granted >= bytes) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess) granted = bytes;

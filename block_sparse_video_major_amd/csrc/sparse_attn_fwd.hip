@@ -63,6 +63,8 @@
 //     gains about 5%; the per-step barrier and the scalar bookkeeping of the
 //     schedule (slot, offset and wait arithmetic) cost more, because every
 //     wave issues them between its MFMAs.
+#include <mutex>
+
 #include "mfma_util.h"
 #include "token_map.h"
 #include "vsa_internal.h"
@@ -739,6 +741,7 @@ struct DevState {
 };
 
 constexpr int kLdsMax = 160 * 1024;
+std::mutex dev_state_mutex;
 
 template <int D, int RK, int RV, bool PAD>
 hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
@@ -754,21 +757,27 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   size_t lds = (size_t)(RK + RV) * C::TILE + sched_bytes;
   if (lds < (size_t)C::EPI_BYTES) lds = C::EPI_BYTES;
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
-  if (st.lds_granted[slot] < (int)lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    st.lds_granted[slot] = (int)lds;
-  }
-  if (st.cus == 0) {
-    int cus = 0;
-    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (cus <= 0) return hipErrorInvalidDevice;
-    st.cus = cus;
+  int cus = 0;
+  {
+    // host threads may launch concurrently: grant and record under one lock
+    std::lock_guard<std::mutex> lock(dev_state_mutex);
+    if (st.lds_granted[slot] < (int)lds) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      st.lds_granted[slot] = (int)lds;
+    }
+    if (st.cus == 0) {
+      hipError_t e = hipDeviceGetAttribute(&st.cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess || st.cus <= 0) {
+        st.cus = 0;
+        return e != hipSuccess ? e : hipErrorInvalidDevice;
+      }
+    }
+    cus = st.cus;
   }
   const int64_t total_pairs = g.BH * ((g.Nc + 1) / 2);
   // persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD)
-  int64_t grid = ((int64_t)st.cus + 7) / 8 * 8;
+  int64_t grid = ((int64_t)cus + 7) / 8 * 8;
   const int64_t need = (total_pairs + 7) / 8 * 8;
   if (grid > need) grid = need;
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);

@@ -29,6 +29,8 @@
 //     normalised and staged in LDS, then combined with the gates and the
 //     broadcast coarse output and written with 16-byte stores in the token
 //     order of the map (cube-major, raster, or [batch, N, heads, d]).
+#include <mutex>
+
 #include "tile_ops.h"
 #include "token_map.h"
 
@@ -247,10 +249,14 @@ hipError_t launch_dv(const Geom& g, const void* q, const void* k, const void* v,
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   constexpr int lds = DvCfg<DQ, DV>::LDS;
   auto kern = sparse_attn_fwd_dv_kernel<DQ, DV, PAD>;
-  if (granted[dev] < lds) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    granted[dev] = lds;
+  {
+    static std::mutex mu;   // host threads may launch concurrently
+    std::lock_guard<std::mutex> lock(mu);
+    if (granted[dev] < lds) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      granted[dev] = lds;
+    }
   }
   const int64_t total_cubes = g.BH * g.Nc;
   const float c_log2 = kLog2e / sqrtf((float)DQ);
