@@ -120,7 +120,7 @@ enum {
   VSA_ERR_NULL = -1,        /* a required pointer is NULL (or gate_c without oc) */
   VSA_ERR_SHAPE = -2,       /* a size <= 0, heads_kv not dividing heads, or sizes overflow */
   VSA_ERR_TOPK = -3,        /* top_k / max_kv_blocks outside [1, Nc] */
-  VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume this build does not handle */
+  VSA_ERR_UNSUPPORTED = -4, /* head_dim, dtype or cube volume the library does not handle */
   VSA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
   VSA_ERR_LUT = -6,         /* reserved for LUT validation results */
   VSA_ERR_WORKSPACE = -7    /* workspace_bytes below what the workspace query reports */

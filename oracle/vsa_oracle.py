@@ -17,8 +17,7 @@ Every function works in float64 on the exact values it is given (bf16 and
 float32 inputs widen to float64 without rounding).  There is no blocking,
 fusion or reordering beyond what each step states.
 
-Readings taken where the pages leave a step open (each is listed again in
-DESIGN.md):
+Readings taken where the pages leave a step open:
 
 * R1 the "3D space-filling curve" order is cube-major: cubes in raster order
   over the cube grid, tokens in raster order inside a cube.
