@@ -1,4 +1,4 @@
-"""MI355X-native Video Sparse Attention (VSA) forward pass.
+"""MI355X-native Video Sparse Attention (VSA): the forward pass and its backward.
 
 The compute lives in libvsa.so (hand-written HIP kernels for gfx950, C ABI in
 include/vsa.h); this package is its Python binding plus the seeded synthetic
@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
     vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
+    vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT,
 )
 from .pipeline import VsaBackward, VsaForward, vsa_forward  # noqa: F401
 
@@ -25,4 +26,5 @@ __all__ = [
     "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
+    "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT",
 ]
