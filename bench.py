@@ -442,7 +442,39 @@ def main() -> int:
                    "top_k": kp_, "pairs": w.batch * w.heads * pp.n_cubes * kp_, "step_ms": pad_step,
                    "fine_ms": pad_fine, "bwd_ms": pad_bwd}
             del xs, fpad, opad, of_p, lse_p, do_p, gp, wsp
-            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad
+
+            # the large layer: grid 32 x 48 x 80 (122,880 tokens), 40 heads,
+            # Top-K 192 of 1,920 cubes; seeded device inputs, the step timed
+            wL = wl.WORKLOADS["large"]
+            pl = vsa.Problem(wL.batch, wL.heads, wL.T, wL.H, wL.W, *wL.cube, wL.head_dim)
+            xl = [torch.randn((wL.batch, wL.heads, wL.n_tokens, wL.head_dim), generator=gpad, device=dev)
+                  .to(torch.bfloat16) for _ in range(3)]
+            fl_ = vsa.VsaForward(pl, wL.top_k, dev)
+            ol = torch.empty_like(xl[0])
+
+            def lstep(ev=None):
+                for t, a, c in ((xl[0], fl_.qp, fl_.qc), (xl[1], fl_.kp, fl_.kc), (xl[2], fl_.vp, fl_.vc)):
+                    L.vsa_permute_pool(pl, B, t, a, c, stream)
+                L.vsa_coarse_topk(pl, wL.top_k, fl_.qc, fl_.kc, fl_.vc, fl_.lut, fl_.valid, fl_.oc, stream)
+                if ev is not None:
+                    ev[0].record(stream)
+                L.vsa_sparse_attn_fwd_raster(pl, fl_.qp, fl_.kp, fl_.vp, fl_.lut, fl_.valid, ol, oc=fl_.oc,
+                                             stream=stream)
+                if ev is not None:
+                    ev[1].record(stream)
+            lstep()
+            torch.cuda.synchronize()
+            le = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+            p0.record(stream)
+            for i in range(3):
+                lstep(le[i])
+            p1.record(stream)
+            torch.cuda.synchronize()
+            large = {"step_ms": p0.elapsed_time(p1) / 3, "fine_ms": float(np.mean([a.elapsed_time(b) for a, b in le])),
+                     "flops": wL.selected_flops(), "top_k": wL.top_k, "cubes": wL.n_cubes, "heads": wL.heads,
+                     "tokens": wL.n_tokens}
+            del xl, fl_, ol
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
@@ -481,7 +513,7 @@ def main() -> int:
                      "traffic": _measured_traffic()},
     }
     if ex is not None:
-        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad = ex
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large = ex
         pad_fl = 4 * 64 * 64 * w.head_dim * pad["pairs"]   # per selected pair, padded positions included
         rec.update({
             "stages_ms": {n: round(t, 4) for n, t in acc.items()},
@@ -520,6 +552,11 @@ def main() -> int:
                             "fine_tflops": round(pad_fl / (pad["fine_ms"] * 1e-3) / 1e12, 2),
                             "bwd_ms_per_call": round(pad["bwd_ms"], 4),
                             "bwd_tflops": round(2.5 * pad_fl / (pad["bwd_ms"] * 1e-3) / 1e12, 2)},
+            "large_workload": {"note": "grid 32x48x80, 40 heads, d=128, seeded device inputs",
+                               "tokens": large["tokens"], "heads": large["heads"], "cubes": large["cubes"],
+                               "top_k": large["top_k"], "ms_per_step": round(large["step_ms"], 3),
+                               "fine_ms_per_call": round(large["fine_ms"], 3),
+                               "fine_tflops": round(large["flops"] / (large["fine_ms"] * 1e-3) / 1e12, 2)},
             "value_head_size": {
                 "note": "fine stage with d_v != d (its own forward kernel), the step's Top-K LUT, raster output "
                         "with O_c; FLOPs 2*64*64*(d + d_v) per selected pair; fine backward on the same LUT, "
