@@ -61,21 +61,24 @@ def _measured_traffic():
     return float(m_b.group(1))
 
 
-def cpu_baseline(seconds_budget: float = 20.0):
-    """Time the fp64 oracle on a bounded sample of the Wan workload: the whole
-    forward (reorder, pool, coarse, Top-K, fine, combine, reorder back) for
-    one head, extended head by head while the budget allows."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_heads(w, seconds_budget: float, max_heads: int):
+    """Whole oracle forward passes, head by head, while the budget allows.
+    Returns (heads done, seconds, FLOPs counted as in `value`)."""
     import oracle
     from block_sparse_video_major_amd import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
-    w = wl.WAN
     heads_done, t_total, flops = 0, 0.0, 0
-    for h in range(w.heads):
+    for h in range(min(w.heads, max_heads)):
         x = wl.make_inputs(w, heads=[h], workers=1)
         x64 = {n: wl.as_float64(a) for n, a in x.items()}
         t0 = time.perf_counter()
@@ -85,9 +88,38 @@ def cpu_baseline(seconds_budget: float = 20.0):
         flops += 4 * w.n_tokens * w.cube_volume * w.top_k * w.head_dim
         if t_total * (heads_done + 1) / heads_done > seconds_budget:
             break
+    return heads_done, t_total, flops
+
+
+def cpu_baseline(seconds_budget: float = 20.0):
+    """Time the fp64 oracle on a bounded sample of the Wan workload: the whole
+    forward (reorder, pool, coarse, Top-K, fine, combine, reorder back) for
+    whole heads, once with every BLAS thread the host offers and once with a
+    single thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from block_sparse_video_major_amd import workloads as wl
+    w = wl.WAN
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    heads_done, t_total, flops = _oracle_heads(w, seconds_budget, w.heads)
+    with threadpool_limits(limits=1):
+        h1, t1, f1 = _oracle_heads(w, seconds_budget, 1)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        affinity = os.cpu_count() or 1
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads_done} of {w.heads} heads of the 32,768-token workload, full forward in fp64 "
-                      f"({t_total:.1f} s; same FLOP accounting as value)"}
+                      f"({t_total:.1f} s with {threads} BLAS threads; same FLOP accounting as value)",
+            "one_thread": {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                           "sample": f"{h1} head, full forward in fp64 ({t1:.1f} s)"},
+            "nproc": os.cpu_count(), "cpus_allowed": affinity, "cpu_model": _cpu_model()}
+
+
+def _stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4), "n": int(a.size)}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
@@ -104,8 +136,8 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--top-k", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -137,9 +169,10 @@ def main() -> int:
 
     w = wl.WAN if args.top_k is None else wl.WAN.with_top_k(args.top_k)
     p = vsa.Problem(w.batch, w.heads, w.T, w.H, w.W, *w.cube, w.head_dim, cube_order=args.cube_order)
-    x = wl.make_inputs(w)
+    x = wl.make_inputs(w, with_gates=True)   # gates are drawn after V: Q, K, V do not depend on them
     dev = torch.device("cuda:0")
-    q, k, v = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    q, k, v, gate_c, gate_f = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev)
+                               for n in ("q", "k", "v", "gate_c", "gate_f"))
     del x
     f = vsa.VsaForward(p, w.top_k, dev)
     out = torch.empty_like(q)
@@ -147,34 +180,67 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
     B = L.VSA_BF16
 
-    def step(ev0=None, ev1=None, p=p, f=f):
+    def step(ev0=None, ev1=None, p=p, f=f, gates=False):
         L.vsa_permute_pool(p, B, q, f.qp, f.qc, stream)
         L.vsa_permute_pool(p, B, k, f.kp, f.kc, stream)
         L.vsa_permute_pool(p, B, v, f.vp, f.vc, stream)
         L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
         if ev0 is not None:
             ev0.record(stream)
-        L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
+        L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc,
+                                     gate_c=gate_c if gates else None, gate_f=gate_f if gates else None,
+                                     stream=stream)
         if ev1 is not None:
             ev1.record(stream)
+
+    def new_events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def timed_steps(n, gates=False, flush=None):
+        """n steps, each bracketed by its own events (and its fine kernel by
+        another pair); with `flush`, a device write of that buffer (larger
+        than the 256 MB Infinity Cache) runs before every step, outside the
+        events.  Returns per-step and per-fine-kernel ms."""
+        st, fe = new_events(n), new_events(n)
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            st[i][0].record(stream)
+            step(*fe[i], gates=gates)
+            st[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in st], [a.elapsed_time(b) for a, b in fe]
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        ev, sev = new_events(args.steps), new_events(args.steps)
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t_start.record(stream)
         for i in range(args.steps):
+            sev[i][0].record(stream)
             step(*ev[i])
+            sev[i][1].record(stream)
         t_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_total = t_start.elapsed_time(t_end)
         fine_ms = [a.elapsed_time(b) for a, b in ev]
+        step_ms = [a.elapsed_time(b) for a, b in sev]
+        g_step = g_fine = c_step = c_fine = None
+        if not args.skip_extras:
+            # the same step with the gated combination of the fine and the
+            # coarse outputs (seeded gates in raster order), warm cache
+            timed_steps(3, gates=True)
+            g_step, g_fine = timed_steps(args.steps, gates=True)
+            # cold cache: a 1 GiB device write before every step
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            timed_steps(2, flush=flush)
+            c_step, c_fine = timed_steps(max(10, args.steps // 2), flush=flush)
+            del flush
 
         def extras():
             # per-stage breakdown (separate, untimed pass); the step runs the
@@ -393,8 +459,11 @@ def main() -> int:
             pp = dataclasses.replace(p, T=21, H=30, W=52, cube_order="raster")
             kp_ = int(0.3 * pp.n_cubes)
             gpad = torch.Generator(device=dev).manual_seed(7)
-            xs = [torch.randn((w.batch, w.heads, pp.n_tokens, w.head_dim), generator=gpad, device=dev)
-                  .to(torch.bfloat16) for _ in range(3)]
+            # seeded locality inputs (the Wan layer's recipe, field stride 8) on the padded grid
+            wpad = dataclasses.replace(w, name="padded", T=21, H=30, W=52, top_k=kp_, seed=6)
+            xpad = wl.make_inputs(wpad, workers=min(16, os.cpu_count() or 1))
+            xs = [torch.from_numpy(xpad[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v")]
+            del xpad
             fpad = vsa.VsaForward(pp, kp_, dev)
             opad = torch.empty_like(xs[0])
 
@@ -447,32 +516,44 @@ def main() -> int:
             # Top-K 192 of 1,920 cubes; seeded device inputs, the step timed
             wL = wl.WORKLOADS["large"]
             pl = vsa.Problem(wL.batch, wL.heads, wL.T, wL.H, wL.W, *wL.cube, wL.head_dim)
-            xl = [torch.randn((wL.batch, wL.heads, wL.n_tokens, wL.head_dim), generator=gpad, device=dev)
-                  .to(torch.bfloat16) for _ in range(3)]
+            # the seeded locality inputs of this workload (Q and K share a smooth
+            # field of stride 8, V ~ N(0, 1)), drawn on the host head by head
+            xlh = wl.make_inputs(wL, workers=min(16, os.cpu_count() or 1))
+            xl = []
+            for n in ("q", "k", "v"):
+                xl.append(torch.from_numpy(xlh[n].view(np.int16)).view(torch.bfloat16).to(dev))
+                del xlh[n]
+            del xlh
             fl_ = vsa.VsaForward(pl, wL.top_k, dev)
             ol = torch.empty_like(xl[0])
 
             def lstep(ev=None):
+                def mark(i):
+                    if ev is not None:
+                        ev[i].record(stream)
+                mark(0)
                 for t, a, c in ((xl[0], fl_.qp, fl_.qc), (xl[1], fl_.kp, fl_.kc), (xl[2], fl_.vp, fl_.vc)):
                     L.vsa_permute_pool(pl, B, t, a, c, stream)
+                mark(1)
                 L.vsa_coarse_topk(pl, wL.top_k, fl_.qc, fl_.kc, fl_.vc, fl_.lut, fl_.valid, fl_.oc, stream)
-                if ev is not None:
-                    ev[0].record(stream)
+                mark(2)
                 L.vsa_sparse_attn_fwd_raster(pl, fl_.qp, fl_.kp, fl_.vp, fl_.lut, fl_.valid, ol, oc=fl_.oc,
                                              stream=stream)
-                if ev is not None:
-                    ev[1].record(stream)
+                mark(3)
             lstep()
             torch.cuda.synchronize()
-            le = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+            nl = 5
+            le = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nl)]
             p0.record(stream)
-            for i in range(3):
+            for i in range(nl):
                 lstep(le[i])
             p1.record(stream)
             torch.cuda.synchronize()
-            large = {"step_ms": p0.elapsed_time(p1) / 3, "fine_ms": float(np.mean([a.elapsed_time(b) for a, b in le])),
-                     "flops": wL.selected_flops(), "top_k": wL.top_k, "cubes": wL.n_cubes, "heads": wL.heads,
-                     "tokens": wL.n_tokens}
+            lst = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in le]))
+                   for j, n in enumerate(("permute_pool_qkv", "coarse_topk", "sparse_attn_fwd_raster"))}
+            large = {"step_ms": p0.elapsed_time(p1) / nl, "fine_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in le])),
+                     "stages_ms": lst, "flops": wL.selected_flops(), "top_k": wL.top_k, "cubes": wL.n_cubes,
+                     "heads": wL.heads, "tokens": wL.n_tokens}
             del xl, fl_, ol
             return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large
         ex = None if args.skip_extras else extras()
@@ -508,10 +589,26 @@ def main() -> int:
         "fine_ms_per_call": round(fine_avg, 4),
         "fine_tflops": round(achieved, 2),
         "fine_pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
+        "timing": {"note": f"{args.steps} timed steps, each with its own HIP events on the kernels' stream",
+                   "step_ms": _stats(step_ms), "fine_ms": _stats(fine_ms)},
+    }
+    if g_step is not None:
+        rec.update({
+        "gated_step": {"note": "the same step with gate_c and gate_f (seeded U(0,1), raster order): "
+                               "out = g_f * O_f + g_c * O_c broadcast per cube, in the fine kernel's epilogue",
+                       "step_ms": _stats(g_step), "fine_ms": _stats(g_fine),
+                       "tflops_per_step": round(flops / (float(np.median(g_step)) * 1e-3) / 1e12, 2),
+                       "fine_tflops": round(flops / (float(np.median(g_fine)) * 1e-3) / 1e12, 2)},
+        "cold_cache": {"note": "a 1 GiB device write (beyond the 256 MB Infinity Cache) before every step, "
+                               "outside the timed events",
+                       "steps": len(c_step), "step_ms": _stats(c_step), "fine_ms": _stats(c_fine),
+                       "tflops_per_step": round(flops / (float(np.median(c_step)) * 1e-3) / 1e12, 2)},
+        })
+    rec.update({
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},
-    }
+    })
     if ex is not None:
         acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large = ex
         pad_fl = 4 * 64 * 64 * w.head_dim * pad["pairs"]   # per selected pair, padded positions included
@@ -552,10 +649,11 @@ def main() -> int:
                             "fine_tflops": round(pad_fl / (pad["fine_ms"] * 1e-3) / 1e12, 2),
                             "bwd_ms_per_call": round(pad["bwd_ms"], 4),
                             "bwd_tflops": round(2.5 * pad_fl / (pad["bwd_ms"] * 1e-3) / 1e12, 2)},
-            "large_workload": {"note": "grid 32x48x80, 40 heads, d=128, seeded device inputs",
+            "large_workload": {"note": "grid 32x48x80, 40 heads, d=128, seeded locality inputs (field stride 8)",
                                "tokens": large["tokens"], "heads": large["heads"], "cubes": large["cubes"],
                                "top_k": large["top_k"], "ms_per_step": round(large["step_ms"], 3),
                                "fine_ms_per_call": round(large["fine_ms"], 3),
+                               "stages_ms_median": {n: round(t, 3) for n, t in large["stages_ms"].items()},
                                "fine_tflops": round(large["flops"] / (large["fine_ms"] * 1e-3) / 1e12, 2)},
             "value_head_size": {
                 "note": "fine stage with d_v != d (its own forward kernel), the step's Top-K LUT, raster output "
