@@ -75,6 +75,13 @@ hipError_t launch_sparse_attn_fwd_dv(const Geom& g, const void* q, const void* k
                                      const int32_t* lut, const int32_t* valid, int max_kv, const float* oc,
                                      const void* gate_c, const void* gate_f, void* out, float* lse, int out_order,
                                      hipStream_t s);
+// The fine forward over quads of query cubes (d = d_v in {64, 128}), used
+// whenever its step list and load ring fit in LDS; same arguments as below.
+bool sparse_attn_fwd_quad_fits(const Geom& g, int max_kv);
+hipError_t launch_sparse_attn_fwd_quad(const Geom& g, const void* q, const void* k, const void* v,
+                                       const int32_t* lut, const int32_t* valid, int max_kv, const float* oc,
+                                       const void* gate_c, const void* gate_f, void* out, float* lse,
+                                       int out_order, hipStream_t s);
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,

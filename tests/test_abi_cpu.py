@@ -302,9 +302,10 @@ def test_sparse_attn_errors():
     assert call(prob=_prob(H=-4)) == L.VSA_ERR_SHAPE
     # 16-bit cube ids: Nc = 65536 is beyond the fine kernel
     assert call(prob=_prob(T=4, H=4, W=4 * 65536)) == L.VSA_ERR_UNSUPPORTED
-    # the per-row schedule must fit beside the tile ring in LDS (Nc = 4096)
-    big = _prob(T=64, H=64, W=64)
-    assert call(prob=big, maxkv=4000) == L.VSA_ERR_UNSUPPORTED
+    # the per-row (or per-quad) step list must fit beside the tile ring in
+    # LDS (Nc = 16384, 16000 cubes per row)
+    big = _prob(T=64, H=64, W=256)
+    assert call(prob=big, maxkv=16000) == L.VSA_ERR_UNSUPPORTED
 
 
 def test_check_lut_errors():

@@ -694,3 +694,76 @@ def test_dense_topk_equals_full_attention(name):
             e = np.exp(s - s.max(axis=1, keepdims=True))
             want = (e @ v64) / e.sum(axis=1, keepdims=True)
             assert_out_close(got[0, h, toks], want, f"dense wan head {h}")
+
+
+# ------------------------------------------- LUT rows over half the cubes
+# Rows that list at least half of the cubes take the fine kernel that walks
+# four neighbouring query cubes together (their union of key cubes in steps,
+# each step giving every cube at most one key cube).  Every feature of the
+# fine stage on that path: grouped key/value heads, the Hilbert cube order,
+# grids padded to whole cubes, gates with the coarse output, raster and
+# model-layout outputs, LSE; rows with repeated entries (then the quad is
+# walked position by position), empty rows and a last quad with fewer than
+# four cubes.
+WIDE = [((1, 4, 8, 16, 16, 4, 4, 4, 64), 2, "raster"), ((1, 2, 8, 16, 20, 4, 4, 4, 128), 0, "hilbert"),
+        ((1, 3, 6, 10, 9, 4, 4, 4, 128), 3, "raster"), ((2, 2, 5, 7, 9, 4, 4, 4, 64), 1, "hilbert")]
+
+
+@pytest.mark.parametrize("dims,hk,order", WIDE, ids=["8x16x16-d64-gqa2", "8x16x20-d128-hilbert",
+                                                     "6x10x9-d128-padded", "5x7x9-d64-padded-hilbert-gqa"])
+def test_sparse_attn_fwd_wide_rows(dims, hk, order):
+    B, nh, T, H, W, ct, ch, cw, d = dims
+    p = L.Problem(B, nh, T, H, W, ct, ch, cw, d, heads_kv=hk, cube_order=order)
+    nc, hkv = p.n_cubes, p.kv_heads
+    _log(f"sparse_attn_fwd wide rows {dims} kv heads {hkv} {order} ({nc} cubes)")
+    pi = oracle.token_layout(T, H, W, ct, ch, cw, order)
+    real = pi >= 0
+    rng = np.random.default_rng(131)
+
+    def bf(shape, uniform=False):
+        a = rng.random(shape) if uniform else rng.standard_normal(shape)
+        return wl.f32_to_bf16_bits(a.astype(np.float32))
+    q = bf((B, nh, p.n_tokens, d))
+    k, v = bf((B, hkv, p.n_tokens, d)), bf((B, hkv, p.n_tokens, d))
+    gc, gf = bf((B, nh, p.n_tokens, d), True), bf((B, nh, p.n_tokens, d), True)
+    oc = rng.standard_normal((B, nh, nc, d)).astype(np.float32)
+    maxk = max(nc // 2 + 1, min(nc, 12))
+    lut = np.stack([rng.permutation(nc)[:maxk] for _ in range(B * nh * nc)]).reshape(B, nh, nc, maxk)
+    valid = rng.integers(maxk // 2, maxk + 1, size=(B, nh, nc))
+    # sorted rows, unsorted rows, a row listing a cube twice, empty rows
+    lut[..., ::2, :] = np.sort(lut[..., ::2, :], axis=-1)
+    lut[0, 0, 1, :2] = lut[0, 0, 1, 2]
+    valid[0, 0, 4:8] = 0
+    valid[-1, -1, 3] = 0
+    lut, valid = lut.astype(np.int32), valid.astype(np.int32)
+    qp = dev(oracle.gather_padded(wl.as_float64(q), pi).astype(np.float32)).to(torch.bfloat16)
+    kp = dev(oracle.gather_padded(wl.as_float64(k), pi).astype(np.float32)).to(torch.bfloat16)
+    vp = dev(oracle.gather_padded(wl.as_float64(v), pi).astype(np.float32)).to(torch.bfloat16)
+    rs = (B, nh, p.n_tokens, d)
+    o_cube = torch.full((B, nh, p.n_positions, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_cube = torch.full((B, nh, p.n_positions), float("nan"), device="cuda")
+    L.vsa_sparse_attn_fwd(p, qp, kp, vp, dev(lut), dev(valid), o_cube, lse=lse_cube)
+    o_r = torch.full(rs, float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.vsa_sparse_attn_fwd_raster(p, qp, kp, vp, dev(lut), dev(valid), o_r, oc=dev(oc), gate_c=dev(gc),
+                                 gate_f=dev(gf))
+    o_b = torch.full((B, p.n_tokens, nh, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.vsa_sparse_attn_fwd_bnhd(p, qp, kp, vp, dev(lut), dev(valid), o_b, oc=dev(oc),
+                               gate_c=dev(gc).permute(0, 2, 1, 3).contiguous(),
+                               gate_f=dev(gf).permute(0, 2, 1, 3).contiguous())
+    _sync()
+    g = nh // hkv
+    f64 = wl.as_float64
+    kq = oracle.expand_kv_heads(oracle.gather_padded(f64(k), pi), g)
+    vq = oracle.expand_kv_heads(oracle.gather_padded(f64(v), pi), g)
+    of, lse = oracle.fine_attention(oracle.gather_padded(f64(q), pi), kq, vq, lut, valid, 1 / math.sqrt(d), 64,
+                                    key_valid=real)
+    rows = np.nonzero(real)[0]
+    assert_out_close(host64(o_cube)[:, :, rows], of[:, :, rows], "cube-major O_f")
+    empty = np.repeat(valid == 0, 64, axis=-1)
+    assert np.all(host64(o_cube)[empty] == 0.0) and np.all(np.isneginf(host64(lse_cube)[empty]))
+    full = ~empty & real[None, None, :]
+    assert err(host64(lse_cube)[full], lse[full])[0] <= LSE_MAX_ABS
+    outp = oracle.combine(of, oc.astype(np.float64), 64, oracle.gather_padded(f64(gc), pi),
+                          oracle.gather_padded(f64(gf), pi))
+    assert_out_close(host64(o_r)[:, :, pi[rows]], outp[:, :, rows], "raster out")
+    assert np.array_equal(bits(o_b), bits(o_r.permute(0, 2, 1, 3).contiguous()))
