@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     Problem, VsaError, VSA_BF16, VSA_F32, load,
     vsa_permute, vsa_unpermute, vsa_pool, vsa_coarse_topk, vsa_sparse_attn_fwd,
     vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
-    vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size,
+    vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size, vsa_sparse_attn_bwd_noalloc,
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
     vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
@@ -21,7 +21,7 @@ __all__ = [
     "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
     "vsa_permute", "vsa_unpermute", "vsa_pool", "vsa_coarse_topk", "vsa_sparse_attn_fwd",
     "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
-    "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size",
+    "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size", "vsa_sparse_attn_bwd_noalloc",
     "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
     "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",

@@ -151,6 +151,7 @@ def load() -> ctypes.CDLL:
         "vsa_mask_to_lut": [P, vp, i32, vp, vp, vp, vp],
         "vsa_sparse_attn_bwd_workspace_size": [P, i32, ctypes.POINTER(ctypes.c_size_t)],
         "vsa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "vsa_sparse_attn_bwd_noalloc": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp],
         "vsa_combine_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "vsa_coarse_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "vsa_coarse_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
@@ -447,6 +448,37 @@ def vsa_sparse_attn_bwd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.T
                                       _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
                                       _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       int(workspace.numel()), _stream(stream, dev)), "vsa_sparse_attn_bwd")
+
+
+def vsa_sparse_attn_bwd_noalloc(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                                o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor,
+                                dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, stream=None) -> None:
+    """As vsa_sparse_attn_bwd, with the library's fixed per-GPU workspace
+    (VSA_NOALLOC_SCRATCH_BYTES) instead of a caller workspace: nothing is
+    allocated.  Calls that overlap in time on one GPU race on that workspace.
+    (A Hilbert-order problem builds its cube table once per device here.)"""
+    dev = q.device
+    ts, ks = _pos_shape(p), _kv_pos_shape(p)
+    tv, kv = _pos_shape(p, p.v_dim), _kv_pos_shape(p, p.v_dim)
+    _need(q, "q", ts, torch.bfloat16, dev)
+    for name, t in (("o", o), ("d_o", d_o)):
+        _need(t, name, tv, torch.bfloat16, dev)
+    _need(k, "k", ks, torch.bfloat16, dev)
+    _need(v, "v", kv, torch.bfloat16, dev)
+    _need(dq, "dq", ts, torch.float32, dev)
+    _need(dk, "dk", ks, torch.float32, dev)
+    _need(dv, "dv", kv, torch.float32, dev)
+    if kv_block_idx.dim() != 4:
+        raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
+    max_kv = kv_block_idx.shape[-1]
+    _need(kv_block_idx, "kv_block_idx", (p.batch, p.heads, p.n_cubes, max_kv), torch.int32, dev)
+    _need(valid_block_num, "valid_block_num", (p.batch, p.heads, p.n_cubes), torch.int32, dev)
+    _need(lse, "lse", (p.batch, p.heads, p.n_positions), torch.float32, dev)
+    _check(load().vsa_sparse_attn_bwd_noalloc(ctypes.byref(p.c_struct(dev)), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
+                                              _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              _stream(stream, dev)), "vsa_sparse_attn_bwd_noalloc")
 
 
 def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: torch.Tensor,

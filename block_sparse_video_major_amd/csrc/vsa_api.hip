@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "vsa_internal.h"
 
@@ -113,7 +114,9 @@ const char* vsa_status_str(int status) {
     case VSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, cube volume, cube count or cube order";
     case VSA_ERR_HIP: return "HIP runtime error at launch";
     case VSA_ERR_LUT: return "invalid LUT";
-    case VSA_ERR_WORKSPACE: return "workspace smaller than vsa_sparse_attn_bwd_workspace_size reports";
+    case VSA_ERR_WORKSPACE:
+      return "workspace smaller than the workspace query reports (or, for the _noalloc entry point, needing more "
+             "than VSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -320,6 +323,57 @@ int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k, cons
   if (workspace_bytes < vsa::sparse_attn_bwd_workspace(g, max_kv_blocks)) return VSA_ERR_WORKSPACE;
   return hip_status(vsa::launch_sparse_attn_bwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, o, lse,
                                                 d_o, dq, dk, dv, workspace, (hipStream_t)stream));
+}
+
+namespace {
+// Workspace of vsa_sparse_attn_bwd_noalloc: one fixed array per GPU, held
+// until the process ends.  Host code only ever uses the device address that
+// hipGetSymbolAddress reports for the current device (the array's name in
+// host code is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[VSA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on its first use on
+// that device (with that device current) and kept.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+int vsa_sparse_attn_bwd_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
+                                const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                                int32_t max_kv_blocks, const void* o, const float* lse, const void* d_o, float* dq,
+                                float* dk, float* dv, void* stream) {
+  const int st = sparse_attn_bwd_check(p, max_kv_blocks);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
+      o == nullptr || lse == nullptr || d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (vsa::sparse_attn_bwd_workspace(g, max_kv_blocks) > (size_t)VSA_NOALLOC_SCRATCH_BYTES)
+    return VSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return VSA_ERR_HIP;
+  // every byte of the workspace the kernels read is written by them first
+  // (per-token records, list counts, offsets and the list itself), so the
+  // previous call's contents need no clearing
+  return hip_status(vsa::launch_sparse_attn_bwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, o, lse,
+                                                d_o, dq, dk, dv, ws, (hipStream_t)stream));
 }
 
 int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f, const float* oc, const void* gate_c,

@@ -325,6 +325,27 @@ int vsa_sparse_attn_bwd(const vsa_problem* p, const void* q, const void* k,
                         float* dq, float* dk, float* dv, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward as vsa_sparse_attn_bwd with the same arguments except the
+ * workspace, which is a fixed device array of VSA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, kept until the process ends.  Calls on
+ * one GPU share that array: two calls that overlap in time on the same GPU
+ * (different streams, or host threads without ordering) race and give
+ * unspecified results; calls queued on one stream are ordered and safe.
+ * Problems whose workspace (vsa_sparse_attn_bwd_workspace_size) exceeds
+ * VSA_NOALLOC_SCRATCH_BYTES return VSA_ERR_WORKSPACE and launch nothing.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call (the
+ * array's device address is looked up once per GPU with
+ * hipGetSymbolAddress, on the first call there).  Outputs are bit-identical
+ * to vsa_sparse_attn_bwd's. */
+#define VSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int vsa_sparse_attn_bwd_noalloc(const vsa_problem* p, const void* q, const void* k,
+                                const void* v, const int32_t* kv_block_idx,
+                                const int32_t* valid_block_num, int32_t max_kv_blocks,
+                                const void* o, const float* lse, const void* d_o,
+                                float* dq, float* dk, float* dv, void* stream);
+
 /* Backward of the gated combination ([VSA-ROCm] §Two-Stage Architecture:
  * gates between the coarse and fine outputs; [VSA-arXiv] Abstract: trained
  * end to end).  For out[p] = g_f[p] * O_f[p] + g_c[p] * oc[c(p)], c(p) the cube

@@ -325,3 +325,32 @@ def test_python_binding_rejects_wrong_shapes_before_the_library():
         L.vsa_permute(p, L.VSA_BF16, cpu, cpu)                # not device tensors
     with pytest.raises(ValueError):
         L._token_dtype(5)
+
+
+def test_sparse_attn_bwd_noalloc_errors():
+    """The allocation-free backward checks everything on the host before it
+    looks up its fixed workspace: wrong arguments and problems whose
+    workspace exceeds VSA_NOALLOC_SCRATCH_BYTES (16 MiB) are refused with no
+    device work."""
+    lib = _raw()
+    pr = ctypes.byref(_prob(head_dim=128))
+
+    def call(q=DUMMY, k=DUMMY, v=DUMMY, lut=DUMMY, valid=DUMMY, maxkv=8, o=DUMMY, lse=DUMMY, do=DUMMY,
+             dq=DUMMY, dk=DUMMY, dv=DUMMY, prob=pr):
+        return lib.vsa_sparse_attn_bwd_noalloc(prob, q, k, v, lut, valid, maxkv, o, lse, do, dq, dk, dv, None)
+    for name in ("q", "k", "v", "lut", "valid", "o", "lse", "do", "dq", "dk", "dv"):
+        assert call(**{name: None}) == L.VSA_ERR_NULL, name
+    assert call(maxkv=0) == L.VSA_ERR_TOPK
+    assert call(maxkv=33) == L.VSA_ERR_TOPK
+    assert call(prob=ctypes.byref(_prob(head_dim=96))) == L.VSA_ERR_UNSUPPORTED
+    assert call(prob=None) == L.VSA_ERR_NULL
+    # the 122,880-token layer with 40 heads needs 39 MB of per-token records alone
+    large = L.Problem(1, 40, 32, 48, 80, 4, 4, 4, 128)
+    n = ctypes.c_size_t(0)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(large.c_struct()), 192, ctypes.byref(n)) == L.VSA_OK
+    assert n.value > 16 << 20
+    assert call(prob=ctypes.byref(large.c_struct()), maxkv=192) == L.VSA_ERR_WORKSPACE
+    # the 32,768-token layer with 12 heads fits
+    wan = L.Problem(1, 12, 16, 32, 64, 4, 4, 4, 128)
+    assert lib.vsa_sparse_attn_bwd_workspace_size(ctypes.byref(wan.c_struct()), 154, ctypes.byref(n)) == L.VSA_OK
+    assert n.value <= 16 << 20
