@@ -175,17 +175,24 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   // ---- per-lane constant offsets ------------------------------------------
   // Direct loads (issued by half A only): lane i of load n of wave w fills
   // LDS chunk L = (w*LOADS+n)*64+i of a tile, which holds logical chunk
-  // (L % CPR) ^ f(row) of row L / CPR.
-  uint32_t kg_off[C::LOADS], vg_off[C::LOADS];
+  // (L % CPR) ^ f(row) of row L / CPR.  The load's instruction offset adds
+  // n * 1024 to both the source and the LDS destination, so the lane's
+  // source offset is taken relative to it.  The V swizzle depends on the row
+  // mod 4 only and a 1 KiB piece spans whole groups of 4 rows (4 rows at
+  // d = 128, 8 at d = 64), so one offset serves every load; the K swizzle
+  // depends on the row mod 16 and each load has its own.
+  uint32_t kg_off[C::LOADS];
 #pragma unroll
   for (int n = 0; n < C::LOADS; ++n) {
     const int L = ((wave & 3) * C::LOADS + n) * 64 + lane;
     const int r = L / C::CPR, x = L % C::CPR;
-    // minus n * 1024: the load's instruction offset adds it back (>= 0,
-    // since piece n of the tile covers source bytes [L0, L0 + 1024) with
-    // L0 >= n * 1024)
     kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16) - n * 1024;
-    vg_off[n] = r * C::ROWB + ((x ^ C::vswz(r)) * 16) - n * 1024;
+  }
+  uint32_t vg;
+  {
+    const int L = (wave & 3) * C::LOADS * 64 + lane;
+    const int r = L / C::CPR, x = L % C::CPR;
+    vg = (uint32_t)(r * C::ROWB + ((x ^ C::vswz(r)) * 16));
   }
   const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)((wave & 3) * C::LOADS * 1024));
   // K A-operand reads: key row 32*kh + n32, logical chunk 2*ks + g.
@@ -481,10 +488,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       for (int c = 0; c < count; ++c, ++i_tile) {
         const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)tw, i_tile - twin);
         const uint32_t blk = e & 0xffffu, slot = (e >> 16) & 15u;
-        if (e & (1u << 20))
+        if (e & (1u << 20)) {
+          uint32_t vg_off[C::LOADS];
+#pragma unroll
+          for (int n = 0; n < C::LOADS; ++n) vg_off[n] = vg;
           dma_tile(uniform_ptr(v_head + (int64_t)blk * C::TILE), vg_off, lds_ring + V_BASE + slot * C::TILE);
-        else
+        } else {
           dma_tile(uniform_ptr(k_head + (int64_t)blk * C::TILE), kg_off, lds_ring + slot * C::TILE);
+        }
       }
     };
     if (grp == 0) issue(n_init);
@@ -694,7 +705,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     if (my_valid && mq.ok) {
       const int64_t my_row = rowA + grp;
       const float* ocrow = oc ? oc + my_row * (int64_t)D : nullptr;
-      const int gt = tid & 255;   // thread index within the half
+      // thread index within the half, as an opaque copy: the rows and
+      // columns below are then derived here, instead of once before the pair
+      // loop and held (spilled) through the step loop
+      int gt = tid & 255;
+      asm volatile("" : "+v"(gt));
 #pragma unroll
       for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
         const int c = gt + u * 256;

@@ -311,6 +311,255 @@ __device__ __forceinline__ int step_distinct(const uint2 w, int* first_idx) {
   return n;
 }
 
+// Builds the step list, the per-step descriptors and the tile list of the
+// quad whose first query cube is cube0 (LUT row row0) in LDS; every thread
+// of the workgroup (NT of them) takes part.  Returns the step count S and
+// sets t_init (the tiles issued before the first step) and n_list (all of
+// the quad's tiles).
+template <bool PAD, int NT>
+__device__ __forceinline__ int build_quad(const BuildScratch& bs, uint2* sched, uint4* dsc, uint32_t* tlist,
+                                          const int32_t* __restrict__ lut, const int32_t* __restrict__ valid,
+                                          int max_kv, int Nc, int64_t row0, int cube0, int R, const TokenMap& tmap,
+                                          int tid, int lane, int wave, int& t_init, int& n_list) {
+  const int nwords = (Nc + 31) >> 5, nchunks = (Nc + 63) >> 6;
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  auto count_of = [&](int c) {
+    if (cube0 + c >= Nc) return 0;
+    const int n = valid[row0 + c];
+    return n < 0 ? 0 : (n > max_kv ? max_kv : n);
+  };
+  int ncnt[kQuad];
+#pragma unroll
+  for (int c = 0; c < kQuad; ++c) ncnt[c] = count_of(c);
+  const int ntot = ncnt[0] + ncnt[1] + ncnt[2] + ncnt[3];
+  auto clampc = [&](int b) { return b < 0 ? 0 : (b >= Nc ? Nc - 1 : b); };   // memory-safety clamp
+  auto entry = [&](int c, int j) { return clampc(lut[(row0 + c) * (int64_t)max_kv + j]); };
+
+  // ---- step schedule -------------------------------------------------------
+  for (int i = tid; i < 4 * nwords; i += NT) bs.bm[i] = 0u;
+  if (tid < 32) bs.info[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < ntot; i += NT) {
+    int c = 0, j = i;
+    while (c < kQuad - 1 && j >= ncnt[c]) { j -= ncnt[c]; ++c; }
+    const int u = entry(c, j);
+    const uint32_t bit = 1u << (u & 31);
+    if (atomicOr(&bs.bm[c * nwords + (u >> 5)], bit) & bit) bs.info[0] = 1;   // listed twice
+  }
+  __syncthreads();
+  const bool dup = bs.info[0] != 0;
+  int S;
+  if (dup) {
+    // position by position
+    S = max(max(ncnt[0], ncnt[1]), max(ncnt[2], ncnt[3]));
+    for (int s = tid; s < S; s += NT) {
+      uint32_t e[kQuad];
+#pragma unroll
+      for (int c = 0; c < kQuad; ++c) e[c] = s < ncnt[c] ? (uint32_t)entry(c, s) : kNone;
+      sched[s] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+    __syncthreads();
+  } else {
+    // class of key cube u: bit c = cube c lists it.  Per 64-cube chunk the
+    // class sizes (ballots), then exclusive prefixes over the chunks, then
+    // every cube's rank within its class gives its step.
+    auto cls = [&](int u) {
+      if (u >= Nc) return 0;
+      const int w = u >> 5, b = u & 31;
+      return (int)(((bs.bm[w] >> b) & 1u) | (((bs.bm[nwords + w] >> b) & 1u) << 1) |
+                   (((bs.bm[2 * nwords + w] >> b) & 1u) << 2) | (((bs.bm[3 * nwords + w] >> b) & 1u) << 3));
+    };
+    for (int ch = wave; ch < nchunks; ch += NT / 64) {
+      const int m = cls(ch * 64 + lane);
+      int mine = 0;
+      for (int x = 1; x < 16; ++x) {
+        const int cnt = __popcll(__ballot(m == x));
+        if (lane == x) mine = cnt;
+      }
+      if (lane < 16) bs.cc[ch * 16 + lane] = lane == 0 ? 0 : mine;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      // (the opaque copy keeps the compiler from holding this address
+      // in a register across the whole kernel)
+      int cls_id = tid;
+      asm volatile("" : "+v"(cls_id));
+      int run = 0;
+      for (int ch = 0; ch < nchunks; ++ch) {
+        const int x = bs.cc[ch * 16 + cls_id];
+        bs.cc[ch * 16 + cls_id] = run;
+        run += x;
+      }
+      bs.info[16 + cls_id] = cls_id == 0 ? 0 : run;
+    }
+    __syncthreads();
+    const int* ncls = bs.info + 16;
+    int B;
+    (void)class_base(ncls, 15, &B);
+    // holes of each cube before B, and its own cubes
+    int tail = 0;
+#pragma unroll
+    for (int c = 0; c < kQuad; ++c) {
+      int nonsingle = 0;
+      for (int x = 1; x < 16; ++x)
+        if (((x >> c) & 1) && x != (1 << c)) nonsingle += ncls[x];
+      const int holes = B - nonsingle;
+      const int own = ncls[1 << c];
+      tail = max(tail, own - holes);
+    }
+    S = B + max(tail, 0);
+    for (int s = tid; s < S; s += NT) bs.tmp[s] = make_uint2(kNone | (kNone << 16), kNone | (kNone << 16));
+    for (int i = tid; i < nwords; i += NT) bs.mk[i] = 0u;
+    __syncthreads();
+    for (int ch = wave; ch < nchunks; ch += NT / 64) {
+      const int u = ch * 64 + lane;
+      const int m = cls(u);
+      int rank = 0;
+      for (int x = 1; x < 16; ++x) {
+        const uint64_t b = __ballot(m == x);
+        if (m == x) rank = bs.cc[ch * 16 + x] + __popcll(b & lt_mask);
+      }
+      if (m != 0) {
+        int pos;
+        if (__popc(m) == 1) pos = single_pos(ncls, __ffs(m) - 1, rank);
+        else pos = class_base(ncls, m, nullptr) + rank;
+        uint16_t* e = reinterpret_cast<uint16_t*>(&bs.tmp[pos]);
+#pragma unroll
+        for (int c = 0; c < kQuad; ++c)
+          if ((m >> c) & 1) e[c] = (uint16_t)u;
+      }
+    }
+    __syncthreads();
+    // Steps in ascending order of their smallest key cube (each key cube
+    // sits in one step, so these are distinct): the workgroups of an XCD
+    // then sweep the key cubes of a head together, which keeps their
+    // tiles in the XCD's L2 while several quads use them.
+    auto step_min = [&](const uint2 w2) {
+      uint32_t mn = kNone;
+#pragma unroll
+      for (int c = 0; c < kQuad; ++c) mn = min(mn, step_cube(w2, c));
+      return mn;
+    };
+    for (int s = tid; s < S; s += NT) {
+      const uint32_t mn = step_min(bs.tmp[s]);   // < Nc: every step holds a key cube
+      if (mn < (uint32_t)Nc) atomicOr(&bs.mk[mn >> 5], 1u << (mn & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < nwords; base += 64) {
+        const int wi = base + lane;
+        const int cnt = wi < nwords ? __popc(bs.mk[wi]) : 0;
+        int x = cnt;   // inclusive scan over the wavefront
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        if (wi < nwords) bs.wpre[wi] = carry + x - cnt;
+        carry += __shfl(x, 63);
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < S; s += NT) {
+      const uint2 w2 = bs.tmp[s];
+      const uint32_t mn = step_min(w2);
+      if (mn >= (uint32_t)Nc) continue;
+      const int rank = bs.wpre[mn >> 5] + __popc(bs.mk[mn >> 5] & ((1u << (mn & 31)) - 1u));
+      sched[rank] = w2;
+    }
+    __syncthreads();
+  }
+
+  // ---- load plan ------------------------------------------------------------
+  // d(s) = distinct key cubes of step s.  Group g = the K tiles of step g,
+  // then the V tiles of step g - 1: u(g) = d(g) + d(g - 1) tiles, the first
+  // at running index gpos(g).
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base <= S; base += 64) {
+      const int gi = base + lane;
+      int u = 0;
+      if (gi <= S) {
+        if (gi < S) u += step_distinct(sched[gi], nullptr);
+        if (gi > 0) u += step_distinct(sched[gi - 1], nullptr);
+      }
+      int x = u;   // inclusive scan over the wavefront
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      if (gi <= S) bs.gpos[gi] = carry + x - u;
+      carry += __shfl(x, 63);
+    }
+    if (lane == 0) bs.gpos[S + 1] = carry;
+  }
+  __syncthreads();
+  // last(p) = the last group that fits in the ring at barrier p (groups < p
+  // are dead then): gpos(g + 1) - gpos(p) <= R.  A group holds at most 8
+  // tiles, so last(p) >= p.
+  for (int pp = tid; pp <= S; pp += NT) {
+    int glo = pp, ghi = S;
+    const int cap = bs.gpos[pp] + R;
+    while (glo < ghi) {
+      const int mid = (glo + ghi + 1) >> 1;
+      if (bs.gpos[mid + 1] <= cap) glo = mid; else ghi = mid - 1;
+    }
+    bs.last[pp] = glo;
+  }
+  __syncthreads();
+  // descriptors and the tile list
+  for (int pp = tid; pp <= S; pp += NT) {
+    uint32_t x = 0xffffffffu, w = 0;
+    const int gp = bs.gpos[pp];
+    int fi[kQuad];
+    int dk = 0;
+    if (pp < S) {
+      const uint2 w2 = sched[pp];
+      dk = step_distinct(w2, fi);
+#pragma unroll
+      for (int c = 0; c < kQuad; ++c) {
+        if (fi[c] < 0) continue;
+        x = (x & ~(15u << (4 * c))) | ((uint32_t)((gp + fi[c]) % R) << (4 * c));
+        bool first = true;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2)
+          if (fi[c2] == fi[c]) first = false;
+        if (first) tlist[gp + fi[c]] = step_cube(w2, c);
+        if constexpr (PAD) {
+          if (cube_partial(tmap, cube_at(tmap, (int)step_cube(w2, c)))) w |= 2u << c;
+        }
+      }
+    }
+    if (pp > 0) {
+      const uint2 w2 = sched[pp - 1];
+      (void)step_distinct(w2, fi);
+#pragma unroll
+      for (int c = 0; c < kQuad; ++c) {
+        if (fi[c] < 0) continue;
+        const int ti = gp + dk + fi[c];
+        x = (x & ~(15u << (16 + 4 * c))) | ((uint32_t)(ti % R) << (16 + 4 * c));
+        bool first = true;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2)
+          if (fi[c2] == fi[c]) first = false;
+        if (first) tlist[ti] = step_cube(w2, c) | (1u << 16);
+      }
+    }
+    // Before barrier pp the groups <= last(pp - 1) are issued (before the
+    // loop: groups <= last(0)); if that does not include group pp, it is
+    // issued after the barrier and met at a second one.
+    const int prev = pp == 0 ? bs.last[0] : bs.last[pp - 1];
+    if (prev < pp) w |= 1u;
+    dsc[pp] = make_uint4(x, (uint32_t)bs.gpos[bs.last[pp] + 1], (uint32_t)bs.gpos[pp + 1], w);
+  }
+  t_init = bs.gpos[bs.last[0] + 1];
+  n_list = bs.gpos[S + 1];
+  __syncthreads();   // descriptors and list done; the build scratch (the ring) is free
+  return S;
+}
+
 template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_quad_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -396,153 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_quad_kernel(
     const int64_t kv_off = (bh / group) * (int64_t)Nc * kBlk * D;
     const char* k_head = reinterpret_cast<const char*>(k + kv_off);
     const char* v_head = reinterpret_cast<const char*>(v + kv_off);
-    auto count_of = [&](int c) {
-      if (cube0 + c >= Nc) return 0;
-      const int n = valid[row0 + c];
-      return n < 0 ? 0 : (n > max_kv ? max_kv : n);
-    };
-    int ncnt[kQuad];
-#pragma unroll
-    for (int c = 0; c < kQuad; ++c) ncnt[c] = count_of(c);
-    const int ntot = ncnt[0] + ncnt[1] + ncnt[2] + ncnt[3];
-    auto clampc = [&](int b) { return b < 0 ? 0 : (b >= Nc ? Nc - 1 : b); };   // memory-safety clamp
-    auto entry = [&](int c, int j) { return clampc(lut[(row0 + c) * (int64_t)max_kv + j]); };
-
-    // ---- step schedule -------------------------------------------------------
-    for (int i = tid; i < 4 * nwords; i += kThreads) bs.bm[i] = 0u;
-    if (tid < 32) bs.info[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < ntot; i += kThreads) {
-      int c = 0, j = i;
-      while (c < kQuad - 1 && j >= ncnt[c]) { j -= ncnt[c]; ++c; }
-      const int u = entry(c, j);
-      const uint32_t bit = 1u << (u & 31);
-      if (atomicOr(&bs.bm[c * nwords + (u >> 5)], bit) & bit) bs.info[0] = 1;   // listed twice
-    }
-    __syncthreads();
-    const bool dup = bs.info[0] != 0;
-    int S;
-    if (dup) {
-      // position by position
-      S = max(max(ncnt[0], ncnt[1]), max(ncnt[2], ncnt[3]));
-      for (int s = tid; s < S; s += kThreads) {
-        uint32_t e[kQuad];
-#pragma unroll
-        for (int c = 0; c < kQuad; ++c) e[c] = s < ncnt[c] ? (uint32_t)entry(c, s) : kNone;
-        sched[s] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-      }
-      __syncthreads();
-    } else {
-      // class of key cube u: bit c = cube c lists it.  Per 64-cube chunk the
-      // class sizes (ballots), then exclusive prefixes over the chunks, then
-      // every cube's rank within its class gives its step.
-      auto cls = [&](int u) {
-        if (u >= Nc) return 0;
-        const int w = u >> 5, b = u & 31;
-        return (int)(((bs.bm[w] >> b) & 1u) | (((bs.bm[nwords + w] >> b) & 1u) << 1) |
-                     (((bs.bm[2 * nwords + w] >> b) & 1u) << 2) | (((bs.bm[3 * nwords + w] >> b) & 1u) << 3));
-      };
-      for (int ch = wave; ch < nchunks; ch += kThreads / 64) {
-        const int m = cls(ch * 64 + lane);
-        int mine = 0;
-        for (int x = 1; x < 16; ++x) {
-          const int cnt = __popcll(__ballot(m == x));
-          if (lane == x) mine = cnt;
-        }
-        if (lane < 16) bs.cc[ch * 16 + lane] = lane == 0 ? 0 : mine;
-      }
-      __syncthreads();
-      if (tid < 16) {
-        // (the opaque copy keeps the compiler from holding this address
-        // in a register across the whole kernel)
-        int cls_id = tid;
-        asm volatile("" : "+v"(cls_id));
-        int run = 0;
-        for (int ch = 0; ch < nchunks; ++ch) {
-          const int x = bs.cc[ch * 16 + cls_id];
-          bs.cc[ch * 16 + cls_id] = run;
-          run += x;
-        }
-        bs.info[16 + cls_id] = cls_id == 0 ? 0 : run;
-      }
-      __syncthreads();
-      const int* ncls = bs.info + 16;
-      int B;
-      (void)class_base(ncls, 15, &B);
-      // holes of each cube before B, and its own cubes
-      int tail = 0;
-#pragma unroll
-      for (int c = 0; c < kQuad; ++c) {
-        int nonsingle = 0;
-        for (int x = 1; x < 16; ++x)
-          if (((x >> c) & 1) && x != (1 << c)) nonsingle += ncls[x];
-        const int holes = B - nonsingle;
-        const int own = ncls[1 << c];
-        tail = max(tail, own - holes);
-      }
-      S = B + max(tail, 0);
-      for (int s = tid; s < S; s += kThreads) bs.tmp[s] = make_uint2(kNone | (kNone << 16), kNone | (kNone << 16));
-      for (int i = tid; i < nwords; i += kThreads) bs.mk[i] = 0u;
-      __syncthreads();
-      for (int ch = wave; ch < nchunks; ch += kThreads / 64) {
-        const int u = ch * 64 + lane;
-        const int m = cls(u);
-        int rank = 0;
-        for (int x = 1; x < 16; ++x) {
-          const uint64_t b = __ballot(m == x);
-          if (m == x) rank = bs.cc[ch * 16 + x] + __popcll(b & lt_mask);
-        }
-        if (m != 0) {
-          int pos;
-          if (__popc(m) == 1) pos = single_pos(ncls, __ffs(m) - 1, rank);
-          else pos = class_base(ncls, m, nullptr) + rank;
-          uint16_t* e = reinterpret_cast<uint16_t*>(&bs.tmp[pos]);
-#pragma unroll
-          for (int c = 0; c < kQuad; ++c)
-            if ((m >> c) & 1) e[c] = (uint16_t)u;
-        }
-      }
-      __syncthreads();
-      // Steps in ascending order of their smallest key cube (each key cube
-      // sits in one step, so these are distinct): the workgroups of an XCD
-      // then sweep the key cubes of a head together, which keeps their
-      // tiles in the XCD's L2 while several quads use them.
-      auto step_min = [&](const uint2 w2) {
-        uint32_t mn = kNone;
-#pragma unroll
-        for (int c = 0; c < kQuad; ++c) mn = min(mn, step_cube(w2, c));
-        return mn;
-      };
-      for (int s = tid; s < S; s += kThreads) {
-        const uint32_t mn = step_min(bs.tmp[s]);   // < Nc: every step holds a key cube
-        if (mn < (uint32_t)Nc) atomicOr(&bs.mk[mn >> 5], 1u << (mn & 31));
-      }
-      __syncthreads();
-      if (wave == 0) {
-        int carry = 0;
-        for (int base = 0; base < nwords; base += 64) {
-          const int wi = base + lane;
-          const int cnt = wi < nwords ? __popc(bs.mk[wi]) : 0;
-          int x = cnt;   // inclusive scan over the wavefront
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-          }
-          if (wi < nwords) bs.wpre[wi] = carry + x - cnt;
-          carry += __shfl(x, 63);
-        }
-      }
-      __syncthreads();
-      for (int s = tid; s < S; s += kThreads) {
-        const uint2 w2 = bs.tmp[s];
-        const uint32_t mn = step_min(w2);
-        if (mn >= (uint32_t)Nc) continue;
-        const int rank = bs.wpre[mn >> 5] + __popc(bs.mk[mn >> 5] & ((1u << (mn & 31)) - 1u));
-        sched[rank] = w2;
-      }
-      __syncthreads();
-    }
+    int t_init = 0, n_list = 0;
+    const int S = build_quad<PAD, kThreads>(bs, sched, dsc, tlist, lut, valid, max_kv, Nc, row0, cube0, R, tmap, tid,
+                                            lane, wave, t_init, n_list);
 
     // Q of this wave's cube as the B operand: query 32*qh + n32, d = 16*s + 8*g + 0..7
     const int my_cube = cube0 + cq;
@@ -559,92 +664,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_quad_kernel(
         for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)0.f;
     }
 
-    // ---- load plan ------------------------------------------------------------
-    // d(s) = distinct key cubes of step s.  Group g = the K tiles of step g,
-    // then the V tiles of step g - 1: u(g) = d(g) + d(g - 1) tiles, the first
-    // at running index gpos(g).
-    if (wave == 0) {
-      int carry = 0;
-      for (int base = 0; base <= S; base += 64) {
-        const int gi = base + lane;
-        int u = 0;
-        if (gi <= S) {
-          if (gi < S) u += step_distinct(sched[gi], nullptr);
-          if (gi > 0) u += step_distinct(sched[gi - 1], nullptr);
-        }
-        int x = u;   // inclusive scan over the wavefront
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(x, off);
-          if (lane >= off) x += y;
-        }
-        if (gi <= S) bs.gpos[gi] = carry + x - u;
-        carry += __shfl(x, 63);
-      }
-      if (lane == 0) bs.gpos[S + 1] = carry;
-    }
-    __syncthreads();
-    // last(p) = the last group that fits in the ring at barrier p (groups < p
-    // are dead then): gpos(g + 1) - gpos(p) <= R.  A group holds at most 8
-    // tiles, so last(p) >= p.
-    for (int pp = tid; pp <= S; pp += kThreads) {
-      int glo = pp, ghi = S;
-      const int cap = bs.gpos[pp] + R;
-      while (glo < ghi) {
-        const int mid = (glo + ghi + 1) >> 1;
-        if (bs.gpos[mid + 1] <= cap) glo = mid; else ghi = mid - 1;
-      }
-      bs.last[pp] = glo;
-    }
-    __syncthreads();
-    // descriptors and the tile list
-    for (int pp = tid; pp <= S; pp += kThreads) {
-      uint32_t x = 0xffffffffu, w = 0;
-      const int gp = bs.gpos[pp];
-      int fi[kQuad];
-      int dk = 0;
-      if (pp < S) {
-        const uint2 w2 = sched[pp];
-        dk = step_distinct(w2, fi);
-#pragma unroll
-        for (int c = 0; c < kQuad; ++c) {
-          if (fi[c] < 0) continue;
-          x = (x & ~(15u << (4 * c))) | ((uint32_t)((gp + fi[c]) % R) << (4 * c));
-          bool first = true;
-#pragma unroll
-          for (int c2 = 0; c2 < c; ++c2)
-            if (fi[c2] == fi[c]) first = false;
-          if (first) tlist[gp + fi[c]] = step_cube(w2, c);
-          if constexpr (PAD) {
-            if (cube_partial(tmap, cube_at(tmap, (int)step_cube(w2, c)))) w |= 2u << c;
-          }
-        }
-      }
-      if (pp > 0) {
-        const uint2 w2 = sched[pp - 1];
-        (void)step_distinct(w2, fi);
-#pragma unroll
-        for (int c = 0; c < kQuad; ++c) {
-          if (fi[c] < 0) continue;
-          const int ti = gp + dk + fi[c];
-          x = (x & ~(15u << (16 + 4 * c))) | ((uint32_t)(ti % R) << (16 + 4 * c));
-          bool first = true;
-#pragma unroll
-          for (int c2 = 0; c2 < c; ++c2)
-            if (fi[c2] == fi[c]) first = false;
-          if (first) tlist[ti] = step_cube(w2, c) | (1u << 16);
-        }
-      }
-      // Before barrier pp the groups <= last(pp - 1) are issued (before the
-      // loop: groups <= last(0)); if that does not include group pp, it is
-      // issued after the barrier and met at a second one.
-      const int prev = pp == 0 ? bs.last[0] : bs.last[pp - 1];
-      if (prev < pp) w |= 1u;
-      dsc[pp] = make_uint4(x, (uint32_t)bs.gpos[bs.last[pp] + 1], (uint32_t)bs.gpos[pp + 1], w);
-    }
-    const int t_init = bs.gpos[bs.last[0] + 1];
-    const int n_list = bs.gpos[S + 1];
-    __syncthreads();   // descriptors and list done; the build scratch (the ring) is free
 
     // The tile list is read from registers: lane j of tw holds
     // tlist[twin + j].  The window only slides at a step barrier (by 32
