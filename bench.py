@@ -34,9 +34,10 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, published
 MI355X_HBM_PEAK_GBPS = 8000.0        # HBM3E, published
-# the fine kernel's source and the headers it includes
+# the fine kernels' sources (pairs and quads of query cubes) and the headers they include
 FINE_SOURCES = [os.path.join(ROOT, "block_sparse_video_major_amd", "csrc", n)
-                for n in ("sparse_attn_fwd.hip", "token_map.h", "mfma_util.h", "vsa_internal.h")]
+                for n in ("sparse_attn_fwd.hip", "sparse_attn_fwd_quad.hip", "token_map.h", "mfma_util.h",
+                          "vsa_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_wan_traffic.md")
 
 
