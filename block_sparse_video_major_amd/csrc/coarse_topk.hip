@@ -90,6 +90,69 @@ struct ChunkStage {
   }
 };
 
+// Top-K of one score row (one wavefront): the selected cube indices in
+// ascending order to out_idx and K to *valid_row; with want_p the row is
+// replaced by its softmax numerators p_j = exp(scale * (s_j - max)) (pad
+// columns 0) and 1 / sum_j p_j goes to *inv_sum_r.
+template <int NS>
+__device__ __forceinline__ void select_row(float* sr, int Nc, int NcP, int top_k, int32_t* out_idx,
+                                           int32_t* valid_row, bool want_p, float scale, float* inv_sum_r,
+                                           int lane) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Keys of this row, slot s = cube s*64 + lane; 0 (below every candidate
+  // threshold, which always has a bit set) past Nc.
+  uint32_t key[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = s * 64 + lane;
+    key[s] = j < Nc ? order_key(sr[j]) : 0u;
+  }
+  // K-th largest key: build the threshold from the top bit down.
+  uint32_t thr = 0u;
+  if (top_k < Nc) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) cnt += popc64(__ballot(key[s] >= cand));
+      if (cnt >= top_k) thr = cand;
+    }
+  }
+  int gt = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) gt += popc64(__ballot(s * 64 + lane < Nc && key[s] > thr));
+  const int need = top_k - gt;   // >= 1 entries equal to thr are taken
+  int eq_before = 0, sel_before = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = s * 64 + lane;
+    const bool in = j < Nc;
+    const bool eq = in && key[s] == thr;
+    const uint64_t eqm = __ballot(eq);
+    const int eq_rank = eq_before + popc64(eqm & lt_mask);
+    const bool take = in && (key[s] > thr || (eq && eq_rank < need));
+    const uint64_t tm = __ballot(take);
+    if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
+    sel_before += popc64(tm);
+    eq_before += popc64(eqm);
+  }
+  if (lane == 0) *valid_row = top_k;
+
+  if (want_p) {
+    float m = -INFINITY;
+    for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[j]);
+    m = wave_max(m);
+    float sum = 0.f;
+    for (int j = lane; j < NcP; j += 64) {
+      const float p = j < Nc ? expf(scale * (sr[j] - m)) : 0.f;
+      sr[j] = p;   // the pad columns hold 0
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) *inv_sum_r = 1.f / sum;
+  }
+}
+
 // DQ: query/key head size (scores); DV: value head size (O_c).
 template <int DQ, int DV, int R, int NS, int kThreads>
 __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
@@ -157,64 +220,9 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   __syncthreads();
 
   // phase 2: per-row Top-K and softmax weights, one wavefront per row
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = wave; r < rows; r += kWaves) {
-    float* sr = srow + (int64_t)r * NcP;
-    const int64_t row = bh * Nc + i0 + r;
-    int32_t* out_idx = lut + row * top_k;
-    // Keys of this row, slot s = cube s*64 + lane; 0 (below every candidate
-    // threshold, which always has a bit set) past Nc.
-    uint32_t key[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int j = s * 64 + lane;
-      key[s] = j < Nc ? order_key(sr[j]) : 0u;
-    }
-    // K-th largest key: build the threshold from the top bit down.
-    uint32_t thr = 0u;
-    if (top_k < Nc) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) cnt += popc64(__ballot(key[s] >= cand));
-        if (cnt >= top_k) thr = cand;
-      }
-    }
-    int gt = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) gt += popc64(__ballot(s * 64 + lane < Nc && key[s] > thr));
-    const int need = top_k - gt;   // >= 1 entries equal to thr are taken
-    int eq_before = 0, sel_before = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int j = s * 64 + lane;
-      const bool in = j < Nc;
-      const bool eq = in && key[s] == thr;
-      const uint64_t eqm = __ballot(eq);
-      const int eq_rank = eq_before + popc64(eqm & lt_mask);
-      const bool take = in && (key[s] > thr || (eq && eq_rank < need));
-      const uint64_t tm = __ballot(take);
-      if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
-      sel_before += popc64(tm);
-      eq_before += popc64(eqm);
-    }
-    if (lane == 0) valid[row] = top_k;
-
-    if (oc != nullptr) {
-      float m = -INFINITY;
-      for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[j]);
-      m = wave_max(m);
-      float sum = 0.f;
-      for (int j = lane; j < NcP; j += 64) {
-        const float p = j < Nc ? expf(scale * (sr[j] - m)) : 0.f;
-        sr[j] = p;   // the pad columns hold 0
-        sum += p;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) inv_sum[r] = 1.f / sum;
-    }
-  }
+  for (int r = wave; r < rows; r += kWaves)
+    select_row<NS>(srow + (int64_t)r * NcP, Nc, NcP, top_k, lut + (bh * Nc + i0 + r) * top_k,
+                   valid + bh * Nc + i0 + r, oc != nullptr, scale, inv_sum + r, lane);
   if (oc == nullptr) return;
 
   // phase 3: O_c rows
@@ -284,6 +292,198 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
   }
 }
 
+// ---- sixteen query cubes per workgroup, products on the matrix cores ----
+// Used whenever sixteen score rows fit in LDS.  Both products run as
+// v_mfma_f32_16x16x4_f32 (float32 operands and accumulation, so the scores
+// keep the precision the ranking needs):
+//   phase 1  S[i][j] = sum_d Q[i][d] K[j][d] for the 16 query cubes i of the
+//            workgroup.  Keys are staged 128 at a time, half of d per stage;
+//            wave w owns keys 16w .. 16w + 15 of the stage.  Q is held in
+//            registers (A operand: lane l holds row l % 16 and, for product
+//            s of stage h, d = h*d/2 + (d/8)*(l/16) + s; the k index of a
+//            product may map to any d as long as A and B agree); B is key
+//            16w + l % 16 at the same d, so each lane reads four
+//            consecutive d with one 16-byte LDS read for four products.
+//   phase 3  O_c[i][:] = sum_j P[i][j] V[j][:]; wave w owns 16 columns of O_c
+//            (d_v = 128; at d_v = 64 two waves share a column tile and split
+//            the keys, their partial sums added once at the end).  A operand:
+//            P[l % 16][key(l / 16, s)] with key = 16*(l/16) + s in a 64-key
+//            chunk, four consecutive keys per 16-byte read; B: V[key][column].
+// Phase 2 (Top-K and softmax weights) is the same as in the kernel above,
+// two rows per wavefront.
+template <int ROWS, int COLS, int STRIDE, int kThreads>
+struct TileStage {   // ROWS x COLS floats of a row-major [rows][ld] matrix -> LDS rows of STRIDE floats
+  static constexpr int C4 = COLS / 4;
+  static constexpr int PER = ROWS * C4 / kThreads;
+  static_assert(PER * kThreads == ROWS * C4, "stage shape");
+  float4 v[PER];
+  __device__ __forceinline__ void load(const float* src, int ld, int r0, int col0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / C4, c4 = e - row * C4;
+      v[i] = r0 + row < nrows ? *reinterpret_cast<const float4*>(src + (int64_t)(r0 + row) * ld + col0 + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / C4, c4 = e - row * C4;
+      *reinterpret_cast<float4*>(dst + row * STRIDE + 4 * c4) = v[i];
+    }
+  }
+};
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));   // MFMA 16x16 accumulator
+constexpr int kMR = 16;            // query cubes per workgroup
+constexpr int kMThreads = 512;     // 8 wavefronts
+constexpr int kMKeys = 128;        // keys per phase-1 stage
+
+template <int DQ, int DV>
+__host__ __device__ constexpr int mfma_stage_floats() {
+  return kMKeys * (DQ / 2 + 4) > kChunk * (DV + 4) ? kMKeys * (DQ / 2 + 4) : kChunk * (DV + 4);
+}
+
+template <int DQ, int DV, int NS>
+__global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
+    const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
+    int32_t* __restrict__ lut, int32_t* __restrict__ valid, float* __restrict__ oc, int Nc, int top_k,
+    int tiles_per_head, float scale, int group) {
+  constexpr int kWaves = kMThreads / 64;
+  constexpr int DH = DQ / 2;        // d per phase-1 stage
+  constexpr int KSTR = DH + 4;      // LDS row stride of a key stage
+  constexpr int VSTR = DV + 4;      // ... of a value chunk
+  extern __shared__ float smem[];
+  const int NcP = padded_cols(Nc);
+  float* stage = smem;                                       // key stage / value chunk
+  float* srow = stage + mfma_stage_floats<DQ, DV>();        // [16][NcP]
+  float* inv_sum = srow + (int64_t)kMR * NcP;                // [16]
+
+  const int64_t bh = blockIdx.x / tiles_per_head;
+  const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * kMR;
+  const int rows = min(kMR, Nc - i0);
+  const int64_t kvh = bh / group;
+  const float* kh = kc + kvh * (int64_t)Nc * DQ;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, kq = lane >> 4;
+
+  // ---- phase 1: scores ----
+  // Stage h holds d in [h*DH, h*DH + DH).  Its product s (0 <= s < DH/4)
+  // takes, in lane group kq, d = h*DH + (DH/4)*kq + s: A = Q[i0 + l16][d]
+  // (from registers; rows past the last cube repeat it), B = K[key][d].
+  constexpr int SPS = DH / 4;       // products per stage
+  float qv[2][SPS];
+  {
+    const float* qr = qc + (bh * Nc + min(i0 + l16, Nc - 1)) * (int64_t)DQ + SPS * kq;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < SPS / 4; ++m) {
+        const float4 t = *reinterpret_cast<const float4*>(qr + h * DH + 4 * m);
+        qv[h][4 * m + 0] = t.x; qv[h][4 * m + 1] = t.y; qv[h][4 * m + 2] = t.z; qv[h][4 * m + 3] = t.w;
+      }
+  }
+  // the two halves of the next key chunk are in flight in registers while
+  // the current chunk's halves are multiplied (two stages of cover)
+  TileStage<kMKeys, DH, KSTR, kMThreads> ks[2];
+  ks[0].load(kh, DQ, 0, 0, Nc, tid);
+  ks[1].load(kh, DQ, 0, DH, Nc, tid);
+  for (int c0 = 0; c0 < Nc; c0 += kMKeys) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // the previous stage fully read
+      ks[h].store(stage, tid);
+      __syncthreads();
+      if (c0 + kMKeys < Nc) ks[h].load(kh, DQ, c0 + kMKeys, h * DH, Nc, tid);
+      const float* kr = stage + (16 * wave + l16) * KSTR + SPS * kq;
+#pragma unroll
+      for (int m = 0; m < SPS / 4; ++m) {
+        const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * m);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 0], kk.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 1], kk.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 2], kk.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 3], kk.w, acc, 0, 0, 0);
+      }
+    }
+    // D[i][j]: rows 4*kq + r, key c0 + 16*wave + l16
+    const int j = c0 + 16 * wave + l16;
+    if (j < Nc) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) srow[(4 * kq + r) * NcP + j] = acc[r];
+    }
+  }
+  // value chunks alternate between two register sets (two chunks in flight;
+  // the first two load during phase 2)
+  const float* vh = vc + kvh * (int64_t)Nc * DV;
+  TileStage<kChunk, DV, VSTR, kMThreads> vs[2];
+  if (oc != nullptr) {
+    vs[0].load(vh, DV, 0, 0, Nc, tid);
+    if (kChunk < Nc) vs[1].load(vh, DV, kChunk, 0, Nc, tid);
+  }
+  __syncthreads();
+
+  // ---- phase 2 ----
+  for (int r = wave; r < rows; r += kWaves)
+    select_row<NS>(srow + (int64_t)r * NcP, Nc, NcP, top_k, lut + (bh * Nc + i0 + r) * top_k,
+                   valid + bh * Nc + i0 + r, oc != nullptr, scale, inv_sum + r, lane);
+  if (oc == nullptr) return;
+
+  // ---- phase 3: O_c ----
+  constexpr int NT = DV / 16;                 // column tiles
+  constexpr int KSPLIT = kWaves / NT;         // waves per column tile (key split)
+  constexpr int SPW = 16 / KSPLIT;            // products per chunk per wave
+  const int ct = wave % NT, ksp = wave / NT;
+  floatx4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int c2 = 0; c2 < Nc; c2 += 2 * kChunk) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int c0 = c2 + b * kChunk;
+      if (c0 >= Nc) break;
+      __syncthreads();   // phase 2 done / the previous chunk fully read
+      vs[b].store(stage, tid);
+      __syncthreads();
+      if (c0 + 2 * kChunk < Nc) vs[b].load(vh, DV, c0 + 2 * kChunk, 0, Nc, tid);
+      // product s covers keys c0 + 16*kq + s (s in [SPW*ksp, SPW*ksp + SPW));
+      // P past the padded row is not read (zero A value), V past Nc is zero
+      const int kb = 16 * kq + SPW * ksp;
+      const float* pr = srow + (int64_t)l16 * NcP + c0 + kb;
+      const float* vr = stage + kb * VSTR + 16 * ct + l16;
+#pragma unroll
+      for (int m = 0; m < SPW / 4; ++m) {
+        const bool in = c0 + kb + 4 * m < NcP;
+        const float4 pp = in ? *reinterpret_cast<const float4*>(pr + 4 * m) : make_float4(0.f, 0.f, 0.f, 0.f);
+        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.x, vr[(4 * m + 0) * VSTR], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.y, vr[(4 * m + 1) * VSTR], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.z, vr[(4 * m + 2) * VSTR], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.w, vr[(4 * m + 3) * VSTR], o, 0, 0, 0);
+      }
+    }
+  }
+  if (KSPLIT > 1) {
+    // partial sums of the key splits, added in split order
+    __syncthreads();
+    floatx4* part = reinterpret_cast<floatx4*>(stage);   // [KSPLIT][NT][64]
+    part[(ksp * NT + ct) * 64 + lane] = o;
+    __syncthreads();
+    if (ksp != 0) return;
+    for (int k2 = 1; k2 < KSPLIT; ++k2) {
+      const floatx4 t = part[(k2 * NT + ct) * 64 + lane];
+      o[0] += t[0]; o[1] += t[1]; o[2] += t[2]; o[3] += t[3];
+    }
+  }
+  // D[i][n]: rows 4*kq + r, column 16*ct + l16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * kq + r;
+    if (i < rows) oc[(bh * Nc + i0 + i) * (int64_t)DV + 16 * ct + l16] = o[r] * inv_sum[i];
+  }
+}
+
 }  // namespace
 
 static size_t coarse_lds_bytes(int R, int Nc, int D) {   // D: the wider of the two head sizes
@@ -329,12 +529,55 @@ static hipError_t launch_r(const Geom& g, int top_k, const float* qc, const floa
   return launch_rns<DQ, DV, R, 64, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
 }
 
-// Eight query cubes per 512-thread workgroup where their score rows fit in
-// LDS, else four per 256 threads: measured on 12 heads x 512 cubes, more,
-// smaller workgroups hide the staging latency better than larger ones.
+static size_t coarse_mfma_lds_bytes(int Nc, int stage_floats) {
+  return sizeof(float) * ((size_t)stage_floats + (size_t)kMR * padded_cols(Nc) + kMR);
+}
+
+template <int DQ, int DV, int NS>
+static hipError_t launch_mfma_ns(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
+                                 int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  const int Nc = (int)g.Nc;
+  const int tiles = (Nc + kMR - 1) / kMR;
+  const int64_t blocks = g.BH * tiles;
+  const size_t lds = coarse_mfma_lds_bytes(Nc, mfma_stage_floats<DQ, DV>());
+  const float scale = 1.0f / sqrtf((float)DQ);
+  auto k = coarse_topk_mfma_kernel<DQ, DV, NS>;
+  if (lds > 65536) {
+    static std::mutex mu;
+    static int granted[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (granted[dev] < (int)lds) {
+      const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      granted[dev] = (int)lds;
+    }
+  }
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMThreads), lds, s, qc, kc, vc, lut, valid, oc, Nc, top_k,
+                     tiles, scale, g.group);
+  return hipGetLastError();
+}
+
+template <int DQ, int DV>
+static hipError_t launch_mfma(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
+                              int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  const int slots = (int)((g.Nc + 63) / 64);
+  if (slots <= 8) return launch_mfma_ns<DQ, DV, 8>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 16) return launch_mfma_ns<DQ, DV, 16>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  if (slots <= 32) return launch_mfma_ns<DQ, DV, 32>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+  return launch_mfma_ns<DQ, DV, 64>(g, top_k, qc, kc, vc, lut, valid, oc, s);
+}
+
+// Sixteen query cubes per workgroup with the products on the matrix cores
+// where their score rows fit in LDS; else eight per 512-thread workgroup
+// where those fit, else four per 256 threads (measured on 12 heads x 512
+// cubes: more, smaller workgroups hide the staging latency better).
 template <int DQ, int DV>
 static hipError_t launch_d(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                            int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
+  if (coarse_mfma_lds_bytes((int)g.Nc, mfma_stage_floats<DQ, DV>()) <= kCoarseLdsMax)
+    return launch_mfma<DQ, DV>(g, top_k, qc, kc, vc, lut, valid, oc, s);
   if (coarse_lds_bytes(8, (int)g.Nc, DQ > DV ? DQ : DV) <= kCoarseLdsMax)
     return launch_r<DQ, DV, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);
   return launch_r<DQ, DV, 4, 256>(g, top_k, qc, kc, vc, lut, valid, oc, s);
