@@ -13,9 +13,9 @@ from ._lib import (  # noqa: F401
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
     vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
-    vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT,
+    vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables,
 )
-from .pipeline import VsaBackward, VsaForward, vsa_forward  # noqa: F401
+from .pipeline import VsaBackward, VsaForward, vsa_forward, clear_forward_cache  # noqa: F401
 
 __all__ = [
     "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
@@ -26,5 +26,5 @@ __all__ = [
     "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
-    "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT",
+    "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT", "clear_cube_tables", "clear_forward_cache",
 ]

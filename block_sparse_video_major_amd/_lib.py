@@ -8,9 +8,11 @@ kernels.  There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import dataclasses
 import os
+import threading
 from typing import Optional
 
 import torch
@@ -46,7 +48,11 @@ class _Problem(ctypes.Structure):
 
 VSA_CUBES_RASTER, VSA_CUBES_HILBERT = 0, 1
 _CUBE_ORDERS = {"raster": VSA_CUBES_RASTER, "hilbert": VSA_CUBES_HILBERT}
-_tables: dict = {}   # (grid, cube, order, device) -> device table of packed cube coordinates
+# (grid, cube, order, device) -> device table of packed cube coordinates, for
+# the last _TABLE_CACHE_SIZE keys (a table is 4 bytes per cube)
+_TABLE_CACHE_SIZE = 16
+_tables: "collections.OrderedDict" = collections.OrderedDict()
+_tables_lock = threading.Lock()
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,12 +191,29 @@ def _cube_table(p: "Problem", device: torch.device) -> torch.Tensor:
     if device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
     key = (p.T, p.H, p.W, p.ct, p.ch, p.cw, p.cube_order, str(device))
-    t = _tables.get(key)
-    if t is None:
-        t = vsa_cube_table(p).to(device)
-        torch.cuda.synchronize(device)
+    with _tables_lock:
+        t = _tables.get(key)
+        if t is not None:
+            _tables.move_to_end(key)
+            return t
+    t = vsa_cube_table(p).to(device)
+    torch.cuda.synchronize(device)
+    with _tables_lock:
         _tables[key] = t
+        while len(_tables) > _TABLE_CACHE_SIZE:
+            # kernels already queued may still read the oldest table: let
+            # them finish before its memory can be reused
+            _, old = _tables.popitem(last=False)
+            torch.cuda.synchronize(old.device)
     return t
+
+
+def clear_cube_tables() -> None:
+    """Drop the cached cube-coordinate tables (they are rebuilt on demand)."""
+    with _tables_lock:
+        for t in _tables.values():
+            torch.cuda.synchronize(t.device)
+        _tables.clear()
 
 
 def vsa_status_str(status: int) -> str:

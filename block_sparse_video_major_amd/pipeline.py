@@ -14,7 +14,9 @@ kernels of libvsa.so.
 """
 from __future__ import annotations
 
+import collections
 import dataclasses
+import threading
 from typing import Dict, Optional
 
 import torch
@@ -81,11 +83,45 @@ class VsaForward:
         return d
 
 
+# Buffers of vsa_forward, per calling thread, kept for the last few (problem,
+# Top-K, device, stream) keys: successive calls on one stream are ordered by
+# that stream, so they may share intermediates; calls on other streams or
+# threads get buffers of their own.
+_FORWARD_CACHE_SIZE = 4
+_forward_cache = threading.local()
+
+
+def _cached_forward(p: Problem, top_k: int, device: torch.device, stream) -> "VsaForward":
+    cache = getattr(_forward_cache, "entries", None)
+    if cache is None:
+        cache = _forward_cache.entries = collections.OrderedDict()
+    key = (p, top_k, str(device), L._stream(stream, device))
+    f = cache.get(key)
+    if f is None:
+        f = VsaForward(p, top_k, device)
+        cache[key] = f
+        while len(cache) > _FORWARD_CACHE_SIZE:
+            cache.popitem(last=False)
+    else:
+        cache.move_to_end(key)
+    return f
+
+
+def clear_forward_cache() -> None:
+    """Drop the calling thread's cached vsa_forward buffers."""
+    _forward_cache.entries = collections.OrderedDict()
+
+
 def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, top_k: int,
                 gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
-    """One VSA forward pass on raster bf16 inputs [B, heads, N, d]."""
-    f = VsaForward(p, top_k, q.device, with_gates=gate_c is not None or gate_f is not None)
+    """One VSA forward pass on raster bf16 inputs [B, heads, N, d].  The
+    intermediates (cube-major copies, pooled tensors, the index list) live in
+    buffers reused by later calls with the same problem on the same stream
+    and thread; the returned output is a new tensor."""
+    if not 1 <= top_k <= p.n_cubes:
+        raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
+    f = _cached_forward(p, top_k, q.device, stream)
     out = q.new_empty(q.shape[:-1] + (p.v_dim,))
     return f(q, k, v, out, gate_c, gate_f, stream)
 

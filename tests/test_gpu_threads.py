@@ -66,3 +66,38 @@ def test_concurrent_forward_passes_equal_sequential():
     torch.cuda.synchronize()
     for kk in ks:
         assert np.array_equal(bits(outs[kk]), want[kk]), f"Top-K {kk}: concurrent result differs"
+
+
+def test_vsa_forward_reuses_buffers_per_stream():
+    """vsa_forward keeps its intermediates per (problem, Top-K, stream,
+    thread): repeated calls with other inputs give the same bits as a fresh
+    VsaForward, and a second stream gets buffers of its own."""
+    import block_sparse_video_major_amd as vsa
+    from block_sparse_video_major_amd import pipeline
+    w = wl.SMALL
+    print("\n[case] vsa_forward cache, small grid, Top-K 8", flush=True)
+    p = problem(w)
+    x = inputs(w.name)
+    q, k, v, gc, gf = (dev(x[n]) for n in ("q", "k", "v", "gate_c", "gate_f"))
+    q2 = torch.flip(q, dims=[2]).contiguous()
+    vsa.clear_forward_cache()
+    want = {}
+    for name, qq in (("a", q), ("b", q2)):
+        out = torch.empty_like(q)
+        VsaForward(p, 8)(qq, k, v, out, gc, gf)
+        torch.cuda.synchronize()
+        want[name] = bits(out).copy()
+    got = []
+    for qq in (q, q2, q):
+        got.append(vsa.vsa_forward(qq, k, v, p, 8, gc, gf))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got[0]), want["a"])
+    assert np.array_equal(bits(got[1]), want["b"])
+    assert np.array_equal(bits(got[2]), want["a"])
+    assert len(pipeline._forward_cache.entries) == 1
+    s2 = torch.cuda.Stream()
+    o2 = vsa.vsa_forward(q2, k, v, p, 8, gc, gf, stream=s2)
+    s2.synchronize()
+    assert np.array_equal(bits(o2), want["b"])
+    assert len(pipeline._forward_cache.entries) == 2
+    vsa.clear_forward_cache()
