@@ -273,6 +273,20 @@ def main() -> int:
                 torch.cuda.synchronize()
                 for i, n in enumerate(names):
                     acc[n] += e[i].elapsed_time(e[i + 1]) / reps
+            # the practical HBM ceiling for these passes: a plain device copy
+            # (torch's copy kernel) of the bytes the three reorders read and write
+            csrc = torch.empty(3 * q.numel(), dtype=torch.bfloat16, device=dev).fill_(0.5)
+            cdst = torch.empty_like(csrc)
+            cdst.copy_(csrc)
+            acc["copy_qkv"] = 0.0
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                cdst.copy_(csrc)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                acc["copy_qkv"] += e0.elapsed_time(e1) / reps
+            del csrc, cdst
             # second workload: a block relation matrix (union of importance,
             # condition and adjacency masks; a different count per row) converted
             # by vsa_mask_to_lut and run through the fine kernel
@@ -619,7 +633,10 @@ def main() -> int:
                             "pool_qkv": round(pool_bytes / (acc["pool_qkv"] * 1e-3) / 1e9, 1),
                             "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9,
                                                       1),
-                            "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1)},
+                            "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1),
+                            "copy_ceiling": round(permute_bytes / (acc["copy_qkv"] * 1e-3) / 1e9, 1),
+                            "note": "copy_ceiling: torch's device copy of the bytes the three reorders move, "
+                                    "timed in the same run; HBM peak 8000 GB/s"},
             "topk_sweep": sweep,
             "mask_workload": {"pattern": "union of 48 random + 4 fixed + 3x3x3-neighbour key cubes per query cube",
                               "mean_key_cubes_per_query_cube": round(pairs_m / (w.batch * w.heads * w.n_cubes), 1),
