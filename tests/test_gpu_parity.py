@@ -412,21 +412,30 @@ def test_sparse_attn_raster_output_matches_unpermute():
         assert np.array_equal(lse_r.cpu().numpy().view(np.uint32), lse_back.view(np.uint32)), name
 
 
-def test_sparse_attn_deterministic():
-    _log("sparse_attn_fwd determinism")
+# Top-154 of 512 cubes runs the kernel over pairs of query cubes, Top-300
+# the one over quads (rows listing at least half of the cubes).
+@pytest.mark.parametrize("kk", [154, 300])
+def test_sparse_attn_deterministic(kk):
+    _log(f"sparse_attn_fwd determinism K={kk}")
     w = wl.WAN
     p = problem(w)
     x = inputs(w.name)
     q, k, v = (dev(x[n]) for n in ("q", "k", "v"))
     rng = np.random.default_rng(4)
-    lut = np.sort(np.stack([rng.permutation(512)[:154] for _ in range(12 * 512)]), axis=1)
-    lut = dev(lut.reshape(1, 12, 512, 154).astype(np.int32))
-    valid = torch.full((1, 12, 512), 154, dtype=torch.int32, device="cuda")
-    o1, o2 = torch.empty_like(q), torch.empty_like(q)
-    L.vsa_sparse_attn_fwd(p, q, k, v, lut, valid, o1)
-    L.vsa_sparse_attn_fwd(p, q, k, v, lut, valid, o2)
+    lut = np.sort(np.stack([rng.permutation(512)[:kk] for _ in range(12 * 512)]), axis=1)
+    lut = dev(lut.reshape(1, 12, 512, kk).astype(np.int32))
+    valid = torch.full((1, 12, 512), kk, dtype=torch.int32, device="cuda")
+    outs, lses = [], []
+    for _ in range(3):
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 12, p.n_positions), dtype=torch.float32, device="cuda")
+        L.vsa_sparse_attn_fwd(p, q, k, v, lut, valid, o, lse=lse)
+        outs.append(o)
+        lses.append(lse)
     _sync()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for o, lse in zip(outs[1:], lses[1:]):
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+        assert torch.equal(lses[0].view(torch.int32), lse.view(torch.int32))
 
 
 def test_errors_leave_outputs_untouched():
