@@ -218,9 +218,14 @@ def test_coarse_topk_ties_take_lower_index():
 # Cube counts outside the workloads: the largest Nc the coarse stage accepts
 # at both head sizes (fewer query rows per workgroup, the key range split
 # across row groups for the coarse output, keys in 64 slots per lane), a
-# count that is not a multiple of 4 (padded score rows) and one between.
+# count that is not a multiple of 4 (padded score rows), one between, and
+# the two sides of the limit of the sixteen-row kernel.
 COARSE_GEOM = [(128, (64, 64, 64), 192), (64, (64, 64, 64), 100),
-               (64, (20, 36, 44), 37), (128, (4, 4, 6124), 64)]
+               (64, (20, 36, 44), 37), (128, (4, 4, 6124), 64),
+               # the largest count whose sixteen score rows fit in LDS beside
+               # the staging buffer at d = 128 (the matrix-core kernel), and
+               # the next one up (the vector kernel)
+               (128, (4, 4, 8048), 201), (128, (4, 4, 8064), 201)]
 
 
 @pytest.mark.parametrize("d,dims,k", COARSE_GEOM, ids=[f"d{c[0]}-nc{c[1][0] * c[1][1] * c[1][2] // 64}"
