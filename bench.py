@@ -624,6 +624,14 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
                      "traffic": _measured_traffic()},
     })
+    cus, khz, peak_rt = L.vsa_device_peak(torch.cuda.current_device())
+    rec["device"] = {"name": torch.cuda.get_device_properties(0).name, "compute_units": cus,
+                     "max_sclk_mhz": round(khz / 1e3, 1),
+                     "bf16_peak_tflops_runtime": round(peak_rt, 1),
+                     "bf16_peak_tflops_spec": MI355X_BF16_PEAK_TFLOPS,
+                     "fine_frac_of_runtime_peak": round(achieved / peak_rt, 4) if peak_rt > 0 else None,
+                     "note": "runtime peak = compute units x peak shader clock x 4096 bf16 flop per clock "
+                             "per CU, from HIP's device attributes; roofline.peak is the published figure"}
     if ex is not None:
         acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large = ex
         pad_fl = 4 * 64 * 64 * w.head_dim * pad["pairs"]   # per selected pair, padded positions included

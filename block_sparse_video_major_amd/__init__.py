@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
     vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
-    vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables,
+    vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables, vsa_device_peak,
 )
 from .pipeline import VsaBackward, VsaForward, vsa_forward, clear_forward_cache  # noqa: F401
 
@@ -27,4 +27,5 @@ __all__ = [
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
     "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT", "clear_cube_tables", "clear_forward_cache",
+    "vsa_device_peak",
 ]

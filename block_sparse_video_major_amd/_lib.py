@@ -13,7 +13,7 @@ import ctypes
 import dataclasses
 import os
 import threading
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -170,6 +170,7 @@ def load() -> ctypes.CDLL:
         "vsa_cube_table": [P, vp],
         "vsa_status_str": [ctypes.c_int],
         "vsa_abi_version": [],
+        "vsa_device_peak": [i32, vp, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -222,6 +223,15 @@ def vsa_status_str(status: int) -> str:
 
 def vsa_abi_version() -> int:
     return int(load().vsa_abi_version())
+
+
+def vsa_device_peak(device: int = 0) -> Tuple[int, int, float]:
+    """(compute units, peak shader clock in kHz, dense bf16 MFMA peak in
+    TFLOP/s = CUs x clock x 4096 flop per clock) as HIP reports them."""
+    cus, khz, tf = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_double(0.0)
+    _check(load().vsa_device_peak(int(device), ctypes.byref(cus), ctypes.byref(khz), ctypes.byref(tf)),
+           "vsa_device_peak")
+    return int(cus.value), int(khz.value), float(tf.value)
 
 
 # ---------------------------------------------------------------- helpers

@@ -103,7 +103,18 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (3 << 16) | 0; }
+int vsa_abi_version(void) { return (3 << 16) | 1; }
+
+int vsa_device_peak(int32_t device, int32_t* cu_count, int32_t* clock_khz, double* bf16_tflops) {
+  int cus = 0, khz = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device) != hipSuccess)
+    return VSA_ERR_HIP;
+  if (cu_count) *cu_count = cus;
+  if (clock_khz) *clock_khz = khz;
+  if (bf16_tflops) *bf16_tflops = (double)cus * (double)khz * 1e3 * 4096.0 / 1e12;
+  return VSA_OK;
+}
 
 const char* vsa_status_str(int status) {
   switch (status) {

@@ -407,6 +407,15 @@ int vsa_perm_index(const vsa_problem* p, int32_t* perm_host);
  * cubes (VSA_ERR_UNSUPPORTED).  No device work, no allocation. */
 int vsa_cube_table(const vsa_problem* p, int32_t* coords_host);
 
+/* Host helper for measurement: the compute-unit count and peak shader clock
+ * (kHz) HIP reports for `device`, and the dense bf16 matrix-core peak they
+ * imply, cu_count * clock * 4096 flop per clock per CU (four SIMDs, each
+ * retiring one 32x32x16 bf16 product of 32768 flop every 32 clocks), in
+ * TFLOP/s.  Any output pointer may be NULL.  VSA_ERR_HIP when the device
+ * cannot be queried; no device work, no allocation. */
+int vsa_device_peak(int32_t device, int32_t* cu_count, int32_t* clock_khz,
+                    double* bf16_tflops);
+
 /* Static description of a status code (never NULL). */
 const char* vsa_status_str(int status);
 

@@ -43,6 +43,16 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def test_device_peak_query():
+    """The measurement helper reports what the runtime reports, and the peak is
+    the product CUs x clock x 4096 flop per clock per CU."""
+    _log("vsa_device_peak")
+    cus, khz, tf = L.vsa_device_peak(0)
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert khz > 0
+    assert tf == pytest.approx(cus * khz * 1e3 * 4096 / 1e12, rel=1e-12)
+
+
 # ------------------------------------------------------------------ reorder
 REORDER = [
     ("tiny-f32", (1, 1, 4, 8, 8, 4, 4, 4, 64), L.VSA_F32),
