@@ -14,8 +14,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef const __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  // built as a two-element vector so that both roundings are one packed
+  // conversion instruction
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4& raw, float* f) {

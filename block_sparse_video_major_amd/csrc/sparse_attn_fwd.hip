@@ -64,6 +64,7 @@
 //     schedule (slot, offset and wait arithmetic) cost more, because every
 //     wave issues them between its MFMAs.
 #include <mutex>
+#include <type_traits>
 
 #include "mfma_util.h"
 #include "token_map.h"
@@ -86,7 +87,7 @@ struct Cfg {
   static constexpr int LOADS = TILE / (kIssueThreads * 16);  // 16-byte loads per issuing wave per tile
   static constexpr int OT = D / 32;                  // 32-row tiles of O^T
   static constexpr int NOV = OT * 16;                // O^T accumulators per lane
-  static constexpr int MERGE_G = 2 * (NOV + 2) * 64 * 4;   // merge buffer of one half
+  static constexpr int MERGE_G = 2 * (NOV + 4) * 64 * 4;   // merge buffer of one half
   static constexpr int OSTR = D + 4;                 // fp32 staging row stride
   static constexpr int OST_G = kBlk * OSTR * 4;      // staging of one half
   static constexpr int EPI_BYTES = 2 * (MERGE_G + OST_G);
@@ -233,6 +234,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const int64_t kv_off = (bh / group) * (int64_t)Nc * kBlk * D;   // its key/value head
     const char* k_head = reinterpret_cast<const char*>(k + kv_off);
     const char* v_head = reinterpret_cast<const char*>(v + kv_off);
+
+    // Q of this half's cube as the B operand: query 32*qh + n32, d = 16*s + 8*g
+    // + 0..7.  Issued before the schedule is built, so that its latency
+    // overlaps that of the index rows and the build itself.
+    const int my_cube = cubeA + grp;
+    const bool my_valid = grp == 0 || hasB;
+    bf16x8 qf[D / 16];
+    if (my_valid) {
+      const __bf16* qrow = q + head_off + (int64_t)(my_cube * kBlk + 32 * qh + n32) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    }
     auto count_of = [&](int64_t row) {
       const int n = valid[row];
       return n < 0 ? 0 : (n > max_kv ? max_kv : n);
@@ -340,16 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       }
     }
 
-    // Q of this half's cube as the B operand: query 32*qh + n32, d = 16*s + 8*g + 0..7
-    const int my_cube = cubeA + grp;
-    const bool my_valid = grp == 0 || hasB;
-    bf16x8 qf[D / 16];
-    if (my_valid) {
-      const __bf16* qrow = q + head_off + (int64_t)(my_cube * kBlk + 32 * qh + n32) * D + 8 * g;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
-    }
-    wait_vmem<0>();
+    wait_vmem<0>();    // Q has landed (issued at the top of the pair)
     __syncthreads();   // schedule complete; bitmaps no longer needed
 
     // ---- load plan ----------------------------------------------------------
@@ -658,43 +662,61 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     __syncthreads();   // every wave is done with the ring before it is reused
 
     // ---- merge the two key halves, normalise, combine, store ----
+    // Each key half finishes half of the d tiles (kh 0 the first OT / 2, kh 1
+    // the rest): it hands the other half's tiles over through LDS with its
+    // (offset, row sum), then merges both halves' partials of its own tiles.
+    // Either wave forms the merged value as fma(x0, a0, x1 * a1) * inv with
+    // x0, x1 the partials of key halves 0 and 1, so every tile is merged the
+    // same way whichever half finishes it.
     const float l_row = pair_sum(l_part);
-    float* mbuf = reinterpret_cast<float*>(smem + grp * C::MERGE_G);                 // [qh][2 + NOV][64]
+    constexpr int HT = C::OT / 2;    // d tiles each key half finishes
+    constexpr int HV = HT * 16;      // their accumulators per lane
+    float* mbuf = reinterpret_cast<float*>(smem + grp * C::MERGE_G);                 // [qh][4 + NOV][64]
     float* ost = reinterpret_cast<float*>(smem + 2 * C::MERGE_G + grp * C::OST_G);   // [64][OSTR]
-    if (kh == 1) {
-      float* b = mbuf + qh * (C::NOV + 2) * 64;
-      b[lane] = m_used;
-      b[64 + lane] = l_row;
+    float* b = mbuf + qh * (C::NOV + 4) * 64;   // rows 0-3: (offset, sum) of kh 0, of kh 1; then kh 0's, kh 1's hand-over
+    auto hand_over = [&](auto khc) {
+      constexpr int KH = decltype(khc)::value;
 #pragma unroll
-      for (int t = 0; t < C::OT; ++t)
+      for (int u = 0; u < HT; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) b[(2 + t * 16 + r) * 64 + lane] = o[t][r];
-    }
+        for (int r = 0; r < 16; ++r) b[(4 + KH * HV + u * 16 + r) * 64 + lane] = o[(1 - KH) * HT + u][r];
+    };
+    b[(2 * kh) * 64 + lane] = m_used;
+    b[(2 * kh + 1) * 64 + lane] = l_row;
+    if (kh == 0) hand_over(std::integral_constant<int, 0>{}); else hand_over(std::integral_constant<int, 1>{});
     __syncthreads();
-    if (kh == 0) {
-      const float* b = mbuf + qh * (C::NOV + 2) * 64;
-      const float m1 = b[lane], l1 = b[64 + lane];
-      const float m = fmaxf(m_used, m1);
-      const float a0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_used - m);
+    {
+      const float m0 = b[lane], l0 = b[64 + lane], m1 = b[128 + lane], l1 = b[192 + lane];
+      const float m = fmaxf(m0, m1);
+      const float a0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
       const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-      const float l = l_row * a0 + l1 * a1;
+      const float l = fmaf(l0, a0, l1 * a1);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float* orow = ost + (32 * qh + n32) * C::OSTR;
+      auto finish = [&](auto khc) {
+        constexpr int KH = decltype(khc)::value;
+        const float* other = b + (4 + (1 - KH) * HV) * 64;   // the other half's partials of these tiles
 #pragma unroll
-      for (int t = 0; t < C::OT; ++t)
+        for (int u = 0; u < HT; ++u)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float4 w;
-          w.x = (o[t][4 * rq + 0] * a0 + b[(2 + t * 16 + 4 * rq + 0) * 64 + lane] * a1) * inv;
-          w.y = (o[t][4 * rq + 1] * a0 + b[(2 + t * 16 + 4 * rq + 1) * 64 + lane] * a1) * inv;
-          w.z = (o[t][4 * rq + 2] * a0 + b[(2 + t * 16 + 4 * rq + 2) * 64 + lane] * a1) * inv;
-          w.w = (o[t][4 * rq + 3] * a0 + b[(2 + t * 16 + 4 * rq + 3) * 64 + lane] * a1) * inv;
-          // d = 32*t + 8*rq + 4*g + 0..3
-          *reinterpret_cast<float4*>(orow + 32 * t + 8 * rq + 4 * g) = w;
-        }
+          for (int rq = 0; rq < 4; ++rq) {
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float own = o[KH * HT + u][4 * rq + e];
+              const float oth = other[(u * 16 + 4 * rq + e) * 64 + lane];
+              const float x0 = KH == 0 ? own : oth, x1 = KH == 0 ? oth : own;
+              w[e] = fmaf(x0, a0, x1 * a1) * inv;
+            }
+            // d = 32*t + 8*rq + 4*g + 0..3
+            *reinterpret_cast<float4*>(orow + 32 * (KH * HT + u) + 8 * rq + 4 * g) = make_float4(w[0], w[1], w[2], w[3]);
+          }
+      };
+      if (kh == 0) finish(std::integral_constant<int, 0>{}); else finish(std::integral_constant<int, 1>{});
       const int32_t my_tok = 32 * qh + n32;
       const CubeAt mq = tmap.on ? cube_at(tmap, my_cube) : CubeAt{0, 0, 0, true};
-      if (lse != nullptr && g == 0 && my_valid && mq.ok && (!PAD || !tmap.on || token_real(tmap, mq, my_tok))) {
+      if (kh == 0 && lse != nullptr && g == 0 && my_valid && mq.ok &&
+          (!PAD || !tmap.on || token_real(tmap, mq, my_tok))) {
         const float val = (l > 0.f) ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
         lse[bh * (int64_t)(tmap.on ? tmap.N : tmap.Np) + token_pos(tmap, my_cube, mq, my_tok)] = val;
       }
@@ -710,38 +732,58 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       // loop and held (spilled) through the step loop
       int gt = tid & 255;
       asm volatile("" : "+v"(gt));
+      // Without gates (and without padding) the rows are written by a loop
+      // with no branch, so that its staging reads can all be issued before
+      // the first store; the general loop below tests the gates per row.
+      if (!PAD && gate_f == nullptr && gate_c == nullptr) {
 #pragma unroll
-      for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
-        const int c = gt + u * 256;
-        const int row = c / C::CPR, col = c % C::CPR;
-        if (PAD && tmap.on && !token_real(tmap, mq, row)) continue;   // padding: no raster row
-        const int64_t gidx = token_elem(tmap, bh, my_cube, mq, row, D) + col * 8;
-        float val[8];
-        const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
-        const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
-        val[0] = v0.x; val[1] = v0.y; val[2] = v0.z; val[3] = v0.w;
-        val[4] = v1.x; val[5] = v1.y; val[6] = v1.z; val[7] = v1.w;
-        if (gate_f != nullptr) {
-          float gf[8];
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_f + gidx), gf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) val[e] *= gf[e];
+        for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
+          const int c = gt + u * 256;
+          const int row = c / C::CPR, col = c % C::CPR;
+          const int64_t gidx = token_elem(tmap, bh, my_cube, mq, row, D) + col * 8;
+          const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
+          const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
+          uint4 packed;
+          packed.x = pack_bf16x2(v0.x, v0.y);
+          packed.y = pack_bf16x2(v0.z, v0.w);
+          packed.z = pack_bf16x2(v1.x, v1.y);
+          packed.w = pack_bf16x2(v1.z, v1.w);
+          *reinterpret_cast<uint4*>(out + gidx) = packed;
         }
-        if (gate_c != nullptr) {
-          float gc[8];
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_c + gidx), gc);
-          const float4 c0 = *reinterpret_cast<const float4*>(ocrow + col * 8);
-          const float4 c1 = *reinterpret_cast<const float4*>(ocrow + col * 8 + 4);
-          const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) val[e] = fmaf(gc[e], cv[e], val[e]);
+        for (int u = 0; u < kBlk * C::CPR / 256; ++u) {
+          const int c = gt + u * 256;
+          const int row = c / C::CPR, col = c % C::CPR;
+          if (PAD && tmap.on && !token_real(tmap, mq, row)) continue;   // padding: no raster row
+          const int64_t gidx = token_elem(tmap, bh, my_cube, mq, row, D) + col * 8;
+          float val[8];
+          const float4 v0 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8);
+          const float4 v1 = *reinterpret_cast<const float4*>(ost + row * C::OSTR + col * 8 + 4);
+          val[0] = v0.x; val[1] = v0.y; val[2] = v0.z; val[3] = v0.w;
+          val[4] = v1.x; val[5] = v1.y; val[6] = v1.z; val[7] = v1.w;
+          if (gate_f != nullptr) {
+            float gf[8];
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_f + gidx), gf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] *= gf[e];
+          }
+          if (gate_c != nullptr) {
+            float gc[8];
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_c + gidx), gc);
+            const float4 c0 = *reinterpret_cast<const float4*>(ocrow + col * 8);
+            const float4 c1 = *reinterpret_cast<const float4*>(ocrow + col * 8 + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] = fmaf(gc[e], cv[e], val[e]);
+          }
+          uint4 packed;
+          packed.x = pack_bf16x2(val[0], val[1]);
+          packed.y = pack_bf16x2(val[2], val[3]);
+          packed.z = pack_bf16x2(val[4], val[5]);
+          packed.w = pack_bf16x2(val[6], val[7]);
+          *reinterpret_cast<uint4*>(out + gidx) = packed;
         }
-        uint4 packed;
-        packed.x = pack_bf16x2(val[0], val[1]);
-        packed.y = pack_bf16x2(val[2], val[3]);
-        packed.z = pack_bf16x2(val[4], val[5]);
-        packed.w = pack_bf16x2(val[6], val[7]);
-        *reinterpret_cast<uint4*>(out + gidx) = packed;
       }
     }
     __syncthreads();   // staging reads done before the next pair reuses LDS

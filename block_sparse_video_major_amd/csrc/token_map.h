@@ -31,7 +31,18 @@ struct TokenMap {
   int32_t N;            // real tokens per (batch, head): raster rows
   int32_t Np;           // cube-major positions per (batch, head)
   int32_t padded;       // the grid was padded up to whole cubes
+  int32_t mag_plane;    // ceil(2^16 / (ch * cw)): see small_div
+  int32_t mag_cw;       // ceil(2^16 / cw)
 };
+
+// l / d for 0 <= l < 64 and 1 <= d <= 64, as (l * ceil(2^16 / d)) >> 16.
+// With ceil(2^16 / d) = (2^16 + e) / d, 0 <= e < d, the product over 2^16
+// is l / d + l e / (d 2^16), and the added term is below l / 2^16 < 1 / d,
+// so it never carries the quotient past the next multiple: the result is
+// exact.  One 24-bit multiply and a shift instead of an integer division.
+__device__ __forceinline__ int32_t small_div(int32_t l, int32_t mag) {
+  return (int32_t)(((uint32_t)l * (uint32_t)mag) >> 16);
+}
 
 // Grid coordinates of cube c: raster order over the cube grid, or the
 // problem's table of packed coordinates.  A table entry outside the grid
@@ -61,9 +72,8 @@ __device__ __forceinline__ CubeAt cube_at(const TokenMap& m, int32_t c) {
 
 // Whether position l of cube q holds a real token (not padding).
 __device__ __forceinline__ bool token_real(const TokenMap& m, const CubeAt& q, int32_t l) {
-  const int32_t plane = m.ch * m.cw;
-  const int32_t lt = l / plane, rem = l - lt * plane;
-  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
+  const int32_t lt = small_div(l, m.mag_plane), rem = l - lt * (m.ch * m.cw);
+  const int32_t lh = small_div(rem, m.mag_cw), lw = rem - lh * m.cw;
   return q.ok && q.t * m.ct + lt < m.T && q.h * m.ch + lh < m.H && q.w * m.cw + lw < m.W;
 }
 
@@ -88,9 +98,8 @@ __device__ __forceinline__ bool cube_partial(const TokenMap& m, const CubeAt& q)
 // head) in the order the map selects.
 __device__ __forceinline__ int32_t token_pos(const TokenMap& m, int32_t c, const CubeAt& q, int32_t l) {
   if (!m.on) return c * kCubeTokens + l;
-  const int32_t plane = m.ch * m.cw;
-  const int32_t lt = l / plane, rem = l - lt * plane;
-  const int32_t lh = rem / m.cw, lw = rem - lh * m.cw;
+  const int32_t lt = small_div(l, m.mag_plane), rem = l - lt * (m.ch * m.cw);
+  const int32_t lh = small_div(rem, m.mag_cw), lw = rem - lh * m.cw;
   return ((q.t * m.ct + lt) * m.H + q.h * m.ch + lh) * m.W + q.w * m.cw + lw;
 }
 
@@ -119,6 +128,8 @@ inline TokenMap make_token_map(const Geom& g, int out_order) {
   m.ct = g.ct; m.ch = g.ch; m.cw = g.cw;
   m.gT = g.gT; m.gH = g.gH; m.gW = g.gW;
   m.coords = g.coords;
+  m.mag_plane = (int32_t)((65536 + g.ch * g.cw - 1) / (g.ch * g.cw));
+  m.mag_cw = (int32_t)((65536 + g.cw - 1) / g.cw);
   return m;
 }
 
