@@ -427,6 +427,37 @@ def test_sparse_attn_raster_output_matches_unpermute():
         assert np.array_equal(lse_r.cpu().numpy().view(np.uint32), lse_back.view(np.uint32)), name
 
 
+@pytest.mark.parametrize("kk", [154, 300])
+def test_sparse_attn_without_gates_equals_unit_gates(kk):
+    """Without gates out = O_f; with g_f = 1 and g_c = 0 the gated epilogue
+    forms fma(0, O_c, 1 * O_f) = O_f exactly.  The two take different output
+    loops (the gate-free one has no per-row gate tests), so they must agree
+    bit for bit, in cube-major and in raster order, for pairs (Top-154) and
+    quads (Top-300) of query cubes."""
+    _log(f"fine gate-free output K={kk}")
+    w = wl.WAN
+    p = problem(w)
+    x = inputs("wan")
+    q, k, v = (dev(x[n]) for n in ("q", "k", "v"))
+    qp, kp, vp = (torch.empty_like(q) for _ in range(3))
+    for t, c in ((q, qp), (k, kp), (v, vp)):
+        L.vsa_permute(p, L.VSA_BF16, t, c)
+    rng = np.random.default_rng(11)
+    lut = np.sort(np.stack([rng.permutation(w.n_cubes)[:kk] for _ in range(w.heads * w.n_cubes)]), axis=1)
+    lut_d = dev(lut.reshape(1, w.heads, w.n_cubes, kk).astype(np.int32))
+    valid_d = torch.full((1, w.heads, w.n_cubes), kk, dtype=torch.int32, device="cuda")
+    oc = torch.randn((1, w.heads, w.n_cubes, w.head_dim), device="cuda")
+    ones = torch.ones_like(q)
+    zeros = torch.zeros_like(q)
+    for fwd in (L.vsa_sparse_attn_fwd, L.vsa_sparse_attn_fwd_raster):
+        plain = torch.full_like(q, float("nan"))
+        unit = torch.full_like(q, float("nan"))
+        fwd(p, qp, kp, vp, lut_d, valid_d, plain)
+        fwd(p, qp, kp, vp, lut_d, valid_d, unit, oc=oc, gate_c=zeros, gate_f=ones)
+        _sync()
+        assert np.array_equal(bits(plain), bits(unit)), fwd.__name__
+
+
 # Top-154 of 512 cubes runs the kernel over pairs of query cubes, Top-300
 # the one over quads (rows listing at least half of the cubes).
 @pytest.mark.parametrize("kk", [154, 300])
