@@ -47,3 +47,21 @@ def test_workload_sizes():
     assert abs(wl.WAN.sparsity - 0.6992) < 1e-3
     assert wl.LARGE.n_tokens == 122880 and wl.LARGE.n_cubes == 1920
     assert wl.WAN.selected_flops() == 4 * 12 * 32768 * 64 * 154 * 128
+
+
+def test_wan_workload_matches_the_pages_benchmark_configuration():
+    """The 32K-token workload is the configuration the pages print for their
+    headline benchmark (tests/golden/vsa_rocm_benchmark_config.json, each
+    value with its section)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "vsa_rocm_benchmark_config.json")))["values"]
+    w = wl.WAN
+    assert [w.batch, w.heads, w.n_tokens, w.head_dim] == g["qkv_shape"]["value"]
+    assert list(w.cube) == g["cube"]["value"]
+    assert w.cube[0] * w.cube[1] * w.cube[2] == g["tokens_per_cube"]["value"]
+    # Top-K 154 of 512 cubes is the nearest whole count to 70% sparsity
+    target = 1.0 - g["headline_sparsity"]["value"]
+    assert abs(w.top_k / w.n_cubes - target) <= 0.5 / w.n_cubes
+    # N^2 is "about one billion" (within a factor of 1.1)
+    assert 1.0 <= w.n_tokens ** 2 / g["attention_ops_per_layer"]["value"] < 1.1
