@@ -15,7 +15,8 @@ from ._lib import (  # noqa: F401
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
     vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables, vsa_device_peak,
 )
-from .pipeline import VsaBackward, VsaForward, vsa_forward, clear_forward_cache  # noqa: F401
+from .pipeline import (VsaAttentionFunction, VsaBackward, VsaForward, clear_forward_cache,  # noqa: F401
+                       vsa_attention, vsa_forward)
 
 __all__ = [
     "Problem", "VsaError", "VSA_BF16", "VSA_F32", "load", "VsaForward", "vsa_forward",
@@ -27,5 +28,5 @@ __all__ = [
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
     "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT", "clear_cube_tables", "clear_forward_cache",
-    "vsa_device_peak",
+    "vsa_device_peak", "vsa_attention", "VsaAttentionFunction",
 ]

@@ -190,3 +190,70 @@ class VsaBackward:
             L.vsa_pool_unpermute_bwd(po, self.dgcp, None, dgate_c, stream)
         if gfp is not None and dgate_f is not None:
             L.vsa_pool_unpermute_bwd(po, self.dgfp, None, dgate_f, stream)
+
+
+class VsaAttentionFunction(torch.autograd.Function):
+    """One VSA layer as a differentiable PyTorch operation ("VSA: Faster Video
+    Diffusion with Trainable Sparse Attention", Abstract: the sparse attention
+    is trained end to end).  The forward pass keeps what the backward needs:
+    the cube-major intermediates, the index list, and the fine output O_f
+    without gates with its log-sum-exp.  The index list is held fixed in the
+    backward (a Top-K selection has no gradient).  Every step runs in the
+    library's kernels; this class only sequences the calls and owns the
+    buffers.  Raster [batch, heads, N, d] layout, bf16 inputs; the gradients
+    come back in the inputs' dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gate_c, gate_f, p: Problem, top_k: int):
+        dev = q.device
+        f = VsaForward(p, top_k, dev)
+        B = L.VSA_BF16
+        L.vsa_permute_pool(p, B, q, f.qp, f.qc)
+        L.vsa_permute_pool(p.kv_problem(), B, k, f.kp, f.kc)
+        L.vsa_permute_pool(p.v_problem(), B, v, f.vp, f.vc)
+        L.vsa_coarse_topk(p, top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc)
+        # the fine stage without gates, cube-major, for O_f and its LSE
+        o_f = torch.empty((p.batch, p.heads, p.n_positions, p.v_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((p.batch, p.heads, p.n_positions), dtype=torch.float32, device=dev)
+        L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse)
+        out = q.new_empty(q.shape[:-1] + (p.v_dim,))
+        if gate_c is None and gate_f is None:
+            # no gates: the output is O_f in raster order
+            L.vsa_unpermute(dataclasses.replace(p, head_dim=p.v_dim, head_dim_v=0), B, o_f, out)
+        else:
+            # the gated combination is formed in the fine kernel's epilogue
+            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc,
+                                         gate_c=gate_c, gate_f=gate_f)
+        ctx.p, ctx.top_k, ctx.fwd = p, top_k, f
+        ctx.save_for_backward(o_f, lse, gate_c, gate_f)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        o_f, lse, gate_c, gate_f = ctx.saved_tensors
+        p, f = ctx.p, ctx.fwd
+        dev = o_f.device
+        bw = VsaBackward(p, ctx.top_k, dev)
+        f32 = torch.float32
+        dq = torch.empty((p.batch, p.heads, p.n_tokens, p.head_dim), dtype=f32, device=dev)
+        dk = torch.empty((p.batch, p.kv_heads, p.n_tokens, p.head_dim), dtype=f32, device=dev)
+        dv = torch.empty((p.batch, p.kv_heads, p.n_tokens, p.v_dim), dtype=f32, device=dev)
+        gshape = (p.batch, p.heads, p.n_tokens, p.v_dim)
+        dgc = torch.empty(gshape, dtype=f32, device=dev) if gate_c is not None and ctx.needs_input_grad[3] else None
+        dgf = torch.empty(gshape, dtype=f32, device=dev) if gate_f is not None and ctx.needs_input_grad[4] else None
+        dout_bf = dout if dout.dtype == torch.bfloat16 and dout.is_contiguous() else \
+            dout.to(torch.bfloat16).contiguous()
+        bw(f.intermediates(), o_f, lse, dout_bf, dq, dk, dv, gate_c=gate_c, gate_f=gate_f,
+           dgate_c=dgc, dgate_f=dgf)
+        # autograd casts each gradient to its input's dtype
+        return dq, dk, dv, dgc, dgf, None, None
+
+
+def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, top_k: int,
+                  gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Differentiable VSA layer on raster bf16 inputs [batch, heads, N, d]:
+    out = g_f * O_f + g_c * O_c (O_f alone without gates).  Backward gives
+    the gradients of q, k, v and the gates with the Top-K index list fixed."""
+    if not 1 <= top_k <= p.n_cubes:
+        raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
+    return VsaAttentionFunction.apply(q, k, v, gate_c, gate_f, p, top_k)
