@@ -147,6 +147,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2,
     TokenMap tmap, int group) {
   using C = Cfg<D>;
+  // The load plan issues group p (K tiles of step p, V tiles of step p - 1)
+  // by barrier p - 1, while the tiles of the two steps before it are still
+  // held; a step has up to two tiles, so each ring needs four positions
+  // (with three, two consecutive two-tile steps leave no room for group p).
+  static_assert(RK >= 4 && RV >= 4, "each ring holds two steps of up to two tiles");
   constexpr int V_BASE = RK * C::TILE;           // V ring after the K ring
   constexpr int RING = (RK + RV) * C::TILE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
