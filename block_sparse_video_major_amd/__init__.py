@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
     vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size, vsa_sparse_attn_bwd_noalloc,
     vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
-    vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
+    vsa_combine, vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
     vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables, vsa_device_peak,
 )
@@ -24,7 +24,7 @@ __all__ = [
     "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
     "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size", "vsa_sparse_attn_bwd_noalloc",
     "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
-    "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
+    "vsa_combine", "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",
     "vsa_cube_table", "VSA_CUBES_RASTER", "VSA_CUBES_HILBERT", "clear_cube_tables", "clear_forward_cache",

@@ -159,6 +159,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "vsa_sparse_attn_bwd_noalloc": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp],
         "vsa_combine_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "vsa_combine": [P, vp, vp, vp, vp, vp, vp],
         "vsa_coarse_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "vsa_coarse_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "vsa_pool_unpermute_bwd": [P, vp, vp, vp, vp],
@@ -512,6 +513,22 @@ def vsa_sparse_attn_bwd_noalloc(p: Problem, q: torch.Tensor, k: torch.Tensor, v:
                                               _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(o),
                                               _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
                                               _stream(stream, dev)), "vsa_sparse_attn_bwd_noalloc")
+
+
+def vsa_combine(p: Problem, o_f: torch.Tensor, out: torch.Tensor, oc: Optional[torch.Tensor] = None,
+                gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out (raster) = g_f * O_f (cube-major) + g_c * O_c per cube, bf16; a
+    missing gate_f reads as 1 and a missing gate_c as 0."""
+    dev = o_f.device
+    _need(o_f, "o_f", _pos_shape(p, p.v_dim), torch.bfloat16, dev)
+    _need(out, "out", _tok_shape(p, p.v_dim), torch.bfloat16, dev)
+    for name, t in (("gate_c", gate_c), ("gate_f", gate_f)):
+        if t is not None:
+            _need(t, name, _tok_shape(p, p.v_dim), torch.bfloat16, dev)
+    if oc is not None:
+        _need(oc, "oc", _cube_shape(p, p.v_dim), torch.float32, dev)
+    _check(load().vsa_combine(ctypes.byref(p.c_struct(dev)), _ptr(o_f), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
+                              _ptr(out), _stream(stream, dev)), "vsa_combine")
 
 
 def vsa_combine_bwd(p: Problem, dout: torch.Tensor, d_of: torch.Tensor, d_oc: torch.Tensor,

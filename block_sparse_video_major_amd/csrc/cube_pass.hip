@@ -38,6 +38,7 @@
 // pass produces exactly the bits of the separate reorder and pool passes.
 #include <type_traits>
 
+#include "mfma_util.h"
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -107,6 +108,56 @@ __device__ __forceinline__ int32_t row_offset(int32_t l, const CubeArgs& a) {
   return (lt * a.H + lh) * a.W + lw;
 }
 
+// Where cube `unit` = (batch*head) * Nc + c lives on both sides: the raster
+// row of its first token (row of token n of the (batch, head) = rbase + n *
+// tstride), its first cube-major row, and its real extent along each axis
+// (the cube edge unless the grid was padded).  ok is false for a table entry
+// outside the grid (a table written for another problem).
+struct UnitPos {
+  bool ok;
+  int64_t raster0, cube0, tstride;
+  int32_t rem_t, rem_h, rem_w;
+  // whether position l of the cube holds a real token
+  __device__ __forceinline__ bool real(int32_t l, const CubeArgs& a) const {
+    const int32_t plane = a.ch * a.cw;
+    const int32_t lt = l / plane, rem = l - lt * plane;
+    const int32_t lh = rem / a.cw;
+    return lt < rem_t && lh < rem_h && rem - lh * a.cw < rem_w;
+  }
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const CubeArgs& a, int64_t unit) {
+  UnitPos u;
+  const int64_t bh = unit / a.Nc;
+  const int32_t c = (int32_t)(unit - bh * a.Nc);
+  int32_t ct_i, ch_i, cw_i;
+  if (a.coords != nullptr) {
+    const int32_t e = a.coords[c];   // the same for the whole workgroup
+    ct_i = (e >> 20) & 1023;
+    ch_i = (e >> 10) & 1023;
+    cw_i = e & 1023;
+    u.ok = ct_i < a.gT && ch_i < a.gH && cw_i < a.gW;
+  } else {
+    cw_i = c % a.gW;
+    ch_i = (c / a.gW) % a.gH;
+    ct_i = c / (a.gW * a.gH);
+    u.ok = true;
+  }
+  int64_t rbase = bh * (int64_t)a.N;
+  u.tstride = 1;
+  if (a.bnhd) {
+    const int64_t b = bh / a.heads;
+    rbase = b * a.N * (int64_t)a.heads + (bh - b * a.heads);
+    u.tstride = a.heads;
+  }
+  u.raster0 = rbase + (int64_t)((ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw) * u.tstride;
+  u.cube0 = bh * (int64_t)a.Np + (int64_t)c * a.vol;
+  u.rem_t = min(a.ct, a.T - ct_i * a.ct);
+  u.rem_h = min(a.ch, a.H - ch_i * a.ch);
+  u.rem_w = min(a.cw, a.W - cw_i * a.cw);
+  return u;
+}
+
 // T = element type (pool modes), D = head_dim; CPR = 16-byte chunks per row.
 // Grid-stride over units = (batch*head) * Nc + cube.
 template <typename T, int D, int MODE, bool PAD>
@@ -128,38 +179,13 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
   const int phase = threadIdx.x / CPR;
 
   for (int64_t unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
-    const int64_t bh = unit / a.Nc;
-    const int32_t c = (int32_t)(unit - bh * a.Nc);
-    int32_t ct_i, ch_i, cw_i;
-    if (a.coords != nullptr) {
-      const int32_t e = a.coords[c];   // the same for the whole workgroup
-      ct_i = (e >> 20) & 1023;
-      ch_i = (e >> 10) & 1023;
-      cw_i = e & 1023;
-      if (ct_i >= a.gT || ch_i >= a.gH || cw_i >= a.gW) continue;   // not a table for this grid
-    } else {
-      cw_i = c % a.gW;
-      ch_i = (c / a.gW) % a.gH;
-      ct_i = c / (a.gW * a.gH);
-    }
-    // raster side: row of token n of this (batch, head) is rbase + n * tstride
-    int64_t rbase = bh * (int64_t)a.N, tstride = 1;
-    if (a.bnhd) {
-      const int64_t b = bh / a.heads;
-      rbase = b * a.N * (int64_t)a.heads + (bh - b * a.heads);
-      tstride = a.heads;
-    }
-    const int64_t raster0 = rbase + (int64_t)((ct_i * a.ct * a.H + ch_i * a.ch) * a.W + cw_i * a.cw) * tstride;
-    const int64_t cube0 = bh * (int64_t)a.Np + (int64_t)c * a.vol;
-    // real extent of this cube along each axis (the edge unless padded)
-    const int32_t rem_t = min(a.ct, a.T - ct_i * a.ct), rem_h = min(a.ch, a.H - ch_i * a.ch),
-                  rem_w = min(a.cw, a.W - cw_i * a.cw);
+    const UnitPos u = unit_pos(a, unit);
+    if (!u.ok) continue;   // not a table for this grid
+    const int64_t raster0 = u.raster0, cube0 = u.cube0, tstride = u.tstride;
+    const int32_t rem_t = u.rem_t, rem_h = u.rem_h, rem_w = u.rem_w;
     auto real = [&](int32_t l) {
       if constexpr (!PAD) return true;
-      const int32_t plane = a.ch * a.cw;
-      const int32_t lt = l / plane, rem = l - lt * plane;
-      const int32_t lh = rem / a.cw;
-      return lt < rem_t && lh < rem_h && rem - lh * a.cw < rem_w;
+      return u.real(l, a);
     };
     float acc[kPooling ? E : 1];
 #pragma unroll
@@ -231,6 +257,61 @@ __global__ __launch_bounds__(kThreads) void cube_pass_kernel(const uint4* __rest
   }
 }
 
+// The combination of the fine and coarse outputs as a pass of its own ("VSA:
+// Accelerating Video Diffusion Inference with Sparse Attention on AMD GPUs",
+// §Two-Stage Architecture: the output combines the coarse-stage and the
+// fine-stage outputs through gates), for callers that keep the fine output O_f
+// itself (a training forward: the backward needs O_f without gates).  Token l
+// of cube c leaves for its raster row as g_f * O_f + g_c * O_c[c], formed in
+// float32 from the bf16 O_f and gates in the order the fine kernel's epilogue
+// uses (the product with g_f, then one fused multiply-add with g_c), rounded
+// to bf16 once.  A missing gate_f reads as 1 and a missing gate_c as 0 (O_c
+// is then not read): without gates the pass is the reorder back.  Padded
+// positions have no raster row.  D = the output's head size; one workgroup
+// per cube as in the passes above.
+template <int D, bool PAD>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ o_f,
+                                                           const float* __restrict__ oc,
+                                                           const uint4* __restrict__ gate_c,
+                                                           const uint4* __restrict__ gate_f,
+                                                           uint4* __restrict__ out, CubeArgs a) {
+  constexpr int CPR = D / 8;   // 16-byte chunks (8 bf16) per row
+  constexpr int RG = kThreads / CPR;
+  const int col = threadIdx.x % CPR;
+  const int phase = threadIdx.x / CPR;
+  for (int64_t unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
+    const UnitPos u = unit_pos(a, unit);
+    if (!u.ok) continue;
+    float cv[8];
+    if (gate_c != nullptr) {
+      const float4 c0 = reinterpret_cast<const float4*>(oc + unit * D)[2 * col];
+      const float4 c1 = reinterpret_cast<const float4*>(oc + unit * D)[2 * col + 1];
+      cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
+      cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
+    }
+    for (int32_t l = phase; l < a.vol; l += RG) {
+      if (PAD && !u.real(l, a)) continue;   // padding: no raster row
+      const int64_t rrow = u.raster0 + (int64_t)row_offset(l, a) * u.tstride;
+      float v[8];
+      widen<__bf16>(o_f[(u.cube0 + l) * CPR + col], v);
+      if (gate_f != nullptr) {
+        float gf[8];
+        widen<__bf16>(gate_f[rrow * CPR + col], gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= gf[e];
+      }
+      if (gate_c != nullptr) {
+        float gc[8];
+        widen<__bf16>(gate_c[rrow * CPR + col], gc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(gc[e], cv[e], v[e]);
+      }
+      out[rrow * CPR + col] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+  }
+}
+
 CubeArgs cube_args(const Geom& g, RasterLayout layout) {
   CubeArgs a;
   a.heads = g.heads;
@@ -298,6 +379,27 @@ hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const 
                                      hipStream_t s, RasterLayout layout) {
   if (dxc == nullptr) return launch_mode<float, kToRaster>(g, dx_cube, dx_raster, nullptr, s, layout);
   return launch_mode<float, kToRasterAddPooled>(g, dx_cube, dx_raster, const_cast<float*>(dxc), s, layout);
+}
+
+hipError_t launch_combine(const Geom& g, const void* o_f, const float* oc, const void* gate_c, const void* gate_f,
+                          void* out, hipStream_t s) {
+  const CubeArgs a = cube_args(g, kBHND);
+  const dim3 grid((unsigned)(a.units < kMaxGrid ? a.units : kMaxGrid));
+  const auto* of4 = static_cast<const uint4*>(o_f);
+  const auto* gc4 = static_cast<const uint4*>(gate_c);
+  const auto* gf4 = static_cast<const uint4*>(gate_f);
+  auto* out4 = static_cast<uint4*>(out);
+  if (g.Dv == 64 && g.padded)
+    hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(kThreads), 0, s, of4, oc, gc4, gf4, out4, a);
+  else if (g.Dv == 64)
+    hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(kThreads), 0, s, of4, oc, gc4, gf4, out4, a);
+  else if (g.Dv == 128 && g.padded)
+    hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(kThreads), 0, s, of4, oc, gc4, gf4, out4, a);
+  else if (g.Dv == 128)
+    hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(kThreads), 0, s, of4, oc, gc4, gf4, out4, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace vsa

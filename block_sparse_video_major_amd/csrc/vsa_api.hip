@@ -103,7 +103,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (3 << 16) | 1; }
+int vsa_abi_version(void) { return (3 << 16) | 2; }
 
 int vsa_device_peak(int32_t device, int32_t* cu_count, int32_t* clock_khz, double* bf16_tflops) {
   int cus = 0, khz = 0;
@@ -385,6 +385,16 @@ int vsa_sparse_attn_bwd_noalloc(const vsa_problem* p, const void* q, const void*
   // previous call's contents need no clearing
   return hip_status(vsa::launch_sparse_attn_bwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, o, lse,
                                                 d_o, dq, dk, dv, ws, (hipStream_t)stream));
+}
+
+int vsa_combine(const vsa_problem* p, const void* o_f, const float* oc, const void* gate_c, const void* gate_f,
+                void* out, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (o_f == nullptr || out == nullptr) return VSA_ERR_NULL;
+  if (gate_c != nullptr && oc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  return hip_status(vsa::launch_combine(g, o_f, oc, gate_c, gate_f, out, (hipStream_t)stream));
 }
 
 int vsa_combine_bwd(const vsa_problem* p, const void* dout, const void* o_f, const float* oc, const void* gate_c,

@@ -112,6 +112,10 @@ hipError_t launch_coarse_bwd(const Geom& g, const float* qc, const float* kc, co
                              const float* doc, float* dqc, float* dkc, float* dvc, void* workspace, hipStream_t s);
 hipError_t launch_pool_unpermute_bwd(const Geom& g, const float* dx_cube, const float* dxc, float* dx_raster,
                                      hipStream_t s, RasterLayout layout = kBHND);
+// out (raster, Dv wide) = g_f * O_f (cube-major) + g_c * O_c per cube; null
+// gates read as g_f = 1, g_c = 0.
+hipError_t launch_combine(const Geom& g, const void* o_f, const float* oc, const void* gate_c, const void* gate_f,
+                          void* out, hipStream_t s);
 
 // Largest number of cubes per (batch, head) the coarse stage handles.
 constexpr int64_t kMaxCoarseCubes = 4096;

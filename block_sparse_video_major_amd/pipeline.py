@@ -197,7 +197,9 @@ class VsaAttentionFunction(torch.autograd.Function):
     Diffusion with Trainable Sparse Attention", Abstract: the sparse attention
     is trained end to end).  The forward pass keeps what the backward needs:
     the cube-major intermediates, the index list, and the fine output O_f
-    without gates with its log-sum-exp.  The index list is held fixed in the
+    without gates with its log-sum-exp; the output is then formed from O_f by
+    vsa_combine (so it differs from VsaForward's fused epilogue by one bf16
+    rounding of O_f).  The index list is held fixed in the
     backward (a Top-K selection has no gradient).  Every step runs in the
     library's kernels; this class only sequences the calls and owns the
     buffers.  Raster [batch, heads, N, d] layout, bf16 inputs; the gradients
@@ -216,14 +218,10 @@ class VsaAttentionFunction(torch.autograd.Function):
         o_f = torch.empty((p.batch, p.heads, p.n_positions, p.v_dim), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((p.batch, p.heads, p.n_positions), dtype=torch.float32, device=dev)
         L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse)
+        # the layer's output from O_f: the gated combination in raster order
+        # (without gates, O_f reordered back)
         out = q.new_empty(q.shape[:-1] + (p.v_dim,))
-        if gate_c is None and gate_f is None:
-            # no gates: the output is O_f in raster order
-            L.vsa_unpermute(dataclasses.replace(p, head_dim=p.v_dim, head_dim_v=0), B, o_f, out)
-        else:
-            # the gated combination is formed in the fine kernel's epilogue
-            L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc,
-                                         gate_c=gate_c, gate_f=gate_f)
+        L.vsa_combine(p, o_f, out, oc=f.oc if gate_c is not None else None, gate_c=gate_c, gate_f=gate_f)
         ctx.p, ctx.top_k, ctx.fwd = p, top_k, f
         ctx.save_for_backward(o_f, lse, gate_c, gate_f)
         return out

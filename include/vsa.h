@@ -17,7 +17,8 @@
  *   5. vsa_unpermute    cube-major -> raster order
  * and, for training a layer end to end, the backward of each step:
  *   vsa_combine_bwd, vsa_sparse_attn_bwd, vsa_coarse_bwd and
- *   vsa_pool_unpermute_bwd (the index list held fixed).
+ *   vsa_pool_unpermute_bwd (the index list held fixed); a training forward
+ *   keeps O_f (step 4 without gates) and forms the output with vsa_combine.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -345,6 +346,26 @@ int vsa_sparse_attn_bwd_noalloc(const vsa_problem* p, const void* q, const void*
                                 const int32_t* valid_block_num, int32_t max_kv_blocks,
                                 const void* o, const float* lse, const void* d_o,
                                 float* dq, float* dk, float* dv, void* stream);
+
+/* The gated combination as a pass of its own ([VSA-ROCm] §Two-Stage
+ * Architecture: the output combines the coarse and fine outputs through
+ * gates), for callers that keep the fine output O_f itself, such as a
+ * training forward (run vsa_sparse_attn_fwd without gates for O_f and its
+ * LSE, then this call for the layer's output):
+ *   out[b, h, pi(p), :] = g_f[b, h, pi(p), :] * o_f[b, h, p, :]
+ *                         + g_c[b, h, pi(p), :] * oc[b, h, c(p), :]
+ * formed in float32 (the product with g_f, then one fused multiply-add with
+ * g_c, as in vsa_sparse_attn_fwd's epilogue) and rounded to bf16 once.
+ * Because o_f is already bf16 this differs from the fused epilogue by that
+ * one rounding of O_f.  gate_f == NULL means g_f = 1; gate_c == NULL means
+ * g_c = 0 (oc may then be NULL); without gates this is vsa_unpermute of o_f.
+ * o_f:  [batch, heads, Np, head_dim_v] bf16, cube-major (padded positions
+ *       are not read); oc: [batch, heads, Nc, head_dim_v] float32.
+ * gate_c, gate_f, out: [batch, heads, N, head_dim_v] bf16, raster order.
+ * Errors: VSA_ERR_NULL (o_f or out NULL, or gate_c without oc), the
+ * vsa_problem checks; nothing is written then. */
+int vsa_combine(const vsa_problem* p, const void* o_f, const float* oc,
+                const void* gate_c, const void* gate_f, void* out, void* stream);
 
 /* Backward of the gated combination ([VSA-ROCm] §Two-Stage Architecture:
  * gates between the coarse and fine outputs; [VSA-arXiv] Abstract: trained

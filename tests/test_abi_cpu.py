@@ -177,6 +177,18 @@ def test_permute_pool_errors():
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 2, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
 
 
+def test_combine_errors():
+    lib = _raw()
+    pr = ctypes.byref(_prob())
+    assert lib.vsa_combine(None, DUMMY, DUMMY, None, None, DUMMY, None) == L.VSA_ERR_NULL
+    assert lib.vsa_combine(pr, None, DUMMY, None, None, DUMMY, None) == L.VSA_ERR_NULL      # no O_f
+    assert lib.vsa_combine(pr, DUMMY, DUMMY, None, None, None, None) == L.VSA_ERR_NULL      # no out
+    assert lib.vsa_combine(pr, DUMMY, None, DUMMY, None, DUMMY, None) == L.VSA_ERR_NULL     # gate_c without oc
+    assert lib.vsa_combine(ctypes.byref(_prob(H=0)), DUMMY, DUMMY, None, None, DUMMY, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_combine(ctypes.byref(_prob(head_dim_v=96)), DUMMY, None, None, None, DUMMY,
+                           None) == L.VSA_ERR_UNSUPPORTED
+
+
 def test_mask_to_lut_errors():
     lib = _raw()
     pr = ctypes.byref(_prob())          # Nc = 32

@@ -1,7 +1,9 @@
 """GPU checks of vsa_attention, the differentiable layer (VsaAttentionFunction).
 
-* Its output equals VsaForward's bit for bit (the same kernels in the same
-  order), with and without gates.
+* Its output equals the hand-sequenced training forward (the fine stage
+  without gates, then vsa_combine) bit for bit, and VsaForward's fused
+  epilogue within the one extra bf16 rounding of O_f (bit for bit without
+  gates).
 * Its gradients equal a hand-sequenced VsaBackward on the same forward
   intermediates bit for bit (after the cast to the inputs' bf16 dtype that
   autograd applies), for plain, grouped-head and padded problems.
@@ -38,14 +40,17 @@ def _log(msg):
 
 
 def _manual(p, top_k, q, k, v, gc, gf, dout):
-    """The same layer sequenced by hand: VsaForward for the output, the
-    cube-major fine pass for O_f and LSE, then VsaBackward."""
+    """The same layer sequenced by hand: VsaForward (its fused output, and the
+    intermediates), the cube-major fine pass for O_f and LSE, vsa_combine for
+    the training output, then VsaBackward."""
     f = VsaForward(p, top_k)
-    out = q.new_empty(q.shape[:-1] + (p.v_dim,))
-    f(q, k, v, out, gc, gf)
+    fused = q.new_empty(q.shape[:-1] + (p.v_dim,))
+    f(q, k, v, fused, gc, gf)
     o_f = torch.empty((p.batch, p.heads, p.n_positions, p.v_dim), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((p.batch, p.heads, p.n_positions), dtype=torch.float32, device="cuda")
     L.vsa_sparse_attn_fwd(p, f.qp, f.kp, f.vp, f.lut, f.valid, o_f, lse=lse)
+    out = torch.empty_like(fused)
+    L.vsa_combine(p, o_f, out, oc=f.oc if gc is not None else None, gate_c=gc, gate_f=gf)
     f32 = torch.float32
     dq = torch.empty((p.batch, p.heads, p.n_tokens, p.head_dim), dtype=f32, device="cuda")
     dk = torch.empty((p.batch, p.kv_heads, p.n_tokens, p.head_dim), dtype=f32, device="cuda")
@@ -55,7 +60,7 @@ def _manual(p, top_k, q, k, v, gc, gf, dout):
     dgf = torch.empty(gs, dtype=f32, device="cuda") if gf is not None else None
     VsaBackward(p, top_k)(f.intermediates(), o_f, lse, dout, dq, dk, dv, gate_c=gc, gate_f=gf,
                           dgate_c=dgc, dgate_f=dgf)
-    return out, (dq, dk, dv, dgc, dgf), f
+    return out, fused, (dq, dk, dv, dgc, dgf)
 
 
 def _inputs(p, seed, gates):
@@ -89,9 +94,16 @@ def test_autograd_matches_hand_sequenced_layer(name, repl, top_k, gates):
     out = vsa_attention(*leaves, p, top_k, gate_c=gleaves[0], gate_f=gleaves[1])
     out.backward(dout)
     torch.cuda.synchronize()
-    want_out, want_grads, _ = _manual(p, top_k, q, k, v, gc, gf, dout)
+    want_out, fused, want_grads = _manual(p, top_k, q, k, v, gc, gf, dout)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out.detach()), bits(want_out)), "output"
+    if not gates:
+        assert np.array_equal(bits(out.detach()), bits(fused)), "output without gates"
+    else:
+        # one more rounding of O_f to bf16 (relative 2^-9, times g_f <= 1) and
+        # possibly one bf16 ulp (2^-8) of the result apart
+        a, b = host64(out.detach()), host64(fused)
+        assert np.all(np.abs(a - b) <= 2 ** -7 * np.abs(b) + 2 ** -9 * np.abs(b).max()), "output vs fused"
     got = [t.grad for t in leaves] + [t.grad if t is not None else None for t in gleaves]
     for nm, g, w in zip(("dq", "dk", "dv", "dgate_c", "dgate_f"), got, want_grads):
         if w is None:
