@@ -391,7 +391,36 @@ def main() -> int:
                 torch.cuda.synchronize()
                 for i, n in enumerate(lnames):
                     lt[n] += e[i].elapsed_time(e[i + 1]) / reps
-            del bw, lgrads, gate_c, gate_f
+
+            # the differentiable layer (vsa_attention) with the same gates and
+            # output gradient: its training forward (reorders and pools, coarse
+            # stage, fine stage without gates keeping O_f and LSE, vsa_combine)
+            # and its backward through autograd, buffers allocated per call
+            leaves = [t.detach().clone().requires_grad_(True) for t in (q, k, v, gate_c, gate_f)]
+
+            def train_layer(ev=None):
+                with torch.cuda.stream(stream):
+                    if ev is not None:
+                        ev[0].record(stream)
+                    o = vsa.vsa_attention(leaves[0], leaves[1], leaves[2], p, w.top_k,
+                                          gate_c=leaves[3], gate_f=leaves[4])
+                    if ev is not None:
+                        ev[1].record(stream)
+                    o.backward(d_o)
+                    if ev is not None:
+                        ev[2].record(stream)
+                for t in leaves:
+                    t.grad = None
+            train_layer()
+            torch.cuda.synchronize()
+            tr = {"forward": 0.0, "backward": 0.0}
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                train_layer(e)
+                torch.cuda.synchronize()
+                tr["forward"] += e[0].elapsed_time(e[1]) / reps
+                tr["backward"] += e[1].elapsed_time(e[2]) / reps
+            del bw, lgrads, gate_c, gate_f, leaves
 
             # the same step and fine backward with the cubes in Hilbert order
             # (same inputs; the LUT is the Hilbert-order coarse stage's own)
@@ -570,7 +599,7 @@ def main() -> int:
                      "stages_ms": lst, "flops": wL.selected_flops(), "top_k": wL.top_k, "cubes": wL.n_cubes,
                      "heads": wL.heads, "tokens": wL.n_tokens}
             del xl, fl_, ol
-            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large
+            return acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, tr, hil, dvres, pad, large
         ex = None if args.skip_extras else extras()
     torch.cuda.synchronize()
 
@@ -633,7 +662,7 @@ def main() -> int:
                      "note": "runtime peak = compute units x peak shader clock x 4096 bf16 flop per clock "
                              "per CU, from HIP's device attributes; roofline.peak is the published figure"}
     if ex is not None:
-        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, hil, dvres, pad, large = ex
+        acc, mt, pairs_m, over_m, sweep, flops_m, t_bwd, lt, tr, hil, dvres, pad, large = ex
         pad_fl = 4 * 64 * 64 * w.head_dim * pad["pairs"]   # per selected pair, padded positions included
         rec.update({
             "stages_ms": {n: round(t, 4) for n, t in acc.items()},
@@ -659,6 +688,11 @@ def main() -> int:
                          "layer_ms": round(sum(lt.values()), 4),
                          "layer_stages_ms": {n: round(t, 4) for n, t in lt.items()},
                          "layer_note": "whole-layer backward with gates (VsaBackward steps), LUT fixed"},
+            "training_layer": {"note": "vsa_attention with gates: its forward keeps O_f and LSE for the backward "
+                                       "and forms the output with vsa_combine; backward through autograd, "
+                                       "gradients cast to bf16; buffers allocated on every call",
+                               "forward_ms": round(tr["forward"], 4), "backward_ms": round(tr["backward"], 4),
+                               "total_ms": round(tr["forward"] + tr["backward"], 4)},
             "hilbert_order": {"note": "the same step and fine backward with the cubes in 3D Hilbert order",
                               "ms_per_step": round(hil["step_ms"], 4),
                               "tflops_per_step": round(flops / (hil["step_ms"] * 1e-3) / 1e12, 2),
