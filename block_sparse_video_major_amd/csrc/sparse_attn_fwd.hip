@@ -78,6 +78,7 @@ constexpr int kThreads = 512;     // two query cubes x 4 wavefronts
 constexpr int kIssueThreads = 256;   // the four wavefronts of half A issue every tile load
 constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // initial exponent offset
+constexpr int kLdsMax = 160 * 1024;   // LDS of one CU
 
 template <int D>
 struct Cfg {
@@ -139,7 +140,11 @@ __device__ __forceinline__ void wait_parts(int parts) {
 // PAD: the grid was padded up to whole cubes (the key masking of partial
 // tiles is compiled only into this variant, so the divisible case keeps its
 // loop as it is).
-template <int D, int RK, int RV, bool PAD>
+// ZT: the last TILE bytes of the CU's LDS hold a tile of zeros (beyond the
+// ring, the schedule and the epilogue's buffers), read as the operands of a
+// half that has no tile in a step.  The operands are then the same zeros as
+// in the variant without it, which branches around its operand reads.
+template <int D, int RK, int RV, bool PAD, bool ZT>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
@@ -154,6 +159,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   static_assert(RK >= 4 && RV >= 4, "each ring holds two steps of up to two tiles");
   constexpr int V_BASE = RK * C::TILE;           // V ring after the K ring
   constexpr int RING = (RK + RV) * C::TILE;
+  constexpr int ZERO_OFF = kLdsMax - C::TILE;    // the zero tile (ZT)
+  static_assert(!ZT || (C::EPI_BYTES <= ZERO_OFF && RING < ZERO_OFF), "zero tile clear of the ring and epilogue");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // schedule after the ring: sched[s] packs the key cube of half A (low 16
   // bits) and of half B (high 16 bits) of step s; 0xffff = none.
@@ -223,6 +230,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     }
   }
 
+  if constexpr (ZT) {
+    // written once; nothing else writes there (the first pair's schedule
+    // build passes several barriers before the first operand read)
+    for (int i = tid; i < C::TILE / 16; i += kThreads)
+      *reinterpret_cast<uint4*>(smem + ZERO_OFF + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+  }
   const int pairs_per_head = (Nc + 1) >> 1;
   const int64_t per_xcd = (total_pairs + 7) / 8;
   const int xcd = blockIdx.x % 8;
@@ -557,7 +570,24 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       const uint32_t vslot = (d_c >> (8 + 4 * grp)) & 15u;
       bf16x8 ka[D / 16];
       bf16x8 va[C::OT][2];
-      if (has_c) {
+      if constexpr (ZT) {
+        // a half without a tile reads the zero tile: no branch
+        const char* kbase = smem + (has_c ? kslot * C::TILE : (uint32_t)ZERO_OFF);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(kbase + k_off[ks]);
+        // v_off includes the V ring base
+        const char* vbase = smem + (has_p ? vslot * C::TILE : (uint32_t)(ZERO_OFF - V_BASE));
+#pragma unroll
+        for (int t = 0; t < C::OT; ++t)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vbase + v_off[t] + (16 * j) * C::ROWB));
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vbase + v_off[t] + (16 * j + 8) * C::ROWB));
+            va[t][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+      } else if (has_c) {
         const char* base = smem + kslot * C::TILE;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(base + k_off[ks]);
@@ -567,7 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) ka[ks][e] = (__bf16)0.f;
       }
-      if (has_p) {
+      if (ZT) {
+      } else if (has_p) {
         // For k-step j the A operand of lane (g, d-row) holds keys base +
         // 0..3 and base + 8..11 with base = 32*kh + 16*j + 4*g: exactly the
         // keys of pb[j]'s slots.
@@ -799,13 +830,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
 // granted to each instantiation.
 struct DevState {
   int cus = 0;
-  int lds_granted[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int lds_granted[16] = {};
 };
 
-constexpr int kLdsMax = 160 * 1024;
 std::mutex dev_state_mutex;
 
-template <int D, int RK, int RV, bool PAD>
+template <int D, int RK, int RV, bool PAD, bool ZT>
 hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                        const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                        const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot,
@@ -815,9 +845,13 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   DevState& st = dev_state[dev];
-  auto kern = sparse_attn_fwd_kernel<D, RK, RV, PAD>;
+  auto kern = sparse_attn_fwd_kernel<D, RK, RV, PAD, ZT>;
   size_t lds = (size_t)(RK + RV) * C::TILE + sched_bytes;
   if (lds < (size_t)C::EPI_BYTES) lds = C::EPI_BYTES;
+  if (ZT) {
+    if (lds > (size_t)(kLdsMax - C::TILE)) return hipErrorInvalidValue;
+    lds = kLdsMax;   // the zero tile is the last TILE bytes
+  }
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
   int cus = 0;
   {
@@ -859,27 +893,38 @@ size_t sched_bytes(const Geom& g, int max_kv) {
 
 constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8 at d = 64
 
-// The deeper ring is used whenever the schedule (and the schedule build's
-// scratch, which lives in the ring) fits beside it in LDS.
+// Ring shapes: at d = 128 four K and four V positions (measured as fast as
+// five and four); at d = 64 ten and eight whenever the schedule fits beside
+// them, else eight and eight.  The zero tile (ZT) takes the last tile of LDS
+// whenever the ring and the schedule leave it free (not with padded grids at
+// d = 128).
 template <int D, bool PAD>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                     const void* gate_f, void* out, float* lse, hipStream_t s, const TokenMap& tmap) {
   using C = Cfg<D>;
-  constexpr int RK_DEEP = D == 128 ? 5 : 10, RV_DEEP = D == 128 ? 4 : 8;
+  constexpr int RK_DEEP = D == 128 ? 4 : 10, RV_DEEP = D == 128 ? 4 : 8;
   constexpr int R_BASE = D == 128 ? 4 : 8;
   static_assert((size_t)2 * R_BASE * C::TILE == kBaseRingBytes, "base ring size");
   if (!sparse_attn_fwd_fits(g, max_kv)) return hipErrorInvalidValue;
   const size_t sched = sched_bytes(g, max_kv);
   const size_t build_scratch = 16 * (size_t)max_kv;   // SH, EXA, EXB, PK
-  const int base_slot = (D == 128 ? 2 : 0) + (PAD ? 4 : 0);
-  if ((size_t)(RK_DEEP + RV_DEEP) * C::TILE + sched <= (size_t)kLdsMax &&
-      build_scratch <= (size_t)(RK_DEEP + RV_DEEP) * C::TILE)
-    return launch_ring<D, RK_DEEP, RV_DEEP, PAD>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
-                                            sched, base_slot, tmap);
-  if (build_scratch > (size_t)(2 * R_BASE) * C::TILE) return hipErrorInvalidValue;
-  return launch_ring<D, R_BASE, R_BASE, PAD>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, sched,
-                                        base_slot + 1, tmap);
+  const size_t zfree = (size_t)kLdsMax - C::TILE;     // LDS below the zero tile
+  const int slot0 = (D == 128 ? 3 : 0) + (PAD ? 6 : 0);
+  constexpr size_t DEEP = (size_t)(RK_DEEP + RV_DEEP) * C::TILE;
+  if constexpr (RK_DEEP != R_BASE) {
+    if (DEEP + sched <= zfree && build_scratch <= DEEP)
+      return launch_ring<D, RK_DEEP, RV_DEEP, PAD, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out,
+                                                        lse, s, sched, slot0, tmap);
+  }
+  if (build_scratch > kBaseRingBytes) return hipErrorInvalidValue;
+  // (the padded d = 128 variant keeps its branches: with the zero tile it
+  // spills a register)
+  if (!(PAD && D == 128) && kBaseRingBytes + sched <= zfree)
+    return launch_ring<D, R_BASE, R_BASE, PAD, !(PAD && D == 128)>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
+                                                    sched, slot0 + 1, tmap);
+  return launch_ring<D, R_BASE, R_BASE, PAD, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
+                                                   sched, slot0 + 2, tmap);
 }
 
 }  // namespace
