@@ -44,9 +44,11 @@
 //     step schedule is read with one readlane from a 64-entry register
 //     window that slides every 32 steps.
 //   * Tiles arrive by direct global->LDS loads (16 bytes per lane, no
-//     registers).  K and V have separate rings (5 + 4 tiles at d = 128 when
-//     the schedule fits beside them, else 4 + 4; twice that at d = 64)
-//     because V is consumed one step after K.  Ring positions and, for
+//     registers).  K and V have separate rings (4 + 4 tiles at d = 128;
+//     10 + 8 at d = 64 when the schedule fits beside them, else 8 + 8)
+//     because V is consumed one step after K.  A half with no tile in a step
+//     reads a tile of zeros kept at the top of LDS instead of branching
+//     around its operand reads.  Ring positions and, for
 //     every step, the last load group the rings can take are computed once
 //     per pair; the four waves of half A issue all loads right after the step
 //     barrier, as far ahead as the rings allow, and wait for them with a
