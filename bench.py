@@ -1,10 +1,14 @@
 """Benchmark of the VSA forward pass on one MI355X.
 
 One step = one pass of the whole forward path over one batch of synthetic
-input resident in HBM: reorder Q, K, V into cubes and pool them (one fused
-pass per tensor), coarse attention + Top-K, fine block-sparse attention
-(with the coarse output combined through the gates' default) writing the
-output back in raster order from its epilogue.  The default workload is the
+input resident in HBM: pool Q, K, V into cubes (one pass per tensor over its
+raster rows), coarse attention + Top-K, fine block-sparse attention (with
+the coarse output combined through the gates' default) that gathers each
+64-token cube of Q, K, V straight from the raster rows in its tile loads
+(the reorder into cubes) and writes the output back in raster order from its
+epilogue (the reorder back).  The same step with explicit cube-major copies
+(the reorder fused with the pool, the fine stage reading the copies) writes
+the same bits and is reported as `reorder_step`.  The default workload is the
 32,768-token Wan2.1-scale layer (16x32x64 grid, 4x4x4 cubes, 12 heads,
 d=128, bf16, Top-K 154 of 512 cubes = 70% sparsity).
 
@@ -158,6 +162,7 @@ def main() -> int:
     import torch
     import block_sparse_video_major_amd as vsa
     from block_sparse_video_major_amd import _lib as L
+    from block_sparse_video_major_amd.pipeline import gather_supported
     from block_sparse_video_major_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -175,13 +180,17 @@ def main() -> int:
     q, k, v, gate_c, gate_f = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev)
                                for n in ("q", "k", "v", "gate_c", "gate_f"))
     del x
-    f = vsa.VsaForward(p, w.top_k, dev)
+    f = vsa.VsaForward(p, w.top_k, dev)   # with cube-major copies: the reordering step and the extras
+    gather = gather_supported(p)
+    fg = vsa.VsaForward(p, w.top_k, dev, gather=True) if gather else f
     out = torch.empty_like(q)
     out_cube = torch.empty_like(q)   # cube-major output of the separate fine + unpermute breakdown
     stream = torch.cuda.Stream(device=dev)
     B = L.VSA_BF16
 
-    def step(ev0=None, ev1=None, p=p, f=f, gates=False):
+    def reorder_step(ev0=None, ev1=None, p=p, f=f, gates=False):
+        """Reorder + pool (one fused pass per tensor), coarse + Top-K, fine
+        stage on the cube-major copies with the reorder back in its epilogue."""
         L.vsa_permute_pool(p, B, q, f.qp, f.qc, stream)
         L.vsa_permute_pool(p, B, k, f.kp, f.kc, stream)
         L.vsa_permute_pool(p, B, v, f.vp, f.vc, stream)
@@ -194,20 +203,39 @@ def main() -> int:
         if ev1 is not None:
             ev1.record(stream)
 
+    def gather_step(ev0=None, ev1=None, p=p, f=fg, gates=False):
+        """Pool from the raster rows, coarse + Top-K, fine stage gathering its
+        cube tiles from the raster rows (the reorder in its loads, the reorder
+        back in its epilogue): the same output bits as reorder_step."""
+        L.vsa_permute_pool(p, B, q, None, f.qc, stream)
+        L.vsa_permute_pool(p, B, k, None, f.kc, stream)
+        L.vsa_permute_pool(p, B, v, None, f.vc, stream)
+        L.vsa_coarse_topk(p, w.top_k, f.qc, f.kc, f.vc, f.lut, f.valid, f.oc, stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        L.vsa_sparse_attn_fwd_gather(p, q, k, v, f.lut, f.valid, out, oc=f.oc,
+                                     gate_c=gate_c if gates else None, gate_f=gate_f if gates else None,
+                                     stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    step = gather_step if gather else reorder_step
+
     def new_events(n):
         return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
-    def timed_steps(n, gates=False, flush=None):
-        """n steps, each bracketed by its own events (and its fine kernel by
-        another pair); with `flush`, a device write of that buffer (larger
-        than the 256 MB Infinity Cache) runs before every step, outside the
-        events.  Returns per-step and per-fine-kernel ms."""
+    def timed_steps(n, gates=False, flush=None, fn=None):
+        """n steps (of `fn`, by default the timed step), each bracketed by its
+        own events (and its fine kernel by another pair); with `flush`, a
+        device write of that buffer (larger than the 256 MB Infinity Cache)
+        runs before every step, outside the events.  Returns per-step and
+        per-fine-kernel ms."""
         st, fe = new_events(n), new_events(n)
         for i in range(n):
             if flush is not None:
                 flush.fill_(i & 0x7F)
             st[i][0].record(stream)
-            step(*fe[i], gates=gates)
+            (fn or step)(*fe[i], gates=gates)
             st[i][1].record(stream)
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in st], [a.elapsed_time(b) for a, b in fe]
@@ -231,7 +259,7 @@ def main() -> int:
         ms_total = t_start.elapsed_time(t_end)
         fine_ms = [a.elapsed_time(b) for a, b in ev]
         step_ms = [a.elapsed_time(b) for a, b in sev]
-        g_step = g_fine = c_step = c_fine = None
+        g_step = g_fine = c_step = c_fine = r_step = r_fine = None
         if not args.skip_extras:
             # the same step with the gated combination of the fine and the
             # coarse outputs (seeded gates in raster order), warm cache
@@ -242,12 +270,17 @@ def main() -> int:
             timed_steps(2, flush=flush)
             c_step, c_fine = timed_steps(max(10, args.steps // 2), flush=flush)
             del flush
+            if gather:
+                # the step with explicit cube-major copies of q, k and v (the
+                # reorder fused with the pool), for comparison
+                timed_steps(3, fn=reorder_step)
+                r_step, r_fine = timed_steps(args.steps, fn=reorder_step)
 
         def extras():
             # per-stage breakdown (separate, untimed pass); the step runs the
             # fused permute_pool, the separate permute and pool are timed too
             names = ["permute_qkv", "pool_qkv", "permute_pool_qkv", "coarse_topk", "sparse_attn_fwd", "unpermute",
-                     "sparse_attn_fwd_raster"]
+                     "sparse_attn_fwd_raster"] + (["pool_from_raster_qkv", "sparse_attn_fwd_gather"] if gather else [])
             reps = max(3, min(10, args.steps))
             acc = {n: 0.0 for n in names}
             for _ in range(reps):
@@ -270,6 +303,12 @@ def main() -> int:
                 e[6].record(stream)
                 L.vsa_sparse_attn_fwd_raster(p, f.qp, f.kp, f.vp, f.lut, f.valid, out, oc=f.oc, stream=stream)
                 e[7].record(stream)
+                if gather:
+                    for t, dc in ((q, fg.qc), (k, fg.kc), (v, fg.vc)):
+                        L.vsa_permute_pool(p, B, t, None, dc, stream)
+                    e[8].record(stream)
+                    L.vsa_sparse_attn_fwd_gather(p, q, k, v, f.lut, f.valid, out, oc=f.oc, stream=stream)
+                    e[9].record(stream)
                 torch.cuda.synchronize()
                 for i, n in enumerate(names):
                     acc[n] += e[i].elapsed_time(e[i + 1]) / reps
@@ -648,6 +687,14 @@ def main() -> int:
                        "steps": len(c_step), "step_ms": _stats(c_step), "fine_ms": _stats(c_fine),
                        "tflops_per_step": round(flops / (float(np.median(c_step)) * 1e-3) / 1e12, 2)},
         })
+    if r_step is not None:
+        rec["reorder_step"] = {
+            "note": "the step with explicit cube-major copies: reorder + pool of q, k, v in one pass per tensor, "
+                    "coarse + Top-K, the fine stage on the copies (vsa_sparse_attn_fwd_raster); the same output "
+                    "bits as the timed step, which pools from the raster rows and gathers the cube tiles in the "
+                    "fine kernel's loads (vsa_sparse_attn_fwd_gather)",
+            "step_ms": _stats(r_step), "fine_ms": _stats(r_fine),
+            "tflops_per_step": round(flops / (float(np.median(r_step)) * 1e-3) / 1e12, 2)}
     rec.update({
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
@@ -671,6 +718,8 @@ def main() -> int:
                             "permute_pool_qkv": round(permute_pool_bytes / (acc["permute_pool_qkv"] * 1e-3) / 1e9,
                                                       1),
                             "unpermute": round(unpermute_bytes / (acc["unpermute"] * 1e-3) / 1e9, 1),
+                            **({"pool_from_raster_qkv": round(pool_bytes / (acc["pool_from_raster_qkv"] * 1e-3) / 1e9,
+                                                              1)} if gather else {}),
                             "copy_ceiling": round(permute_bytes / (acc["copy_qkv"] * 1e-3) / 1e9, 1),
                             "note": "copy_ceiling: torch's device copy of the bytes the three reorders move, "
                                     "timed in the same run; HBM peak 8000 GB/s"},

@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     vsa_permute, vsa_unpermute, vsa_pool, vsa_coarse_topk, vsa_sparse_attn_fwd,
     vsa_check_lut, vsa_perm_index, vsa_status_str, vsa_abi_version,
     vsa_sparse_attn_bwd, vsa_sparse_attn_bwd_workspace_size, vsa_sparse_attn_bwd_noalloc,
-    vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_mask_to_lut,
+    vsa_permute_pool, vsa_sparse_attn_fwd_raster, vsa_sparse_attn_fwd_gather, vsa_mask_to_lut,
     vsa_combine, vsa_combine_bwd, vsa_coarse_bwd, vsa_coarse_bwd_workspace_size, vsa_pool_unpermute_bwd,
     vsa_permute_bnhd, vsa_permute_pool_bnhd, vsa_sparse_attn_fwd_bnhd, vsa_pool_unpermute_bwd_bnhd,
     vsa_cube_table, VSA_CUBES_RASTER, VSA_CUBES_HILBERT, clear_cube_tables, vsa_device_peak,
@@ -23,7 +23,7 @@ __all__ = [
     "vsa_permute", "vsa_unpermute", "vsa_pool", "vsa_coarse_topk", "vsa_sparse_attn_fwd",
     "vsa_check_lut", "vsa_perm_index", "vsa_status_str", "vsa_abi_version",
     "vsa_sparse_attn_bwd", "vsa_sparse_attn_bwd_workspace_size", "vsa_sparse_attn_bwd_noalloc",
-    "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_mask_to_lut",
+    "vsa_permute_pool", "vsa_sparse_attn_fwd_raster", "vsa_sparse_attn_fwd_gather", "vsa_mask_to_lut",
     "vsa_combine", "vsa_combine_bwd", "vsa_coarse_bwd", "vsa_coarse_bwd_workspace_size", "vsa_pool_unpermute_bwd",
     "VsaBackward",
     "vsa_permute_bnhd", "vsa_permute_pool_bnhd", "vsa_sparse_attn_fwd_bnhd", "vsa_pool_unpermute_bwd_bnhd",

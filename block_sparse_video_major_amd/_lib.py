@@ -153,6 +153,7 @@ def load() -> ctypes.CDLL:
         "vsa_coarse_topk": [P, i32, vp, vp, vp, vp, vp, vp, vp],
         "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_sparse_attn_fwd_raster": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
+        "vsa_sparse_attn_fwd_gather": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
         "vsa_check_lut": [P, vp, vp, i32, vp, vp],
         "vsa_mask_to_lut": [P, vp, i32, vp, vp, vp, vp],
         "vsa_sparse_attn_bwd_workspace_size": [P, i32, ctypes.POINTER(ctypes.c_size_t)],
@@ -333,11 +334,13 @@ def vsa_pool(p: Problem, dtype: int, x_cube: torch.Tensor, xc: torch.Tensor, str
                            _stream(stream, x_cube.device)), "vsa_pool")
 
 
-def vsa_permute_pool(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: torch.Tensor, xc: torch.Tensor,
-                     stream=None) -> None:
+def vsa_permute_pool(p: Problem, dtype: int, x_raster: torch.Tensor, x_cube: Optional[torch.Tensor],
+                     xc: torch.Tensor, stream=None) -> None:
+    """Reorder into cubes and pool in one pass; with x_cube None only the pool (xc) is written."""
     td = _token_dtype(dtype)
     _need(x_raster, "x_raster", _tok_shape(p), td)
-    _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
+    if x_cube is not None:
+        _need(x_cube, "x_cube", _pos_shape(p), td, x_raster.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_raster.device)
     _check(load().vsa_permute_pool(ctypes.byref(p.c_struct(x_raster.device)), dtype, _ptr(x_raster), _ptr(x_cube), _ptr(xc),
                                    _stream(stream, x_raster.device)), "vsa_permute_pool")
@@ -377,6 +380,15 @@ def vsa_sparse_attn_fwd_raster(p: Problem, q: torch.Tensor, k: torch.Tensor, v: 
     _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, True)
 
 
+def vsa_sparse_attn_fwd_gather(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
+                               out: torch.Tensor, oc: Optional[torch.Tensor] = None,
+                               gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """As vsa_sparse_attn_fwd_raster with q, k and v in raster order too (the kernel gathers their cubes)."""
+    _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, "gather")
+
+
 def vsa_sparse_attn_fwd_bnhd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor,
                              out: torch.Tensor, oc: Optional[torch.Tensor] = None,
@@ -388,12 +400,17 @@ def vsa_sparse_attn_fwd_bnhd(p: Problem, q: torch.Tensor, k: torch.Tensor, v: to
 
 def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, lse, stream, raster):
     dev = q.device
-    ts = _pos_shape(p)
     dv = p.v_dim
-    os_ = {"bnhd": _bnhd_shape(p, dv), True: _tok_shape(p, dv), False: _pos_shape(p, dv)}[raster]
-    _need(q, "q", ts, torch.bfloat16, dev)
-    _need(k, "k", _kv_pos_shape(p), torch.bfloat16, dev)
-    _need(v, "v", _kv_pos_shape(p, dv), torch.bfloat16, dev)
+    os_ = {"bnhd": _bnhd_shape(p, dv), True: _tok_shape(p, dv), "gather": _tok_shape(p, dv),
+           False: _pos_shape(p, dv)}[raster]
+    if raster == "gather":   # raster token tensors: [batch, heads(_kv), N, d]
+        _need(q, "q", _tok_shape(p), torch.bfloat16, dev)
+        _need(k, "k", (p.batch, p.kv_heads, p.n_tokens, p.head_dim), torch.bfloat16, dev)
+        _need(v, "v", (p.batch, p.kv_heads, p.n_tokens, dv), torch.bfloat16, dev)
+    else:
+        _need(q, "q", _pos_shape(p), torch.bfloat16, dev)
+        _need(k, "k", _kv_pos_shape(p), torch.bfloat16, dev)
+        _need(v, "v", _kv_pos_shape(p, dv), torch.bfloat16, dev)
     _need(out, "out", os_, torch.bfloat16, dev)
     if kv_block_idx.dim() != 4:
         raise ValueError("kv_block_idx must be [batch, heads, Nc, max_kv_blocks]")
@@ -408,7 +425,7 @@ def _fine(p, q, k, v, kv_block_idx, valid_block_num, out, oc, gate_c, gate_f, ls
     if lse is not None:
         _need(lse, "lse", (p.batch, p.heads, p.n_positions if raster is False else p.n_tokens), torch.float32, dev)
     name = {"bnhd": "vsa_sparse_attn_fwd_bnhd", True: "vsa_sparse_attn_fwd_raster",
-            False: "vsa_sparse_attn_fwd"}[raster]
+            "gather": "vsa_sparse_attn_fwd_gather", False: "vsa_sparse_attn_fwd"}[raster]
     _check(getattr(load(), name)(ctypes.byref(p.c_struct(dev)), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(kv_block_idx), _ptr(valid_block_num), int(max_kv), _ptr(oc),
                                  _ptr(gate_c), _ptr(gate_f), _ptr(out), _ptr(lse),
@@ -599,12 +616,13 @@ def vsa_permute_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch
                                    _stream(stream, x_bnhd.device)), "vsa_permute_bnhd")
 
 
-def vsa_permute_pool_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: torch.Tensor, xc: torch.Tensor,
-                          stream=None) -> None:
-    """vsa_permute_pool reading the model layout [batch, N, heads, d]."""
+def vsa_permute_pool_bnhd(p: Problem, dtype: int, x_bnhd: torch.Tensor, x_cube: Optional[torch.Tensor],
+                          xc: torch.Tensor, stream=None) -> None:
+    """vsa_permute_pool reading the model layout [batch, N, heads, d] (x_cube None: pool only)."""
     td = _token_dtype(dtype)
     _need(x_bnhd, "x_bnhd", _bnhd_shape(p), td)
-    _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
+    if x_cube is not None:
+        _need(x_cube, "x_cube", _pos_shape(p), td, x_bnhd.device)
     _need(xc, "xc", _cube_shape(p), torch.float32, x_bnhd.device)
     _check(load().vsa_permute_pool_bnhd(ctypes.byref(p.c_struct(x_bnhd.device)), dtype, _ptr(x_bnhd), _ptr(x_cube), _ptr(xc),
                                         _stream(stream, x_bnhd.device)), "vsa_permute_pool_bnhd")

@@ -68,6 +68,40 @@ __device__ __forceinline__ void dma_tile(const void* base, const uint32_t (&voff
   }
 }
 
+// Direct global->LDS loads of one wave's N pieces of a tile whose pieces lie
+// at their own offsets from the tile base: piece n moves the 16 bytes at
+// base + pd[n] + voff + 1024 n of every lane to LDS byte address lds_base +
+// 1024 n + 16 * lane (pd[n]: wave-uniform byte offsets, voff: the lane's
+// offset within a piece).  The tile's rows are then gathered from a layout
+// in which they are not contiguous, one contiguous 1 KiB run per piece.
+template <int N>
+__device__ __forceinline__ void dma_pieces(const char* base, const int64_t (&pd)[N], uint32_t voff,
+                                           uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  static_assert(N == 2 || N == 4, "loads per tile");
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %3 offset:1024\n\t"
+        "global_load_lds_dwordx4 %0, %4 offset:2048\n\t"
+        "global_load_lds_dwordx4 %0, %5 offset:3072"
+        :
+        : "v"(voff), "s"(lds_base), "s"(base + pd[0]), "s"(base + pd[1]), "s"(base + pd[2]), "s"(base + pd[3])
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %3 offset:1024"
+        :
+        : "v"(voff), "s"(lds_base), "s"(base + pd[0]), "s"(base + pd[1])
+        : "memory", "m0");
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }

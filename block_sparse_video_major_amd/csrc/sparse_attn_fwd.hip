@@ -152,8 +152,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const int32_t* __restrict__ lut, const int32_t* __restrict__ valid, int max_kv,
     const float* __restrict__ oc, const __bf16* __restrict__ gate_c, const __bf16* __restrict__ gate_f,
     __bf16* __restrict__ out, float* __restrict__ lse, int Nc, int64_t total_pairs, float c_log2,
-    TokenMap tmap, int group) {
+    TokenMap tmap, int group, int gather_arg) {
   using C = Cfg<D>;
+  // q, k, v in raster order, cube tiles gathered by the loads (only the
+  // divisible d = 128 variants are ever launched that way)
+  const bool gather = !PAD && D == 128 && gather_arg != 0;
   // The load plan issues group p (K tiles of step p, V tiles of step p - 1)
   // by barrier p - 1, while the tiles of the two steps before it are still
   // held; a step has up to two tiles, so each ring needs four positions
@@ -190,25 +193,47 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   // ---- per-lane constant offsets ------------------------------------------
   // Direct loads (issued by half A only): lane i of load n of wave w fills
   // LDS chunk L = (w*LOADS+n)*64+i of a tile, which holds logical chunk
-  // (L % CPR) ^ f(row) of row L / CPR.  The load's instruction offset adds
-  // n * 1024 to both the source and the LDS destination, so the lane's
-  // source offset is taken relative to it.  The V swizzle depends on the row
-  // mod 4 only and a 1 KiB piece spans whole groups of 4 rows (4 rows at
-  // d = 128, 8 at d = 64), so one offset serves every load; the K swizzle
-  // depends on the row mod 16 and each load has its own.
+  // (L % CPR) ^ f(row) of row L / CPR.  Load n of wave w is one 1 KiB piece
+  // P = w*LOADS + n of the tile: its rows 1024/ROWB * P onward.  In
+  // cube-major order the piece starts P * 1024 bytes after the tile's first
+  // row; with gather set the tensors are in raster order and a piece, one
+  // run of cw = 1024/ROWB tokens along w, starts (lt*H + lh)*W rows after
+  // the cube's first token (lt, lh: the piece's frame and row in the cube).
+  // The load's instruction offset adds n * 1024 to both the source and the
+  // LDS destination, so source offsets are taken relative to it.
+  auto piece_off = [&](int P) -> int64_t {
+    if (!gather) return (int64_t)P * 1024;
+    const int lt = P / tmap.ch, lh = P - lt * tmap.ch;
+    return ((int64_t)lt * tmap.H * tmap.W + (int64_t)lh * tmap.W) * C::ROWB;
+  };
+  // K: the swizzle depends on the row mod 16, so each load has its own
+  // lane offset (and absorbs its piece's offset).  V: the swizzle depends on
+  // the row mod 4 only and a piece spans whole groups of 4 rows (4 rows at
+  // d = 128, 8 at d = 64), so one lane offset serves every piece and the
+  // piece offsets vpd[n] are wave-uniform.
   uint32_t kg_off[C::LOADS];
+  int64_t vpd[C::LOADS];
 #pragma unroll
   for (int n = 0; n < C::LOADS; ++n) {
-    const int L = ((wave & 3) * C::LOADS + n) * 64 + lane;
+    const int P = (wave & 3) * C::LOADS + n;
+    const int L = P * 64 + lane;
     const int r = L / C::CPR, x = L % C::CPR;
-    kg_off[n] = r * C::ROWB + ((x ^ C::kswz(r)) * 16) - n * 1024;
+    kg_off[n] = (uint32_t)(piece_off(P) + (r - P * (1024 / C::ROWB)) * C::ROWB + ((x ^ C::kswz(r)) * 16) - n * 1024);
+    vpd[n] = piece_off(P) - n * 1024;
   }
   uint32_t vg;
   {
-    const int L = (wave & 3) * C::LOADS * 64 + lane;
-    const int r = L / C::CPR, x = L % C::CPR;
+    const int r = lane / C::CPR, x = lane % C::CPR;   // row within the piece (a multiple of 4 rows in)
     vg = (uint32_t)(r * C::ROWB + ((x ^ C::vswz(r)) * 16));
   }
+  // first token row of cube c in the token tensors (tile rows follow it at
+  // the piece offsets above)
+  auto cube_row = [&](int c) -> uint32_t {
+    if (!gather) return (uint32_t)c * kBlk;
+    const CubeAt a = cube_at(tmap, c);
+    if (!a.ok) return 0u;   // a table entry outside the grid: stay inside the tensors (no output is written for it)
+    return (uint32_t)(((a.t * tmap.ct) * tmap.H + a.h * tmap.ch) * tmap.W + a.w * tmap.cw);
+  };
   const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)((wave & 3) * C::LOADS * 1024));
   // K A-operand reads: key row 32*kh + n32, logical chunk 2*ks + g.
   int k_off[D / 16];
@@ -262,7 +287,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const bool my_valid = grp == 0 || hasB;
     bf16x8 qf[D / 16];
     if (my_valid) {
-      const __bf16* qrow = q + head_off + (int64_t)(my_cube * kBlk + 32 * qh + n32) * D + 8 * g;
+      const int rq = 32 * qh + n32;   // token rq of the cube
+      int64_t qr = (int64_t)my_cube * kBlk + rq;
+      if (gather) {
+        const int lt = small_div(rq, tmap.mag_plane), rem = rq - lt * (tmap.ch * tmap.cw);
+        const int lh = small_div(rem, tmap.mag_cw), lw = rem - lh * tmap.cw;
+        qr = (int64_t)cube_row(my_cube) + ((int64_t)lt * tmap.H + lh) * tmap.W + lw;
+      }
+      const __bf16* qrow = q + head_off + qr * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
     }
@@ -425,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     // ---- per-step descriptors and the tile list --------------------------
     // Loads are issued group by group (group g = the K tiles of step g, then
     // the V tiles of step g - 1), so the tiles of group g occupy list entries
-    // kpos(g) + kpos(g - 1) onward.  tlist[i] = cube | ring slot << 16 |
-    // (1 if V) << 20.  Before the loop groups 0..F(0) are issued; after
+    // kpos(g) + kpos(g - 1) onward.  tlist[i] = ring slot | (1 if V) << 4 |
+    // the cube's first token row (cube_row) << 5.  Before the loop groups 0..F(0) are issued; after
     // barrier p, groups F(p - 1) + 1 .. F(p).  issued(p) = the list length
     // issued before barrier p; at barrier p the wave waits until only the
     // tiles after group p, issued(p) - kpos(p + 1) - kpos(p), remain in
@@ -476,15 +508,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
           const uint32_t e = sched[gg];
           const uint32_t a = e & 0xffffu, b = e >> 16;
           const int k0 = kpos(gg), nk = kpos(gg + 1) - k0;
-          if (nk >= 1) tlist[i++] = (a != 0xffffu ? a : b) | ((uint32_t)(k0 % RK) << 16);
-          if (nk == 2) tlist[i++] = b | ((uint32_t)((k0 + 1) % RK) << 16);
+          if (nk >= 1) tlist[i++] = (cube_row((int)(a != 0xffffu ? a : b)) << 5) | (uint32_t)(k0 % RK);
+          if (nk == 2) tlist[i++] = (cube_row((int)b) << 5) | (uint32_t)((k0 + 1) % RK);
         }
         if (gg > 0) {
           const uint32_t e = sched[gg - 1];
           const uint32_t a = e & 0xffffu, b = e >> 16;
           const int v0 = kpos(gg - 1), nv = kpos(gg) - v0;
-          if (nv >= 1) tlist[i++] = (a != 0xffffu ? a : b) | ((uint32_t)(v0 % RV) << 16) | (1u << 20);
-          if (nv == 2) tlist[i++] = b | ((uint32_t)((v0 + 1) % RV) << 16) | (1u << 20);
+          if (nv >= 1) tlist[i++] = (cube_row((int)(a != 0xffffu ? a : b)) << 5) | (uint32_t)(v0 % RV) | 16u;
+          if (nv == 2) tlist[i++] = (cube_row((int)b) << 5) | (uint32_t)((v0 + 1) % RV) | 16u;
         }
       }
       __syncthreads();
@@ -511,14 +543,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
       }
       for (int c = 0; c < count; ++c, ++i_tile) {
         const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)tw, i_tile - twin);
-        const uint32_t blk = e & 0xffffu, slot = (e >> 16) & 15u;
-        if (e & (1u << 20)) {
-          uint32_t vg_off[C::LOADS];
-#pragma unroll
-          for (int n = 0; n < C::LOADS; ++n) vg_off[n] = vg;
-          dma_tile(uniform_ptr(v_head + (int64_t)blk * C::TILE), vg_off, lds_ring + V_BASE + slot * C::TILE);
+        const uint32_t row = e >> 5, slot = e & 15u;
+        if (e & 16u) {
+          dma_pieces(uniform_ptr(v_head + (int64_t)row * C::ROWB), vpd, vg, lds_ring + V_BASE + slot * C::TILE);
         } else {
-          dma_tile(uniform_ptr(k_head + (int64_t)blk * C::TILE), kg_off, lds_ring + slot * C::TILE);
+          dma_tile(uniform_ptr(k_head + (int64_t)row * C::ROWB), kg_off, lds_ring + slot * C::TILE);
         }
       }
     };
@@ -841,7 +870,7 @@ template <int D, int RK, int RV, bool PAD, bool ZT>
 hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                        const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
                        const void* gate_f, void* out, float* lse, hipStream_t s, size_t sched_bytes, int slot,
-                       const TokenMap& tmap) {
+                       const TokenMap& tmap, bool gather) {
   using C = Cfg<D>;
   static DevState dev_state[64];
   int dev = 0;
@@ -881,7 +910,7 @@ hipError_t launch_ring(const Geom& g, const void* q, const void* k, const void* 
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, lut, valid, max_kv, oc, (const __bf16*)gate_c, (const __bf16*)gate_f,
-                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2, tmap, g.group);
+                     (__bf16*)out, lse, (int)g.Nc, total_pairs, c_log2, tmap, g.group, gather ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -903,7 +932,8 @@ constexpr size_t kBaseRingBytes = 128 * 1024;   // 4 + 4 tiles at d = 128, 8 + 8
 template <int D, bool PAD>
 hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, const int32_t* lut,
                     const int32_t* valid, int max_kv, const float* oc, const void* gate_c,
-                    const void* gate_f, void* out, float* lse, hipStream_t s, const TokenMap& tmap) {
+                    const void* gate_f, void* out, float* lse, hipStream_t s, const TokenMap& tmap,
+                    bool gather) {
   using C = Cfg<D>;
   constexpr int RK_DEEP = D == 128 ? 4 : 10, RV_DEEP = D == 128 ? 4 : 8;
   constexpr int R_BASE = D == 128 ? 4 : 8;
@@ -917,16 +947,16 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
   if constexpr (RK_DEEP != R_BASE) {
     if (DEEP + sched <= zfree && build_scratch <= DEEP)
       return launch_ring<D, RK_DEEP, RV_DEEP, PAD, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out,
-                                                        lse, s, sched, slot0, tmap);
+                                                        lse, s, sched, slot0, tmap, gather);
   }
   if (build_scratch > kBaseRingBytes) return hipErrorInvalidValue;
   // (the padded d = 128 variant keeps its branches: with the zero tile it
   // spills a register)
   if (!(PAD && D == 128) && kBaseRingBytes + sched <= zfree)
     return launch_ring<D, R_BASE, R_BASE, PAD, !(PAD && D == 128)>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
-                                                    sched, slot0 + 1, tmap);
+                                                    sched, slot0 + 1, tmap, gather);
   return launch_ring<D, R_BASE, R_BASE, PAD, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
-                                                   sched, slot0 + 2, tmap);
+                                                   sched, slot0 + 2, tmap, gather);
 }
 
 }  // namespace
@@ -934,17 +964,34 @@ hipError_t launch_d(const Geom& g, const void* q, const void* k, const void* v, 
 // Cube ids and ring positions are 16-bit fields of the step list and the
 // load plan, and the per-pair schedule must fit in LDS beside the base ring
 // (its build scratch, 16 bytes per entry, lives in the ring).
-bool sparse_attn_fwd_fits(const Geom& g, int max_kv) {
-  if (sparse_attn_fwd_quad_fits(g, max_kv)) return true;
+static bool pair_fits(const Geom& g, int max_kv) {
   if (g.Nc < 1 || g.Nc > 0xfffe || max_kv < 1 || max_kv > 0x7fff) return false;
   if (kBaseRingBytes + sched_bytes(g, max_kv) > (size_t)kLdsMax) return false;
   return 16 * (size_t)max_kv <= kBaseRingBytes;
 }
 
+bool sparse_attn_fwd_fits(const Geom& g, int max_kv) {
+  return sparse_attn_fwd_quad_fits(g, max_kv) || pair_fits(g, max_kv);
+}
+
+// The gathering pair kernel reads each 1 KiB piece of a cube tile as one run
+// of tokens along w: at d = 128 that is cw = 4 tokens.  Grids padded up to
+// whole cubes have positions with no raster row, so they are not gathered;
+// token rows are 27-bit fields of the tile list.
+bool sparse_attn_fwd_gather_fits(const Geom& g, int max_kv) {
+  return g.D == 128 && g.Dv == 128 && g.cw * 128 * 2 == 1024 && !g.padded && g.vol == kBlk &&
+         g.N < ((int64_t)1 << 27) && pair_fits(g, max_kv);
+}
+
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, int out_order, hipStream_t s) {
+                                  void* out, float* lse, int out_order, hipStream_t s, bool gather) {
+  if (gather) {   // q, k, v in raster order: the pair kernel gathers their cube tiles
+    if (!sparse_attn_fwd_gather_fits(g, max_kv) || out_order != 1) return hipErrorInvalidValue;
+    return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s,
+                                make_token_map(g, out_order), true);
+  }
   // Quads of query cubes when the rows list at least half of the cubes
   // (measured on the 32K-token layer: Top-256 3.62 ms against 3.7, all 512
   // cubes 6.17 against 6.5); below that, neighbouring quads' key sets cover
@@ -953,10 +1000,12 @@ hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, c
   if (2 * (int64_t)max_kv >= g.Nc && sparse_attn_fwd_quad_fits(g, max_kv))
     return launch_sparse_attn_fwd_quad(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, out_order, s);
   const TokenMap m = make_token_map(g, out_order);
-  if (g.D == 128 && g.padded) return launch_d<128, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
-  if (g.D == 128) return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
-  if (g.D == 64 && g.padded) return launch_d<64, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
-  if (g.D == 64) return launch_d<64, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m);
+  if (g.D == 128 && g.padded)
+    return launch_d<128, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m, false);
+  if (g.D == 128) return launch_d<128, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m, false);
+  if (g.D == 64 && g.padded)
+    return launch_d<64, true>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m, false);
+  if (g.D == 64) return launch_d<64, false>(g, q, k, v, lut, valid, max_kv, oc, gate_c, gate_f, out, lse, s, m, false);
   return hipErrorInvalidValue;
 }
 

@@ -103,7 +103,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 extern "C" {
 
-int vsa_abi_version(void) { return (3 << 16) | 2; }
+int vsa_abi_version(void) { return (3 << 16) | 3; }
 
 int vsa_device_peak(int32_t device, int32_t* cu_count, int32_t* clock_khz, double* bf16_tflops) {
   int cus = 0, khz = 0;
@@ -213,7 +213,7 @@ int vsa_permute_pool(const vsa_problem* p, int32_t dtype, const void* x_raster, 
   int st = check_problem(p);
   if (st == VSA_OK) st = check_dtype(dtype);
   if (st != VSA_OK) return st;
-  if (x_raster == nullptr || x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
+  if (x_raster == nullptr || xc == nullptr) return VSA_ERR_NULL;   // x_cube == NULL: pool only
   const Geom g = vsa::make_geom(*p);
   return hip_status(vsa::launch_permute_pool(g, dtype, x_raster, x_cube, xc, (hipStream_t)stream));
 }
@@ -273,6 +273,23 @@ int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q, const void* 
                                 out, lse, 1, stream);
 }
 
+int vsa_sparse_attn_fwd_gather(const vsa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                               int32_t max_kv_blocks, const float* oc, const void* gate_c, const void* gate_f,
+                               void* out, float* lse, void* stream) {
+  int st = check_problem(p);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr ||
+      out == nullptr)
+    return VSA_ERR_NULL;
+  if (gate_c != nullptr && oc == nullptr) return VSA_ERR_NULL;
+  const Geom g = vsa::make_geom(*p);
+  if (max_kv_blocks < 1 || max_kv_blocks > g.Nc) return VSA_ERR_TOPK;
+  if (!vsa::sparse_attn_fwd_gather_fits(g, max_kv_blocks)) return VSA_ERR_UNSUPPORTED;
+  return hip_status(vsa::launch_sparse_attn_fwd(g, q, k, v, kv_block_idx, valid_block_num, max_kv_blocks, oc,
+                                                gate_c, gate_f, out, lse, 1, (hipStream_t)stream, true));
+}
+
 int vsa_sparse_attn_fwd_bnhd(const vsa_problem* p, const void* q, const void* k, const void* v,
                              const int32_t* kv_block_idx, const int32_t* valid_block_num, int32_t max_kv_blocks,
                              const float* oc, const void* gate_c, const void* gate_f, void* out, float* lse,
@@ -295,7 +312,7 @@ int vsa_permute_pool_bnhd(const vsa_problem* p, int32_t dtype, const void* x_bnh
   int st = check_problem(p);
   if (st == VSA_OK) st = check_dtype(dtype);
   if (st != VSA_OK) return st;
-  if (x_bnhd == nullptr || x_cube == nullptr || xc == nullptr) return VSA_ERR_NULL;
+  if (x_bnhd == nullptr || xc == nullptr) return VSA_ERR_NULL;   // x_cube == NULL: pool only
   const Geom g = vsa::make_geom(*p);
   return hip_status(vsa::launch_permute_pool(g, dtype, x_bnhd, x_cube, xc, (hipStream_t)stream, vsa::kBNHD));
 }

@@ -82,10 +82,18 @@ hipError_t launch_sparse_attn_fwd_quad(const Geom& g, const void* q, const void*
                                        const int32_t* lut, const int32_t* valid, int max_kv, const float* oc,
                                        const void* gate_c, const void* gate_f, void* out, float* lse,
                                        int out_order, hipStream_t s);
+// out_order: 0 cube-major, 1 raster, 2 raster [batch, N, heads, d].  With
+// gather, q, k and v are in raster [batch, heads, N, d] order and the pair
+// kernel gathers their cube tiles itself (out_order 1 only; see
+// sparse_attn_fwd_gather_fits).
 hipError_t launch_sparse_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
                                   const int32_t* lut, const int32_t* valid, int max_kv,
                                   const float* oc, const void* gate_c, const void* gate_f,
-                                  void* out, float* lse, int out_order, hipStream_t s);   // 0 cube, 1 raster, 2 raster bnhd
+                                  void* out, float* lse, int out_order, hipStream_t s, bool gather = false);
+// Whether the gathering pair kernel handles this problem: d = d_v = 128,
+// cubes 4 tokens wide (one 1 KiB run per piece of a tile), a grid that
+// divides into cubes, and the pair kernel's limits.
+bool sparse_attn_fwd_gather_fits(const Geom& g, int max_kv);
 hipError_t launch_check_lut(const Geom& g, const int32_t* lut, const int32_t* valid, int max_kv,
                             int32_t* bad_rows, hipStream_t s);
 hipError_t launch_mask_to_lut(const Geom& g, const uint8_t* mask, int max_kv, int32_t* lut, int32_t* valid,

@@ -6,6 +6,9 @@ and mean-pool them (one fused pass per tensor), coarse cube attention with
 Top-K selection, fine block-sparse attention over the selected cubes combined
 with the coarse output through the gates, written straight back in the
 model's token order (the reorder back runs in the fine kernel's epilogue).
+Where the shapes allow, the reorder runs in the fine kernel's tile loads
+instead (it gathers every cube from the raster rows), and the first pass
+only pools.
 The backward ("VSA: Faster Video Diffusion with Trainable Sparse
 Attention", Abstract: trained end to end) takes those steps in reverse with
 the index list held fixed.  This module only allocates the intermediate
@@ -25,20 +28,33 @@ from . import _lib as L
 from ._lib import Problem
 
 
+def gather_supported(p: Problem) -> bool:
+    """Whether vsa_sparse_attn_fwd_gather takes this problem's shapes: head
+    sizes 128, cubes of 64 tokens 4 wide, a grid that divides into cubes (the
+    LUT row length is checked by the library at the call)."""
+    return (p.head_dim == 128 and p.v_dim == 128 and p.cw == 4 and p.cube_volume == 64 and not p.padded)
+
+
 class VsaForward:
     """Preallocated buffers for one problem size; call() runs one forward pass."""
 
     def __init__(self, p: Problem, top_k: int, device="cuda", with_gates: bool = False,
-                 with_lse: bool = False, layout: str = "bhnd"):
+                 with_lse: bool = False, layout: str = "bhnd", gather: bool = False):
         # with_gates is accepted for callers that pass gates; the raster-order
         # gates are read directly, so no buffer is needed for them.  lse (if
         # kept) is in raster token order.  layout "bnhd" takes q, k, v, the
-        # gates and out in the model's [batch, N, heads, d] order.
+        # gates and out in the model's [batch, N, heads, d] order.  With
+        # gather, no cube-major copies of q, k, v are made: the pool reads the
+        # raster rows and the fine stage gathers its cube tiles from them
+        # (vsa_sparse_attn_fwd_gather; see gather_supported).
         if not 1 <= top_k <= p.n_cubes:
             raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
         if layout not in ("bhnd", "bnhd"):
             raise ValueError(f"layout {layout!r} is not 'bhnd' or 'bnhd'")
-        self.p, self.top_k, self.layout = p, top_k, layout
+        if gather and (layout != "bhnd" or not gather_supported(p)):
+            raise ValueError("the gathering fine stage needs the [batch, heads, N, d] layout, head sizes 128, "
+                             "cubes 4 tokens wide and a grid that divides into cubes")
+        self.p, self.top_k, self.layout, self.gather = p, top_k, layout, gather
         ts = (p.batch, p.heads, p.n_positions, p.head_dim)   # cube-major (padded) rows
         cs = (p.batch, p.heads, p.n_cubes, p.head_dim)
         kts = (p.batch, p.kv_heads, p.n_positions, p.head_dim)
@@ -46,9 +62,9 @@ class VsaForward:
         vts = (p.batch, p.kv_heads, p.n_positions, p.v_dim)   # values may be narrower or wider
         vcs = (p.batch, p.kv_heads, p.n_cubes, p.v_dim)
         bf, f32 = torch.bfloat16, torch.float32
-        self.qp = torch.empty(ts, dtype=bf, device=device)
-        self.kp = torch.empty(kts, dtype=bf, device=device)
-        self.vp = torch.empty(vts, dtype=bf, device=device)
+        self.qp = None if gather else torch.empty(ts, dtype=bf, device=device)
+        self.kp = None if gather else torch.empty(kts, dtype=bf, device=device)
+        self.vp = None if gather else torch.empty(vts, dtype=bf, device=device)
         self.qc = torch.empty(cs, dtype=f32, device=device)
         self.oc = torch.empty((p.batch, p.heads, p.n_cubes, p.v_dim), dtype=f32, device=device)
         self.kc = torch.empty(kcs, dtype=f32, device=device)
@@ -64,20 +80,26 @@ class VsaForward:
         bnhd = self.layout == "bnhd"
         permute_pool = L.vsa_permute_pool_bnhd if bnhd else L.vsa_permute_pool
         # K and V may have fewer (grouped) heads, and V its own head size
-        permute_pool(p, B, q, self.qp, self.qc, stream)
+        permute_pool(p, B, q, self.qp, self.qc, stream)   # the cube-major copy is None when gathering
         permute_pool(p.kv_problem(), B, k, self.kp, self.kc, stream)
         permute_pool(p.v_problem(), B, v, self.vp, self.vc, stream)
         L.vsa_coarse_topk(p, self.top_k, self.qc, self.kc, self.vc, self.lut, self.valid, self.oc, stream)
         # fine attention reading the raster-order gates and writing the
         # raster-order output directly (the reorder back is in its epilogue)
+        if self.gather:   # q, k, v themselves: the fine kernel gathers their cubes
+            L.vsa_sparse_attn_fwd_gather(p, q, k, v, self.lut, self.valid, out,
+                                         oc=self.oc, gate_c=gate_c, gate_f=gate_f, lse=self.lse, stream=stream)
+            return out
         fine = L.vsa_sparse_attn_fwd_bnhd if bnhd else L.vsa_sparse_attn_fwd_raster
         fine(p, self.qp, self.kp, self.vp, self.lut, self.valid, out,
              oc=self.oc, gate_c=gate_c, gate_f=gate_f, lse=self.lse, stream=stream)
         return out
 
     def intermediates(self) -> Dict[str, torch.Tensor]:
-        d = dict(qp=self.qp, kp=self.kp, vp=self.vp, qc=self.qc, kc=self.kc, vc=self.vc,
-                 oc=self.oc, kv_block_idx=self.lut, valid_block_num=self.valid)
+        d = dict(qc=self.qc, kc=self.kc, vc=self.vc, oc=self.oc, kv_block_idx=self.lut,
+                 valid_block_num=self.valid)
+        if not self.gather:
+            d.update(qp=self.qp, kp=self.kp, vp=self.vp)
         if self.lse is not None:
             d["lse"] = self.lse
         return d
@@ -88,17 +110,21 @@ class VsaForward:
 # that stream, so they may share intermediates; calls on other streams or
 # threads get buffers of their own.
 _FORWARD_CACHE_SIZE = 4
+# LUT rows of up to this many cubes always fit the gathering pair kernel's
+# on-chip schedule (28 bytes per entry beside the tile ring and the zero tile)
+_GATHER_MAX_KV = 512
 _forward_cache = threading.local()
 
 
 def _cached_forward(p: Problem, top_k: int, device: torch.device, stream) -> "VsaForward":
+    # raster inputs the fine stage can gather from need no cube-major copies
     cache = getattr(_forward_cache, "entries", None)
     if cache is None:
         cache = _forward_cache.entries = collections.OrderedDict()
     key = (p, top_k, str(device), L._stream(stream, device))
     f = cache.get(key)
     if f is None:
-        f = VsaForward(p, top_k, device)
+        f = VsaForward(p, top_k, device, gather=gather_supported(p) and top_k <= _GATHER_MAX_KV)
         cache[key] = f
         while len(cache) > _FORWARD_CACHE_SIZE:
             cache.popitem(last=False)
@@ -116,9 +142,11 @@ def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Problem, t
                 gate_c: Optional[torch.Tensor] = None, gate_f: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
     """One VSA forward pass on raster bf16 inputs [B, heads, N, d].  The
-    intermediates (cube-major copies, pooled tensors, the index list) live in
-    buffers reused by later calls with the same problem on the same stream
-    and thread; the returned output is a new tensor."""
+    intermediates (pooled tensors, the index list, and cube-major copies of
+    q, k, v unless the fine stage gathers its cubes from the raster rows: see
+    gather_supported) live in buffers reused by later calls with the same
+    problem on the same stream and thread; the returned output is a new
+    tensor."""
     if not 1 <= top_k <= p.n_cubes:
         raise ValueError(f"top_k={top_k} outside [1, {p.n_cubes}]")
     f = _cached_forward(p, top_k, q.device, stream)

@@ -158,7 +158,10 @@ int vsa_pool(const vsa_problem* p, int32_t dtype, const void* x_cube,
  *   x_cube[b, h, p, :] = x_raster[b, h, pi(p), :]
  *   xc[b, h, c, :]     = (1/vol) * sum_{l < vol} x_cube[b, h, c*vol + l, :]
  * Same layouts and rules as vsa_permute and vsa_pool; x_cube and xc hold
- * exactly the bits the two separate calls produce. */
+ * exactly the bits the two separate calls produce.  x_cube may be NULL:
+ * then only xc is written, read straight from the raster rows (the same
+ * bits), for a fine stage that gathers its cube tiles from raster order
+ * (vsa_sparse_attn_fwd_gather). */
 int vsa_permute_pool(const vsa_problem* p, int32_t dtype, const void* x_raster,
                      void* x_cube, float* xc, void* stream);
 
@@ -215,6 +218,31 @@ int vsa_sparse_attn_fwd(const vsa_problem* p, const void* q, const void* k,
  * vsa_sparse_attn_fwd writes to its out[b, h, p, :] when given the
  * cube-major gates.  Same requirements and errors as vsa_sparse_attn_fwd. */
 int vsa_sparse_attn_fwd_raster(const vsa_problem* p, const void* q,
+                               const void* k, const void* v,
+                               const int32_t* kv_block_idx,
+                               const int32_t* valid_block_num,
+                               int32_t max_kv_blocks, const float* oc,
+                               const void* gate_c, const void* gate_f,
+                               void* out, float* lse, void* stream);
+
+/* vsa_permute of q, k and v followed by vsa_sparse_attn_fwd_raster, with
+ * the reorder done by the fine kernel's own tile loads ([VSA-ROCm]
+ * §Two-Stage Architecture: the pre-stage reordering groups each cube's
+ * tokens together; here the kernel fetches every 64-token key, value and
+ * query cube straight from the raster rows, one run of 4 tokens along w per
+ * 1 KiB load, instead of reading a reordered copy).
+ * q: [batch, heads, N, head_dim] bf16, k, v: [batch, heads_kv, N, head_dim]
+ * bf16, all in raster (t, h, w) token order; kv_block_idx, valid_block_num
+ * and oc as for vsa_sparse_attn_fwd (cube-major, per cube); gate_c, gate_f,
+ * out and lse in raster order as for vsa_sparse_attn_fwd_raster.  out and
+ * lse hold exactly the bits vsa_sparse_attn_fwd_raster writes when given
+ * vsa_permute of q, k and v.  Requires head_dim = head_dim_v = 128, cubes 4
+ * tokens wide (cw = 4; cube volume 64), a grid that divides into cubes and
+ * the schedule limit of vsa_sparse_attn_fwd; otherwise VSA_ERR_UNSUPPORTED.
+ * Every LUT row length runs the pair-of-cubes kernel (the quad kernel, which
+ * vsa_sparse_attn_fwd uses for rows listing at least half of the cubes,
+ * does not gather).  out must not alias an input. */
+int vsa_sparse_attn_fwd_gather(const vsa_problem* p, const void* q,
                                const void* k, const void* v,
                                const int32_t* kv_block_idx,
                                const int32_t* valid_block_num,

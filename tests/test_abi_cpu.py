@@ -170,8 +170,10 @@ def test_pool_errors():
 def test_permute_pool_errors():
     lib = _raw()
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, None, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
-    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, None, DUMMY, None) == L.VSA_ERR_NULL
+    # (x_cube == NULL is the pool on its own, a valid call: not made here)
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, DUMMY, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, DUMMY, None, None, None) == L.VSA_ERR_NULL
+    assert lib.vsa_permute_pool(ctypes.byref(_prob()), 0, None, None, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_permute_pool(None, 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_NULL
     assert lib.vsa_permute_pool(ctypes.byref(_prob(T=0)), 0, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_SHAPE
     assert lib.vsa_permute_pool(ctypes.byref(_prob()), 2, DUMMY, DUMMY, DUMMY, None) == L.VSA_ERR_UNSUPPORTED
@@ -318,6 +320,34 @@ def test_sparse_attn_errors():
     # LDS (Nc = 16384, 16000 cubes per row)
     big = _prob(T=64, H=64, W=256)
     assert call(prob=big, maxkv=16000) == L.VSA_ERR_UNSUPPORTED
+
+
+def test_sparse_attn_gather_errors():
+    """The gathering entry point validates like the others, and refuses the
+    shapes its loads do not cover (head size other than 128, cubes not 4
+    tokens wide, grids that do not divide into cubes, a value head size of
+    its own) before any launch."""
+    lib = _raw()
+
+    def call(prob=None, q=DUMMY, k=DUMMY, v=DUMMY, lut=DUMMY, valid=DUMMY, maxkv=8, oc=None,
+             gc=None, gf=None, out=DUMMY, lse=None):
+        prob = ctypes.byref(prob or _prob(head_dim=128))
+        return lib.vsa_sparse_attn_fwd_gather(prob, q, k, v, lut, valid, maxkv, oc, gc, gf, out, lse, None)
+
+    assert call(q=None) == L.VSA_ERR_NULL
+    assert call(k=None) == L.VSA_ERR_NULL
+    assert call(v=None) == L.VSA_ERR_NULL
+    assert call(out=None) == L.VSA_ERR_NULL
+    assert call(lut=None) == L.VSA_ERR_NULL
+    assert call(valid=None) == L.VSA_ERR_NULL
+    assert call(gc=DUMMY) == L.VSA_ERR_NULL
+    assert call(maxkv=0) == L.VSA_ERR_TOPK
+    assert call(maxkv=33) == L.VSA_ERR_TOPK
+    assert call(prob=_prob(head_dim=64)) == L.VSA_ERR_UNSUPPORTED
+    assert call(prob=_prob(head_dim=128, ch=8, cw=2)) == L.VSA_ERR_UNSUPPORTED       # 2 tokens wide
+    assert call(prob=_prob(head_dim=128, T=8, H=16, W=14)) == L.VSA_ERR_UNSUPPORTED   # padded
+    assert call(prob=_prob(head_dim=128, head_dim_v=64)) == L.VSA_ERR_UNSUPPORTED
+    assert call(prob=_prob(head_dim=128, H=-4)) == L.VSA_ERR_SHAPE
 
 
 def test_check_lut_errors():
