@@ -107,15 +107,28 @@ __device__ __forceinline__ void select_row(float* sr, int Nc, int NcP, int top_k
     const int j = s * 64 + lane;
     key[s] = j < Nc ? order_key(sr[j]) : 0u;
   }
-  // K-th largest key: build the threshold from the top bit down.
+  // K-th largest key: build the threshold from the top bit down.  Each pass
+  // counts the keys >= the candidate: every lane counts its own slots on the
+  // vector ALU, and the wave total comes from one ballot per bit of those
+  // counts (the scalar unit, shared by the CU's four SIMDs, does a few
+  // popcounts per pass instead of one per slot).  Once exactly top_k keys
+  // are >= the threshold, they are the selection whatever the lower bits,
+  // and no key equals a lower candidate it would still set: stop there.
   uint32_t thr = 0u;
   if (top_k < Nc) {
+    constexpr int NB = NS >= 64 ? 7 : NS >= 32 ? 6 : NS >= 16 ? 5 : 4;   // bits of a count 0..NS
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
+      uint32_t mine = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) mine += key[s] >= cand ? 1u : 0u;
       int cnt = 0;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) cnt += popc64(__ballot(key[s] >= cand));
-      if (cnt >= top_k) thr = cand;
+      for (int b = 0; b < NB; ++b) cnt += popc64(__ballot((mine >> b) & 1u)) << b;
+      if (cnt >= top_k) {
+        thr = cand;
+        if (cnt == top_k) break;
+      }
     }
   }
   int gt = 0;
@@ -143,8 +156,12 @@ __device__ __forceinline__ void select_row(float* sr, int Nc, int NcP, int top_k
     for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[j]);
     m = wave_max(m);
     float sum = 0.f;
+    // exp(scale * (s - m)) as the hardware exp2 of the scaled difference:
+    // about 4e-6 relative for the differences of these rows, far inside
+    // the coarse output's tolerance, and several times cheaper than expf
+    const float scale2 = scale * 1.4426950408889634f;
     for (int j = lane; j < NcP; j += 64) {
-      const float p = j < Nc ? expf(scale * (sr[j] - m)) : 0.f;
+      const float p = j < Nc ? __builtin_amdgcn_exp2f((sr[j] - m) * scale2) : 0.f;
       sr[j] = p;   // the pad columns hold 0
       sum += p;
     }
