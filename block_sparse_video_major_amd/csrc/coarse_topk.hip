@@ -328,7 +328,12 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
 //            chunk, four consecutive keys per 16-byte read; B: V[key][column].
 // Phase 2 (Top-K and softmax weights) is the same as in the kernel above,
 // two rows per wavefront.
-template <int ROWS, int COLS, int STRIDE, int kThreads>
+// LDS row of `row` in a stage: STRIDE floats per row, plus BLOCKPAD floats
+// per block of 16 rows (so that rows 16 apart start in different banks).
+template <int STRIDE, int BLOCKPAD>
+__device__ __forceinline__ int stage_row(int row) { return row * STRIDE + BLOCKPAD * (row >> 4); }
+
+template <int ROWS, int COLS, int STRIDE, int kThreads, int BLOCKPAD = 0>
 struct TileStage {   // ROWS x COLS floats of a row-major [rows][ld] matrix -> LDS rows of STRIDE floats
   static constexpr int C4 = COLS / 4;
   static constexpr int PER = ROWS * C4 / kThreads;
@@ -348,7 +353,7 @@ struct TileStage {   // ROWS x COLS floats of a row-major [rows][ld] matrix -> L
     for (int i = 0; i < PER; ++i) {
       const int e = tid + i * kThreads;
       const int row = e / C4, c4 = e - row * C4;
-      *reinterpret_cast<float4*>(dst + row * STRIDE + 4 * c4) = v[i];
+      *reinterpret_cast<float4*>(dst + stage_row<STRIDE, BLOCKPAD>(row) + 4 * c4) = v[i];
     }
   }
 };
@@ -358,9 +363,34 @@ constexpr int kMR = 16;            // query cubes per workgroup
 constexpr int kMThreads = 512;     // 8 wavefronts
 constexpr int kMKeys = 128;        // keys per phase-1 stage
 
+constexpr int kVBlockPad = 16;     // value-chunk rows: floats added per block of 16 rows
+
 template <int DQ, int DV>
 __host__ __device__ constexpr int mfma_stage_floats() {
-  return kMKeys * (DQ / 2 + 4) > kChunk * (DV + 4) ? kMKeys * (DQ / 2 + 4) : kChunk * (DV + 4);
+  return kMKeys * (DQ / 2 + 4) > kChunk * (DV + 4) + kVBlockPad * (kChunk / 16 - 1)
+             ? kMKeys * (DQ / 2 + 4)
+             : kChunk * (DV + 4) + kVBlockPad * (kChunk / 16 - 1);
+}
+
+constexpr size_t kCoarseLdsMax = 160 * 1024;
+
+// Row stride of the sixteen score rows: the padded row rounded up to 4 more
+// than a multiple of 64 floats, where that still fits in LDS.  Phase 3 reads
+// four consecutive probabilities of sixteen different rows in one 16-byte
+// access per lane; at a stride that is a multiple of 64 floats all sixteen
+// fall in the same four banks.  The largest cube counts keep the plain
+// padded stride (same results, slower reads).
+template <int DQ, int DV>
+__host__ __device__ inline int mfma_row_stride(int Nc) {
+  const int p = padded_cols(Nc);
+  const int q = p + ((68 - p % 64) % 64);
+  return sizeof(float) * ((size_t)mfma_stage_floats<DQ, DV>() + (size_t)kMR * q + kMR) <= kCoarseLdsMax ? q : p;
+}
+
+// LDS of the sixteen-row kernel: one stage, the score rows, 1/sum per row
+template <int DQ, int DV>
+static size_t coarse_mfma_lds_bytes(int Nc) {
+  return sizeof(float) * ((size_t)mfma_stage_floats<DQ, DV>() + (size_t)kMR * mfma_row_stride<DQ, DV>(Nc) + kMR);
 }
 
 template <int DQ, int DV, int NS>
@@ -374,9 +404,10 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
   constexpr int VSTR = DV + 4;      // ... of a value chunk
   extern __shared__ float smem[];
   const int NcP = padded_cols(Nc);
+  const int SP = mfma_row_stride<DQ, DV>(Nc);
   float* stage = smem;                                       // key stage / value chunk
-  float* srow = stage + mfma_stage_floats<DQ, DV>();        // [16][NcP]
-  float* inv_sum = srow + (int64_t)kMR * NcP;                // [16]
+  float* srow = stage + mfma_stage_floats<DQ, DV>();        // [16][SP]
+  float* inv_sum = srow + (int64_t)kMR * SP;                 // [16]
 
   const int64_t bh = blockIdx.x / tiles_per_head;
   const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * kMR;
@@ -431,13 +462,13 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
     const int j = c0 + 16 * wave + l16;
     if (j < Nc) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) srow[(4 * kq + r) * NcP + j] = acc[r];
+      for (int r = 0; r < 4; ++r) srow[(4 * kq + r) * SP + j] = acc[r];
     }
   }
   // value chunks alternate between two register sets (two chunks in flight;
   // the first two load during phase 2)
   const float* vh = vc + kvh * (int64_t)Nc * DV;
-  TileStage<kChunk, DV, VSTR, kMThreads> vs[2];
+  TileStage<kChunk, DV, VSTR, kMThreads, kVBlockPad> vs[2];
   if (oc != nullptr) {
     vs[0].load(vh, DV, 0, 0, Nc, tid);
     if (kChunk < Nc) vs[1].load(vh, DV, kChunk, 0, Nc, tid);
@@ -446,7 +477,7 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
 
   // ---- phase 2 ----
   for (int r = wave; r < rows; r += kWaves)
-    select_row<NS>(srow + (int64_t)r * NcP, Nc, NcP, top_k, lut + (bh * Nc + i0 + r) * top_k,
+    select_row<NS>(srow + (int64_t)r * SP, Nc, NcP, top_k, lut + (bh * Nc + i0 + r) * top_k,
                    valid + bh * Nc + i0 + r, oc != nullptr, scale, inv_sum + r, lane);
   if (oc == nullptr) return;
 
@@ -468,8 +499,10 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
       // product s covers keys c0 + 16*kq + s (s in [SPW*ksp, SPW*ksp + SPW));
       // P past the padded row is not read (zero A value), V past Nc is zero
       const int kb = 16 * kq + SPW * ksp;
-      const float* pr = srow + (int64_t)l16 * NcP + c0 + kb;
-      const float* vr = stage + kb * VSTR + 16 * ct + l16;
+      const float* pr = srow + (int64_t)l16 * SP + c0 + kb;
+      // key rows kb ... kb + SPW - 1 lie in one block of 16: the block pad
+      // puts the four lane groups' rows in different banks
+      const float* vr = stage + stage_row<VSTR, kVBlockPad>(kb) + 16 * ct + l16;
 #pragma unroll
       for (int m = 0; m < SPW / 4; ++m) {
         const bool in = c0 + kb + 4 * m < NcP;
@@ -506,8 +539,6 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
 static size_t coarse_lds_bytes(int R, int Nc, int D) {   // D: the wider of the two head sizes
   return sizeof(float) * ((size_t)kChunk * (D + 4) + (size_t)R * padded_cols(Nc) + R);
 }
-
-constexpr size_t kCoarseLdsMax = 160 * 1024;
 
 template <int DQ, int DV, int R, int NS, int T>
 static hipError_t launch_rns(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
@@ -546,17 +577,13 @@ static hipError_t launch_r(const Geom& g, int top_k, const float* qc, const floa
   return launch_rns<DQ, DV, R, 64, T>(g, top_k, qc, kc, vc, lut, valid, oc, s);
 }
 
-static size_t coarse_mfma_lds_bytes(int Nc, int stage_floats) {
-  return sizeof(float) * ((size_t)stage_floats + (size_t)kMR * padded_cols(Nc) + kMR);
-}
-
 template <int DQ, int DV, int NS>
 static hipError_t launch_mfma_ns(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                                  int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
   const int Nc = (int)g.Nc;
   const int tiles = (Nc + kMR - 1) / kMR;
   const int64_t blocks = g.BH * tiles;
-  const size_t lds = coarse_mfma_lds_bytes(Nc, mfma_stage_floats<DQ, DV>());
+  const size_t lds = coarse_mfma_lds_bytes<DQ, DV>(Nc);
   const float scale = 1.0f / sqrtf((float)DQ);
   auto k = coarse_topk_mfma_kernel<DQ, DV, NS>;
   if (lds > 65536) {
@@ -593,7 +620,7 @@ static hipError_t launch_mfma(const Geom& g, int top_k, const float* qc, const f
 template <int DQ, int DV>
 static hipError_t launch_d(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                            int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
-  if (coarse_mfma_lds_bytes((int)g.Nc, mfma_stage_floats<DQ, DV>()) <= kCoarseLdsMax)
+  if (coarse_mfma_lds_bytes<DQ, DV>((int)g.Nc) <= kCoarseLdsMax)
     return launch_mfma<DQ, DV>(g, top_k, qc, kc, vc, lut, valid, oc, s);
   if (coarse_lds_bytes(8, (int)g.Nc, DQ > DV ? DQ : DV) <= kCoarseLdsMax)
     return launch_r<DQ, DV, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);
