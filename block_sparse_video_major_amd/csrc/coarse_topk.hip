@@ -44,6 +44,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The score of a key (inverse of order_key; -0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -115,6 +120,9 @@ __device__ __forceinline__ void select_row(float* sr, int Nc, int NcP, int top_k
   // are >= the threshold, they are the selection whatever the lower bits,
   // and no key equals a lower candidate it would still set: stop there.
   uint32_t thr = 0u;
+  // exact: exactly top_k keys are >= thr, so they are the selection and no
+  // key equal to thr is left out (always so when every cube is selected)
+  bool exact = top_k >= Nc;
   if (top_k < Nc) {
     constexpr int NB = NS >= 64 ? 7 : NS >= 32 ? 6 : NS >= 16 ? 5 : 4;   // bits of a count 0..NS
     for (int bit = 31; bit >= 0; --bit) {
@@ -127,43 +135,71 @@ __device__ __forceinline__ void select_row(float* sr, int Nc, int NcP, int top_k
       for (int b = 0; b < NB; ++b) cnt += popc64(__ballot((mine >> b) & 1u)) << b;
       if (cnt >= top_k) {
         thr = cand;
-        if (cnt == top_k) break;
+        if (cnt == top_k) {
+          exact = true;
+          break;
+        }
       }
     }
   }
-  int gt = 0;
+  if (exact) {
+    // the keys >= thr, in ascending cube order
+    int sel_before = 0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) gt += popc64(__ballot(s * 64 + lane < Nc && key[s] > thr));
-  const int need = top_k - gt;   // >= 1 entries equal to thr are taken
-  int eq_before = 0, sel_before = 0;
+    for (int s = 0; s < NS; ++s) {
+      const int j = s * 64 + lane;
+      const bool take = j < Nc && key[s] >= thr;
+      const uint64_t tm = __ballot(take);
+      if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
+      sel_before += popc64(tm);
+    }
+  } else {
+    // ties at thr: all keys above it, then the lowest-index keys equal to it
+    int gt = 0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int j = s * 64 + lane;
-    const bool in = j < Nc;
-    const bool eq = in && key[s] == thr;
-    const uint64_t eqm = __ballot(eq);
-    const int eq_rank = eq_before + popc64(eqm & lt_mask);
-    const bool take = in && (key[s] > thr || (eq && eq_rank < need));
-    const uint64_t tm = __ballot(take);
-    if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
-    sel_before += popc64(tm);
-    eq_before += popc64(eqm);
+    for (int s = 0; s < NS; ++s) gt += popc64(__ballot(s * 64 + lane < Nc && key[s] > thr));
+    const int need = top_k - gt;   // >= 1 entries equal to thr are taken
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s * 64 + lane;
+      const bool in = j < Nc;
+      const bool eq = in && key[s] == thr;
+      const uint64_t eqm = __ballot(eq);
+      const int eq_rank = eq_before + popc64(eqm & lt_mask);
+      const bool take = in && (key[s] > thr || (eq && eq_rank < need));
+      const uint64_t tm = __ballot(take);
+      if (take) out_idx[sel_before + popc64(tm & lt_mask)] = j;
+      sel_before += popc64(tm);
+      eq_before += popc64(eqm);
+    }
   }
   if (lane == 0) *valid_row = top_k;
 
   if (want_p) {
-    float m = -INFINITY;
-    for (int j = lane; j < Nc; j += 64) m = fmaxf(m, sr[j]);
-    m = wave_max(m);
+    // the scores come back from the keys held in registers (order_key is
+    // one-to-one except that -0 reads back as +0, which gives the same
+    // weights): the row max is the largest key, and the row is read from
+    // LDS only once, above
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kmax = max(kmax, key[s]);   // slots past Nc hold 0
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    const float m = key_score(kmax);
     float sum = 0.f;
     // exp(scale * (s - m)) as the hardware exp2 of the scaled difference:
     // about 4e-6 relative for the differences of these rows, far inside
     // the coarse output's tolerance, and several times cheaper than expf
     const float scale2 = scale * 1.4426950408889634f;
-    for (int j = lane; j < NcP; j += 64) {
-      const float p = j < Nc ? __builtin_amdgcn_exp2f((sr[j] - m) * scale2) : 0.f;
-      sr[j] = p;   // the pad columns hold 0
-      sum += p;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s * 64 + lane;
+      if (j < NcP) {
+        const float p = j < Nc ? __builtin_amdgcn_exp2f((key_score(key[s]) - m) * scale2) : 0.f;
+        sr[j] = p;   // the pad columns hold 0
+        sum += p;
+      }
     }
     sum = wave_sum(sum);
     if (lane == 0) *inv_sum_r = 1.f / sum;
