@@ -348,67 +348,35 @@ __global__ __launch_bounds__(kThreads) void coarse_topk_kernel(
 // ---- sixteen query cubes per workgroup, products on the matrix cores ----
 // Used whenever sixteen score rows fit in LDS.  Both products run as
 // v_mfma_f32_16x16x4_f32 (float32 operands and accumulation, so the scores
-// keep the precision the ranking needs):
+// keep the precision the ranking needs).  Each wavefront loads its own B
+// operands from global memory into registers, one block ahead, so neither
+// product stages data through LDS or waits at a barrier:
 //   phase 1  S[i][j] = sum_d Q[i][d] K[j][d] for the 16 query cubes i of the
-//            workgroup.  Keys are staged 128 at a time, half of d per stage;
-//            wave w owns keys 16w .. 16w + 15 of the stage.  Q is held in
-//            registers (A operand: lane l holds row l % 16 and, for product
-//            s of stage h, d = h*d/2 + (d/8)*(l/16) + s; the k index of a
-//            product may map to any d as long as A and B agree); B is key
-//            16w + l % 16 at the same d, so each lane reads four
-//            consecutive d with one 16-byte LDS read for four products.
-//   phase 3  O_c[i][:] = sum_j P[i][j] V[j][:]; wave w owns 16 columns of O_c
-//            (d_v = 128; at d_v = 64 two waves share a column tile and split
-//            the keys, their partial sums added once at the end).  A operand:
-//            P[l % 16][key(l / 16, s)] with key = 16*(l/16) + s in a 64-key
-//            chunk, four consecutive keys per 16-byte read; B: V[key][column].
+//            workgroup; wave w owns keys 16w .. 16w + 15 of every block of
+//            128.  Product (s, e) maps the k index l/16 of lane l to
+//            d = 16s + 4(l/16) + e: A = Q[l % 16][d] from registers, B =
+//            K[key l % 16][d]; one 16-byte load feeds four products, and the
+//            four lane groups of a key read 64 contiguous bytes.
+//   phase 3  O_c[i][:] = sum_j P[i][j] V[j][:]; wave w owns one 64-column
+//            group g of O_c (d_v / 64 groups) and every (8 / groups)-th
+//            64-key chunk.  Slice t of chunk c maps lane group l/16 to key
+//            64c + 16(l/16) + t: A = P[l % 16][key], four slices per 16-byte
+//            LDS read; one 16-byte load of V[key][64g + 4(l % 16) ...] holds
+//            the B operands of four products, one per column tile u, whose
+//            column l % 16 stands for column 64g + 4(l % 16) + u.  The key
+//            splits' partial sums are added in split order at the end.
 // Phase 2 (Top-K and softmax weights) is the same as in the kernel above,
 // two rows per wavefront.
-// LDS row of `row` in a stage: STRIDE floats per row, plus BLOCKPAD floats
-// per block of 16 rows (so that rows 16 apart start in different banks).
-template <int STRIDE, int BLOCKPAD>
-__device__ __forceinline__ int stage_row(int row) { return row * STRIDE + BLOCKPAD * (row >> 4); }
-
-template <int ROWS, int COLS, int STRIDE, int kThreads, int BLOCKPAD = 0>
-struct TileStage {   // ROWS x COLS floats of a row-major [rows][ld] matrix -> LDS rows of STRIDE floats
-  static constexpr int C4 = COLS / 4;
-  static constexpr int PER = ROWS * C4 / kThreads;
-  static_assert(PER * kThreads == ROWS * C4, "stage shape");
-  float4 v[PER];
-  __device__ __forceinline__ void load(const float* src, int ld, int r0, int col0, int nrows, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + i * kThreads;
-      const int row = e / C4, c4 = e - row * C4;
-      v[i] = r0 + row < nrows ? *reinterpret_cast<const float4*>(src + (int64_t)(r0 + row) * ld + col0 + 4 * c4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  __device__ __forceinline__ void store(float* dst, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + i * kThreads;
-      const int row = e / C4, c4 = e - row * C4;
-      *reinterpret_cast<float4*>(dst + stage_row<STRIDE, BLOCKPAD>(row) + 4 * c4) = v[i];
-    }
-  }
-};
-
 typedef float floatx4 __attribute__((ext_vector_type(4)));   // MFMA 16x16 accumulator
-constexpr int kMR = 16;            // query cubes per workgroup
-constexpr int kMThreads = 512;     // 8 wavefronts
-constexpr int kMKeys = 128;        // keys per phase-1 stage
-
-constexpr int kVBlockPad = 16;     // value-chunk rows: floats added per block of 16 rows
-
-template <int DQ, int DV>
-__host__ __device__ constexpr int mfma_stage_floats() {
-  return kMKeys * (DQ / 2 + 4) > kChunk * (DV + 4) + kVBlockPad * (kChunk / 16 - 1)
-             ? kMKeys * (DQ / 2 + 4)
-             : kChunk * (DV + 4) + kVBlockPad * (kChunk / 16 - 1);
-}
-
+constexpr int kMR = 16;                 // query cubes per workgroup
+constexpr int kMThreads = 512;          // 8 wavefronts
+constexpr int kMKeys = 128;             // keys per phase-1 block (16 per wave)
+constexpr int kMPart = 8 * kMR * 64;    // floats of the phase-3 partial sums (8 waves x 16 rows x 64 columns)
 constexpr size_t kCoarseLdsMax = 160 * 1024;
+
+// LDS floats of the sixteen-row kernel at score-row stride sp: the score
+// rows (which hold the phase-3 partial sums afterwards), then 1/sum per row.
+__host__ __device__ inline int mfma_lds_floats(int sp) { return (kMR * sp > kMPart ? kMR * sp : kMPart) + kMR; }
 
 // Row stride of the sixteen score rows: the padded row rounded up to 4 more
 // than a multiple of 64 floats, where that still fits in LDS.  Phase 3 reads
@@ -416,18 +384,13 @@ constexpr size_t kCoarseLdsMax = 160 * 1024;
 // access per lane; at a stride that is a multiple of 64 floats all sixteen
 // fall in the same four banks.  The largest cube counts keep the plain
 // padded stride (same results, slower reads).
-template <int DQ, int DV>
 __host__ __device__ inline int mfma_row_stride(int Nc) {
   const int p = padded_cols(Nc);
   const int q = p + ((68 - p % 64) % 64);
-  return sizeof(float) * ((size_t)mfma_stage_floats<DQ, DV>() + (size_t)kMR * q + kMR) <= kCoarseLdsMax ? q : p;
+  return sizeof(float) * (size_t)mfma_lds_floats(q) <= kCoarseLdsMax ? q : p;
 }
 
-// LDS of the sixteen-row kernel: one stage, the score rows, 1/sum per row
-template <int DQ, int DV>
-static size_t coarse_mfma_lds_bytes(int Nc) {
-  return sizeof(float) * ((size_t)mfma_stage_floats<DQ, DV>() + (size_t)kMR * mfma_row_stride<DQ, DV>(Nc) + kMR);
-}
+static size_t coarse_mfma_lds_bytes(int Nc) { return sizeof(float) * (size_t)mfma_lds_floats(mfma_row_stride(Nc)); }
 
 template <int DQ, int DV, int NS>
 __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
@@ -435,64 +398,48 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
     int32_t* __restrict__ lut, int32_t* __restrict__ valid, float* __restrict__ oc, int Nc, int top_k,
     int tiles_per_head, float scale, int group) {
   constexpr int kWaves = kMThreads / 64;
-  constexpr int DH = DQ / 2;        // d per phase-1 stage
-  constexpr int KSTR = DH + 4;      // LDS row stride of a key stage
-  constexpr int VSTR = DV + 4;      // ... of a value chunk
+  constexpr int QS = DQ / 16;        // phase-1 steps of four products
+  constexpr int NG = DV / 64;        // phase-3 column groups
+  constexpr int KS = kWaves / NG;    // phase-3 key splits
   extern __shared__ float smem[];
   const int NcP = padded_cols(Nc);
-  const int SP = mfma_row_stride<DQ, DV>(Nc);
-  float* stage = smem;                                       // key stage / value chunk
-  float* srow = stage + mfma_stage_floats<DQ, DV>();        // [16][SP]
-  float* inv_sum = srow + (int64_t)kMR * SP;                 // [16]
+  const int SP = mfma_row_stride(Nc);
+  float* srow = smem;                                                // [16][SP]
+  float* inv_sum = smem + (kMR * SP > kMPart ? kMR * SP : kMPart);   // [16]
 
   const int64_t bh = blockIdx.x / tiles_per_head;
   const int i0 = (int)(blockIdx.x - bh * tiles_per_head) * kMR;
   const int rows = min(kMR, Nc - i0);
   const int64_t kvh = bh / group;
-  const float* kh = kc + kvh * (int64_t)Nc * DQ;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kq = lane >> 4;
 
   // ---- phase 1: scores ----
-  // Stage h holds d in [h*DH, h*DH + DH).  Its product s (0 <= s < DH/4)
-  // takes, in lane group kq, d = h*DH + (DH/4)*kq + s: A = Q[i0 + l16][d]
-  // (from registers; rows past the last cube repeat it), B = K[key][d].
-  constexpr int SPS = DH / 4;       // products per stage
-  float qv[2][SPS];
+  float4 qv[QS];   // Q[i0 + l16][16s + 4kq ...]; rows past the last cube repeat it
   {
-    const float* qr = qc + (bh * Nc + min(i0 + l16, Nc - 1)) * (int64_t)DQ + SPS * kq;
+    const float* qr = qc + (bh * Nc + min(i0 + l16, Nc - 1)) * (int64_t)DQ + 4 * kq;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int m = 0; m < SPS / 4; ++m) {
-        const float4 t = *reinterpret_cast<const float4*>(qr + h * DH + 4 * m);
-        qv[h][4 * m + 0] = t.x; qv[h][4 * m + 1] = t.y; qv[h][4 * m + 2] = t.z; qv[h][4 * m + 3] = t.w;
-      }
+    for (int s = 0; s < QS; ++s) qv[s] = *reinterpret_cast<const float4*>(qr + 16 * s);
   }
-  // the two halves of the next key chunk are in flight in registers while
-  // the current chunk's halves are multiplied (two stages of cover)
-  TileStage<kMKeys, DH, KSTR, kMThreads> ks[2];
-  ks[0].load(kh, DQ, 0, 0, Nc, tid);
-  ks[1].load(kh, DQ, 0, DH, Nc, tid);
-  for (int c0 = 0; c0 < Nc; c0 += kMKeys) {
+  // this lane's key row in the block at c0 (keys past the last cube repeat
+  // it; their scores are not stored)
+  const float* kh = kc + kvh * (int64_t)Nc * DQ + 4 * kq;
+  auto kload = [&](float4 (&dst)[QS], int c0) {
+    const float* kr = kh + (int64_t)min(c0 + 16 * wave + l16, Nc - 1) * DQ;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) dst[s] = *reinterpret_cast<const float4*>(kr + 16 * s);
+  };
+  auto score_block = [&](const float4 (&cur)[QS], float4 (&nxt)[QS], int c0) {
+    if (c0 + kMKeys < Nc) kload(nxt, c0 + kMKeys);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      __syncthreads();   // the previous stage fully read
-      ks[h].store(stage, tid);
-      __syncthreads();
-      if (c0 + kMKeys < Nc) ks[h].load(kh, DQ, c0 + kMKeys, h * DH, Nc, tid);
-      const float* kr = stage + (16 * wave + l16) * KSTR + SPS * kq;
-#pragma unroll
-      for (int m = 0; m < SPS / 4; ++m) {
-        const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * m);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 0], kk.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 1], kk.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 2], kk.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[h][4 * m + 3], kk.w, acc, 0, 0, 0);
-      }
+    for (int s = 0; s < QS; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s].x, cur[s].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s].y, cur[s].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s].z, cur[s].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s].w, cur[s].w, acc, 0, 0, 0);
     }
     // D[i][j]: rows 4*kq + r, key c0 + 16*wave + l16
     const int j = c0 + 16 * wave + l16;
@@ -500,15 +447,28 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) srow[(4 * kq + r) * SP + j] = acc[r];
     }
+  };
+  {
+    float4 k0[QS], k1[QS];
+    kload(k0, 0);
+    for (int c0 = 0; c0 < Nc; c0 += 2 * kMKeys) {
+      score_block(k0, k1, c0);
+      if (c0 + kMKeys < Nc) score_block(k1, k0, c0 + kMKeys);
+    }
   }
-  // value chunks alternate between two register sets (two chunks in flight;
-  // the first two load during phase 2)
-  const float* vh = vc + kvh * (int64_t)Nc * DV;
-  TileStage<kChunk, DV, VSTR, kMThreads, kVBlockPad> vs[2];
-  if (oc != nullptr) {
-    vs[0].load(vh, DV, 0, 0, Nc, tid);
-    if (kChunk < Nc) vs[1].load(vh, DV, kChunk, 0, Nc, tid);
-  }
+
+  // phase 3's value rows: slices t0 .. t0 + 7 of chunk c (key 64c + 16kq + t;
+  // keys past the last cube repeat it, with P = 0 there)
+  const int nchunks = (Nc + 63) / 64;
+  const int g = wave % NG, ks = wave / NG;
+  const float* vh = vc + kvh * (int64_t)Nc * DV + 64 * g + 4 * l16;
+  auto vload = [&](float4 (&dst)[8], int c, int t0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      dst[t] = *reinterpret_cast<const float4*>(vh + (int64_t)min(64 * c + 16 * kq + t0 + t, Nc - 1) * DV);
+  };
+  float4 v0[8], v1[8];
+  if (oc != nullptr && ks < nchunks) vload(v0, ks, 0);   // in flight during phase 2
   __syncthreads();
 
   // ---- phase 2 ----
@@ -516,57 +476,55 @@ __global__ __launch_bounds__(kMThreads) void coarse_topk_mfma_kernel(
     select_row<NS>(srow + (int64_t)r * SP, Nc, NcP, top_k, lut + (bh * Nc + i0 + r) * top_k,
                    valid + bh * Nc + i0 + r, oc != nullptr, scale, inv_sum + r, lane);
   if (oc == nullptr) return;
+  __syncthreads();   // every P row and 1/sum written
 
   // ---- phase 3: O_c ----
-  constexpr int NT = DV / 16;                 // column tiles
-  constexpr int KSPLIT = kWaves / NT;         // waves per column tile (key split)
-  constexpr int SPW = 16 / KSPLIT;            // products per chunk per wave
-  const int ct = wave % NT, ksp = wave / NT;
-  floatx4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int c2 = 0; c2 < Nc; c2 += 2 * kChunk) {
+  floatx4 o[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int c0 = c2 + b * kChunk;
-      if (c0 >= Nc) break;
-      __syncthreads();   // phase 2 done / the previous chunk fully read
-      vs[b].store(stage, tid);
-      __syncthreads();
-      if (c0 + 2 * kChunk < Nc) vs[b].load(vh, DV, c0 + 2 * kChunk, 0, Nc, tid);
-      // product s covers keys c0 + 16*kq + s (s in [SPW*ksp, SPW*ksp + SPW));
-      // P past the padded row is not read (zero A value), V past Nc is zero
-      const int kb = 16 * kq + SPW * ksp;
-      const float* pr = srow + (int64_t)l16 * SP + c0 + kb;
-      // key rows kb ... kb + SPW - 1 lie in one block of 16: the block pad
-      // puts the four lane groups' rows in different banks
-      const float* vr = stage + stage_row<VSTR, kVBlockPad>(kb) + 16 * ct + l16;
+  for (int u = 0; u < 4; ++u) o[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto oc_half = [&](const float4 (&cur)[8], float4 (&nxt)[8], int c, int t0) {
+    const int nc = t0 == 0 ? c : c + KS, nt = t0 == 0 ? 8 : 0;
+    if (nc < nchunks) vload(nxt, nc, nt);
+    // P past the padded row is not read (zero A value); pad columns hold 0
+    const int kb = 64 * c + 16 * kq + t0;
+    const float* pr = srow + (int64_t)l16 * SP + kb;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 p0 = kb < NcP ? *reinterpret_cast<const float4*>(pr) : z;
+    const float4 p1 = kb + 4 < NcP ? *reinterpret_cast<const float4*>(pr + 4) : z;
+    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-      for (int m = 0; m < SPW / 4; ++m) {
-        const bool in = c0 + kb + 4 * m < NcP;
-        const float4 pp = in ? *reinterpret_cast<const float4*>(pr + 4 * m) : make_float4(0.f, 0.f, 0.f, 0.f);
-        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.x, vr[(4 * m + 0) * VSTR], o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.y, vr[(4 * m + 1) * VSTR], o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.z, vr[(4 * m + 2) * VSTR], o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x4f32(pp.w, vr[(4 * m + 3) * VSTR], o, 0, 0, 0);
+    for (int t = 0; t < 8; ++t) {
+      o[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[t], cur[t].x, o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[t], cur[t].y, o[1], 0, 0, 0);
+      o[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[t], cur[t].z, o[2], 0, 0, 0);
+      o[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[t], cur[t].w, o[3], 0, 0, 0);
+    }
+  };
+  for (int c = ks; c < nchunks; c += KS) {
+    oc_half(v0, v1, c, 0);
+    oc_half(v1, v0, c, 8);
+  }
+  // partial sums [split][row][column] over the score rows, added in split order
+  __syncthreads();   // every wave done reading P
+  float* part = smem;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<float4*>(part + (ks * kMR + 4 * kq + r) * DV + 64 * g + 4 * l16) =
+        make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
+  __syncthreads();
+  for (int e = tid; e < kMR * DV / 4; e += kMThreads) {
+    const int i = e / (DV / 4), c4 = e - i * (DV / 4);
+    if (i < rows) {
+      float4 t = *reinterpret_cast<const float4*>(part + i * DV + 4 * c4);
+#pragma unroll
+      for (int k2 = 1; k2 < KS; ++k2) {
+        const float4 u = *reinterpret_cast<const float4*>(part + (k2 * kMR + i) * DV + 4 * c4);
+        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
       }
+      const float is = inv_sum[i];
+      reinterpret_cast<float4*>(oc + (bh * Nc + i0 + i) * (int64_t)DV)[c4] =
+          make_float4(t.x * is, t.y * is, t.z * is, t.w * is);
     }
-  }
-  if (KSPLIT > 1) {
-    // partial sums of the key splits, added in split order
-    __syncthreads();
-    floatx4* part = reinterpret_cast<floatx4*>(stage);   // [KSPLIT][NT][64]
-    part[(ksp * NT + ct) * 64 + lane] = o;
-    __syncthreads();
-    if (ksp != 0) return;
-    for (int k2 = 1; k2 < KSPLIT; ++k2) {
-      const floatx4 t = part[(k2 * NT + ct) * 64 + lane];
-      o[0] += t[0]; o[1] += t[1]; o[2] += t[2]; o[3] += t[3];
-    }
-  }
-  // D[i][n]: rows 4*kq + r, column 16*ct + l16
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * kq + r;
-    if (i < rows) oc[(bh * Nc + i0 + i) * (int64_t)DV + 16 * ct + l16] = o[r] * inv_sum[i];
   }
 }
 
@@ -619,7 +577,7 @@ static hipError_t launch_mfma_ns(const Geom& g, int top_k, const float* qc, cons
   const int Nc = (int)g.Nc;
   const int tiles = (Nc + kMR - 1) / kMR;
   const int64_t blocks = g.BH * tiles;
-  const size_t lds = coarse_mfma_lds_bytes<DQ, DV>(Nc);
+  const size_t lds = coarse_mfma_lds_bytes(Nc);
   const float scale = 1.0f / sqrtf((float)DQ);
   auto k = coarse_topk_mfma_kernel<DQ, DV, NS>;
   if (lds > 65536) {
@@ -656,7 +614,7 @@ static hipError_t launch_mfma(const Geom& g, int top_k, const float* qc, const f
 template <int DQ, int DV>
 static hipError_t launch_d(const Geom& g, int top_k, const float* qc, const float* kc, const float* vc,
                            int32_t* lut, int32_t* valid, float* oc, hipStream_t s) {
-  if (coarse_mfma_lds_bytes<DQ, DV>((int)g.Nc) <= kCoarseLdsMax)
+  if (coarse_mfma_lds_bytes((int)g.Nc) <= kCoarseLdsMax)
     return launch_mfma<DQ, DV>(g, top_k, qc, kc, vc, lut, valid, oc, s);
   if (coarse_lds_bytes(8, (int)g.Nc, DQ > DV ? DQ : DV) <= kCoarseLdsMax)
     return launch_r<DQ, DV, 8, 512>(g, top_k, qc, kc, vc, lut, valid, oc, s);

@@ -232,10 +232,11 @@ def test_coarse_topk_ties_take_lower_index():
 # the two sides of the limit of the sixteen-row kernel.
 COARSE_GEOM = [(128, (64, 64, 64), 192), (64, (64, 64, 64), 100),
                (64, (20, 36, 44), 37), (128, (4, 4, 6124), 64),
-               # the largest count whose sixteen score rows fit in LDS beside
-               # the staging buffer at d = 128 (the matrix-core kernel), and
-               # the next one up (the vector kernel)
-               (128, (4, 4, 8048), 201), (128, (4, 4, 8064), 201)]
+               # 2,012 cubes (32 key slots per lane), the largest count whose
+               # sixteen score rows fit in LDS (the matrix-core kernel, 40
+               # slots, the plain padded row stride) and the next one up (the
+               # vector kernel)
+               (128, (4, 4, 8048), 201), (128, (4, 4, 10224), 201), (128, (4, 4, 10240), 201)]
 
 
 @pytest.mark.parametrize("d,dims,k", COARSE_GEOM, ids=[f"d{c[0]}-nc{c[1][0] * c[1][1] * c[1][2] // 64}"
