@@ -236,7 +236,10 @@ COARSE_GEOM = [(128, (64, 64, 64), 192), (64, (64, 64, 64), 100),
                # sixteen score rows fit in LDS (the matrix-core kernel, 40
                # slots, the plain padded row stride) and the next one up (the
                # vector kernel)
-               (128, (4, 4, 8048), 201), (128, (4, 4, 10224), 201), (128, (4, 4, 10240), 201)]
+               (128, (4, 4, 8048), 201), (128, (4, 4, 10224), 201), (128, (4, 4, 10240), 201),
+               # 2,500 cubes at d = 64: the matrix-core kernel with 40 key slots
+               # per lane and eight key splits of its coarse output
+               (64, (4, 4, 10000), 150)]
 
 
 @pytest.mark.parametrize("d,dims,k", COARSE_GEOM, ids=[f"d{c[0]}-nc{c[1][0] * c[1][1] * c[1][2] // 64}"
