@@ -763,7 +763,13 @@ def main() -> int:
                                "top_k": large["top_k"], "ms_per_step": round(large["step_ms"], 3),
                                "fine_ms_per_call": round(large["fine_ms"], 3),
                                "stages_ms_median": {n: round(t, 3) for n, t in large["stages_ms"].items()},
-                               "fine_tflops": round(large["flops"] / (large["fine_ms"] * 1e-3) / 1e12, 2)},
+                               "fine_tflops": round(large["flops"] / (large["fine_ms"] * 1e-3) / 1e12, 2),
+                               # the coarse stage's products: S = Qc Kc^T and O_c = P Vc, 2 Nc^2 d each per head,
+                               # against the 157.3 TFLOP/s fp32 matrix peak
+                               "coarse_tflops": round(4.0 * large["cubes"] ** 2 * 128 * large["heads"]
+                                                      / (large["stages_ms"]["coarse_topk"] * 1e-3) / 1e12, 2),
+                               "coarse_pct_fp32_peak": round(100.0 * 4.0 * large["cubes"] ** 2 * 128 * large["heads"]
+                                                             / (large["stages_ms"]["coarse_topk"] * 1e-3) / 157.3e12, 2)},
             "value_head_size": {
                 "note": "fine stage with d_v != d (its own forward kernel), the step's Top-K LUT, raster output "
                         "with O_c; FLOPs 2*64*64*(d + d_v) per selected pair; fine backward on the same LUT, "
